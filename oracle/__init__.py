@@ -1,0 +1,9 @@
+"""CPU oracle for the LoRA SwiGLU MLP (test infrastructure only).
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package. The HIP product path never does.
+"""
+from .lora_mlp_oracle import (ADAPTER_KEYS, WEIGHT_KEYS, backward, base_mlp_rows,  # noqa: F401
+                              bf16_round, bruteforce, dequant_int4, dequant_int4_bits,
+                              flops, forward, forward_backward, merged_reference,
+                              sigmoid, silu, unpack_int4)
