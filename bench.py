@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Throughput of the fused LoRA SwiGLU MLP forward + backward on one MI355X.
+
+One step = lora_mlp_forward + lora_mlp_backward over one batch of synthetic
+tokens (inputs resident in HBM before timing starts). Default workload: the
+Llama-3-8B MLP (hidden 4096, intermediate 14336, rank 16, alpha 16) over 4096
+tokens (batch 2 x seq 2048) in bf16. Prints one JSON line.
+
+Also reported:
+  roofline      the dominant kernel's algorithmic TFLOP/s against the MI355X
+                dense MFMA peak of the workload dtype, from HIP events recorded
+                around each library launch on the launch stream (a second pass
+                of the same steps, so event records do not touch `value`)
+  cpu_baseline  the fp64 CPU oracle on a bounded token sample of the same
+                workload, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LoRA-SwiGLU MLP fwd+bwd tokens/sec + TFLOP/s as % of MI355X bf16 peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}    # MI355X published dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_flops(name: str, T: int, H: int, I: int, r: int) -> int:
+    """Algorithmic FLOPs of one launch (2mnk per product, real rank, no padding)."""
+    return {
+        "gemm(gate/up)": 4 * T * H * I + 4 * T * I * r,
+        "gemm(down)": 2 * T * I * H + 2 * T * H * r,
+        "gemm(dZ)": 2 * T * H * I + 2 * T * r * I,
+        "gemm(dX)": 4 * T * I * H + 4 * T * r * H,
+    }.get(name, 0)
+
+
+def kernel_bytes(name: str, T: int, H: int, I: int, r: int, eb: int) -> int:
+    """Algorithmic HBM bytes of one launch of the rank-r side kernels."""
+    return {
+        "rowproj(X A^T)": T * H * eb + T * 2 * r * (4 + eb),
+        "rowproj(Z A_d^T)": T * I * eb + T * r * (4 + eb),
+        "rowproj(dY B_d)": T * H * eb + T * r * (4 + eb),
+        "rowproj(dG B_g, dU B_u)": 2 * T * I * eb + 2 * T * r * (4 + eb),
+        "colproj": (3 * T * I + 2 * T * H) * eb,
+    }.get(name, 0)
+
+
+def cpu_baseline(inp, wl, seconds: float):
+    import numpy as np
+    import oracle
+    from lora_swiglu_mlp_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    w = {}
+    for k in oracle.WEIGHT_KEYS:
+        if wl.wfmt == "int4_b64" and k in ("w_gate", "w_up", "w_down"):
+            inn = wl.inter if k == "w_down" else wl.hidden
+            w[k] = oracle.dequant_int4(inp[k], inp[k + "_scales"], inn)
+        else:
+            w[k] = I.to_f64(inp[k], wl.dtype)
+
+    def run(n):
+        d = dict(w)
+        d["x"] = I.to_f64(inp["x"][:n], wl.dtype)
+        d["dy"] = I.to_f64(inp["dy"][:n], wl.dtype)
+        t0 = time.perf_counter()
+        oracle.forward_backward(d, wl.scale)
+        return time.perf_counter() - t0
+
+    n, t = 32, run(32)
+    while t < seconds / 4 and n < wl.tokens:
+        n = min(wl.tokens, n * 2)
+        t = run(n)
+    if t < seconds and n < wl.tokens:
+        n = min(wl.tokens, max(n, int(n * seconds / max(t, 1e-3))))
+        t = run(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} of {wl.tokens} tokens of {wl.name}, forward+backward, "
+                      f"fp64 numpy (row-local work per token is the full path), {t:.1f} s",
+            "gflops": oracle.flops(n, wl.hidden, wl.inter, wl.rank) / t / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from lora_swiglu_mlp_amd import abi, mlp
+    from lora_swiglu_mlp_amd import inputs as I
+
+    wl = I.WORKLOADS[args.workload]
+    T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank
+    torch.cuda.set_device(0)
+    inp = I.make_inputs(wl)
+    m, x, dy = mlp.from_inputs(inp, wl, "cuda:0")
+    saved = m.new_saved()
+    y = torch.empty((T, H), dtype=m.tdtype, device="cuda:0")
+    grads = m.new_grads(x.device)
+    m.workspace(True)
+
+    def step():
+        m.forward(x, y, saved)
+        m.backward(dy, x, saved, grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    flops = 12 * T * H * Iw + 18 * T * r * (H + Iw)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+
+    out = {"metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": wl.dtype, "data": "synthetic (seeded normal draws; random-init weights)",
+           "config": {"workload": wl.name, "tokens": T, "hidden": H, "inter": Iw, "rank": r,
+                      "alpha": wl.alpha, "weights": wl.wfmt, "parallelism": "single-gpu"},
+           "tflops": tflops, "pct_of_peak": 100.0 * tflops / peak}
+
+    if not args.no_profile:
+        nprof = max(1, min(args.steps, 10))
+        abi.lora_mlp_profile_begin()
+        for _ in range(nprof):
+            step()
+        recs = abi.lora_mlp_profile_end()
+        agg = {}
+        for name, t in recs:
+            a = agg.setdefault(name, [0.0, 0])
+            a[0] += t
+            a[1] += 1
+        kern = {}
+        for name, (tot, cnt) in agg.items():
+            avg = tot / cnt
+            e = {"ms": avg, "launches_per_step": cnt / nprof}
+            f = kernel_flops(name, T, H, Iw, r)
+            if f:
+                e["tflops"] = f / (avg * 1e-3) / 1e12
+            b = kernel_bytes(name, T, H, Iw, r, 2 if wl.dtype == "bf16" else 4)
+            if b:
+                e["gbps"] = b / (avg * 1e-3) / 1e9
+            kern[name] = e
+        out["kernels"] = kern
+        fwd_names = ("pack(fwd)", "rowproj(X A^T)", "gemm(gate/up)", "rowproj(Z A_d^T)", "gemm(down)")
+        out["kernel_ms_per_step"] = sum(v["ms"] * v["launches_per_step"] for v in kern.values())
+        dom = max((n for n in kern if kernel_flops(n, T, H, Iw, r)),
+                  key=lambda n: kern[n]["ms"] * kern[n]["launches_per_step"])
+        achieved = kern[dom]["tflops"]
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
+                           "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
+        out["fwd_kernel_ms"] = sum(kern[n]["ms"] * kern[n]["launches_per_step"]
+                                   for n in kern if n in fwd_names)
+        out["bwd_kernel_ms"] = out["kernel_ms_per_step"] - out["fwd_kernel_ms"]
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

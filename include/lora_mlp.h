@@ -1,0 +1,153 @@
+/*
+ * lora_mlp.h - C ABI of the MI355X (gfx950) fused LoRA SwiGLU MLP library.
+ *
+ * The operation is the fused LoRA MLP of "Unsloth 深度分析报告"
+ * (nightvoyager.top), section "核心价值提炼 / 创新之处": a SwiGLU MLP whose
+ * gate, up and down projections each add a LoRA adapter to a frozen weight,
+ * with the forward and a hand-derived backward that keeps no per-activation
+ * intermediates beyond the gate/up pre-activations. With T tokens, hidden H,
+ * intermediate I, rank r and scale s:
+ *
+ *   proj(v; W, A, B) = v W^T + s (v A^T) B^T        W [out,in], A [r,in], B [out,r]
+ *   G = proj(X; Wg, Ag, Bg)   U = proj(X; Wu, Au, Bu)   Z = SiLU(G) * U
+ *   Y = proj(Z; Wd, Ad, Bd)   SiLU(g) = g / (1 + exp(-g))
+ *
+ * Backward returns dX and the gradients of all six adapter factors for an
+ * upstream gradient dY. Base weights are frozen: no dW is produced.
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major, contiguous, and in device memory of the
+ *     current HIP device; every pointer must be 16-byte aligned.
+ *   - Activations, adapters, outputs and gradients share one dtype
+ *     (lmlp_dims.dtype). Accumulation is always fp32.
+ *   - The caller owns and allocates every buffer (inputs, outputs, the
+ *     `saved` buffer and the workspace). The library never allocates device
+ *     memory and never synchronises: all work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the null stream) in stream order.
+ *   - Arguments are validated before anything is enqueued; a call that
+ *     returns an error has enqueued no work.
+ *   - Results are deterministic: no atomics, fixed reduction order.
+ *   - Calls on distinct buffers may run concurrently from several threads.
+ */
+#ifndef LORA_MLP_H
+#define LORA_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMLP_OK = 0,
+  LMLP_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad dimension, non-finite scale */
+  LMLP_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement, or not gfx950 */
+  LMLP_ERR_WORKSPACE = 3,   /* saved/workspace buffer smaller than the size query */
+  LMLP_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} lmlp_status;
+
+typedef enum { LMLP_F32 = 0, LMLP_BF16 = 1 } lmlp_dtype;
+
+/* Frozen base-weight storage. INT4_B64: each weight [out, in] is stored as
+ * bytes [out, in/2] (element k of a row in byte k/2: even k in the low
+ * nibble, odd k in the high nibble, two's complement in [-8, 7]) plus fp16
+ * scales [out, in/64] (one per 64 consecutive elements of a row). The weight
+ * value is bf16_round_nearest_even(q * scale) with the product taken in fp32.
+ * This is the "native 4-bit QLoRA" weight path of "Unsloth 还是 AirLLM？一个炼丹，
+ * 一个硬跑" (section 核心原理 / "Why it is fast"); requires dtype BF16 and
+ * hidden % 64 == 0 and inter % 64 == 0. */
+typedef enum { LMLP_W_DENSE = 0, LMLP_W_INT4_B64 = 1 } lmlp_wfmt;
+
+/* flags */
+#define LMLP_CONSUME_SAVED 0x1u /* backward may overwrite `saved` (saves 2*T*I elements of workspace) */
+
+typedef struct {
+  int64_t tokens;  /* T >= 0 (T == 0: forward is a no-op, backward writes zero adapter gradients) */
+  int64_t hidden;  /* H >= 1; multiple of 8 (bf16) or 4 (fp32) */
+  int64_t inter;   /* I >= 1; multiple of 8 (bf16) or 4 (fp32) */
+  int64_t rank;    /* r in [1, 256] */
+  float scale;     /* s = alpha / r, finite */
+  int32_t dtype;   /* lmlp_dtype */
+  int32_t wfmt;    /* lmlp_wfmt */
+  uint32_t flags;  /* LMLP_CONSUME_SAVED or 0 */
+} lmlp_dims;
+
+/* Bytes of the forward->backward `saved` buffer: the gate and up
+ * pre-activations G, U (2*T*I elements of dtype) plus the three rank-r
+ * projections X A_gate^T, X A_up^T and Z A_down^T in fp32, padded.
+ * Returns 0 if dims is invalid. */
+size_t lora_mlp_saved_bytes(const lmlp_dims* dims);
+
+/* Bytes of scratch workspace one forward (is_backward == 0) or one backward
+ * (is_backward != 0) call needs. Contents need not be initialised and are
+ * undefined afterwards. Returns 0 if dims is invalid. */
+size_t lora_mlp_workspace_bytes(const lmlp_dims* dims, int is_backward);
+
+/* Forward. Inputs: x [T,H]; w_gate, w_up [I,H], w_down [H,I] (dense: dtype;
+ * INT4_B64: packed bytes with *_scales as described above, else the scale
+ * pointers must be NULL); a_gate, a_up [r,H]; b_gate, b_up [I,r];
+ * a_down [r,I]; b_down [H,r]. Output: y [T,H]. `saved` (saved_bytes long)
+ * receives what backward needs. */
+int lora_mlp_forward(const lmlp_dims* dims, const void* x,
+                     const void* w_gate, const void* w_gate_scales,
+                     const void* w_up, const void* w_up_scales,
+                     const void* w_down, const void* w_down_scales,
+                     const void* a_gate, const void* b_gate,
+                     const void* a_up, const void* b_up,
+                     const void* a_down, const void* b_down,
+                     void* y, void* saved, size_t saved_bytes,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward for upstream gradient dy [T,H], with the same x and weights as the
+ * forward that filled `saved`. Outputs (overwritten, not accumulated):
+ * dx [T,H]; da_gate, da_up [r,H]; db_gate, db_up [I,r]; da_down [r,I];
+ * db_down [H,r]. Recomputes sigmoid(G), SiLU(G) and Z from the saved G, U.
+ * `saved` is left unchanged unless flags has LMLP_CONSUME_SAVED, in which
+ * case it is overwritten and a second backward needs a new forward. */
+int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x,
+                      const void* w_gate, const void* w_gate_scales,
+                      const void* w_up, const void* w_up_scales,
+                      const void* w_down, const void* w_down_scales,
+                      const void* a_gate, const void* b_gate,
+                      const void* a_up, const void* b_up,
+                      const void* a_down, const void* b_down,
+                      void* saved, size_t saved_bytes,
+                      void* dx, void* da_gate, void* db_gate,
+                      void* da_up, void* db_up, void* da_down, void* db_down,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dequantise one INT4_B64 weight (packed [out, in/2] bytes, fp16 scales
+ * [out, in/64]) to bf16 [out, in] with the same device code the GEMM loaders
+ * use. in % 64 == 0. Exposed so the 4-bit decode can be checked bit for bit. */
+int lora_mlp_dequant_int4(const void* packed, const void* scales, int64_t out,
+                          int64_t in, void* w_bf16, void* stream);
+
+/* Per-kernel timing (measurement support). After lora_mlp_profile_begin(),
+ * every kernel that forward, backward or dequant calls on this thread enqueue
+ * is bracketed by a pair of hipEvents recorded on the call's stream (events
+ * are created by the library on first use and reused; no device memory is
+ * allocated). lora_mlp_profile_end() waits for the last recorded event,
+ * writes up to `capacity` records in launch order (kernel name, duration in
+ * milliseconds), stores the number of records in *count, and stops
+ * recording. At most 65536 launches are recorded per session; later ones are
+ * not timed. Timing adds event records between kernels, so time the plain
+ * path separately. Returns LMLP_OK or LMLP_ERR_HIP. */
+typedef struct {
+  char name[40];
+  float ms;
+} lmlp_kernel_time;
+int lora_mlp_profile_begin(void);
+int lora_mlp_profile_end(lmlp_kernel_time* out, int capacity, int* count);
+
+/* Static name of a status code. */
+const char* lora_mlp_status_string(int status);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* lora_mlp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MLP_H */

@@ -1,0 +1,127 @@
+// Launch parameters and launchers of the gfx950 kernels (host and device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmlp {
+
+enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
+
+// One K segment of a GEMM: C += A[:, seg] * B[seg, :].
+struct GemmSeg {
+  const void* a;    // [M][lda], K contiguous, compute dtype
+  const void* b0;   // NT: [N][ldb] K contiguous; NN: [K][ldb] N contiguous
+  const void* b1;   // gate/up product only: the up-projection rows (b0 = gate)
+  const void* bs0;  // 4-bit B only: fp16 scales of b0 (one per 64 codes)
+  const void* bs1;  // 4-bit B only: scales of b1
+  int64_t lda;      // elements
+  int64_t ldb;      // elements (for 4-bit B: codes per row)
+  int64_t K;        // contraction length (elements), multiple of the 16-byte chunk
+  int32_t bint4;    // B stored as 4-bit blocks
+  int32_t pad_;
+};
+
+struct GemmParams {
+  GemmSeg seg[3];
+  int32_t nseg;
+  int32_t group_m;  // tiles of M visited before moving along N (L2 reuse)
+  int32_t tiles_m, tiles_n;
+  int64_t M, N;     // output rows, columns (gate/up: N = I, pairs of columns)
+  int64_t ldc;      // row stride of every output / saved activation
+  void* c0;         // STORE: C. SWIGLU_FWD: G. SWIGLU_BWD: dG
+  void* c1;         // SWIGLU_FWD: U. SWIGLU_BWD: dU
+  void* c2;         // Z (forward: input of the down product; backward: optional)
+  const void* g_in; // SWIGLU_BWD: saved G
+  const void* u_in; // SWIGLU_BWD: saved U
+};
+
+hipError_t launch_gemm(const GemmParams& p, int dtype_bf16, int nn, int epi, hipStream_t stream);
+
+// Row projection: out[t][n] = sum_k X[t][k] * W[n][k] over all k, for up to
+// two jobs per launch. The result goes to an fp32 matrix and/or a scaled copy
+// in the compute dtype (the adapter K segment of a GEMM operand).
+struct RowProjJob {
+  const void* x;    // [T][ldx]
+  const void* w;    // [n1p][ldw], K contiguous, zero rows past the real rank
+  float* out_f32;   // [T][ld_f32] at column col_off (may be null)
+  void* out_c;      // [T][ld_c] at column col_off, = scale * value (may be null)
+  int64_t ldx, ldw, K;
+  int64_t ld_f32, ld_c;
+  float scale;
+  int32_t n1p;      // multiple of 16, <= 512
+  int32_t col_off;
+  int32_t pad_;
+};
+struct RowProjParams {
+  RowProjJob job[2];
+  int32_t njobs;
+  int32_t pad_;
+  int64_t T;
+};
+hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream);
+
+// Column projection: part[tb][k][n] = sum_{t in block tb} X[t][k] * P[t][n]
+// (fp32 partial sums over token blocks; reduced by launch_reduce).
+struct ColProjJob {
+  const void* x;    // [T][ldx]
+  const float* p;   // [T][ldp] fp32
+  float* part;      // [ntb][K][n2p]
+  int64_t ldx, ldp, K;
+  int64_t tr;       // tokens per block (multiple of 32)
+  int32_t n2p;      // multiple of 16, <= 512
+  int32_t ntb;      // token blocks
+  int32_t kblocks;  // ceil(K / 64)
+  int32_t nchunks;  // ceil(n2p / 64)
+};
+struct ColProjParams {
+  ColProjJob job[5];
+  int32_t njobs;
+  int32_t pad_;
+  int64_t T;
+};
+hipError_t launch_colproj(const ColProjParams& p, int dtype_bf16, hipStream_t stream);
+
+// Fixed-order sum of partials into a final, scaled, optionally transposed
+// matrix in fp32 or bf16: dst(i, j) = scale * sum_c src[c][i][col_off + j].
+struct ReduceJob {
+  const float* src;
+  void* dst;
+  int64_t chunk_stride, ld_src, rows, cols, ld_dst;
+  float scale;
+  int32_t nchunk;
+  int32_t col_off;
+  int32_t transpose;  // write dst[j][i]
+  int32_t dst_bf16;
+  int32_t pad_;
+};
+struct ReduceParams {
+  ReduceJob job[6];
+  int32_t njobs;
+  int32_t pad_;
+};
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+
+// Zero-padded copy of an adapter factor into a GEMM/projection operand
+// layout: dst[i][j] = src(i, j) (or src(j, i) if transpose) inside the source
+// extent, 0 elsewhere, for i < rows, j < cols.
+struct PackJob {
+  void* dst;
+  const void* src;  // null: fill zeros
+  int64_t ld_dst, rows, cols;
+  int64_t ld_src, srows, scols;
+  int32_t transpose;
+  int32_t pad_;
+};
+struct PackParams {
+  PackJob job[8];
+  int32_t njobs;
+  int32_t pad_;
+};
+hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream);
+
+// 4-bit block weight -> bf16 (same decode as the GEMM loaders).
+hipError_t launch_dequant_int4(const void* packed, const void* scales, int64_t out, int64_t in,
+                               void* w_bf16, hipStream_t stream);
+
+}  // namespace lmlp

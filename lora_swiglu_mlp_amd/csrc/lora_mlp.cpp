@@ -1,0 +1,683 @@
+// C ABI of the fused LoRA SwiGLU MLP: argument checks, buffer layout and the
+// launch sequence. See include/lora_mlp.h for the contract.
+//
+// Forward (all on the caller's stream, no host synchronisation):
+//   pack     adapter factors -> zero-padded operand layouts
+//   rowproj  P_gu = X [A_g; A_u]^T            (fp32 -> saved; s*P_gu -> GEMM operand)
+//   gemm     [G|U] = [X | sP_gu] [W|B]^T, epilogue G, U -> saved, Z = SiLU(G) U
+//   rowproj  Pd = Z A_d^T                     (fp32 -> saved; s*Pd -> GEMM operand)
+//   gemm     Y = [Z | sPd] [W_d | B_d]^T
+// Backward:
+//   pack, rowproj Q_d = dY B_d
+//   gemm     dZ = [dY | sQ_d] [W_d ; A_d], epilogue: reload G, U, recompute
+//            sigmoid(G), SiLU(G), Z; dG = dZ U sig (1 + G (1 - sig)), dU = dZ SiLU(G)
+//   rowproj  Q_g = dG B_g, Q_u = dU B_u
+//   gemm     dX = [dG | dU | sQ_g | sQ_u] [W_g ; W_u ; A_g ; A_u]
+//   colproj  dG^T P_g, dU^T P_u, Z^T Q_d, X^T Q_gu, dY^T Pd (per token block)
+//   reduce   fixed-order sums, times s -> dB_g, dB_u, dA_d, dA_g, dA_u, dB_d
+// This is the hand-derived backward of the fused LoRA MLP ("Unsloth 深度分析报告",
+// section 创新之处) with the gate activations recomputed rather than stored
+// (the "no materialised activations" point of the agientry.com unsloth page,
+// section 训练侧).
+#include "../../include/lora_mlp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace lmlp;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+struct Dims {
+  int64_t T, H, I, r, r16;
+  float s;
+  bool bf16, int4, consume;
+  int eb;  // element bytes
+};
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int parse_dims(const lmlp_dims* d, Dims& o) {
+  if (!d) return fail(LMLP_ERR_INVALID_ARG, "dims is NULL");
+  if (d->tokens < 0) return fail(LMLP_ERR_INVALID_ARG, "tokens < 0");
+  if (d->hidden < 1 || d->inter < 1) return fail(LMLP_ERR_INVALID_ARG, "hidden and inter must be >= 1");
+  if (d->rank < 1) return fail(LMLP_ERR_INVALID_ARG, "rank must be >= 1");
+  if (!std::isfinite(d->scale)) return fail(LMLP_ERR_INVALID_ARG, "scale is not finite");
+  if (d->dtype != LMLP_F32 && d->dtype != LMLP_BF16) return fail(LMLP_ERR_INVALID_ARG, "unknown dtype");
+  if (d->wfmt != LMLP_W_DENSE && d->wfmt != LMLP_W_INT4_B64) return fail(LMLP_ERR_INVALID_ARG, "unknown wfmt");
+  if (d->flags & ~LMLP_CONSUME_SAVED) return fail(LMLP_ERR_INVALID_ARG, "unknown flag bits");
+  if (d->rank > 256) return fail(LMLP_ERR_UNSUPPORTED, "rank > 256");
+  const int ch = d->dtype == LMLP_BF16 ? 8 : 4;
+  if (d->hidden % ch || d->inter % ch)
+    return fail(LMLP_ERR_UNSUPPORTED, "hidden and inter must be multiples of 8 (bf16) or 4 (fp32)");
+  if (d->wfmt == LMLP_W_INT4_B64) {
+    if (d->dtype != LMLP_BF16) return fail(LMLP_ERR_UNSUPPORTED, "4-bit weights need dtype bf16");
+    if (d->hidden % 64 || d->inter % 64)
+      return fail(LMLP_ERR_UNSUPPORTED, "4-bit weights need hidden and inter multiples of 64");
+  }
+  // sizes far beyond any one GPU; keeps every offset comfortably in int64
+  if (d->tokens > (int64_t{1} << 31) || d->hidden > (int64_t{1} << 24) || d->inter > (int64_t{1} << 24))
+    return fail(LMLP_ERR_UNSUPPORTED, "dimension too large");
+  o.T = d->tokens;
+  o.H = d->hidden;
+  o.I = d->inter;
+  o.r = d->rank;
+  o.r16 = (d->rank + 15) / 16 * 16;
+  o.s = d->scale;
+  o.bf16 = d->dtype == LMLP_BF16;
+  o.int4 = d->wfmt == LMLP_W_INT4_B64;
+  o.consume = (d->flags & LMLP_CONSUME_SAVED) != 0;
+  o.eb = o.bf16 ? 2 : 4;
+  return LMLP_OK;
+}
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  }
+};
+
+struct SavedLayout {
+  size_t g, u, pgu, pd, total;
+};
+SavedLayout saved_layout(const Dims& d) {
+  Carver c;
+  SavedLayout L;
+  L.g = c.take(size_t(d.T) * d.I * d.eb);
+  L.u = c.take(size_t(d.T) * d.I * d.eb);
+  L.pgu = c.take(size_t(d.T) * 2 * d.r16 * 4);
+  L.pd = c.take(size_t(d.T) * d.r16 * 4);
+  L.total = c.off;
+  return L;
+}
+
+struct FwdLayout {
+  size_t z, aext_gu, aext_d, agu_pad, ad_pad, bext_g, bext_u, bext_d, total;
+};
+FwdLayout fwd_layout(const Dims& d) {
+  Carver c;
+  FwdLayout L;
+  L.z = c.take(size_t(d.T) * d.I * d.eb);
+  L.aext_gu = c.take(size_t(d.T) * 2 * d.r16 * d.eb);
+  L.aext_d = c.take(size_t(d.T) * d.r16 * d.eb);
+  L.agu_pad = c.take(size_t(2 * d.r16) * d.H * d.eb);
+  L.ad_pad = c.take(size_t(d.r16) * d.I * d.eb);
+  L.bext_g = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
+  L.bext_u = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
+  L.bext_d = c.take(size_t(d.H) * d.r16 * d.eb);
+  L.total = c.off;
+  return L;
+}
+
+// token blocks of the column projections (partial sums over tokens)
+int colproj_ntb(int64_t T) {
+  int64_t n = (T + 255) / 256;
+  if (n > 16) n = 16;
+  return static_cast<int>(n);
+}
+int64_t colproj_tr(int64_t T, int ntb) {
+  if (ntb == 0) return 32;
+  const int64_t per = (T + ntb - 1) / ntb;
+  return (per + 31) / 32 * 32;
+}
+
+struct BwdLayout {
+  size_t dg, du, z, qd, aext_d, qgu, aext_gu, bdT, bgT, buT, ad_pad, agu_pad;
+  size_t part_dg, part_du, part_z, part_x, part_dy, total;
+  int ntb;
+  int64_t tr;
+};
+BwdLayout bwd_layout(const Dims& d) {
+  Carver c;
+  BwdLayout L;
+  L.ntb = colproj_ntb(d.T);
+  L.tr = colproj_tr(d.T, L.ntb);
+  const size_t act = size_t(d.T) * d.I * d.eb;
+  L.dg = d.consume ? 0 : c.take(act);
+  L.du = d.consume ? 0 : c.take(act);
+  L.z = c.take(act);
+  L.qd = c.take(size_t(d.T) * d.r16 * 4);
+  L.aext_d = c.take(size_t(d.T) * d.r16 * d.eb);
+  L.qgu = c.take(size_t(d.T) * 2 * d.r16 * 4);
+  L.aext_gu = c.take(size_t(d.T) * 2 * d.r16 * d.eb);
+  L.bdT = c.take(size_t(d.r16) * d.H * d.eb);
+  L.bgT = c.take(size_t(d.r16) * d.I * d.eb);
+  L.buT = c.take(size_t(d.r16) * d.I * d.eb);
+  L.ad_pad = c.take(size_t(d.r16) * d.I * d.eb);
+  L.agu_pad = c.take(size_t(2 * d.r16) * d.H * d.eb);
+  L.part_dg = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
+  L.part_du = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
+  L.part_z = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
+  L.part_x = c.take(size_t(L.ntb) * d.H * 2 * d.r16 * 4);
+  L.part_dy = c.take(size_t(L.ntb) * d.H * d.r16 * 4);
+  L.total = c.off;
+  return L;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int need_ptr(const void* p, const char* name) {
+  if (!p) return fail(LMLP_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned(p)) return fail(LMLP_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+  return LMLP_OK;
+}
+
+#define LMLP_TRY(expr)            \
+  do {                            \
+    const int rc_ = (expr);       \
+    if (rc_ != LMLP_OK) return rc_; \
+  } while (0)
+
+int check_weights(const Dims& d, const void* wg, const void* wgs, const void* wu, const void* wus,
+                  const void* wd, const void* wds) {
+  LMLP_TRY(need_ptr(wg, "w_gate"));
+  LMLP_TRY(need_ptr(wu, "w_up"));
+  LMLP_TRY(need_ptr(wd, "w_down"));
+  if (d.int4) {
+    LMLP_TRY(need_ptr(wgs, "w_gate_scales"));
+    LMLP_TRY(need_ptr(wus, "w_up_scales"));
+    LMLP_TRY(need_ptr(wds, "w_down_scales"));
+  } else if (wgs || wus || wds) {
+    return fail(LMLP_ERR_INVALID_ARG, "scale pointers must be NULL for dense weights");
+  }
+  return LMLP_OK;
+}
+
+int check_adapters(const void* ag, const void* bg, const void* au, const void* bu, const void* ad,
+                   const void* bd) {
+  LMLP_TRY(need_ptr(ag, "a_gate"));
+  LMLP_TRY(need_ptr(bg, "b_gate"));
+  LMLP_TRY(need_ptr(au, "a_up"));
+  LMLP_TRY(need_ptr(bu, "b_up"));
+  LMLP_TRY(need_ptr(ad, "a_down"));
+  LMLP_TRY(need_ptr(bd, "b_down"));
+  return LMLP_OK;
+}
+
+// gfx950 check, cached per device
+int check_device() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LMLP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(LMLP_ERR_UNSUPPORTED, "device index out of range");
+  int st = cache[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(LMLP_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cache[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(LMLP_ERR_UNSUPPORTED, "current device is not gfx950");
+  return LMLP_OK;
+}
+
+int hip_rc(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LMLP_OK;
+  return fail(LMLP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---- optional per-launch timing (lora_mlp_profile_begin / _end)
+struct ProfRec {
+  const char* name;
+  hipEvent_t b, e;
+};
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<ProfRec> recs;
+  hipEvent_t next() {
+    if (used == pool.size()) {
+      hipEvent_t ev = nullptr;
+      if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+      pool.push_back(ev);
+    }
+    return pool[used++];
+  }
+};
+thread_local Profiler g_prof;
+constexpr size_t kMaxProfiled = 65536;
+
+struct ProfScope {
+  hipStream_t st;
+  const char* name;
+  hipEvent_t b = nullptr;
+  ProfScope(hipStream_t s, const char* n) : st(s), name(n) {
+    if (g_prof.on && g_prof.recs.size() < kMaxProfiled) {
+      b = g_prof.next();
+      if (b) hipEventRecord(b, st);
+    }
+  }
+  void done() {
+    if (!b) return;
+    hipEvent_t e = g_prof.next();
+    if (!e) return;
+    hipEventRecord(e, st);
+    g_prof.recs.push_back({name, b, e});
+  }
+};
+
+#define LMLP_LAUNCH(name, expr)                  \
+  do {                                           \
+    ProfScope ps_(st, name);                     \
+    LMLP_TRY(hip_rc((expr), name));              \
+    ps_.done();                                  \
+  } while (0)
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+PackJob pack_job(void* dst, int64_t ld_dst, int64_t rows, int64_t cols, const void* src, int64_t ld_src,
+                 int64_t srows, int64_t scols, bool transpose) {
+  PackJob j{};
+  j.dst = dst;
+  j.ld_dst = ld_dst;
+  j.rows = rows;
+  j.cols = cols;
+  j.src = src;
+  j.ld_src = ld_src;
+  j.srows = srows;
+  j.scols = scols;
+  j.transpose = transpose ? 1 : 0;
+  return j;
+}
+
+GemmSeg seg(const void* a, int64_t lda, const void* b0, const void* b1, int64_t ldb, int64_t K,
+            bool bint4 = false, const void* bs0 = nullptr, const void* bs1 = nullptr) {
+  GemmSeg s{};
+  s.a = a;
+  s.lda = lda;
+  s.b0 = b0;
+  s.b1 = b1;
+  s.ldb = ldb;
+  s.K = K;
+  s.bint4 = bint4 ? 1 : 0;
+  s.bs0 = bs0;
+  s.bs1 = bs1;
+  return s;
+}
+
+RowProjJob rp_job(const void* x, int64_t ldx, int64_t K, const void* w, int64_t ldw, int n1p, float* out_f32,
+                  int64_t ld_f32, void* out_c, int64_t ld_c, float scale, int col_off) {
+  RowProjJob j{};
+  j.x = x;
+  j.ldx = ldx;
+  j.K = K;
+  j.w = w;
+  j.ldw = ldw;
+  j.n1p = n1p;
+  j.out_f32 = out_f32;
+  j.ld_f32 = ld_f32;
+  j.out_c = out_c;
+  j.ld_c = ld_c;
+  j.scale = scale;
+  j.col_off = col_off;
+  return j;
+}
+
+ColProjJob cp_job(const void* x, int64_t ldx, int64_t K, const float* p, int64_t ldp, int n2p, float* part,
+                  int ntb, int64_t tr) {
+  ColProjJob j{};
+  j.x = x;
+  j.ldx = ldx;
+  j.K = K;
+  j.p = p;
+  j.ldp = ldp;
+  j.n2p = n2p;
+  j.part = part;
+  j.ntb = ntb;
+  j.tr = tr;
+  j.kblocks = static_cast<int>((K + 63) / 64);
+  j.nchunks = (n2p + 63) / 64;
+  return j;
+}
+
+ReduceJob rd_job(const float* src, int64_t chunk_stride, int nchunk, int64_t ld_src, int col_off, int64_t rows,
+                 int64_t cols, void* dst, int64_t ld_dst, bool transpose, float scale, bool bf16) {
+  ReduceJob j{};
+  j.src = src;
+  j.chunk_stride = chunk_stride;
+  j.nchunk = nchunk;
+  j.ld_src = ld_src;
+  j.col_off = col_off;
+  j.rows = rows;
+  j.cols = cols;
+  j.dst = dst;
+  j.ld_dst = ld_dst;
+  j.transpose = transpose ? 1 : 0;
+  j.scale = scale;
+  j.dst_bf16 = bf16 ? 1 : 0;
+  return j;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_mlp_saved_bytes(const lmlp_dims* dims) {
+  Dims d;
+  if (parse_dims(dims, d) != LMLP_OK) return 0;
+  return saved_layout(d).total;
+}
+
+size_t lora_mlp_workspace_bytes(const lmlp_dims* dims, int is_backward) {
+  Dims d;
+  if (parse_dims(dims, d) != LMLP_OK) return 0;
+  return is_backward ? bwd_layout(d).total : fwd_layout(d).total;
+}
+
+const char* lora_mlp_status_string(int status) {
+  switch (status) {
+    case LMLP_OK: return "LMLP_OK";
+    case LMLP_ERR_INVALID_ARG: return "LMLP_ERR_INVALID_ARG";
+    case LMLP_ERR_UNSUPPORTED: return "LMLP_ERR_UNSUPPORTED";
+    case LMLP_ERR_WORKSPACE: return "LMLP_ERR_WORKSPACE";
+    case LMLP_ERR_HIP: return "LMLP_ERR_HIP";
+    default: return "LMLP_UNKNOWN_STATUS";
+  }
+}
+
+const char* lora_mlp_last_error(void) { return g_last_error.c_str(); }
+
+int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, const void* w_gate_scales,
+                     const void* w_up, const void* w_up_scales, const void* w_down, const void* w_down_scales,
+                     const void* a_gate, const void* b_gate, const void* a_up, const void* b_up,
+                     const void* a_down, const void* b_down, void* y, void* saved, size_t saved_bytes,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Dims d;
+  LMLP_TRY(parse_dims(dims, d));
+  LMLP_TRY(check_weights(d, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales));
+  LMLP_TRY(check_adapters(a_gate, b_gate, a_up, b_up, a_down, b_down));
+  const SavedLayout SL = saved_layout(d);
+  const FwdLayout FL = fwd_layout(d);
+  if (d.T > 0) {
+    LMLP_TRY(need_ptr(x, "x"));
+    LMLP_TRY(need_ptr(y, "y"));
+    LMLP_TRY(need_ptr(saved, "saved"));
+    LMLP_TRY(need_ptr(workspace, "workspace"));
+  }
+  if (saved_bytes < SL.total) return fail(LMLP_ERR_WORKSPACE, "saved buffer smaller than lora_mlp_saved_bytes()");
+  if (workspace_bytes < FL.total)
+    return fail(LMLP_ERR_WORKSPACE, "workspace smaller than lora_mlp_workspace_bytes(dims, 0)");
+  LMLP_TRY(check_device());
+  if (d.T == 0) return LMLP_OK;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t T = d.T, H = d.H, I = d.I, r = d.r, r16 = d.r16;
+  char* G = at(saved, SL.g);
+  char* U = at(saved, SL.u);
+  float* Pgu = reinterpret_cast<float*>(at(saved, SL.pgu));
+  float* Pd = reinterpret_cast<float*>(at(saved, SL.pd));
+  char* Z = at(workspace, FL.z);
+  char* aext_gu = at(workspace, FL.aext_gu);
+  char* aext_d = at(workspace, FL.aext_d);
+  char* agu_pad = at(workspace, FL.agu_pad);
+  char* ad_pad = at(workspace, FL.ad_pad);
+  char* bext_g = at(workspace, FL.bext_g);
+  char* bext_u = at(workspace, FL.bext_u);
+  char* bext_d = at(workspace, FL.bext_d);
+  const int eb = d.eb;
+
+  PackParams pk{};
+  pk.job[0] = pack_job(agu_pad, H, r16, H, a_gate, H, r, H, false);
+  pk.job[1] = pack_job(agu_pad + size_t(r16) * H * eb, H, r16, H, a_up, H, r, H, false);
+  pk.job[2] = pack_job(ad_pad, I, r16, I, a_down, I, r, I, false);
+  pk.job[3] = pack_job(bext_g, 2 * r16, I, 2 * r16, b_gate, r, I, r, false);
+  pk.job[4] = pack_job(bext_u, 2 * r16, I, r16, nullptr, 0, 0, 0, false);
+  pk.job[5] = pack_job(bext_u + size_t(r16) * eb, 2 * r16, I, r16, b_up, r, I, r, false);
+  pk.job[6] = pack_job(bext_d, r16, H, r16, b_down, r, H, r, false);
+  pk.njobs = 7;
+  LMLP_LAUNCH("pack(fwd)", launch_pack(pk, eb, st));
+
+  RowProjParams rp{};
+  rp.T = T;
+  rp.njobs = 1;
+  rp.job[0] = rp_job(x, H, H, agu_pad, H, int(2 * r16), Pgu, 2 * r16, aext_gu, 2 * r16, d.s, 0);
+  LMLP_LAUNCH("rowproj(X A^T)", launch_rowproj(rp, d.bf16, st));
+
+  GemmParams gp{};
+  gp.nseg = 2;
+  gp.seg[0] = seg(x, H, w_gate, w_up, H, H, d.int4, w_gate_scales, w_up_scales);
+  gp.seg[1] = seg(aext_gu, 2 * r16, bext_g, bext_u, 2 * r16, 2 * r16);
+  gp.M = T;
+  gp.N = I;
+  gp.ldc = I;
+  gp.c0 = G;
+  gp.c1 = U;
+  gp.c2 = Z;
+  gp.group_m = 8;
+  LMLP_LAUNCH("gemm(gate/up)", launch_gemm(gp, d.bf16, 0, EPI_SWIGLU_FWD, st));
+
+  rp.job[0] = rp_job(Z, I, I, ad_pad, I, int(r16), Pd, r16, aext_d, r16, d.s, 0);
+  LMLP_LAUNCH("rowproj(Z A_d^T)", launch_rowproj(rp, d.bf16, st));
+
+  GemmParams gd{};
+  gd.nseg = 2;
+  gd.seg[0] = seg(Z, I, w_down, nullptr, I, I, d.int4, w_down_scales, nullptr);
+  gd.seg[1] = seg(aext_d, r16, bext_d, nullptr, r16, r16);
+  gd.M = T;
+  gd.N = H;
+  gd.ldc = H;
+  gd.c0 = y;
+  gd.group_m = 8;
+  LMLP_LAUNCH("gemm(down)", launch_gemm(gd, d.bf16, 0, EPI_STORE, st));
+  return LMLP_OK;
+}
+
+int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* w_gate,
+                      const void* w_gate_scales, const void* w_up, const void* w_up_scales, const void* w_down,
+                      const void* w_down_scales, const void* a_gate, const void* b_gate, const void* a_up,
+                      const void* b_up, const void* a_down, const void* b_down, void* saved, size_t saved_bytes,
+                      void* dx, void* da_gate, void* db_gate, void* da_up, void* db_up, void* da_down,
+                      void* db_down, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Dims d;
+  LMLP_TRY(parse_dims(dims, d));
+  LMLP_TRY(check_weights(d, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales));
+  LMLP_TRY(check_adapters(a_gate, b_gate, a_up, b_up, a_down, b_down));
+  LMLP_TRY(need_ptr(da_gate, "da_gate"));
+  LMLP_TRY(need_ptr(db_gate, "db_gate"));
+  LMLP_TRY(need_ptr(da_up, "da_up"));
+  LMLP_TRY(need_ptr(db_up, "db_up"));
+  LMLP_TRY(need_ptr(da_down, "da_down"));
+  LMLP_TRY(need_ptr(db_down, "db_down"));
+  const SavedLayout SL = saved_layout(d);
+  const BwdLayout BL = bwd_layout(d);
+  if (d.T > 0) {
+    LMLP_TRY(need_ptr(dy, "dy"));
+    LMLP_TRY(need_ptr(x, "x"));
+    LMLP_TRY(need_ptr(dx, "dx"));
+    LMLP_TRY(need_ptr(saved, "saved"));
+    LMLP_TRY(need_ptr(workspace, "workspace"));
+  }
+  if (saved_bytes < SL.total) return fail(LMLP_ERR_WORKSPACE, "saved buffer smaller than lora_mlp_saved_bytes()");
+  if (workspace_bytes < BL.total)
+    return fail(LMLP_ERR_WORKSPACE, "workspace smaller than lora_mlp_workspace_bytes(dims, 1)");
+  LMLP_TRY(check_device());
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t T = d.T, H = d.H, I = d.I, r = d.r, r16 = d.r16;
+  const int eb = d.eb;
+  const float s = d.s;
+
+  ReduceParams rd{};
+  if (T == 0) {
+    // no tokens: every adapter gradient is an empty sum
+    rd.job[0] = rd_job(nullptr, 0, 0, 0, 0, I, r, db_gate, r, false, s, d.bf16);
+    rd.job[1] = rd_job(nullptr, 0, 0, 0, 0, I, r, db_up, r, false, s, d.bf16);
+    rd.job[2] = rd_job(nullptr, 0, 0, 0, 0, r, I, da_down, I, false, s, d.bf16);
+    rd.job[3] = rd_job(nullptr, 0, 0, 0, 0, r, H, da_gate, H, false, s, d.bf16);
+    rd.job[4] = rd_job(nullptr, 0, 0, 0, 0, r, H, da_up, H, false, s, d.bf16);
+    rd.job[5] = rd_job(nullptr, 0, 0, 0, 0, H, r, db_down, r, false, s, d.bf16);
+    rd.njobs = 6;
+    LMLP_LAUNCH("reduce(zero)", launch_reduce(rd, st));
+    return LMLP_OK;
+  }
+
+  const char* G = at(saved, SL.g);
+  const char* U = at(saved, SL.u);
+  const float* Pgu = reinterpret_cast<const float*>(at(saved, SL.pgu));
+  const float* Pd = reinterpret_cast<const float*>(at(saved, SL.pd));
+  char* dG = d.consume ? at(saved, SL.g) : at(workspace, BL.dg);
+  char* dU = d.consume ? at(saved, SL.u) : at(workspace, BL.du);
+  char* Z = at(workspace, BL.z);
+  float* Qd = reinterpret_cast<float*>(at(workspace, BL.qd));
+  char* aext_d = at(workspace, BL.aext_d);
+  float* Qgu = reinterpret_cast<float*>(at(workspace, BL.qgu));
+  char* aext_gu = at(workspace, BL.aext_gu);
+  char* bdT = at(workspace, BL.bdT);
+  char* bgT = at(workspace, BL.bgT);
+  char* buT = at(workspace, BL.buT);
+  char* ad_pad = at(workspace, BL.ad_pad);
+  char* agu_pad = at(workspace, BL.agu_pad);
+  float* part_dg = reinterpret_cast<float*>(at(workspace, BL.part_dg));
+  float* part_du = reinterpret_cast<float*>(at(workspace, BL.part_du));
+  float* part_z = reinterpret_cast<float*>(at(workspace, BL.part_z));
+  float* part_x = reinterpret_cast<float*>(at(workspace, BL.part_x));
+  float* part_dy = reinterpret_cast<float*>(at(workspace, BL.part_dy));
+
+  PackParams pk{};
+  pk.job[0] = pack_job(bdT, H, r16, H, b_down, r, H, r, true);   // B_d^T
+  pk.job[1] = pack_job(bgT, I, r16, I, b_gate, r, I, r, true);   // B_g^T
+  pk.job[2] = pack_job(buT, I, r16, I, b_up, r, I, r, true);     // B_u^T
+  pk.job[3] = pack_job(ad_pad, I, r16, I, a_down, I, r, I, false);
+  pk.job[4] = pack_job(agu_pad, H, r16, H, a_gate, H, r, H, false);
+  pk.job[5] = pack_job(agu_pad + size_t(r16) * H * eb, H, r16, H, a_up, H, r, H, false);
+  pk.njobs = 6;
+  LMLP_LAUNCH("pack(bwd)", launch_pack(pk, eb, st));
+
+  RowProjParams rp{};
+  rp.T = T;
+  rp.njobs = 1;
+  rp.job[0] = rp_job(dy, H, H, bdT, H, int(r16), Qd, r16, aext_d, r16, s, 0);
+  LMLP_LAUNCH("rowproj(dY B_d)", launch_rowproj(rp, d.bf16, st));
+
+  GemmParams gz{};
+  gz.nseg = 2;
+  gz.seg[0] = seg(dy, H, w_down, nullptr, I, H, d.int4, w_down_scales, nullptr);
+  gz.seg[1] = seg(aext_d, r16, ad_pad, nullptr, I, r16);
+  gz.M = T;
+  gz.N = I;
+  gz.ldc = I;
+  gz.c0 = dG;
+  gz.c1 = dU;
+  gz.c2 = Z;
+  gz.g_in = G;
+  gz.u_in = U;
+  gz.group_m = 8;
+  LMLP_LAUNCH("gemm(dZ)", launch_gemm(gz, d.bf16, 1, EPI_SWIGLU_BWD, st));
+
+  rp.njobs = 2;
+  rp.job[0] = rp_job(dG, I, I, bgT, I, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, 0);
+  rp.job[1] = rp_job(dU, I, I, buT, I, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, int(r16));
+  LMLP_LAUNCH("rowproj(dG B_g, dU B_u)", launch_rowproj(rp, d.bf16, st));
+
+  GemmParams gx{};
+  gx.nseg = 3;
+  gx.seg[0] = seg(dG, I, w_gate, nullptr, H, I, d.int4, w_gate_scales, nullptr);
+  gx.seg[1] = seg(dU, I, w_up, nullptr, H, I, d.int4, w_up_scales, nullptr);
+  gx.seg[2] = seg(aext_gu, 2 * r16, agu_pad, nullptr, H, 2 * r16);
+  gx.M = T;
+  gx.N = H;
+  gx.ldc = H;
+  gx.c0 = dx;
+  gx.group_m = 8;
+  LMLP_LAUNCH("gemm(dX)", launch_gemm(gx, d.bf16, 1, EPI_STORE, st));
+
+  const int ntb = BL.ntb;
+  const int64_t tr = BL.tr;
+  ColProjParams cp{};
+  cp.T = T;
+  cp.njobs = 5;
+  cp.job[0] = cp_job(dG, I, I, Pgu, 2 * r16, int(r16), part_dg, ntb, tr);
+  cp.job[1] = cp_job(dU, I, I, Pgu + r16, 2 * r16, int(r16), part_du, ntb, tr);
+  cp.job[2] = cp_job(Z, I, I, Qd, r16, int(r16), part_z, ntb, tr);
+  cp.job[3] = cp_job(x, H, H, Qgu, 2 * r16, int(2 * r16), part_x, ntb, tr);
+  cp.job[4] = cp_job(dy, H, H, Pd, r16, int(r16), part_dy, ntb, tr);
+  LMLP_LAUNCH("colproj", launch_colproj(cp, d.bf16, st));
+
+  rd.job[0] = rd_job(part_dg, I * r16, ntb, r16, 0, I, r, db_gate, r, false, s, d.bf16);
+  rd.job[1] = rd_job(part_du, I * r16, ntb, r16, 0, I, r, db_up, r, false, s, d.bf16);
+  rd.job[2] = rd_job(part_z, I * r16, ntb, r16, 0, I, r, da_down, I, true, s, d.bf16);
+  rd.job[3] = rd_job(part_x, H * 2 * r16, ntb, 2 * r16, 0, H, r, da_gate, H, true, s, d.bf16);
+  rd.job[4] = rd_job(part_x, H * 2 * r16, ntb, 2 * r16, int(r16), H, r, da_up, H, true, s, d.bf16);
+  rd.job[5] = rd_job(part_dy, H * r16, ntb, r16, 0, H, r, db_down, r, false, s, d.bf16);
+  rd.njobs = 6;
+  LMLP_LAUNCH("reduce", launch_reduce(rd, st));
+  return LMLP_OK;
+}
+
+int lora_mlp_dequant_int4(const void* packed, const void* scales, int64_t out, int64_t in, void* w_bf16,
+                          void* stream) {
+  g_last_error.clear();
+  if (out < 0 || in < 0) return fail(LMLP_ERR_INVALID_ARG, "negative size");
+  if (in % 64) return fail(LMLP_ERR_UNSUPPORTED, "in must be a multiple of 64");
+  if (out == 0 || in == 0) return LMLP_OK;
+  LMLP_TRY(need_ptr(packed, "packed"));
+  LMLP_TRY(need_ptr(scales, "scales"));
+  LMLP_TRY(need_ptr(w_bf16, "w_bf16"));
+  LMLP_TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  LMLP_LAUNCH("dequant_int4", launch_dequant_int4(packed, scales, out, in, w_bf16, st));
+  return LMLP_OK;
+}
+
+int lora_mlp_profile_begin(void) {
+  g_last_error.clear();
+  g_prof.recs.clear();
+  g_prof.used = 0;
+  g_prof.on = true;
+  return LMLP_OK;
+}
+
+int lora_mlp_profile_end(lmlp_kernel_time* out, int capacity, int* count) {
+  g_last_error.clear();
+  g_prof.on = false;
+  int rc = LMLP_OK;
+  int n = 0;
+  if (!g_prof.recs.empty()) {
+    hipError_t e = hipEventSynchronize(g_prof.recs.back().e);
+    if (e != hipSuccess) rc = fail(LMLP_ERR_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+  }
+  if (rc == LMLP_OK) {
+    for (const ProfRec& r : g_prof.recs) {
+      if (!out || n >= capacity) break;
+      float ms = 0.f;
+      hipError_t e = hipEventElapsedTime(&ms, r.b, r.e);
+      if (e != hipSuccess) {
+        rc = fail(LMLP_ERR_HIP, std::string("hipEventElapsedTime: ") + hipGetErrorString(e));
+        break;
+      }
+      std::snprintf(out[n].name, sizeof(out[n].name), "%s", r.name);
+      out[n].ms = ms;
+      ++n;
+    }
+  }
+  if (count) *count = n;
+  g_prof.recs.clear();
+  g_prof.used = 0;
+  return rc;
+}
+
+}  // extern "C"

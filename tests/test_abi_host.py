@@ -1,0 +1,169 @@
+"""C ABI checks that need no GPU: symbols, size queries, argument validation.
+
+Validation runs before any HIP call, so every error path below returns
+without touching a device. Pointers here are fake aligned addresses; no call
+in this file reaches a kernel launch.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from lora_swiglu_mlp_amd import abi
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def dims(**kw):
+    base = dict(tokens=256, hidden=128, inter=344, rank=8, scale=2.0, dtype="bf16", wfmt="dense")
+    base.update(kw)
+    return abi.make_dims(**base)
+
+
+def test_library_exports_every_header_symbol():
+    names = abi.header_functions()
+    assert set(names) == {"lora_mlp_saved_bytes", "lora_mlp_workspace_bytes", "lora_mlp_forward",
+                          "lora_mlp_backward", "lora_mlp_dequant_int4", "lora_mlp_status_string",
+                          "lora_mlp_last_error", "lora_mlp_profile_begin", "lora_mlp_profile_end"}
+    L = abi.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True)
+    exported = {l.split()[-1] for l in nm.stdout.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_c():
+    src = '#include "lora_mlp.h"\nint main(void){lmlp_dims d; (void)d; return 0;}\n'
+    out = subprocess.run(["gcc", "-x", "c", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                          "-I", os.path.dirname(abi.HEADER), "-"], input=src, capture_output=True,
+                         text=True)
+    assert out.returncode == 0, out.stderr
+
+
+def align(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("T,H,I,r,dt", [(256, 128, 344, 8, "f32"), (4096, 4096, 14336, 16, "bf16"),
+                                        (8192, 3584, 18944, 64, "bf16"), (0, 64, 64, 4, "bf16")])
+def test_saved_bytes_formula(T, H, I, r, dt):
+    eb = 2 if dt == "bf16" else 4
+    r16 = (r + 15) // 16 * 16
+    want = 2 * align(T * I * eb) + align(T * 2 * r16 * 4) + align(T * r16 * 4)
+    assert abi.lora_mlp_saved_bytes(dims(tokens=T, hidden=H, inter=I, rank=r, dtype=dt)) == want
+    # only the gate/up pre-activations are kept at activation size: no SiLU(G), no Z
+    assert want <= 2 * T * I * eb + 3 * T * r16 * 4 + 4 * 256
+
+
+def test_workspace_sizes_positive_and_consume_flag_saves_memory():
+    d = dims(tokens=4096, hidden=4096, inter=14336, rank=16)
+    fw, bw = abi.lora_mlp_workspace_bytes(d, False), abi.lora_mlp_workspace_bytes(d, True)
+    assert fw > 4096 * 14336 * 2 and bw > fw
+    dc = dims(tokens=4096, hidden=4096, inter=14336, rank=16, flags=abi.LMLP_CONSUME_SAVED)
+    assert abi.lora_mlp_workspace_bytes(dc, True) == bw - 2 * align(4096 * 14336 * 2)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rank=0), abi.LMLP_ERR_INVALID_ARG),
+    (dict(tokens=-1), abi.LMLP_ERR_INVALID_ARG),
+    (dict(hidden=0), abi.LMLP_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), abi.LMLP_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), abi.LMLP_ERR_INVALID_ARG),
+    (dict(dtype=7), abi.LMLP_ERR_INVALID_ARG),
+    (dict(wfmt=3), abi.LMLP_ERR_INVALID_ARG),
+    (dict(flags=0x10), abi.LMLP_ERR_INVALID_ARG),
+    (dict(rank=257), abi.LMLP_ERR_UNSUPPORTED),
+    (dict(hidden=132), abi.LMLP_ERR_UNSUPPORTED),          # not a multiple of 8 for bf16
+    (dict(inter=346, dtype="f32"), abi.LMLP_ERR_UNSUPPORTED),  # not a multiple of 4
+    (dict(wfmt="int4_b64", dtype="f32"), abi.LMLP_ERR_UNSUPPORTED),
+    (dict(wfmt="int4_b64", inter=344), abi.LMLP_ERR_UNSUPPORTED),  # not a multiple of 64
+])
+def test_invalid_dims_rejected(kw, code):
+    d = dims(**kw)
+    assert abi.lora_mlp_saved_bytes(d) == 0
+    assert abi.lora_mlp_workspace_bytes(d, True) == 0
+    rc = _forward_raw(d, saved_bytes=1 << 40, workspace_bytes=1 << 40)
+    assert rc == code, abi.lora_mlp_last_error()
+    assert abi.lora_mlp_last_error()
+
+
+def _forward_raw(d, ptrs=None, saved_bytes=0, workspace_bytes=0, scales=(None, None, None)):
+    p = dict.fromkeys(["x", "wg", "wu", "wd", "ag", "bg", "au", "bu", "ad", "bd", "y", "saved", "ws"],
+                      FAKE)
+    p.update(ptrs or {})
+    return abi.lib().lora_mlp_forward(
+        ctypes.byref(d), p["x"], p["wg"], scales[0], p["wu"], scales[1], p["wd"], scales[2],
+        p["ag"], p["bg"], p["au"], p["bu"], p["ad"], p["bd"], p["y"], p["saved"], saved_bytes,
+        p["ws"], workspace_bytes, None)
+
+
+def _backward_raw(d, ptrs=None, saved_bytes=0, workspace_bytes=0):
+    names = ["dy", "x", "wg", "wu", "wd", "ag", "bg", "au", "bu", "ad", "bd", "saved", "dx", "dag",
+             "dbg", "dau", "dbu", "dad", "dbd", "ws"]
+    p = dict.fromkeys(names, FAKE)
+    p.update(ptrs or {})
+    return abi.lib().lora_mlp_backward(
+        ctypes.byref(d), p["dy"], p["x"], p["wg"], None, p["wu"], None, p["wd"], None, p["ag"],
+        p["bg"], p["au"], p["bu"], p["ad"], p["bd"], p["saved"], saved_bytes, p["dx"], p["dag"],
+        p["dbg"], p["dau"], p["dbu"], p["dad"], p["dbd"], p["ws"], workspace_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["x", "wg", "ag", "bd", "y", "saved", "ws"])
+def test_forward_null_and_misaligned_pointers(name):
+    d = dims()
+    big = 1 << 40
+    assert _forward_raw(d, {name: None}, big, big) == abi.LMLP_ERR_INVALID_ARG
+    assert "NULL" in abi.lora_mlp_last_error()
+    assert _forward_raw(d, {name: FAKE + 8}, big, big) == abi.LMLP_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["dy", "dx", "dag", "dbd", "saved", "ws"])
+def test_backward_null_pointers(name):
+    big = 1 << 40
+    assert _backward_raw(dims(), {name: None}, big, big) == abi.LMLP_ERR_INVALID_ARG
+
+
+def test_scale_pointer_rules():
+    big = 1 << 40
+    d = dims()
+    assert _forward_raw(d, None, big, big, scales=(FAKE, None, None)) == abi.LMLP_ERR_INVALID_ARG
+    d4 = dims(wfmt="int4_b64", hidden=128, inter=384)
+    assert _forward_raw(d4, None, big, big, scales=(FAKE, None, FAKE)) == abi.LMLP_ERR_INVALID_ARG
+
+
+def test_small_buffers_rejected():
+    d = dims()
+    sb = abi.lora_mlp_saved_bytes(d)
+    wb = abi.lora_mlp_workspace_bytes(d, False)
+    assert _forward_raw(d, None, sb - 1, wb) == abi.LMLP_ERR_WORKSPACE
+    assert _forward_raw(d, None, sb, wb - 1) == abi.LMLP_ERR_WORKSPACE
+    bb = abi.lora_mlp_workspace_bytes(d, True)
+    assert _backward_raw(d, None, sb, bb - 1) == abi.LMLP_ERR_WORKSPACE
+
+
+def test_dequant_argument_checks():
+    L = abi.lib()
+    assert L.lora_mlp_dequant_int4(FAKE, FAKE, 4, 96, FAKE, None) == abi.LMLP_ERR_UNSUPPORTED
+    assert L.lora_mlp_dequant_int4(FAKE, FAKE, -1, 64, FAKE, None) == abi.LMLP_ERR_INVALID_ARG
+    assert L.lora_mlp_dequant_int4(None, FAKE, 4, 64, FAKE, None) == abi.LMLP_ERR_INVALID_ARG
+    assert L.lora_mlp_dequant_int4(None, None, 0, 64, None, None) == abi.LMLP_OK  # empty
+
+
+def test_status_strings():
+    assert abi.lora_mlp_status_string(0) == "LMLP_OK"
+    assert abi.lora_mlp_status_string(3) == "LMLP_ERR_WORKSPACE"
+    assert abi.lora_mlp_status_string(99) == "LMLP_UNKNOWN_STATUS"
+
+
+def test_python_binding_raises():
+    with pytest.raises(abi.LoraMLPError) as e:
+        abi.lora_mlp_forward(dims(rank=0), *([FAKE] * 14), saved=FAKE, workspace=FAKE, stream=0,
+                             saved_bytes=0, workspace_bytes=0)
+    assert e.value.status == abi.LMLP_ERR_INVALID_ARG
+
+
+def test_profile_session_without_launches():
+    abi.lora_mlp_profile_begin()
+    assert abi.lora_mlp_profile_end() == []
