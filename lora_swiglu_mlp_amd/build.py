@@ -17,12 +17,15 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblora_mlp.so")
-SOURCES = ["gemm.hip", "skinny.hip", "lora_mlp.cpp"]
+SOURCES = ["gemm.hip", "gemm_bf16.hip", "skinny.hip", "lora_mlp.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU ops (kept off on purpose).
 HIPFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # the ILP-first machine scheduler keeps the 256 MFMA accumulators of
+            # the GEMM kernels in place (no AGPR<->VGPR shuffles in the K loop)
+            "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
             "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument"]
 
 

@@ -37,6 +37,8 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm(const GemmParams& p, int dtype_bf16, int nn, int epi, hipStream_t stream);
+// dense bf16 operands only (LDS-DMA staging); needs every row stride * 256 < 2^31 bytes
+hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t stream);
 
 // Row projection: out[t][n] = sum_k X[t][k] * W[n][k] over all k, for up to
 // two jobs per launch. The result goes to an fp32 matrix and/or a scaled copy

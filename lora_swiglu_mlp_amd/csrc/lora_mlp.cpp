@@ -72,8 +72,9 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
       return fail(LMLP_ERR_UNSUPPORTED, "4-bit weights need hidden and inter multiples of 64");
   }
   // sizes far beyond any one GPU; keeps every offset comfortably in int64
-  if (d->tokens > (int64_t{1} << 31) || d->hidden > (int64_t{1} << 24) || d->inter > (int64_t{1} << 24))
-    return fail(LMLP_ERR_UNSUPPORTED, "dimension too large");
+  // the bf16 GEMM addresses a 256-row operand panel with 32-bit buffer offsets
+  if (d->tokens > (int64_t{1} << 31) || d->hidden > (int64_t{1} << 22) || d->inter > (int64_t{1} << 22))
+    return fail(LMLP_ERR_UNSUPPORTED, "dimension too large (tokens <= 2^31, hidden and inter <= 2^22)");
   o.T = d->tokens;
   o.H = d->hidden;
   o.I = d->inter;
@@ -287,6 +288,12 @@ struct ProfScope {
 
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
+// dense bf16 products take the LDS-DMA kernel; fp32 and 4-bit weights the general one
+hipError_t run_gemm(const GemmParams& p, const Dims& d, int nn, int epi, hipStream_t st) {
+  if (d.bf16 && !d.int4) return launch_gemm_bf16(p, nn, epi, st);
+  return launch_gemm(p, d.bf16, nn, epi, st);
+}
+
 PackJob pack_job(void* dst, int64_t ld_dst, int64_t rows, int64_t cols, const void* src, int64_t ld_src,
                  int64_t srows, int64_t scols, bool transpose) {
   PackJob j{};
@@ -467,7 +474,7 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   gp.c1 = U;
   gp.c2 = Z;
   gp.group_m = 8;
-  LMLP_LAUNCH("gemm(gate/up)", launch_gemm(gp, d.bf16, 0, EPI_SWIGLU_FWD, st));
+  LMLP_LAUNCH("gemm(gate/up)", run_gemm(gp, d, 0, EPI_SWIGLU_FWD, st));
 
   rp.job[0] = rp_job(Z, I, I, ad_pad, I, int(r16), Pd, r16, aext_d, r16, d.s, 0);
   LMLP_LAUNCH("rowproj(Z A_d^T)", launch_rowproj(rp, d.bf16, st));
@@ -481,7 +488,7 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   gd.ldc = H;
   gd.c0 = y;
   gd.group_m = 8;
-  LMLP_LAUNCH("gemm(down)", launch_gemm(gd, d.bf16, 0, EPI_STORE, st));
+  LMLP_LAUNCH("gemm(down)", run_gemm(gd, d, 0, EPI_STORE, st));
   return LMLP_OK;
 }
 
@@ -586,7 +593,7 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   gz.g_in = G;
   gz.u_in = U;
   gz.group_m = 8;
-  LMLP_LAUNCH("gemm(dZ)", launch_gemm(gz, d.bf16, 1, EPI_SWIGLU_BWD, st));
+  LMLP_LAUNCH("gemm(dZ)", run_gemm(gz, d, 1, EPI_SWIGLU_BWD, st));
 
   rp.njobs = 2;
   rp.job[0] = rp_job(dG, I, I, bgT, I, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, 0);
@@ -603,7 +610,7 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   gx.ldc = H;
   gx.c0 = dx;
   gx.group_m = 8;
-  LMLP_LAUNCH("gemm(dX)", launch_gemm(gx, d.bf16, 1, EPI_STORE, st));
+  LMLP_LAUNCH("gemm(dX)", run_gemm(gx, d, 1, EPI_STORE, st));
 
   const int ntb = BL.ntb;
   const int64_t tr = BL.tr;
