@@ -1,36 +1,43 @@
-// bf16 MFMA GEMM for gfx950 with LDS-DMA operand staging.
+// bf16 MFMA GEMM for gfx950 with an LDS-DMA ring.
 //
 // Same products, K segments and epilogues as the general kernel in gemm.hip
 // (base K loop plus the appended rank-r adapter K-steps of the fused LoRA MLP,
-// "Unsloth 深度分析报告", section 创新之处), specialised for dense bf16:
+// "Unsloth 深度分析报告", section 创新之处), specialised for dense bf16.
 //
-//  * Operands go global -> LDS with buffer_load ... lds (16 bytes per lane),
-//    so no VGPRs hold staged tiles and no VALU moves data. Each instruction
-//    writes 1 KB of LDS linearly; the XOR swizzle is applied by choosing which
-//    global chunk each lane fetches. Out-of-range rows, columns and K tails
-//    read as zero through the buffer range check (the offset of an invalid
-//    chunk is set past the range), so the loop has no branches.
-//  * K-major operands (A always, B in the NT products) sit in LDS as
-//    [256 rows][128 bytes]; the MFMA operand reads are 16-byte ds_read_b128.
-//  * N-major B operands (the NN products dZ = dY W_d and dX = dG W_g + dU W_u)
-//    sit in LDS exactly as in memory, [64 k][256 n], and are transposed on the
-//    way to registers by ds_read_b64_tr_b16: within each 16-lane group, lane j
-//    names 4 consecutive n of row k0 + j/4, and lane i receives column i of
-//    the four rows, i.e. 4 consecutive k of one n (the MFMA operand layout).
-//  * Two LDS stages of 64 KB: the DMA for tile k+1 is issued right after the
-//    barrier that opens tile k and runs under tile k's 128 MFMAs per wave.
+// Workgroup tile 256x256, 4 waves in 2x2, each wave 128x128 = 8x8 MFMA
+// 16x16x32 tiles (256 fp32 accumulators per lane). K advances 32 elements
+// (64 bytes) per k-tile: one MFMA k-step, 64 MFMAs per wave in 8 groups of 8
+// (group a = A fragment a times all eight B fragments).
+//
+// Operand staging:
+//  * buffer_load ... lds moves 16 bytes per lane straight from global memory
+//    into LDS (no staging registers). Each instruction fills 1 KB of LDS
+//    linearly; the XOR swizzle is applied by choosing which global chunk a
+//    lane fetches. Rows past M/N, columns past N and K tails read as zero
+//    through the buffer range check (invalid chunks get an offset past the
+//    range), so nothing branches.
+//  * K-major tiles (A always, B in the NT products) sit in LDS as
+//    [256 rows][64 bytes]; chunk c of row r is stored at position
+//    c ^ ((r >> 2) & 3), so the 16 rows of one operand read hit 16 distinct
+//    bank groups. Operand reads are ds_read_b128.
+//  * N-major B tiles (the NN products dZ = dY W_d and dX = dG W_g + dU W_u)
+//    sit in LDS as in memory, [32 k][256 n], and are transposed on the way to
+//    registers by ds_read_b64_tr_b16: in each 16-lane group, lane j names 4
+//    consecutive n of row k0 + j/4 and lane i receives column i of the four
+//    rows, i.e. 4 consecutive k of one n (the MFMA operand layout).
+//  * A ring of STAGES k-tiles (32 KB each). The DMA of tile kt+STAGES-1 is
+//    issued while tile kt is multiplied, one instruction per MFMA group, so
+//    STAGES-2 tiles of loads are in flight besides the one being consumed.
+//  * The DMA instruction is issued from a one-instruction asm block. It
+//    writes no register (only LDS), so the compiler has nothing to wait for;
+//    issued through the builtin, the compiler would make every later LDS read
+//    wait until all outstanding DMA had landed (it cannot tell the ring's
+//    stages apart), which drains the ring at each fragment read. Completion
+//    is waited for explicitly instead: vmcnt before the barrier that opens a
+//    k-tile, and vmcnt(0) before the epilogue and before the workgroup exits.
 #include "common.h"
 #include "gemm_epilogue.h"
 #include "kernels.h"
-
-#ifndef LMLP_SCHED_FENCES
-#define LMLP_SCHED_FENCES 1
-#endif
-#if LMLP_SCHED_FENCES
-#define LMLP_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define LMLP_SCHED_FENCE() ((void)0)
-#endif
 
 namespace lmlp {
 
@@ -38,29 +45,47 @@ namespace {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;              // bf16 elements of K per tile (128 bytes)
+constexpr int BK = 32;                   // bf16 elements of K per k-tile (64 bytes)
 constexpr int NTHREADS = 256;
-constexpr int TILE_BYTES = 32768;   // one operand tile
+constexpr int TILE_BYTES = BM * BK * 2;  // one operand tile: 16 KB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-constexpr uint32_t OOB = 0x80000000u;  // buffer offset that fails the range check
+constexpr int STAGES = 5;                // 160 KB of LDS
+constexpr uint32_t OOB = 0x80000000u;    // buffer offset that fails the range check
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4i16_t;
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(nbytes), 0x00020000);
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+
+// buffer descriptor: base address, stride 0, num_records = nbytes (offsets at
+// or past it read zero), raw-buffer flags
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  rsrc_t r;
+  r.x = static_cast<uint32_t>(a);
+  r.y = static_cast<uint32_t>(a >> 32) & 0xFFFFu;
+  r.z = nbytes;
+  r.w = 0x00020000u;
+  return r;
 }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_dst), 16,
-                                           static_cast<int>(voff), 0, 0, 0);
+// 16 bytes per lane from global (descriptor r, byte offset voff + soff) to
+// LDS at lds + 16 * lane. M0 carries the LDS address; s_nop 0 covers the
+// M0-write-to-LDS-DMA hazard.
+__device__ __forceinline__ void dma16(rsrc_t r, const void* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds));
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
+      : "memory");
 }
 
-// swizzle of 16-byte chunk positions in an N-major [k][256 n] tile row:
-// the rows one transposing read touches (4 consecutive k, and k + 8) map a
-// pair of chunks to 8 distinct pairs of bank groups
+// swizzle of 16-byte chunk positions in an N-major [k][256 n] tile row: the
+// rows one transposing read touches (4 consecutive k, and k + 8) map a pair of
+// chunks to 8 distinct pairs of bank groups
 __device__ __forceinline__ int nn_swz(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
 // one K segment of the product (all values uniform)
@@ -97,86 +122,80 @@ __device__ __forceinline__ Seg seg_pick(int sg, const Seg& s0, const Seg& s1, co
 
 // where this workgroup's output tile sits, and the lane's roles
 struct TileCtx {
-  int64_t m0, n0, j0;     // j0: first gate/up column (n0 / 2)
+  int64_t m0, n0, j0;  // j0: first gate/up column (n0 / 2)
   uint32_t m_rows, n_rows;
   int64_t N;
-  int wave, lane, c0;     // c0 = (lane & 7) ^ (lane >> 3)
+  int wave, lane, c1;  // c1 = (lane & 3) ^ ((lane >> 4) & 3)
 };
 
-// DMA state of the tile fetched next
+// DMA state of the next k-tile to fetch
 struct Dma {
-  __amdgpu_buffer_rsrc_t rA, rB0, rB1;
-  uint32_t offA[8], offB[8];
+  rsrc_t rA, rB0, rB1;
+  uint32_t offA[4], offB[4];
   Seg S;
   int seg, k0, kt;
 };
 
 // Per-lane offsets of the DMA pattern for segment S.
 // K-major tiles: instruction i of this wave fills tile rows
-// 64*wave + 8*i + (lane >> 3), chunk position lane & 7; with row & 7 ==
-// lane >> 3 and (row >> 3) & 7 == i (mod 8) the logical chunk swz(row, lane&7)
-// there is c0 ^ i. Gate/up B operand: tile rows alternate gate/up every 16,
-// so instruction i reads weight row (2*wave + i/4)*16 + 8*(i&1) + lane/8 of
-// the gate (i&2 == 0) or up panel. N-major B tiles: instruction i fills rows
-// k = 2*(8*wave + i) + (lane >> 5), chunk position lane & 31 holding n-chunk
-// (lane & 31) ^ nn_swz(k); chunks past N are never fetched.
+// 64*wave + 16*i + (lane >> 2), chunk position lane & 3; that position holds
+// logical chunk (lane & 3) ^ ((row >> 2) & 3) = c1 for every i.
+// Gate/up B operand: tile rows alternate gate/up every 16, so instruction i
+// reads weight row (2*wave + i/2)*16 + lane/4 of the gate (i even) or up panel.
+// N-major B tiles: instruction i fills rows k = 2*(4*wave + i) + (lane >> 5),
+// chunk position lane & 31 holding n-chunk (lane & 31) ^ nn_swz(k); chunks
+// past N are never fetched.
 template <bool NN, int EPI>
 __device__ __forceinline__ void dma_load_seg(Dma& d, const Seg& S, const TileCtx& t) {
   d.S = S;
   d.rA = make_rsrc(S.a + t.m0 * S.lda_b, t.m_rows * S.lda_b);
-  const uint32_t rowA = static_cast<uint32_t>(64 * t.wave + (t.lane >> 3)) * S.lda_b;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) d.offA[i] = rowA + static_cast<uint32_t>(8 * i) * S.lda_b + ((t.c0 ^ i) << 4);
+  for (int i = 0; i < 4; ++i)
+    d.offA[i] = static_cast<uint32_t>(64 * t.wave + 16 * i + (t.lane >> 2)) * S.lda_b + (t.c1 << 4);
   if (!NN) {
     const int64_t nb = EPI == EPI_SWIGLU_FWD ? t.j0 : t.n0;
     d.rB0 = make_rsrc(S.b0 + nb * S.ldb_b, t.n_rows * S.ldb_b);
     d.rB1 = EPI == EPI_SWIGLU_FWD ? make_rsrc(S.b1 + nb * S.ldb_b, t.n_rows * S.ldb_b) : d.rB0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = EPI == EPI_SWIGLU_FWD ? (2 * t.wave + i / 4) * 16 + 8 * (i & 1) + (t.lane >> 3)
-                                            : 64 * t.wave + 8 * i + (t.lane >> 3);
-      d.offB[i] = static_cast<uint32_t>(row) * S.ldb_b + ((t.c0 ^ i) << 4);
+    for (int i = 0; i < 4; ++i) {
+      const int row = EPI == EPI_SWIGLU_FWD ? (2 * t.wave + i / 2) * 16 + (t.lane >> 2)
+                                            : 64 * t.wave + 16 * i + (t.lane >> 2);
+      d.offB[i] = static_cast<uint32_t>(row) * S.ldb_b + (t.c1 << 4);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = 2 * (8 * t.wave + i) + (t.lane >> 5);
+    for (int i = 0; i < 4; ++i) {
+      const int k = 2 * (4 * t.wave + i) + (t.lane >> 5);
       const int nc = (t.lane & 31) ^ nn_swz(k);
       d.offB[i] = (t.n0 + nc * 8 < t.N) ? static_cast<uint32_t>(k) * S.ldb_b + nc * 16 : OOB;
     }
   }
 }
 
-// DMA instructions [i0, i0+4) of operand A (op 0) or B (op 1) of tile d.kt
-// into stage `buf`. A K-major chunk is fetched iff its first element is below
-// the tile's valid K; past the last tile the valid K is 0, so those loads
-// only write zeros into the idle stage.
+// DMA instruction j (0..7) of k-tile d.kt into stage `buf`: j < 4 are A's,
+// j >= 4 are B's. A K-major chunk is fetched iff its first element is below
+// the tile's valid K; past the last tile the valid K is 0 and the loads only
+// write zeros into an idle stage.
 template <bool NN, int EPI>
-__device__ __forceinline__ void dma_issue(const Dma& d, int op, int i0, char* buf, int nk, const TileCtx& t) {
+__device__ __forceinline__ void dma_issue(const Dma& d, int j, char* buf, int nk, const TileCtx& t) {
   const int kv = d.kt < nk ? d.S.K - d.k0 : 0;
   const int soff = d.k0 * 2;
-  if (op == 0) {
-#pragma unroll
-    for (int i = i0; i < i0 + 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rA, (lds_void_t*)(buf + (64 * t.wave + 8 * i) * 128), 16,
-                                               ((t.c0 ^ i) << 3) < kv ? d.offA[i] : OOB, soff, 0, 0);
+  const bool cval = (t.c1 << 3) < kv;
+  if (j < 4) {
+    const int i = j;
+    dma16(d.rA, buf + (64 * t.wave + 16 * i) * 64, cval ? d.offA[i] : OOB, soff);
   } else if (!NN) {
-    char* bbuf = buf + TILE_BYTES;
-#pragma unroll
-    for (int i = i0; i < i0 + 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((EPI == EPI_SWIGLU_FWD && (i & 2)) ? d.rB1 : d.rB0,
-                                               (lds_void_t*)(bbuf + (64 * t.wave + 8 * i) * 128), 16,
-                                               ((t.c0 ^ i) << 3) < kv ? d.offB[i] : OOB, soff, 0, 0);
+    const int i = j - 4;
+    dma16((EPI == EPI_SWIGLU_FWD && (i & 1)) ? d.rB1 : d.rB0, buf + TILE_BYTES + (64 * t.wave + 16 * i) * 64,
+          cval ? d.offB[i] : OOB, soff);
   } else {
+    const int i = j - 4;
     // clamp on the scalar unit: the descriptor must stay uniform
-    const uint32_t krows = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(kv >= BK ? BK : (kv > 0 ? kv : 0)));
-    const __amdgpu_buffer_rsrc_t r =
+    const uint32_t krows =
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(kv >= BK ? BK : (kv > 0 ? kv : 0)));
+    const rsrc_t r =
         make_rsrc(d.S.b0 + static_cast<int64_t>(d.k0) * d.S.ldb_b + t.n0 * 2, krows * d.S.ldb_b);
-    char* bbuf = buf + TILE_BYTES;
-#pragma unroll
-    for (int i = i0; i < i0 + 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(bbuf + (8 * t.wave + i) * 1024), 16, d.offB[i], 0,
-                                               0, 0);
+    dma16(r, buf + TILE_BYTES + (4 * t.wave + i) * 1024, d.offB[i], 0);
   }
 }
 
@@ -193,27 +212,26 @@ __device__ __forceinline__ void dma_advance(Dma& d, int nseg, const Seg& s0, con
 }
 
 // Lane-constant parts of the fragment read addresses.
-// K-major tile, fragment row r = w*128 + a*16 + (lane & 15), chunk
-// ks*4 + (lane >> 4): swz = (lane >> 4) ^ (lane & 7) ^ ((lane >> 3) & 1) ^
-// 4*ks ^ (2a & 7), so the byte address is a per-lane base, XOR a constant of
-// (ks, a mod 4), plus the immediate a*2048.
-// N-major tile: k = ks*32 + hh*4 + (lane >> 4)*8 + (lrow >> 2),
-// n = wn*128 + b*16 + 4*(lrow & 3): nn_swz(k) depends on the lane only and the
-// chunk is wn*16 + ((2b) ^ nn_swz) + ((lrow & 3) >> 1).
+// K-major tile, fragment row r = w*128 + a*16 + (lane & 15), chunk lane >> 4:
+// position (lane >> 4) ^ ((r >> 2) & 3) = (lane >> 4) ^ ((lane >> 2) & 3), so
+// the address is a per-lane base plus the immediate a*1024.
+// N-major tile: k = hh*4 + (lane >> 4)*8 + (lrow >> 2), n = wn*128 + b*16 +
+// 4*(lrow & 3): nn_swz(k) depends on the lane only and the chunk is
+// wn*16 + ((2b) ^ nn_swz) + ((lrow & 3) >> 1).
 struct ReadCtx {
   uint32_t rdA, rdB, rdN;
   int nsw;
 };
 
-__device__ __forceinline__ uint4 read_a(const ReadCtx& rc, const char* buf, int ks, int a) {
-  return *reinterpret_cast<const uint4*>(buf + (rc.rdA ^ ((4 * ks ^ (2 * a & 7)) << 4)) + a * 2048);
+__device__ __forceinline__ uint4 read_a(const ReadCtx& rc, const char* buf, int a) {
+  return *reinterpret_cast<const uint4*>(buf + rc.rdA + a * 1024);
 }
 
 template <bool NN>
-__device__ __forceinline__ uint4 read_b(const ReadCtx& rc, const char* buf, int ks, int b) {
+__device__ __forceinline__ uint4 read_b(const ReadCtx& rc, const char* buf, int b) {
   const char* bbuf = buf + TILE_BYTES;
-  if (!NN) return *reinterpret_cast<const uint4*>(bbuf + (rc.rdB ^ ((4 * ks ^ (2 * b & 7)) << 4)) + b * 2048);
-  const uint32_t base = rc.rdN + ((((2 * b) ^ rc.nsw) & 15) << 4) + ks * 32 * 512;
+  if (!NN) return *reinterpret_cast<const uint4*>(bbuf + rc.rdB + b * 1024);
+  const uint32_t base = rc.rdN + ((((2 * b) ^ rc.nsw) & 15) << 4);
   const v4i16_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(bbuf + base));
   const v4i16_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(bbuf + base + 4 * 512));
   const uint2 u0 = __builtin_bit_cast(uint2, t0);
@@ -226,14 +244,60 @@ __device__ __forceinline__ void mfma_group(f32x4_t (&acc)[8][8], int a, const ui
   for (int b = 0; b < 8; ++b) acc[a][b] = mma<bf16_t>::step(fb[b], fa[a], acc[a][b]);
 }
 
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// One k-tile of the pipeline. Tile kt lives in stage st_cur. While it is
+// multiplied (8 MFMA groups), the fragments of tile kt+1 are read (A slot g
+// refilled after group g; the B fragments go to the other set fbn) and the
+// DMA of tile kt+STAGES-1 is issued into tile kt-1's stage, one instruction
+// per group. After group 0 each wave waits for its DMA of tile kt+1 and the
+// workgroup meets at a barrier: tile kt+1 is then in LDS for every wave and
+// every read of tile kt-1 has retired.
+template <bool NN, int EPI>
+__device__ __forceinline__ void pipeline_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[8], const uint4 (&fb)[8],
+                                              uint4 (&fbn)[8], Dma& d, int& st_cur, char* smem,
+                                              const ReadCtx& rc, const TileCtx& t, int nk, int nseg,
+                                              const Seg& s0, const Seg& s1, const Seg& s2) {
+  const int st_nxt = st_cur + 1 == STAGES ? 0 : st_cur + 1;
+  const int st_dma = st_cur == 0 ? STAGES - 1 : st_cur - 1;  // tile kt-1's stage
+  const char* nxt = smem + st_nxt * STAGE_BYTES;
+  char* dbuf = smem + st_dma * STAGE_BYTES;
+  mfma_group(acc, 0, fa, fb);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<8 * (STAGES - 3)>();  // DMA of tile kt+1 landed (this wave)
+  __syncthreads();
+#pragma unroll
+  for (int g = 1; g < 8; ++g) {
+    mfma_group(acc, g, fa, fb);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_issue<NN, EPI>(d, g - 1, dbuf, nk, t);
+    fa[g - 1] = read_a(rc, nxt, g - 1);
+    if (g <= 4) {
+      fbn[2 * g - 2] = read_b<NN>(rc, nxt, 2 * g - 2);
+      fbn[2 * g - 1] = read_b<NN>(rc, nxt, 2 * g - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  dma_issue<NN, EPI>(d, 7, dbuf, nk, t);
+  dma_advance<NN, EPI>(d, nseg, s0, s1, s2, t);
+  fa[7] = read_a(rc, nxt, 7);
+  __builtin_amdgcn_sched_barrier(0);
+  st_cur = st_nxt;
+}
+
 template <bool NN, int EPI>
 __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
   TileCtx t;
   t.lane = threadIdx.x & 63;
   t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  t.c0 = (t.lane & 7) ^ (t.lane >> 3);
+  t.c1 = (t.lane & 3) ^ ((t.lane >> 4) & 3);
   const int wm = t.wave >> 1;
   const int wn = t.wave & 1;
 
@@ -258,7 +322,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
                                                          : min<int64_t>(BN, p.N - t.n0));
 
   const Seg s0 = seg_at(p, 0), s1 = seg_at(p, 1), s2 = seg_at(p, 2);
-  const int nk = (s0.K + BK - 1) / BK + (s1.K + BK - 1) / BK + (s2.K + BK - 1) / BK;
+  int nk = (s0.K + BK - 1) / BK + (s1.K + BK - 1) / BK + (s2.K + BK - 1) / BK;
+  nk += nk & 1;  // the loop runs k-tiles in pairs; an odd count gets one empty tile
 
   f32x4_t acc[8][8];
 #pragma unroll
@@ -269,103 +334,41 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   const int lrow = t.lane & 15;
   const int lgrp = t.lane >> 4;
   ReadCtx rc;
-  rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 128 + ((lgrp ^ (lrow & 7) ^ (lrow >> 3)) << 4));
-  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 128 + ((lgrp ^ (lrow & 7) ^ (lrow >> 3)) << 4));
+  rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
+  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
   rc.nsw = 2 * ((lrow >> 2) | ((lgrp & 1) << 2));
   rc.rdN = static_cast<uint32_t>((lgrp * 8 + (lrow >> 2)) * 512 + (wn * 16 + ((lrow & 3) >> 1)) * 16 +
                                  8 * (lrow & 1));
 
-  // ---- software pipeline. Tile t lives in stage t & 1; k-step 0 of a tile
-  // (k 0..31) uses B fragments fb0, k-step 1 (k 32..63) uses fb1, and the A
-  // fragments stream through fa: slot a is refilled for the next k-step as
-  // soon as MFMA group a (8 MFMAs, all B fragments times A fragment a) has
-  // been issued. Per tile kt:
-  //   step 0: after group a, read A fragment a of step 1 and, for a < 4,
-  //           B fragments 2a, 2a+1 of step 1
-  //   step 1: after group 2, wait for this wave's DMA of tile kt+1 and
-  //           barrier (tile kt+1 is in LDS everywhere and every read of tile
-  //           kt has retired); groups 3-7 then carry the reads of tile kt+1's
-  //           step-0 fragments and the DMA of tile kt+2 into tile kt's stage
+  // ---- prologue: DMA of tiles 0 .. STAGES-2, then tile 0's fragments
   Dma d;
   d.seg = 0;
-  d.k0 = 0;
   d.kt = 0;
+  d.k0 = 0;
   dma_load_seg<NN, EPI>(d, s0, t);
-  uint4 fa[8], fb0[8], fb1[8];
-  if (nk > 0) {
-    dma_issue<NN, EPI>(d, 0, 0, smem, nk, t);
-    dma_issue<NN, EPI>(d, 0, 4, smem, nk, t);
-    dma_issue<NN, EPI>(d, 1, 0, smem, nk, t);
-    dma_issue<NN, EPI>(d, 1, 4, smem, nk, t);
-    dma_advance<NN, EPI>(d, p.nseg, s0, s1, s2, t);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    char* st1 = smem + STAGE_BYTES;
-    dma_issue<NN, EPI>(d, 0, 0, st1, nk, t);
-    dma_issue<NN, EPI>(d, 0, 4, st1, nk, t);
-    dma_issue<NN, EPI>(d, 1, 0, st1, nk, t);
-    dma_issue<NN, EPI>(d, 1, 4, st1, nk, t);
-    dma_advance<NN, EPI>(d, p.nseg, s0, s1, s2, t);
+  uint4 fa[8], fbA[8], fbB[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) fb0[b] = read_b<NN>(rc, smem, 0, b);
+  for (int s = 0; s < STAGES - 1; ++s) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, 0, a);
+    for (int j = 0; j < 8; ++j) dma_issue<NN, EPI>(d, j, smem + s * STAGE_BYTES, nk, t);
+    dma_advance<NN, EPI>(d, p.nseg, s0, s1, s2, t);
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = smem + (kt & 1) * STAGE_BYTES;
-    const char* nxt = smem + ((kt + 1) & 1) * STAGE_BYTES;
-    char* dma_buf = smem + (kt & 1) * STAGE_BYTES;  // tile kt+2 reuses tile kt's stage
+  wait_vmcnt<8 * (STAGES - 2)>();  // tile 0 landed (this wave)
+  __syncthreads();
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      mfma_group(acc, g, fa, fb0);
-      LMLP_SCHED_FENCE();
-      fa[g] = read_a(rc, cur, 1, g);
-      if (g < 4) {
-        fb1[2 * g] = read_b<NN>(rc, cur, 1, 2 * g);
-        fb1[2 * g + 1] = read_b<NN>(rc, cur, 1, 2 * g + 1);
-      }
-      LMLP_SCHED_FENCE();
-    }
+  for (int b = 0; b < 8; ++b) fbA[b] = read_b<NN>(rc, smem, b);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      mfma_group(acc, g, fa, fb1);
-      LMLP_SCHED_FENCE();
-      if (g == 2) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): DMA of tile kt+1 landed
-        __syncthreads();
-      }
-      if (g == 3) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) fb0[b] = read_b<NN>(rc, nxt, 0, b);
-        fa[0] = read_a(rc, nxt, 0, 0);
-        fa[1] = read_a(rc, nxt, 0, 1);
-      }
-      if (g == 4) {
-#pragma unroll
-        for (int b = 4; b < 8; ++b) fb0[b] = read_b<NN>(rc, nxt, 0, b);
-        fa[2] = read_a(rc, nxt, 0, 2);
-        fa[3] = read_a(rc, nxt, 0, 3);
-        fa[4] = read_a(rc, nxt, 0, 4);
-      }
-      if (g == 5) {
-        dma_issue<NN, EPI>(d, 0, 0, dma_buf, nk, t);
-        dma_issue<NN, EPI>(d, 0, 4, dma_buf, nk, t);
-        fa[5] = read_a(rc, nxt, 0, 5);
-      }
-      if (g == 6) {
-        dma_issue<NN, EPI>(d, 1, 0, dma_buf, nk, t);
-        dma_issue<NN, EPI>(d, 1, 4, dma_buf, nk, t);
-        dma_advance<NN, EPI>(d, p.nseg, s0, s1, s2, t);
-        fa[6] = read_a(rc, nxt, 0, 6);
-      }
-      if (g == 7) fa[7] = read_a(rc, nxt, 0, 7);
-      LMLP_SCHED_FENCE();
-    }
+  for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, a);
+
+  int st_cur = 0;
+  for (int kt = 0; kt < nk; kt += 2) {
+    pipeline_tile<NN, EPI>(acc, fa, fbA, fbB, d, st_cur, smem, rc, t, nk, p.nseg, s0, s1, s2);
+    pipeline_tile<NN, EPI>(acc, fa, fbB, fbA, d, st_cur, smem, rc, t, nk, p.nseg, s0, s1, s2);
   }
 
-  // the last trip prefetched empty tiles: let that DMA retire before the
+  // the last tiles prefetched empty k-tiles: let that DMA retire before the
   // workgroup can exit and hand its LDS to another workgroup
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  wait_vmcnt<0>();
 
   gemm_epilogue<bf16_t, EPI>(p, acc, t.m0, t.n0, wm, wn, t.lane);
 }
