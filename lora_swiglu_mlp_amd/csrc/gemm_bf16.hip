@@ -36,7 +36,6 @@
 //    is waited for explicitly instead: vmcnt before the barrier that opens a
 //    k-tile, and vmcnt(0) before the epilogue and before the workgroup exits.
 #include "common.h"
-#include "gemm_epilogue.h"
 #include "kernels.h"
 
 namespace lmlp {
@@ -290,6 +289,180 @@ __device__ __forceinline__ void pipeline_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[
   st_cur = st_nxt;
 }
 
+// ---- epilogue through LDS ----------------------------------------------
+// Once the K loop has drained, the LDS ring is free. Accumulators go to LDS in
+// their MFMA layout (lane l: row l & 15, columns 4*(l >> 4) .. +3 of each
+// 16x16 tile) and come back row-contiguous, so every global access is 16
+// bytes per lane and a wave instruction covers whole row segments (512 bytes
+// of a 256-column output, 256 bytes of a 128-column gate/up output). Row
+// pitches carry 16 bytes of padding to spread the tile-layout writes over the
+// LDS banks. The SwiGLU arithmetic is the one of the register epilogue: G and
+// U rounded to bf16 first, Z = SiLU(G) U from the rounded values; backward
+// dG = dZ U sig (1 + G (1 - sig)), dU = dZ SiLU(G).
+constexpr int EP_PITCH_C = 256 * 2 + 16;   // bf16 [256 rows][256]
+constexpr int EP_PITCH_GU = 128 * 2 + 16;  // bf16 [256 rows][128], G and U side by side
+constexpr int EP_PITCH_DZ = 256 * 4 + 16;  // fp32 [128 rows][256], one half of dZ at a time
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 f32x8_to_bf16(const float (&f)[8]) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// [rows][cols] bf16 in LDS (pitch bytes) -> global, 16 bytes per lane,
+// CHUNKS 16-byte chunks per row, NT threads. Rows past m_rows and chunks past
+// the valid columns are not stored.
+template <int CHUNKS>
+__device__ __forceinline__ void lds_rows_to_global(const char* lds, int pitch, int rows, bf16_t* dst,
+                                                   int64_t ldc, uint32_t m_rows, int64_t ncols) {
+  const int tid = threadIdx.x;
+  const int chunk = tid % CHUNKS;
+  const int rsub = tid / CHUNKS;
+  constexpr int RSTEP = NTHREADS / CHUNKS;
+  const bool cval = chunk * 8 < ncols;
+#pragma unroll 4
+  for (int r = rsub; r < rows; r += RSTEP) {
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + r * pitch + chunk * 16);
+    if (cval && static_cast<uint32_t>(r) < m_rows)
+      *reinterpret_cast<uint4*>(dst + r * ldc + chunk * 8) = v;
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)[8][8], const TileCtx& t,
+                                             int wm, int wn, char* smem) {
+  const int lrow = t.lane & 15;
+  const int lcol = 4 * (t.lane >> 4);
+  if (EPI == EPI_STORE) {
+    __syncthreads();  // every wave is done with the ring
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int r = wm * 128 + a * 16 + lrow;
+        const int c = wn * 128 + b * 16 + lcol;
+        *reinterpret_cast<uint2*>(smem + r * EP_PITCH_C + c * 2) =
+            make_uint2(pack_bf16x2(acc[a][b][0], acc[a][b][1]), pack_bf16x2(acc[a][b][2], acc[a][b][3]));
+      }
+    __syncthreads();
+    bf16_t* C = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
+    lds_rows_to_global<32>(smem, EP_PITCH_C, 256, C, p.ldc, t.m_rows, p.N - t.n0);
+  } else if (EPI == EPI_SWIGLU_FWD) {
+    // tiles (a, 2q) hold G and (a, 2q+1) hold U of gate/up columns
+    // j0 + wn*64 + 16q + lcol .. +3
+    char* gbuf = smem;
+    char* ubuf = smem + 256 * EP_PITCH_GU;
+    uint32_t zp[8][4][2];
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float g[4], u[4], z[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          g[i] = elem<bf16_t>::round(acc[a][2 * q][i]);
+          u[i] = elem<bf16_t>::round(acc[a][2 * q + 1][i]);
+          z[i] = g[i] * sigmoidf_fast(g[i]) * u[i];
+        }
+        const int off = (wm * 128 + a * 16 + lrow) * EP_PITCH_GU + (wn * 64 + q * 16 + lcol) * 2;
+        *reinterpret_cast<uint2*>(gbuf + off) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+        *reinterpret_cast<uint2*>(ubuf + off) = make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
+        zp[a][q][0] = pack_bf16x2(z[0], z[1]);
+        zp[a][q][1] = pack_bf16x2(z[2], z[3]);
+      }
+    __syncthreads();
+    const int64_t base = t.m0 * p.ldc + t.j0;
+    const int64_t ncols = p.N - t.j0;
+    lds_rows_to_global<16>(gbuf, EP_PITCH_GU, 256, static_cast<bf16_t*>(p.c0) + base, p.ldc, t.m_rows, ncols);
+    lds_rows_to_global<16>(ubuf, EP_PITCH_GU, 256, static_cast<bf16_t*>(p.c1) + base, p.ldc, t.m_rows, ncols);
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int off = (wm * 128 + a * 16 + lrow) * EP_PITCH_GU + (wn * 64 + q * 16 + lcol) * 2;
+        *reinterpret_cast<uint2*>(gbuf + off) = make_uint2(zp[a][q][0], zp[a][q][1]);
+      }
+    __syncthreads();
+    lds_rows_to_global<16>(gbuf, EP_PITCH_GU, 256, static_cast<bf16_t*>(p.c2) + base, p.ldc, t.m_rows, ncols);
+  } else {  // EPI_SWIGLU_BWD: acc = dZ; reload G, U; recompute the gate
+    const bf16_t* Gp = static_cast<const bf16_t*>(p.g_in) + t.m0 * p.ldc + t.n0;
+    const bf16_t* Up = static_cast<const bf16_t*>(p.u_in) + t.m0 * p.ldc + t.n0;
+    bf16_t* dGp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
+    bf16_t* dUp = static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.n0;
+    bf16_t* Zp = p.c2 ? static_cast<bf16_t*>(p.c2) + t.m0 * p.ldc + t.n0 : nullptr;
+    // thread -> 8 consecutive columns (chunk) of rows rsub, rsub + 8, ... of a half
+    const int tid = threadIdx.x;
+    const int chunk = tid & 31;
+    const int rsub = tid >> 5;
+    const bool cval = t.n0 + chunk * 8 < p.N;
+    // G and U of one half-tile (16 rows per thread), fetched before they are
+    // needed; invalid positions read element 0 and are never stored
+    uint4 gv[16], uv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * i + rsub;
+      const int64_t off = (cval && static_cast<uint32_t>(r) < t.m_rows) ? r * p.ldc + chunk * 8 : 0;
+      gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
+      uv[i] = *reinterpret_cast<const uint4*>(Up + off);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            *reinterpret_cast<f32x4_t*>(smem + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 128 + b * 16 + lcol) * 4) =
+                acc[a][b];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = 8 * i + rsub;  // row within the half
+        const int r = h * 128 + rl;   // row within the tile
+        const float4 d0 = *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + chunk * 32);
+        const float4 d1 = *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + chunk * 32 + 16);
+        const float dz[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        float g[8], u[8], dg[8], du[8], z[8];
+        bf16x8_to_f32(gv[i], g);
+        bf16x8_to_f32(uv[i], u);
+        if (h == 0) {  // this slot is free: fetch the same position of the second half
+          const int r2 = 128 + rl;
+          const int64_t off = (cval && static_cast<uint32_t>(r2) < t.m_rows) ? r2 * p.ldc + chunk * 8 : 0;
+          gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
+          uv[i] = *reinterpret_cast<const uint4*>(Up + off);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = sigmoidf_fast(g[e]);
+          const float act = g[e] * sg;
+          dg[e] = dz[e] * u[e] * sg * (1.0f + g[e] * (1.0f - sg));
+          du[e] = dz[e] * act;
+          z[e] = act * u[e];
+        }
+        if (cval && static_cast<uint32_t>(r) < t.m_rows) {
+          const int64_t off = r * p.ldc + chunk * 8;
+          *reinterpret_cast<uint4*>(dGp + off) = f32x8_to_bf16(dg);
+          *reinterpret_cast<uint4*>(dUp + off) = f32x8_to_bf16(du);
+          if (Zp) *reinterpret_cast<uint4*>(Zp + off) = f32x8_to_bf16(z);
+        }
+      }
+      if (h == 0) __syncthreads();  // the second half overwrites the staging area
+    }
+  }
+}
+
 template <bool NN, int EPI>
 __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
@@ -370,7 +543,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   // workgroup can exit and hand its LDS to another workgroup
   wait_vmcnt<0>();
 
-  gemm_epilogue<bf16_t, EPI>(p, acc, t.m0, t.n0, wm, wn, t.lane);
+  epilogue_lds<EPI>(p, acc, t, wm, wn, smem);
 }
 
 template <bool NN, int EPI>
