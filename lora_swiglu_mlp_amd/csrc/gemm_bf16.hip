@@ -28,15 +28,12 @@
 //  * A ring of STAGES k-tiles (32 KB each). The DMA of tile kt+STAGES-1 is
 //    issued while tile kt is multiplied, one instruction per MFMA group, so
 //    STAGES-2 tiles of loads are in flight besides the one being consumed.
-//  * The DMA instruction is issued from a one-instruction asm block. It
-//    writes no register (only LDS), so the compiler has nothing to wait for;
-//    issued through the builtin, the compiler would make every later LDS read
-//    wait until all outstanding DMA had landed (it cannot tell the ring's
-//    stages apart), which drains the ring at each fragment read. Completion
-//    is waited for explicitly instead: vmcnt before the barrier that opens a
-//    k-tile, and vmcnt(0) before the epilogue and before the workgroup exits.
+//  * The DMA instruction comes from lds_dma.h (an asm block the compiler does
+//    not track); completion is waited for explicitly: vmcnt before the
+//    barrier that opens a k-tile, and vmcnt(0) before the epilogue.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace lmlp {
 
@@ -49,43 +46,10 @@ constexpr int NTHREADS = 256;
 constexpr int TILE_BYTES = BM * BK * 2;  // one operand tile: 16 KB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr int STAGES = 5;                // 160 KB of LDS
-constexpr uint32_t OOB = 0x80000000u;    // buffer offset that fails the range check
+constexpr uint32_t OOB = DMA_OOB;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4i16_t;
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
-
-// buffer descriptor: base address, stride 0, num_records = nbytes (offsets at
-// or past it read zero), raw-buffer flags
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  rsrc_t r;
-  r.x = static_cast<uint32_t>(a);
-  r.y = static_cast<uint32_t>(a >> 32) & 0xFFFFu;
-  r.z = nbytes;
-  r.w = 0x00020000u;
-  return r;
-}
-
-// 16 bytes per lane from global (descriptor r, byte offset voff + soff) to
-// LDS at lds + 16 * lane. M0 carries the LDS address; s_nop 0 covers the
-// M0-write-to-LDS-DMA hazard.
-__device__ __forceinline__ void dma16(rsrc_t r, const void* lds, uint32_t voff, uint32_t soff) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds));
-  asm volatile(
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
-      : "memory");
-}
-
-// swizzle of 16-byte chunk positions in an N-major [k][256 n] tile row: the
-// rows one transposing read touches (4 consecutive k, and k + 8) map a pair of
-// chunks to 8 distinct pairs of bank groups
-__device__ __forceinline__ int nn_swz(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
 // one K segment of the product (all values uniform)
 struct Seg {
@@ -243,12 +207,6 @@ __device__ __forceinline__ void mfma_group(f32x4_t (&acc)[8][8], int a, const ui
   for (int b = 0; b < 8; ++b) acc[a][b] = mma<bf16_t>::step(fb[b], fa[a], acc[a][b]);
 }
 
-// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 // One k-tile of the pipeline. Tile kt lives in stage st_cur. While it is
 // multiplied (8 MFMA groups), the fragments of tile kt+1 are read (A slot g

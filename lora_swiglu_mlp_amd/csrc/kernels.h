@@ -40,41 +40,69 @@ hipError_t launch_gemm(const GemmParams& p, int dtype_bf16, int nn, int epi, hip
 // dense bf16 operands only (LDS-DMA staging); needs every row stride * 256 < 2^31 bytes
 hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t stream);
 
-// Row projection: out[t][n] = sum_k X[t][k] * W[n][k] over all k, for up to
-// two jobs per launch. The result goes to an fp32 matrix and/or a scaled copy
-// in the compute dtype (the adapter K segment of a GEMM operand).
+// Row projection, split along K: part[ks][t][n] = sum over k in slice ks of
+// X[t][k] * W[n][k] (slice ks = [ks*kb, (ks+1)*kb)), for up to two jobs per
+// launch. launch_proj_finish sums the slices.
 struct RowProjJob {
   const void* x;    // [T][ldx]
   const void* w;    // [n1p][ldw], K contiguous, zero rows past the real rank
-  float* out_f32;   // [T][ld_f32] at column col_off (may be null)
-  void* out_c;      // [T][ld_c] at column col_off, = scale * value (may be null)
+  float* part;      // [kslices][T][n1p]
   int64_t ldx, ldw, K;
-  int64_t ld_f32, ld_c;
-  float scale;
-  int32_t n1p;      // multiple of 16, <= 512
-  int32_t col_off;
-  int32_t pad_;
+  int64_t kb;       // elements per slice, a multiple of four MFMA k-steps
+  int32_t n1p;      // multiple of 16
+  int32_t kslices;
 };
 struct RowProjParams {
   RowProjJob job[2];
   int32_t njobs;
-  int32_t pad_;
+  int32_t nsl;      // set by the launcher: 64-column slices of the widest job
   int64_t T;
 };
 hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream);
 
+// v(t, n) = sum_k part[k][t][n] (k < nparts, in order), n < n1p; written as
+// out_f32[t][col_off + n] (fp32), out_c[t][col_off + n] = scale * v (compute
+// dtype) and outT[col_off + n][t] (compute dtype, zero for T <= t < ldT);
+// each output optional. A saved fp32 matrix with nparts = 1 gives its
+// transposed copy.
+struct ProjFinishJob {
+  const float* part;
+  int64_t part_stride;  // elements between partials
+  int64_t ld_part;      // row stride of a partial (elements)
+  float* out_f32;
+  int64_t ld_f32;
+  void* out_c;
+  int64_t ld_c;
+  void* outT;
+  int64_t ldT;          // multiple of 64
+  float scale;
+  int32_t nparts;
+  int32_t n1p;          // multiple of 4
+  int32_t col_off;
+};
+struct ProjFinishParams {
+  ProjFinishJob job[4];
+  int32_t njobs;
+  int32_t pad_;
+  int64_t T;
+};
+hipError_t launch_proj_finish(const ProjFinishParams& p, int dtype_bf16, hipStream_t stream);
+
 // Column projection: part[tb][k][n] = sum_{t in block tb} X[t][k] * P[t][n]
-// (fp32 partial sums over token blocks; reduced by launch_reduce).
+// (fp32 partials over token blocks; reduced by launch_reduce). bf16 reads the
+// transposed P (pT, compute dtype, token-contiguous, zero past T) and covers
+// 256 features x 128 columns per workgroup; fp32 reads P and covers 64 x 64.
 struct ColProjJob {
   const void* x;    // [T][ldx]
-  const float* p;   // [T][ldp] fp32
+  const float* p;   // fp32 path: [T][ldp]
+  const void* pT;   // bf16 path: [n2p][ldpT]
   float* part;      // [ntb][K][n2p]
-  int64_t ldx, ldp, K;
+  int64_t ldx, ldp, ldpT, K;
   int64_t tr;       // tokens per block (multiple of 32)
   int32_t n2p;      // multiple of 16, <= 512
   int32_t ntb;      // token blocks
-  int32_t kblocks;  // ceil(K / 64)
-  int32_t nchunks;  // ceil(n2p / 64)
+  int32_t kblocks;  // feature blocks (256 bf16, 64 fp32)
+  int32_t nchunks;  // column chunks (128 bf16, 64 fp32)
 };
 struct ColProjParams {
   ColProjJob job[5];

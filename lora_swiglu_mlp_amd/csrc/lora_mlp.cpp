@@ -23,6 +23,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdio>
@@ -71,10 +72,10 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
     if (d->hidden % 64 || d->inter % 64)
       return fail(LMLP_ERR_UNSUPPORTED, "4-bit weights need hidden and inter multiples of 64");
   }
-  // sizes far beyond any one GPU; keeps every offset comfortably in int64
-  // the bf16 GEMM addresses a 256-row operand panel with 32-bit buffer offsets
-  if (d->tokens > (int64_t{1} << 31) || d->hidden > (int64_t{1} << 22) || d->inter > (int64_t{1} << 22))
-    return fail(LMLP_ERR_UNSUPPORTED, "dimension too large (tokens <= 2^31, hidden and inter <= 2^22)");
+  // sizes far beyond any one GPU; the DMA kernels address a 256-row operand
+  // panel, or 128 token-contiguous rows, with 32-bit buffer offsets
+  if (d->tokens > (int64_t{1} << 24) || d->hidden > (int64_t{1} << 22) || d->inter > (int64_t{1} << 22))
+    return fail(LMLP_ERR_UNSUPPORTED, "dimension too large (tokens <= 2^24, hidden and inter <= 2^22)");
   o.T = d->tokens;
   o.H = d->hidden;
   o.I = d->inter;
@@ -111,8 +112,40 @@ SavedLayout saved_layout(const Dims& d) {
   return L;
 }
 
+// Split-K plan of a row projection over a [T, K] activation with n1p output
+// columns: about 1024 workgroups of 64 rows, at least 256 elements per slice.
+struct RpPlan {
+  int ks;
+  int64_t kb;
+};
+RpPlan rp_plan(const Dims& d, int64_t K, int n1p) {
+  const int64_t unit = 4 * (d.bf16 ? 32 : 16);  // one load batch: four MFMA k-steps
+  const int64_t work = std::max<int64_t>(1, (d.T + 63) / 64 * ((n1p + 63) / 64));
+  int64_t ks = (1024 + work - 1) / work;
+  ks = std::min(std::max<int64_t>(ks, 1), std::max<int64_t>(1, K / 256));
+  int64_t kb = (K + ks - 1) / ks;
+  kb = (kb + unit - 1) / unit * unit;
+  return {static_cast<int>((K + kb - 1) / kb), kb};
+}
+size_t rp_part_bytes(const Dims& d, int64_t K, int n1p) {
+  return size_t(rp_plan(d, K, n1p).ks) * size_t(d.T) * size_t(n1p) * 4;
+}
+
+// token blocks of the column projections (partial sums over tokens)
+int colproj_ntb(const Dims& d) {
+  if (d.T <= 0) return 0;
+  if (d.bf16) return static_cast<int>(std::min<int64_t>(32, std::max<int64_t>(1, (d.T + 511) / 512)));
+  return static_cast<int>(std::min<int64_t>(16, (d.T + 255) / 256));
+}
+int64_t colproj_tr(int64_t T, int ntb) {
+  if (ntb == 0) return 32;
+  const int64_t per = (T + ntb - 1) / ntb;
+  return (per + 31) / 32 * 32;
+}
+int64_t ld_tok(const Dims& d) { return (d.T + 63) / 64 * 64; }  // token-contiguous rows
+
 struct FwdLayout {
-  size_t z, aext_gu, aext_d, agu_pad, ad_pad, bext_g, bext_u, bext_d, total;
+  size_t z, aext_gu, aext_d, agu_pad, ad_pad, bext_g, bext_u, bext_d, rp_part, total;
 };
 FwdLayout fwd_layout(const Dims& d) {
   Carver c;
@@ -125,24 +158,14 @@ FwdLayout fwd_layout(const Dims& d) {
   L.bext_g = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.bext_u = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.bext_d = c.take(size_t(d.H) * d.r16 * d.eb);
+  L.rp_part = c.take(std::max(rp_part_bytes(d, d.H, int(2 * d.r16)), rp_part_bytes(d, d.I, int(d.r16))));
   L.total = c.off;
   return L;
 }
 
-// token blocks of the column projections (partial sums over tokens)
-int colproj_ntb(int64_t T) {
-  int64_t n = (T + 255) / 256;
-  if (n > 16) n = 16;
-  return static_cast<int>(n);
-}
-int64_t colproj_tr(int64_t T, int ntb) {
-  if (ntb == 0) return 32;
-  const int64_t per = (T + ntb - 1) / ntb;
-  return (per + 31) / 32 * 32;
-}
-
 struct BwdLayout {
   size_t dg, du, z, qd, aext_d, qgu, aext_gu, bdT, bgT, buT, ad_pad, agu_pad;
+  size_t rp_a, rp_b, pguT, pdT, qdT, qguT;
   size_t part_dg, part_du, part_z, part_x, part_dy, total;
   int ntb;
   int64_t tr;
@@ -150,7 +173,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(const Dims& d) {
   Carver c;
   BwdLayout L;
-  L.ntb = colproj_ntb(d.T);
+  L.ntb = colproj_ntb(d);
   L.tr = colproj_tr(d.T, L.ntb);
   const size_t act = size_t(d.T) * d.I * d.eb;
   L.dg = d.consume ? 0 : c.take(act);
@@ -165,6 +188,15 @@ BwdLayout bwd_layout(const Dims& d) {
   L.buT = c.take(size_t(d.r16) * d.I * d.eb);
   L.ad_pad = c.take(size_t(d.r16) * d.I * d.eb);
   L.agu_pad = c.take(size_t(2 * d.r16) * d.H * d.eb);
+  L.rp_a = c.take(std::max(rp_part_bytes(d, d.H, int(d.r16)), rp_part_bytes(d, d.I, int(d.r16))));
+  L.rp_b = c.take(rp_part_bytes(d, d.I, int(d.r16)));
+  // transposed, token-contiguous copies of the [T, r] operands of the column
+  // projections (bf16 path only)
+  const size_t trow = d.bf16 ? size_t(ld_tok(d)) * d.eb : 0;
+  L.pguT = c.take(2 * d.r16 * trow);
+  L.pdT = c.take(d.r16 * trow);
+  L.qdT = c.take(d.r16 * trow);
+  L.qguT = c.take(2 * d.r16 * trow);
   L.part_dg = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
   L.part_du = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
   L.part_z = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
@@ -324,8 +356,9 @@ GemmSeg seg(const void* a, int64_t lda, const void* b0, const void* b1, int64_t 
   return s;
 }
 
-RowProjJob rp_job(const void* x, int64_t ldx, int64_t K, const void* w, int64_t ldw, int n1p, float* out_f32,
-                  int64_t ld_f32, void* out_c, int64_t ld_c, float scale, int col_off) {
+RowProjJob rp_job(const Dims& d, const void* x, int64_t ldx, int64_t K, const void* w, int64_t ldw, int n1p,
+                  float* part) {
+  const RpPlan pl = rp_plan(d, K, n1p);
   RowProjJob j{};
   j.x = x;
   j.ldx = ldx;
@@ -333,29 +366,47 @@ RowProjJob rp_job(const void* x, int64_t ldx, int64_t K, const void* w, int64_t 
   j.w = w;
   j.ldw = ldw;
   j.n1p = n1p;
+  j.part = part;
+  j.kb = pl.kb;
+  j.kslices = pl.ks;
+  return j;
+}
+
+ProjFinishJob fin_job(const float* part, int nparts, int64_t part_stride, int64_t ld_part, int n1p, float* out_f32,
+                      int64_t ld_f32, void* out_c, int64_t ld_c, float scale, void* outT, int64_t ldT, int col_off) {
+  ProjFinishJob j{};
+  j.part = part;
+  j.nparts = nparts;
+  j.part_stride = part_stride;
+  j.ld_part = ld_part;
+  j.n1p = n1p;
   j.out_f32 = out_f32;
   j.ld_f32 = ld_f32;
   j.out_c = out_c;
   j.ld_c = ld_c;
   j.scale = scale;
+  j.outT = outT;
+  j.ldT = ldT;
   j.col_off = col_off;
   return j;
 }
 
-ColProjJob cp_job(const void* x, int64_t ldx, int64_t K, const float* p, int64_t ldp, int n2p, float* part,
-                  int ntb, int64_t tr) {
+ColProjJob cp_job(const Dims& d, const void* x, int64_t ldx, int64_t K, const float* p, int64_t ldp, const void* pT,
+                  int64_t ldpT, int n2p, float* part, int ntb, int64_t tr) {
   ColProjJob j{};
   j.x = x;
   j.ldx = ldx;
   j.K = K;
   j.p = p;
   j.ldp = ldp;
+  j.pT = pT;
+  j.ldpT = ldpT;
   j.n2p = n2p;
   j.part = part;
   j.ntb = ntb;
   j.tr = tr;
-  j.kblocks = static_cast<int>((K + 63) / 64);
-  j.nchunks = (n2p + 63) / 64;
+  j.kblocks = static_cast<int>(d.bf16 ? (K + 255) / 256 : (K + 63) / 64);
+  j.nchunks = d.bf16 ? (n2p + 127) / 128 : (n2p + 63) / 64;
   return j;
 }
 
@@ -457,11 +508,18 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   pk.njobs = 7;
   LMLP_LAUNCH("pack(fwd)", launch_pack(pk, eb, st));
 
+  float* rpp = reinterpret_cast<float*>(at(workspace, FL.rp_part));
   RowProjParams rp{};
   rp.T = T;
   rp.njobs = 1;
-  rp.job[0] = rp_job(x, H, H, agu_pad, H, int(2 * r16), Pgu, 2 * r16, aext_gu, 2 * r16, d.s, 0);
+  rp.job[0] = rp_job(d, x, H, H, agu_pad, H, int(2 * r16), rpp);
   LMLP_LAUNCH("rowproj(X A^T)", launch_rowproj(rp, d.bf16, st));
+  ProjFinishParams fp{};
+  fp.T = T;
+  fp.njobs = 1;
+  fp.job[0] = fin_job(rpp, rp.job[0].kslices, T * 2 * r16, 2 * r16, int(2 * r16), Pgu, 2 * r16, aext_gu, 2 * r16,
+                      d.s, nullptr, 0, 0);
+  LMLP_LAUNCH("finish(P_gu)", launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gp{};
   gp.nseg = 2;
@@ -476,8 +534,10 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   gp.group_m = 8;
   LMLP_LAUNCH("gemm(gate/up)", run_gemm(gp, d, 0, EPI_SWIGLU_FWD, st));
 
-  rp.job[0] = rp_job(Z, I, I, ad_pad, I, int(r16), Pd, r16, aext_d, r16, d.s, 0);
+  rp.job[0] = rp_job(d, Z, I, I, ad_pad, I, int(r16), rpp);
   LMLP_LAUNCH("rowproj(Z A_d^T)", launch_rowproj(rp, d.bf16, st));
+  fp.job[0] = fin_job(rpp, rp.job[0].kslices, T * r16, r16, int(r16), Pd, r16, aext_d, r16, d.s, nullptr, 0, 0);
+  LMLP_LAUNCH("finish(Pd)", launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gd{};
   gd.nseg = 2;
@@ -558,6 +618,13 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   char* buT = at(workspace, BL.buT);
   char* ad_pad = at(workspace, BL.ad_pad);
   char* agu_pad = at(workspace, BL.agu_pad);
+  float* rpa = reinterpret_cast<float*>(at(workspace, BL.rp_a));
+  float* rpb = reinterpret_cast<float*>(at(workspace, BL.rp_b));
+  const int64_t ldT = ld_tok(d);
+  char* pguT = d.bf16 ? at(workspace, BL.pguT) : nullptr;
+  char* pdT = d.bf16 ? at(workspace, BL.pdT) : nullptr;
+  char* qdT = d.bf16 ? at(workspace, BL.qdT) : nullptr;
+  char* qguT = d.bf16 ? at(workspace, BL.qguT) : nullptr;
   float* part_dg = reinterpret_cast<float*>(at(workspace, BL.part_dg));
   float* part_du = reinterpret_cast<float*>(at(workspace, BL.part_du));
   float* part_z = reinterpret_cast<float*>(at(workspace, BL.part_z));
@@ -577,8 +644,19 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   RowProjParams rp{};
   rp.T = T;
   rp.njobs = 1;
-  rp.job[0] = rp_job(dy, H, H, bdT, H, int(r16), Qd, r16, aext_d, r16, s, 0);
+  rp.job[0] = rp_job(d, dy, H, H, bdT, H, int(r16), rpa);
   LMLP_LAUNCH("rowproj(dY B_d)", launch_rowproj(rp, d.bf16, st));
+  // Q_d, and (bf16) the transposed copies the column projections read
+  ProjFinishParams fp{};
+  fp.T = T;
+  fp.njobs = 1;
+  fp.job[0] = fin_job(rpa, rp.job[0].kslices, T * r16, r16, int(r16), Qd, r16, aext_d, r16, s, qdT, ldT, 0);
+  if (d.bf16) {
+    fp.job[1] = fin_job(Pgu, 1, 0, 2 * r16, int(2 * r16), nullptr, 0, nullptr, 0, 1.f, pguT, ldT, 0);
+    fp.job[2] = fin_job(Pd, 1, 0, r16, int(r16), nullptr, 0, nullptr, 0, 1.f, pdT, ldT, 0);
+    fp.njobs = 3;
+  }
+  LMLP_LAUNCH("finish(Q_d, P^T)", launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gz{};
   gz.nseg = 2;
@@ -596,9 +674,14 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   LMLP_LAUNCH("gemm(dZ)", run_gemm(gz, d, 1, EPI_SWIGLU_BWD, st));
 
   rp.njobs = 2;
-  rp.job[0] = rp_job(dG, I, I, bgT, I, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, 0);
-  rp.job[1] = rp_job(dU, I, I, buT, I, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, int(r16));
+  rp.job[0] = rp_job(d, dG, I, I, bgT, I, int(r16), rpa);
+  rp.job[1] = rp_job(d, dU, I, I, buT, I, int(r16), rpb);
   LMLP_LAUNCH("rowproj(dG B_g, dU B_u)", launch_rowproj(rp, d.bf16, st));
+  fp.njobs = 2;
+  fp.job[0] = fin_job(rpa, rp.job[0].kslices, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT, 0);
+  fp.job[1] = fin_job(rpb, rp.job[1].kslices, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT,
+                      int(r16));
+  LMLP_LAUNCH("finish(Q_gu)", launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gx{};
   gx.nseg = 3;
@@ -617,11 +700,13 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   ColProjParams cp{};
   cp.T = T;
   cp.njobs = 5;
-  cp.job[0] = cp_job(dG, I, I, Pgu, 2 * r16, int(r16), part_dg, ntb, tr);
-  cp.job[1] = cp_job(dU, I, I, Pgu + r16, 2 * r16, int(r16), part_du, ntb, tr);
-  cp.job[2] = cp_job(Z, I, I, Qd, r16, int(r16), part_z, ntb, tr);
-  cp.job[3] = cp_job(x, H, H, Qgu, 2 * r16, int(2 * r16), part_x, ntb, tr);
-  cp.job[4] = cp_job(dy, H, H, Pd, r16, int(r16), part_dy, ntb, tr);
+  const size_t trow = size_t(ldT) * eb;  // bytes of one transposed row
+  cp.job[0] = cp_job(d, dG, I, I, Pgu, 2 * r16, pguT, ldT, int(r16), part_dg, ntb, tr);
+  cp.job[1] = cp_job(d, dU, I, I, Pgu + r16, 2 * r16, pguT ? pguT + r16 * trow : nullptr, ldT, int(r16), part_du,
+                     ntb, tr);
+  cp.job[2] = cp_job(d, Z, I, I, Qd, r16, qdT, ldT, int(r16), part_z, ntb, tr);
+  cp.job[3] = cp_job(d, x, H, H, Qgu, 2 * r16, qguT, ldT, int(2 * r16), part_x, ntb, tr);
+  cp.job[4] = cp_job(d, dy, H, H, Pd, r16, pdT, ldT, int(r16), part_dy, ntb, tr);
   LMLP_LAUNCH("colproj", launch_colproj(cp, d.bf16, st));
 
   rd.job[0] = rd_job(part_dg, I * r16, ntb, r16, 0, I, r, db_gate, r, false, s, d.bf16);

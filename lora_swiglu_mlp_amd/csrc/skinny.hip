@@ -12,86 +12,141 @@
 // what the fp32 vector units sustain at 8 TB/s.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace lmlp {
 
 namespace {
 
 // ---------------------------------------------------------------------------
-// Row projection. Workgroup = 16 token rows x up to 128 output columns; the
-// four waves split K (wave w takes k-steps w, w+4, ...), each feeding its own
-// accumulators, and the four partial tiles are summed in LDS in fixed order.
-// A operand chunks come straight from global memory (one 16-byte load per
-// lane per k-step, each 64-byte row segment fully used); the small W factor
-// is L2-resident.
+// Row projection, split along K. Workgroup = 64 token rows (16 per wave) x one
+// K slice x up to 64 output columns (four MFMA column tiles). Each wave issues
+// the loads of four k-steps (its activation chunks and the matching factor
+// chunks) before their MFMAs, and many workgroups share a CU, so enough loads
+// are in flight to stream the activation at HBM rate; the factor (a few
+// hundred KB) stays in L2. The slice partials are summed in fixed order by
+// proj_finish_kernel.
 template <typename T>
 __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
   constexpr int CH = elem<T>::CH;
-  const RowProjJob& jb = p.job[blockIdx.y];
-  const int n_base = blockIdx.z * 128;
-  if (n_base >= jb.n1p) return;
-  const int nfr = min(8, (jb.n1p - n_base) / 16);
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
-  if (t0 >= p.T) return;
+  constexpr int KSTEP = 4 * CH;  // elements per MFMA k-step
+  const RowProjJob& jb = p.job[blockIdx.z / p.nsl];
+  const int n_base = (blockIdx.z % p.nsl) * 64;
+  if (n_base >= jb.n1p || static_cast<int>(blockIdx.y) >= jb.kslices) return;
+  const int nfr = min(4, (jb.n1p - n_base) / 16);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lrow = lane & 15, lch = lane >> 4;
-  const int64_t row = t0 + lrow;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16 + lrow;
   const bool rval = row < p.T;
+  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * jb.kb;
+  const int64_t k1 = min(jb.K, k0 + jb.kb);
   const T* X = static_cast<const T*>(jb.x) + (rval ? row : 0) * jb.ldx;
   const T* W = static_cast<const T*>(jb.w) + static_cast<int64_t>(n_base + lrow) * jb.ldw;
-  const int64_t nchunks = jb.K / CH;
-  const int64_t nsteps = (nchunks + 3) / 4;
 
-  f32x4_t acc[8];
+  f32x4_t acc[4];
 #pragma unroll
-  for (int f = 0; f < 8; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll 2
-  for (int64_t s = wave; s < nsteps; s += 4) {
-    const int64_t c = s * 4 + lch;
-    const bool cval = c < nchunks;
-    const uint4 a = (rval && cval) ? *reinterpret_cast<const uint4*>(X + c * CH) : zero4();
+  for (int f = 0; f < 4; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t kk = k0; kk < k1; kk += 4 * KSTEP) {
+    uint4 a[4], b[4][4];
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      if (f < nfr) {
-        const uint4 b = cval ? *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(f) * 16 * jb.ldw + c * CH)
-                             : zero4();
-        acc[f] = mma<T>::step(b, a, acc[f]);
-      }
+    for (int s = 0; s < 4; ++s) {
+      const int64_t c = kk + s * KSTEP + lch * CH;  // first element of this lane's chunk
+      const bool cval = c < k1;
+      a[s] = (rval && cval) ? *reinterpret_cast<const uint4*>(X + c) : zero4();
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        b[s][f] = (f < nfr && cval) ? *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(f) * 16 * jb.ldw + c)
+                                    : zero4();
     }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        if (f < nfr) acc[f] = mma<T>::step(b[s][f], a[s], acc[f]);
   }
-
-  __shared__ f32x4_t red[4][8][64];
+  if (!rval) return;
+  // lane holds columns n_base + 16f + 4*lch .. +3 of token row `row`
+  float* out = jb.part + (static_cast<int64_t>(blockIdx.y) * p.T + row) * jb.n1p + n_base + 4 * lch;
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
-    if (f < nfr) red[wave][f][lane] = acc[f];
-  __syncthreads();
-  for (int f = wave; f < nfr; f += 4) {
-    f32x4_t v = red[0][f][lane];
-    v += red[1][f][lane];
-    v += red[2][f][lane];
-    v += red[3][f][lane];
-    if (!rval) continue;
-    // lane holds columns n .. n+3 of token row `row`
-    const int n = jb.col_off + n_base + f * 16 + 4 * lch;
-    if (jb.out_f32)
-      *reinterpret_cast<float4*>(jb.out_f32 + row * jb.ld_f32 + n) = make_float4(v[0], v[1], v[2], v[3]);
-    if (jb.out_c) {
-      T* o = static_cast<T*>(jb.out_c) + row * jb.ld_c + n;
-      store4(o, jb.scale * v[0], jb.scale * v[1], jb.scale * v[2], jb.scale * v[3]);
+  for (int f = 0; f < 4; ++f)
+    if (f < nfr) *reinterpret_cast<float4*>(out + f * 16) = make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
+}
+
+// Finish of a split-K row projection: v(t, n) = sum of the slice partials in
+// slice order. Writes v to out_f32, scale * v in the compute dtype to out_c,
+// and v in the compute dtype, transposed and token-contiguous ([n][ldT],
+// zero for T <= t < ldT), to outT; each output is optional. Workgroup = one
+// wave on 16 tokens x 64 columns; eight partials are loaded before they are
+// added (still in slice order), and the transposed write goes through LDS.
+template <typename T>
+__global__ __launch_bounds__(64) void proj_finish_kernel(ProjFinishParams p) {
+  const ProjFinishJob& jb = p.job[blockIdx.z];
+  const int n0 = blockIdx.y * 64;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t tmax = jb.outT ? jb.ldT : p.T;
+  if (n0 >= jb.n1p || t0 >= tmax) return;
+  const int nc = min(64, jb.n1p - n0);  // a multiple of 4
+  const int cpr = nc / 4;               // float4 items per token row
+  __shared__ float tile[64][17];
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int it = lane + 64 * q;
+    if (it >= 16 * cpr) break;
+    const int tl = it / cpr, c = it % cpr;
+    const int64_t t = t0 + tl;
+    const int n = n0 + 4 * c;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < p.T) {
+      const float* src = jb.part + t * jb.ld_part + n;
+      int k = 0;
+      for (; k + 8 <= jb.nparts; k += 8) {
+        float4 x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(k + e) * jb.part_stride);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v.x += x[e].x;
+          v.y += x[e].y;
+          v.z += x[e].z;
+          v.w += x[e].w;
+        }
+      }
+      for (; k < jb.nparts; ++k) {
+        const float4 x = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(k) * jb.part_stride);
+        v.x += x.x;
+        v.y += x.y;
+        v.z += x.z;
+        v.w += x.w;
+      }
+      if (jb.out_f32) *reinterpret_cast<float4*>(jb.out_f32 + t * jb.ld_f32 + jb.col_off + n) = v;
+      if (jb.out_c)
+        store4(static_cast<T*>(jb.out_c) + t * jb.ld_c + jb.col_off + n, jb.scale * v.x, jb.scale * v.y,
+               jb.scale * v.z, jb.scale * v.w);
     }
+    tile[4 * c + 0][tl] = v.x;
+    tile[4 * c + 1][tl] = v.y;
+    tile[4 * c + 2][tl] = v.z;
+    tile[4 * c + 3][tl] = v.w;
+  }
+  if (!jb.outT) return;  // uniform over the workgroup
+  __syncthreads();
+  if (lane < nc) {  // t0 + 16 <= ldT: ldT is a multiple of 64
+    T* dst = static_cast<T*>(jb.outT) + static_cast<int64_t>(jb.col_off + n0 + lane) * jb.ldT + t0;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) store4(dst + e, tile[lane][e], tile[lane][e + 1], tile[lane][e + 2], tile[lane][e + 3]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Column projection. Workgroup = 64 columns k of X (16 per wave) x up to 64
+// Column projection, fp32 activations. Workgroup = 64 columns k of X (16 per wave) x up to 64
 // columns n of P, over one block of tokens, in steps of 32 tokens staged in
 // LDS. The MFMA contraction runs over tokens: the P operand is stored
 // transposed ([n][t], 16-byte reads) and the X operand is gathered down the
 // token axis from a padded row-major tile.
 template <typename T>
-__global__ __launch_bounds__(256) void colproj_kernel(ColProjParams p) {
+__global__ __launch_bounds__(256) void colproj_f32_kernel(ColProjParams p) {
   constexpr int CH = elem<T>::CH;
   constexpr int EB = elem<T>::BYTES;
   constexpr int TS = 32;                 // tokens per step
@@ -187,19 +242,206 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColProjParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Column projection, bf16 activations. Workgroup = 256 features x one block of
+// tokens x up to 128 output columns. The activation streams through an LDS
+// ring of [32 tokens][256 features] tiles (LDS DMA, the N-major tile layout
+// and swizzle of the GEMM's B operand), together with the matching
+// [n][32 tokens] tile of the transposed P operand (token-contiguous rows,
+// chunk c of row r at position c ^ ((r >> 2) & 3)). Transposing reads
+// (ds_read_b64_tr_b16) make the token axis the MFMA contraction axis. Wave w
+// owns features 64w .. 64w + 63 (four 16-feature MFMA tiles). Every vector
+// memory access of this kernel is DMA, so the explicit vmcnt waits are exact.
+constexpr int CP_TS = 32;                    // tokens per step
+constexpr int CP_XT = CP_TS * 256 * 2;       // activation tile, 16 KB
+constexpr int CP_PT = 128 * CP_TS * 2;       // P^T tile, up to 128 columns, 8 KB
+constexpr int CP_STAGE = CP_XT + CP_PT;
+constexpr int CP_STAGES = 3;                 // 72 KB: two workgroups per CU
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short cp_v4i16_t;
+typedef __attribute__((address_space(3))) cp_v4i16_t cp_lds_v4i16_t;
+
+struct CpDma {
+  const char* xrow;  // activation at (first token of the block, first feature)
+  uint32_t ldx_b;    // activation row stride, bytes
+  int64_t tleft;     // tokens of the block from the step being fetched on
+  rsrc_t rp;         // P^T rows n0 ..
+  uint32_t xoff[4], poff[2];
+};
+
+template <int PI>
+__device__ __forceinline__ void cp_issue(CpDma& d, char* stage, int step, int wave) {
+  const int64_t kr = d.tleft - static_cast<int64_t>(step) * CP_TS;
+  const uint32_t krows = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+      static_cast<int>(kr >= CP_TS ? CP_TS : (kr > 0 ? kr : 0))));
+  const rsrc_t rx = make_rsrc(d.xrow + static_cast<int64_t>(step) * CP_TS * d.ldx_b, krows * d.ldx_b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16(rx, stage + (4 * wave + i) * 1024, d.xoff[i], 0);
+  // prefetches past the block's last step read P^T at step 0 (never used):
+  // the uniform offset then stays inside the P^T rows
+  const uint32_t soff = kr > 0 ? static_cast<uint32_t>(step) * CP_TS * 2 : 0u;
+#pragma unroll
+  for (int j = 0; j < PI; ++j) dma16(d.rp, stage + CP_XT + (wave + 4 * j) * 1024, d.poff[j], soff);
+}
+
+template <int PI>
+__global__ __launch_bounds__(256, 2) void colproj_bf16_kernel(ColProjParams p) {
+  const ColProjJob& jb = p.job[blockIdx.z];
+  const int nblocks = jb.kblocks * jb.ntb * jb.nchunks;
+  if (static_cast<int>(blockIdx.x) >= nblocks) return;
+  int b = blockIdx.x;
+  const int kb = b % jb.kblocks;
+  b /= jb.kblocks;
+  const int nc = b % jb.nchunks;
+  const int tb = b / jb.nchunks;
+  const int64_t f0 = static_cast<int64_t>(kb) * 256;
+  const int n0 = nc * 128;
+  const int nfr = min(8, (jb.n2p - n0) / 16);
+  const int64_t tbeg = static_cast<int64_t>(tb) * jb.tr;
+  const int64_t tend = min(p.T, tbeg + jb.tr);
+  if (tbeg >= tend) return;
+  const int nsteps = static_cast<int>((tend - tbeg + CP_TS - 1) / CP_TS);
+
+  __shared__ __attribute__((aligned(1024))) char ring[CP_STAGES * CP_STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 15, lgrp = lane >> 4;
+
+  CpDma d;
+  d.ldx_b = static_cast<uint32_t>(jb.ldx * 2);
+  d.xrow = static_cast<const char*>(jb.x) + (tbeg * jb.ldx + f0) * 2;
+  d.tleft = tend - tbeg;
+  const uint32_t ldp_b = static_cast<uint32_t>(jb.ldpT * 2);
+  d.rp = make_rsrc(static_cast<const char*>(jb.pT) + static_cast<int64_t>(n0) * jb.ldpT * 2 + tbeg * 2,
+                   static_cast<uint32_t>(16 * nfr) * ldp_b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = 2 * (4 * wave + i) + (lane >> 5);
+    const int fc = (lane & 31) ^ nn_swz(k);
+    d.xoff[i] = (f0 + fc * 8 < jb.K) ? static_cast<uint32_t>(k) * d.ldx_b + fc * 16 : DMA_OOB;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int f = wave + 4 * j;  // P^T row tile of instruction j
+    const int rr = lane >> 2;
+    const int lc = (lane & 3) ^ ((rr >> 2) & 3);
+    d.poff[j] = f < nfr ? static_cast<uint32_t>(16 * f + rr) * ldp_b + lc * 16 : DMA_OOB;
+  }
+
+  // fragment read addresses: activation (transposing), P^T (16-byte rows)
+  const uint32_t rdN = static_cast<uint32_t>((lgrp * 8 + (lrow >> 2)) * 512 +
+                                             ((wave >> 1) * 16 + ((lrow & 3) >> 1)) * 16 + 8 * (lrow & 1));
+  const int nsw = 2 * ((lrow >> 2) | ((lgrp & 1) << 2));
+  const uint32_t rdP = static_cast<uint32_t>(CP_XT + lrow * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
+
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) acc[j][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  cp_issue<PI>(d, ring, 0, wave);
+  cp_issue<PI>(d, ring + CP_STAGE, 1, wave);
+  wait_vmcnt<4 + PI>();  // step 0 landed (this wave)
+  __syncthreads();
+  int cur = 0;
+  for (int s = 0; s < nsteps; ++s) {
+    const char* st = ring + cur * CP_STAGE;
+    const int nx = cur == 0 ? CP_STAGES - 1 : cur - 1;  // stage of step s+2 (step s-1's)
+    cp_issue<PI>(d, ring + nx * CP_STAGE, s + 2, wave);
+    uint4 xf[4], pf[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int bb = 4 * (wave & 1) + j;
+      const uint32_t base = rdN + ((((2 * bb) ^ nsw) & 15) << 4);
+      const cp_v4i16_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((cp_lds_v4i16_t*)(st + base));
+      const cp_v4i16_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((cp_lds_v4i16_t*)(st + base + 4 * 512));
+      const uint2 u0 = __builtin_bit_cast(uint2, t0);
+      const uint2 u1 = __builtin_bit_cast(uint2, t1);
+      xf[j] = make_uint4(u0.x, u0.y, u1.x, u1.y);
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+      if (f < nfr) pf[f] = *reinterpret_cast<const uint4*>(st + rdP + f * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+        if (f < nfr) acc[j][f] = mma<bf16_t>::step(pf[f], xf[j], acc[j][f]);
+    wait_vmcnt<4 + PI>();  // step s+1 landed (this wave); step s+2 may still fly
+    __syncthreads();       // ... everywhere, and every read of stage `cur` is done
+    cur = cur + 1 == CP_STAGES ? 0 : cur + 1;
+  }
+  wait_vmcnt<0>();  // the prefetches past the last step
+  // lane holds n = n0 + 16f + 4*lgrp .. +3 for feature f0 + 64*wave + 16j + lrow
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t feat = f0 + 64 * wave + 16 * j + lrow;
+    if (feat >= jb.K) continue;
+    float* out = jb.part + (static_cast<int64_t>(tb) * jb.K + feat) * jb.n2p + n0 + 4 * lgrp;
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+      if (f < nfr)
+        *reinterpret_cast<float4*>(out + 16 * f) = make_float4(acc[j][f][0], acc[j][f][1], acc[j][f][2], acc[j][f][3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-order sum of partials: v(i, j) = scale * sum_c src[c][i][col_off + j]
+// for i < rows, j < cols, written to dst[i][j] or, with transpose, dst[j][i],
+// in fp32 or bf16. Workgroup = a 64 x 64 source tile; reads are 16 bytes per
+// lane along source rows, and the transposed case goes through LDS so that
+// its writes also run along destination rows. nchunk = 0 writes zeros.
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
-  const ReduceJob& jb = p.job[blockIdx.y];
-  const int64_t n = jb.rows * jb.cols;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < n;
-       idx += static_cast<int64_t>(gridDim.x) * 256) {
-    int64_t i, j;
-    if (jb.transpose) { i = idx % jb.rows; j = idx / jb.rows; }   // consecutive dst columns
-    else { j = idx % jb.cols; i = idx / jb.cols; }
-    const float* s = jb.src + i * jb.ld_src + jb.col_off + j;
-    float v = 0.f;
-    for (int c = 0; c < jb.nchunk; ++c) v += s[static_cast<int64_t>(c) * jb.chunk_stride];
-    v *= jb.scale;
-    const int64_t o = jb.transpose ? j * jb.ld_dst + i : i * jb.ld_dst + j;
+  const ReduceJob& jb = p.job[blockIdx.z];
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.y) * 64;
+  if (i0 >= jb.rows || j0 >= jb.cols) return;
+  __shared__ float tile[64][65];
+  const int tid = threadIdx.x, c4 = tid & 15, rr = tid >> 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int il = 16 * q + rr;
+    const int64_t i = i0 + il;
+    const int64_t j = j0 + 4 * c4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (i < jb.rows && j < jb.cols) {
+      const float* s = jb.src + i * jb.ld_src + jb.col_off + j;
+      for (int c = 0; c < jb.nchunk; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(c) * jb.chunk_stride);
+        v[0] += x.x;
+        v[1] += x.y;
+        v[2] += x.z;
+        v[3] += x.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= jb.scale;
+    if (!jb.transpose) {
+      if (i < jb.rows) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (j + e >= jb.cols) break;
+          const int64_t o = i * jb.ld_dst + j + e;
+          if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(v[e]);
+          else static_cast<float*>(jb.dst)[o] = v[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[4 * c4 + e][il] = v[e];
+    }
+  }
+  if (!jb.transpose) return;  // uniform over the workgroup
+  __syncthreads();
+  const int jl = tid >> 2, iq = tid & 3;
+  const int64_t j = j0 + jl;
+  if (j >= jb.cols) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int64_t i = i0 + 16 * iq + e;
+    if (i >= jb.rows) break;
+    const int64_t o = j * jb.ld_dst + i;
+    const float v = tile[jl][16 * iq + e];
     if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(v);
     else static_cast<float*>(jb.dst)[o] = v;
   }
@@ -245,34 +487,64 @@ int grid_for(int64_t n) {
 
 hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream) {
   if (p.T <= 0 || p.njobs <= 0) return hipSuccess;
+  RowProjParams q = p;
+  int maxn = 0, maxks = 0;
+  for (int i = 0; i < q.njobs; ++i) {
+    maxn = q.job[i].n1p > maxn ? q.job[i].n1p : maxn;
+    maxks = q.job[i].kslices > maxks ? q.job[i].kslices : maxks;
+  }
+  q.nsl = (maxn + 63) / 64;
+  if (q.nsl == 0 || maxks == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((q.T + 63) / 64), maxks, q.njobs * q.nsl);
+  if (dtype_bf16) hipLaunchKernelGGL(rowproj_kernel<bf16_t>, grid, dim3(256), 0, stream, q);
+  else hipLaunchKernelGGL(rowproj_kernel<float>, grid, dim3(256), 0, stream, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_finish(const ProjFinishParams& p, int dtype_bf16, hipStream_t stream) {
+  if (p.njobs <= 0) return hipSuccess;
+  int64_t maxt = 0;
   int maxn = 0;
-  for (int i = 0; i < p.njobs; ++i) maxn = p.job[i].n1p > maxn ? p.job[i].n1p : maxn;
-  dim3 grid(static_cast<unsigned>((p.T + 15) / 16), p.njobs, (maxn + 127) / 128);
-  if (dtype_bf16) hipLaunchKernelGGL(rowproj_kernel<bf16_t>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(rowproj_kernel<float>, grid, dim3(256), 0, stream, p);
+  for (int i = 0; i < p.njobs; ++i) {
+    const int64_t t = p.job[i].outT ? p.job[i].ldT : p.T;
+    maxt = t > maxt ? t : maxt;
+    maxn = p.job[i].n1p > maxn ? p.job[i].n1p : maxn;
+  }
+  if (maxt <= 0 || maxn <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((maxt + 15) / 16), (maxn + 63) / 64, p.njobs);
+  if (dtype_bf16) hipLaunchKernelGGL(proj_finish_kernel<bf16_t>, grid, dim3(64), 0, stream, p);
+  else hipLaunchKernelGGL(proj_finish_kernel<float>, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_colproj(const ColProjParams& p, int dtype_bf16, hipStream_t stream) {
   if (p.T <= 0 || p.njobs <= 0) return hipSuccess;
-  int maxb = 0;
+  int maxb = 0, maxfr = 0;
   for (int i = 0; i < p.njobs; ++i) {
-    const int nb = p.job[i].kblocks * p.job[i].ntb * p.job[i].nchunks;
+    const ColProjJob& j = p.job[i];
+    const int nb = j.kblocks * j.ntb * j.nchunks;
     maxb = nb > maxb ? nb : maxb;
+    const int fr = (j.n2p < 128 ? j.n2p : 128) / 16;
+    maxfr = fr > maxfr ? fr : maxfr;
   }
   if (maxb == 0) return hipSuccess;
   dim3 grid(maxb, 1, p.njobs);
-  if (dtype_bf16) hipLaunchKernelGGL(colproj_kernel<bf16_t>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(colproj_kernel<float>, grid, dim3(256), 0, stream, p);
+  if (!dtype_bf16) hipLaunchKernelGGL(colproj_f32_kernel<float>, grid, dim3(256), 0, stream, p);
+  else if (maxfr <= 4) hipLaunchKernelGGL(colproj_bf16_kernel<1>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(colproj_bf16_kernel<2>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream) {
   if (p.njobs <= 0) return hipSuccess;
-  int64_t maxn = 0;
-  for (int i = 0; i < p.njobs; ++i) maxn = p.job[i].rows * p.job[i].cols > maxn ? p.job[i].rows * p.job[i].cols : maxn;
-  if (maxn == 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_kernel, dim3(grid_for(maxn), p.njobs), dim3(256), 0, stream, p);
+  int64_t maxr = 0, maxc = 0;
+  for (int i = 0; i < p.njobs; ++i) {
+    maxr = p.job[i].rows > maxr ? p.job[i].rows : maxr;
+    maxc = p.job[i].cols > maxc ? p.job[i].cols : maxc;
+  }
+  if (maxr == 0 || maxc == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((maxr + 63) / 64), static_cast<unsigned>((maxc + 63) / 64), p.njobs);
+  hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
