@@ -42,6 +42,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// The same rounding as pack_bf16x2 as one packed convert (gfx950
+// v_cvt_pk_bf16_f32); used by the 4-bit decode inside the GEMM K loop.
+__device__ __forceinline__ uint32_t pack_bf16x2_pk(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // ---------------------------------------------------------------------------
 // element traits: CH = elements per 16-byte chunk
 
@@ -132,7 +141,7 @@ __device__ __forceinline__ uint32_t dq_pair(uint32_t byte2, float sc) {
   // byte2 holds two codes: low nibble = even element
   const int q0 = static_cast<int>(byte2 << 28) >> 28;
   const int q1 = static_cast<int>((byte2 >> 4) << 28) >> 28;
-  return pack_bf16x2(static_cast<float>(q0) * sc, static_cast<float>(q1) * sc);
+  return pack_bf16x2_pk(static_cast<float>(q0) * sc, static_cast<float>(q1) * sc);
 }
 __device__ __forceinline__ uint4 dq_chunk(uint32_t w, float sc) {
   // w = 4 bytes = 8 codes -> 8 bf16

@@ -260,6 +260,12 @@ __device__ __forceinline__ void pipeline_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[
 constexpr int EP_PITCH_C = 256 * 2 + 16;   // bf16 [256 rows][256]
 constexpr int EP_PITCH_GU = 128 * 2 + 16;  // bf16 [256 rows][128], G and U side by side
 constexpr int EP_PITCH_DZ = 256 * 4 + 16;  // fp32 [128 rows][256], one half of dZ at a time
+// LDS the staging needs: a kernel's shared array must be at least this large
+constexpr int EP_LDS_BYTES = 256 * EP_PITCH_C > 2 * 256 * EP_PITCH_GU
+                                 ? (256 * EP_PITCH_C > 128 * EP_PITCH_DZ ? 256 * EP_PITCH_C : 128 * EP_PITCH_DZ)
+                                 : (2 * 256 * EP_PITCH_GU > 128 * EP_PITCH_DZ ? 2 * 256 * EP_PITCH_GU
+                                                                             : 128 * EP_PITCH_DZ);
+static_assert(STAGES * STAGE_BYTES >= EP_LDS_BYTES, "the dense ring must hold the epilogue staging");
 
 __device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -421,18 +427,10 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
   }
 }
 
-template <bool NN, int EPI>
-__device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
-
-  TileCtx t;
-  t.lane = threadIdx.x & 63;
-  t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  t.c1 = (t.lane & 3) ^ ((t.lane >> 4) & 3);
-  const int wm = t.wave >> 1;
-  const int wn = t.wave & 1;
-
-  // ---- tile selection: XCD-aware (block b runs on XCD b % 8), grouped along M
+// Output tile of this workgroup: XCD-aware (block b runs on XCD b % 8), each
+// XCD sweeping bands of group_m tiles along M so that its L2 reuses B panels.
+template <int EPI>
+__device__ __forceinline__ void select_tile(const GemmParams& p, TileCtx& t) {
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
   const int per = nblk / 8, rem = nblk % 8, x = bid % 8;
@@ -451,6 +449,21 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   t.m_rows = static_cast<uint32_t>(min<int64_t>(BM, p.M - t.m0));
   t.n_rows = static_cast<uint32_t>(EPI == EPI_SWIGLU_FWD ? min<int64_t>(BN / 2, p.N - t.j0)
                                                          : min<int64_t>(BN, p.N - t.n0));
+
+}
+
+template <bool NN, int EPI>
+__device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+
+  TileCtx t;
+  t.lane = threadIdx.x & 63;
+  t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  t.c1 = (t.lane & 3) ^ ((t.lane >> 4) & 3);
+  const int wm = t.wave >> 1;
+  const int wn = t.wave & 1;
+
+  select_tile<EPI>(p, t);
 
   const Seg s0 = seg_at(p, 0), s1 = seg_at(p, 1), s2 = seg_at(p, 2);
   int nk = (s0.K + BK - 1) / BK + (s1.K + BK - 1) / BK + (s2.K + BK - 1) / BK;
@@ -509,6 +522,240 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmParams p) {
   gemm_bf16_body<NN, EPI>(p);
 }
 
+// ---- 4-bit B operand (NT products with 4-bit block weights) ---------------
+// The weight panel arrives in LDS as codes and scales and is decoded into the
+// MFMA B fragments as they are read:
+//  * ring stage (24 KB): the A tile (16 KB, as in the dense kernel); the codes
+//    [256 packed rows][16 bytes] (one DMA per wave, lane = row); the fp32
+//    scales of the k-tile's 64-block, one 1 KB slot per wave (64 rows; lanes
+//    0-15 carry four rows each, the rest of the slot reads zero).
+//  * a B fragment (tile row R, k-chunk lane >> 4) is one 4-byte code word and
+//    the row's scale, decoded to 8 bf16 by the block rule of the 4-bit
+//    format, w = bf16_rne(q * scale), exact in fp32 before the one rounding
+//    (dq_chunk). Each fragment feeds 8 MFMAs, so the decode (about 30 VALU
+//    instructions per fragment) runs in the shadow of the matrix pipe.
+// Packed row order: gate/up tiles hold gate rows j0 .. j0+127 in packed rows
+// 0-127 and the up rows in 128-255 (waves 0-1 fetch gate, 2-3 up); the tile
+// row R the MFMAs see interleaves them every 16 rows as in the dense kernel.
+// The adapter segment (dense bf16) follows the 4-bit loop as a short
+// unpipelined tail.
+constexpr int Q4_CODES = TILE_BYTES;          // offset of the codes in a stage
+constexpr int Q4_SCALES = TILE_BYTES + 4096;  // offset of the scale slots
+constexpr int Q4_STAGE = TILE_BYTES + 8192;   // 24 KB
+constexpr int Q4_STAGES = 5;
+constexpr int Q4_RING = Q4_STAGES * Q4_STAGE;  // 120 KB
+// the epilogue stages through the same LDS after the loop
+constexpr int Q4_LDS = Q4_RING > EP_LDS_BYTES ? Q4_RING : EP_LDS_BYTES;
+
+struct Q4Dma {
+  rsrc_t rA;            // activation panel of this tile row block
+  uint32_t offA[4];
+  uint32_t lda_b;
+  const char* codes;    // first packed row of this wave's 64 rows
+  uint32_t ldq_b;       // bytes per packed row (K / 2)
+  uint32_t qrows;       // valid rows of this wave's 64 (0 or 64)
+  const char* scales;   // fp32 [K/64][N] at this wave's first row
+  uint32_t ld_sc_b;     // bytes per scale block row (N * 4)
+  int k0, kt;
+};
+
+template <int EPI>
+__device__ __forceinline__ void q4_dma_init(Q4Dma& d, const GemmParams& p, const TileCtx& t) {
+  const GemmSeg& g = p.seg[0];
+  d.lda_b = static_cast<uint32_t>(g.lda * 2);
+  d.rA = make_rsrc(static_cast<const char*>(g.a) + t.m0 * d.lda_b, t.m_rows * d.lda_b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d.offA[i] = static_cast<uint32_t>(64 * t.wave + 16 * i + (t.lane >> 2)) * d.lda_b + (t.c1 << 4);
+  d.ldq_b = static_cast<uint32_t>(g.ldb / 2);
+  const bool up = EPI == EPI_SWIGLU_FWD && t.wave >= 2;
+  const int64_t row0 = EPI == EPI_SWIGLU_FWD ? t.j0 + 64 * (t.wave & 1) : t.n0 + 64 * t.wave;
+  d.qrows = row0 < p.N ? 64u : 0u;  // N and row0 are multiples of 64
+  d.codes = static_cast<const char*>(up ? g.b1 : g.b0) + row0 * d.ldq_b;
+  d.scales = static_cast<const char*>(up ? g.bs1 : g.bs0) + row0 * 4;
+  d.ld_sc_b = static_cast<uint32_t>(p.N * 4);
+  d.k0 = 0;
+  d.kt = 0;
+}
+
+// DMA instruction j (0..5) of k-tile d.kt into stage `st`: 0-3 the A tile,
+// 4 the codes, 5 the scales. Past the last 4-bit k-tile everything reads zero.
+__device__ __forceinline__ void q4_dma_issue(const Q4Dma& d, int j, char* st, int nkq, const TileCtx& t) {
+  const bool live = d.kt < nkq;
+  if (j < 4) {
+    dma16(d.rA, st + (64 * t.wave + 16 * j) * 64, live ? d.offA[j] : OOB, d.k0 * 2);
+  } else if (j == 4) {
+    const rsrc_t r = make_rsrc(d.codes, (live ? d.qrows : 0u) * d.ldq_b);
+    dma16(r, st + Q4_CODES + t.wave * 1024, static_cast<uint32_t>(t.lane) * d.ldq_b, d.k0 / 2);
+  } else {
+    // one descriptor per 64-block row, so the range check covers exactly
+    // this wave's 64 scales
+    const rsrc_t r = make_rsrc(d.scales + static_cast<int64_t>(d.k0 / 64) * d.ld_sc_b, live ? d.qrows * 4 : 0u);
+    dma16(r, st + Q4_SCALES + t.wave * 1024, t.lane < 16 ? static_cast<uint32_t>(t.lane) * 16 : OOB, 0);
+  }
+}
+
+__device__ __forceinline__ void q4_dma_advance(Q4Dma& d) {
+  ++d.kt;
+  d.k0 += BK;
+}
+
+// Lane-constant parts of a 4-bit fragment read: packed row of tile row
+// R = wn*128 + 16b + (lane & 15) and its k-chunk lane >> 4. With the gate/up
+// interleave, R's packed row is (R >> 4 & 1) * 128 + (R >> 5) * 16 + (R & 15);
+// for b = 2q + h that is h*128 + wn*64 + 16q + (lane & 15).
+struct Q4Read {
+  uint32_t code0;  // byte offset of fragment b = 0's code word in a stage
+  uint32_t sc0;    // byte offset of fragment b = 0's scale in a stage
+};
+
+template <int EPI>
+__device__ __forceinline__ Q4Read q4_read_ctx(int wn, int lane) {
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int pr = EPI == EPI_SWIGLU_FWD ? wn * 64 + lrow : wn * 128 + lrow;
+  Q4Read q;
+  q.code0 = static_cast<uint32_t>(Q4_CODES + pr * 16 + lgrp * 4);
+  q.sc0 = static_cast<uint32_t>(Q4_SCALES + (pr >> 6) * 1024 + (pr & 63) * 4);
+  return q;
+}
+
+// packed-row offset of fragment b relative to fragment 0
+template <int EPI>
+__device__ __forceinline__ int q4_frag_row(int b) {
+  return EPI == EPI_SWIGLU_FWD ? (b & 1) * 128 + (b >> 1) * 16 : b * 16;
+}
+
+template <int EPI>
+__device__ __forceinline__ uint4 read_bq(const Q4Read& q, const char* st, int b) {
+  const int dr = q4_frag_row<EPI>(b);
+  const uint32_t codes = *reinterpret_cast<const uint32_t*>(st + q.code0 + dr * 16);
+  // the scale slot of packed row pr + dr: rows never cross a 64-row slot
+  // within one fragment set (dr keeps pr's position inside its 16-row group)
+  const float sc = *reinterpret_cast<const float*>(st + q.sc0 + (dr >> 6) * 1024 + (dr & 63) * 4);
+  return dq_chunk(codes, sc);
+}
+
+// One 4-bit k-tile: the dense pipeline with 6 DMA instructions per wave and
+// decoded B fragments.
+template <int EPI>
+__device__ __forceinline__ void q4_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[8], const uint4 (&fb)[8],
+                                        uint4 (&fbn)[8], Q4Dma& d, int& st_cur, char* smem, const ReadCtx& rc,
+                                        const Q4Read& qr, const TileCtx& t, int nkq) {
+  const int st_nxt = st_cur + 1 == Q4_STAGES ? 0 : st_cur + 1;
+  const int st_dma = st_cur == 0 ? Q4_STAGES - 1 : st_cur - 1;  // tile kt-1's stage
+  const char* nxt = smem + st_nxt * Q4_STAGE;
+  char* dbuf = smem + st_dma * Q4_STAGE;
+  mfma_group(acc, 0, fa, fb);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<6 * (Q4_STAGES - 3)>();  // DMA of tile kt+1 landed (this wave)
+  __syncthreads();
+#pragma unroll
+  for (int g = 1; g < 8; ++g) {
+    mfma_group(acc, g, fa, fb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g <= 6) q4_dma_issue(d, g - 1, dbuf, nkq, t);
+    fa[g - 1] = read_a(rc, nxt, g - 1);
+    if (g <= 4) {
+      fbn[2 * g - 2] = read_bq<EPI>(qr, nxt, 2 * g - 2);
+      fbn[2 * g - 1] = read_bq<EPI>(qr, nxt, 2 * g - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  q4_dma_advance(d);
+  fa[7] = read_a(rc, nxt, 7);
+  __builtin_amdgcn_sched_barrier(0);
+  st_cur = st_nxt;
+}
+
+template <int EPI>
+__device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
+  __shared__ __attribute__((aligned(1024))) char smem[Q4_LDS];
+
+  TileCtx t;
+  t.lane = threadIdx.x & 63;
+  t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  t.c1 = (t.lane & 3) ^ ((t.lane >> 4) & 3);
+  const int wm = t.wave >> 1;
+  const int wn = t.wave & 1;
+  select_tile<EPI>(p, t);
+
+  const int nkq = static_cast<int>(p.seg[0].K / BK);  // K is a multiple of 64
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int lrow = t.lane & 15;
+  const int lgrp = t.lane >> 4;
+  ReadCtx rc;
+  rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
+  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
+  rc.nsw = 0;
+  rc.rdN = 0;
+  const Q4Read qr = q4_read_ctx<EPI>(wn, t.lane);
+
+  // ---- prologue: DMA of tiles 0 .. Q4_STAGES-2, then tile 0's fragments
+  Q4Dma d;
+  q4_dma_init<EPI>(d, p, t);
+#pragma unroll
+  for (int s = 0; s < Q4_STAGES - 1; ++s) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) q4_dma_issue(d, j, smem + s * Q4_STAGE, nkq, t);
+    q4_dma_advance(d);
+  }
+  wait_vmcnt<6 * (Q4_STAGES - 2)>();  // tile 0 landed (this wave)
+  __syncthreads();
+  uint4 fa[8], fbA[8], fbB[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) fbA[b] = read_bq<EPI>(qr, smem, b);
+#pragma unroll
+  for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, a);
+
+  int st_cur = 0;
+  // one k-tile per trip: with the decode in the groups, a two-tile body
+  // makes the register allocator shuffle the accumulators every trip; the
+  // copy of the next B fragments (32 moves) is the cheaper price
+  for (int kt = 0; kt < nkq; ++kt) {
+    q4_tile<EPI>(acc, fa, fbA, fbB, d, st_cur, smem, rc, qr, t, nkq);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) fbA[b] = fbB[b];
+  }
+  wait_vmcnt<0>();
+
+  // ---- adapter segment: dense bf16 k-tiles, one at a time
+  if (p.nseg > 1 && p.seg[1].K > 0) {
+    const Seg s1 = seg_at(p, 1);
+    Dma da;
+    da.seg = 1;
+    da.kt = 0;
+    da.k0 = 0;
+    dma_load_seg<false, EPI>(da, s1, t);
+    for (int k0 = 0; k0 < s1.K; k0 += BK) {
+      __syncthreads();  // every wave is done with the LDS it is about to reuse
+      da.k0 = k0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dma_issue<false, EPI>(da, j, smem, 1, t);
+      wait_vmcnt<0>();
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < 8; ++b) fbA[b] = read_b<false>(rc, smem, b);
+#pragma unroll
+      for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, a);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) mfma_group(acc, g, fa, fbA);
+    }
+  }
+
+  epilogue_lds<EPI>(p, acc, t, wm, wn, smem);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_q4_kernel(GemmParams p) {
+  gemm_q4_body<EPI>(p);
+}
+
 }  // namespace
 
 template <bool NN, int EPI>
@@ -522,6 +769,25 @@ static hipError_t launch_t(GemmParams p, hipStream_t stream) {
   if (nblk == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_bf16_kernel<NN, EPI>), dim3(nblk), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_q4(GemmParams p, hipStream_t stream) {
+  p.tiles_m = static_cast<int>((p.M + BM - 1) / BM);
+  p.tiles_n = EPI == EPI_SWIGLU_FWD ? static_cast<int>((p.N + BN / 2 - 1) / (BN / 2))
+                                    : static_cast<int>((p.N + BN - 1) / BN);
+  if (p.group_m <= 0) p.group_m = 8;
+  if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
+  const int nblk = p.tiles_m * p.tiles_n;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_q4_kernel<EPI>), dim3(nblk), dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_q4(const GemmParams& p, int epi, hipStream_t stream) {
+  if (epi == EPI_STORE) return launch_q4<EPI_STORE>(p, stream);
+  if (epi == EPI_SWIGLU_FWD) return launch_q4<EPI_SWIGLU_FWD>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t stream) {

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
 #include <stdint.h>
 
 namespace lmlp {
@@ -39,6 +40,11 @@ struct GemmParams {
 hipError_t launch_gemm(const GemmParams& p, int dtype_bf16, int nn, int epi, hipStream_t stream);
 // dense bf16 operands only (LDS-DMA staging); needs every row stride * 256 < 2^31 bytes
 hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t stream);
+// NT products whose segment-0 B operand is 4-bit: seg[0].b0/b1 hold the codes
+// ([N][K/2] bytes, seg[0].ldb = K codes per row), seg[0].bs0/bs1 the block
+// scales as fp32 [K/64][N]; K and N multiples of 64. Segment 1 (the
+// adapter) is dense bf16.
+hipError_t launch_gemm_q4(const GemmParams& p, int epi, hipStream_t stream);
 
 // Row projection, split along K: part[ks][t][n] = sum over k in slice ks of
 // X[t][k] * W[n][k] (slice ks = [ks*kb, (ks+1)*kb)), for up to two jobs per
@@ -149,6 +155,19 @@ struct PackParams {
   int32_t pad_;
 };
 hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream);
+
+// fp16 block scales [rows][nb] -> fp32 [nb][ld_dst]
+struct ScalePackJob {
+  const __half* src;
+  float* dst;
+  int64_t rows, nb, ld_dst;
+};
+struct ScalePackParams {
+  ScalePackJob job[3];
+  int32_t njobs;
+  int32_t pad_;
+};
+hipError_t launch_scale_pack(const ScalePackParams& p, hipStream_t stream);
 
 // 4-bit block weight -> bf16 (same decode as the GEMM loaders).
 hipError_t launch_dequant_int4(const void* packed, const void* scales, int64_t out, int64_t in,

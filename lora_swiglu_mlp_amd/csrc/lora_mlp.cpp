@@ -21,6 +21,7 @@
 // section 训练侧).
 #include "../../include/lora_mlp.h"
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -145,7 +146,7 @@ int64_t colproj_tr(int64_t T, int ntb) {
 int64_t ld_tok(const Dims& d) { return (d.T + 63) / 64 * 64; }  // token-contiguous rows
 
 struct FwdLayout {
-  size_t z, aext_gu, aext_d, agu_pad, ad_pad, bext_g, bext_u, bext_d, rp_part, total;
+  size_t z, aext_gu, aext_d, agu_pad, ad_pad, bext_g, bext_u, bext_d, rp_part, sc_g, sc_u, sc_d, total;
 };
 FwdLayout fwd_layout(const Dims& d) {
   Carver c;
@@ -159,13 +160,17 @@ FwdLayout fwd_layout(const Dims& d) {
   L.bext_u = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.bext_d = c.take(size_t(d.H) * d.r16 * d.eb);
   L.rp_part = c.take(std::max(rp_part_bytes(d, d.H, int(2 * d.r16)), rp_part_bytes(d, d.I, int(d.r16))));
+  // 4-bit weights: block scales as fp32, block-major ([in/64][out])
+  L.sc_g = d.int4 ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
+  L.sc_u = d.int4 ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
+  L.sc_d = d.int4 ? c.take(size_t(d.I / 64) * d.H * 4 + 16) : 0;
   L.total = c.off;
   return L;
 }
 
 struct BwdLayout {
   size_t dg, du, z, qd, aext_d, qgu, aext_gu, bdT, bgT, buT, ad_pad, agu_pad;
-  size_t rp_a, rp_b, pguT, pdT, qdT, qguT;
+  size_t rp_a, rp_b, pguT, pdT, qdT, qguT, wq_g, wq_u, wq_d;
   size_t part_dg, part_du, part_z, part_x, part_dy, total;
   int ntb;
   int64_t tr;
@@ -197,6 +202,10 @@ BwdLayout bwd_layout(const Dims& d) {
   L.pdT = c.take(d.r16 * trow);
   L.qdT = c.take(d.r16 * trow);
   L.qguT = c.take(2 * d.r16 * trow);
+  // 4-bit weights: bf16 copies for the NN products (decoded once per call)
+  L.wq_g = d.int4 ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.wq_u = d.int4 ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.wq_d = d.int4 ? c.take(size_t(d.H) * d.I * 2) : 0;
   L.part_dg = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
   L.part_du = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
   L.part_z = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
@@ -320,10 +329,13 @@ struct ProfScope {
 
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
-// dense bf16 products take the LDS-DMA kernel; fp32 and 4-bit weights the general one
+// bf16 products take the LDS-DMA kernels (4-bit NT weights: the decoding
+// variant); fp32 products the general kernel. The NN products of 4-bit
+// weights run on bf16 copies decoded once per backward call.
 hipError_t run_gemm(const GemmParams& p, const Dims& d, int nn, int epi, hipStream_t st) {
-  if (d.bf16 && !d.int4) return launch_gemm_bf16(p, nn, epi, st);
-  return launch_gemm(p, d.bf16, nn, epi, st);
+  if (!d.bf16) return launch_gemm(p, 0, nn, epi, st);
+  if (p.seg[0].bint4) return launch_gemm_q4(p, epi, st);
+  return launch_gemm_bf16(p, nn, epi, st);
 }
 
 PackJob pack_job(void* dst, int64_t ld_dst, int64_t rows, int64_t cols, const void* src, int64_t ld_src,
@@ -507,6 +519,17 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   pk.job[6] = pack_job(bext_d, r16, H, r16, b_down, r, H, r, false);
   pk.njobs = 7;
   LMLP_LAUNCH("pack(fwd)", launch_pack(pk, eb, st));
+  float* sc_g = d.int4 ? reinterpret_cast<float*>(at(workspace, FL.sc_g)) : nullptr;
+  float* sc_u = d.int4 ? reinterpret_cast<float*>(at(workspace, FL.sc_u)) : nullptr;
+  float* sc_d = d.int4 ? reinterpret_cast<float*>(at(workspace, FL.sc_d)) : nullptr;
+  if (d.int4) {
+    ScalePackParams sp{};
+    sp.job[0] = {static_cast<const __half*>(w_gate_scales), sc_g, I, H / 64, I};
+    sp.job[1] = {static_cast<const __half*>(w_up_scales), sc_u, I, H / 64, I};
+    sp.job[2] = {static_cast<const __half*>(w_down_scales), sc_d, H, I / 64, H};
+    sp.njobs = 3;
+    LMLP_LAUNCH("pack(scales)", launch_scale_pack(sp, st));
+  }
 
   float* rpp = reinterpret_cast<float*>(at(workspace, FL.rp_part));
   RowProjParams rp{};
@@ -523,7 +546,7 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
 
   GemmParams gp{};
   gp.nseg = 2;
-  gp.seg[0] = seg(x, H, w_gate, w_up, H, H, d.int4, w_gate_scales, w_up_scales);
+  gp.seg[0] = seg(x, H, w_gate, w_up, H, H, d.int4, sc_g, sc_u);
   gp.seg[1] = seg(aext_gu, 2 * r16, bext_g, bext_u, 2 * r16, 2 * r16);
   gp.M = T;
   gp.N = I;
@@ -541,7 +564,7 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
 
   GemmParams gd{};
   gd.nseg = 2;
-  gd.seg[0] = seg(Z, I, w_down, nullptr, I, I, d.int4, w_down_scales, nullptr);
+  gd.seg[0] = seg(Z, I, w_down, nullptr, I, I, d.int4, sc_d, nullptr);
   gd.seg[1] = seg(aext_d, r16, bext_d, nullptr, r16, r16);
   gd.M = T;
   gd.N = H;
@@ -640,6 +663,20 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   pk.job[5] = pack_job(agu_pad + size_t(r16) * H * eb, H, r16, H, a_up, H, r, H, false);
   pk.njobs = 6;
   LMLP_LAUNCH("pack(bwd)", launch_pack(pk, eb, st));
+  const void* wg = w_gate;
+  const void* wu = w_up;
+  const void* wd = w_down;
+  if (d.int4) {
+    char* wq_g = at(workspace, BL.wq_g);
+    char* wq_u = at(workspace, BL.wq_u);
+    char* wq_d = at(workspace, BL.wq_d);
+    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_gate, w_gate_scales, I, H, wq_g, st));
+    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_up, w_up_scales, I, H, wq_u, st));
+    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_down, w_down_scales, H, I, wq_d, st));
+    wg = wq_g;
+    wu = wq_u;
+    wd = wq_d;
+  }
 
   RowProjParams rp{};
   rp.T = T;
@@ -660,7 +697,7 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
 
   GemmParams gz{};
   gz.nseg = 2;
-  gz.seg[0] = seg(dy, H, w_down, nullptr, I, H, d.int4, w_down_scales, nullptr);
+  gz.seg[0] = seg(dy, H, wd, nullptr, I, H);
   gz.seg[1] = seg(aext_d, r16, ad_pad, nullptr, I, r16);
   gz.M = T;
   gz.N = I;
@@ -685,8 +722,8 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
 
   GemmParams gx{};
   gx.nseg = 3;
-  gx.seg[0] = seg(dG, I, w_gate, nullptr, H, I, d.int4, w_gate_scales, nullptr);
-  gx.seg[1] = seg(dU, I, w_up, nullptr, H, I, d.int4, w_up_scales, nullptr);
+  gx.seg[0] = seg(dG, I, wg, nullptr, H, I);
+  gx.seg[1] = seg(dU, I, wu, nullptr, H, I);
   gx.seg[2] = seg(aext_gu, 2 * r16, agu_pad, nullptr, H, 2 * r16);
   gx.M = T;
   gx.N = H;

@@ -463,6 +463,19 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// fp16 block scales [rows][nb] -> fp32 [nb][ld_dst] (block-major), so that
+// the scales of one k-block of consecutive weight rows are contiguous.
+__global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackParams p) {
+  const ScalePackJob& jb = p.job[blockIdx.y];
+  const int64_t n = jb.rows * jb.nb;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < n;
+       idx += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t b = idx / jb.rows, r = idx % jb.rows;
+    jb.dst[b * jb.ld_dst + r] = __half2float(jb.src[r * jb.nb + b]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 8 codes (4 bytes) -> 8 bf16 (16 bytes) per thread iteration
 __global__ __launch_bounds__(256) void dequant_int4_kernel(const uint8_t* packed, const __half* scales,
                                                            int64_t out, int64_t in, uint4* w) {
@@ -556,6 +569,15 @@ hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream) 
   dim3 grid(grid_for(maxn), p.njobs);
   if (elem_bytes == 2) hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(pack_kernel<uint32_t>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_pack(const ScalePackParams& p, hipStream_t stream) {
+  if (p.njobs <= 0) return hipSuccess;
+  int64_t maxn = 0;
+  for (int i = 0; i < p.njobs; ++i) maxn = p.job[i].rows * p.job[i].nb > maxn ? p.job[i].rows * p.job[i].nb : maxn;
+  if (maxn == 0) return hipSuccess;
+  hipLaunchKernelGGL(scale_pack_kernel, dim3(grid_for(maxn), p.njobs), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
