@@ -61,6 +61,13 @@ typedef enum { LMLP_W_DENSE = 0, LMLP_W_INT4_B64 = 1 } lmlp_wfmt;
 
 /* flags */
 #define LMLP_CONSUME_SAVED 0x1u /* backward may overwrite `saved` (saves 2*T*I elements of workspace) */
+/* 4-bit weights only. Without this flag, each call decodes the three weights
+ * once into bf16 copies in the workspace and runs the dense bf16 products
+ * (fastest; the workspace grows by 2*(2*I*H + H*I) bytes). With it, the
+ * forward products decode the 4-bit codes inside their operand staging
+ * instead (no bf16 copies in the forward workspace; slower). Backward always
+ * uses the bf16 copies for its two products with the transposed weights. */
+#define LMLP_INT4_INKERNEL 0x2u
 
 typedef struct {
   int64_t tokens;  /* T >= 0 (T == 0: forward is a no-op, backward writes zero adapter gradients) */
@@ -70,7 +77,7 @@ typedef struct {
   float scale;     /* s = alpha / r, finite */
   int32_t dtype;   /* lmlp_dtype */
   int32_t wfmt;    /* lmlp_wfmt */
-  uint32_t flags;  /* LMLP_CONSUME_SAVED or 0 */
+  uint32_t flags;  /* bitwise OR of LMLP_CONSUME_SAVED, LMLP_INT4_INKERNEL, or 0 */
 } lmlp_dims;
 
 /* Bytes of the forward->backward `saved` buffer: the gate and up

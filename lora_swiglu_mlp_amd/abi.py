@@ -21,6 +21,7 @@ LMLP_OK, LMLP_ERR_INVALID_ARG, LMLP_ERR_UNSUPPORTED, LMLP_ERR_WORKSPACE, LMLP_ER
 LMLP_F32, LMLP_BF16 = 0, 1
 LMLP_W_DENSE, LMLP_W_INT4_B64 = 0, 1
 LMLP_CONSUME_SAVED = 0x1
+LMLP_INT4_INKERNEL = 0x2
 
 
 class lmlp_dims(ctypes.Structure):

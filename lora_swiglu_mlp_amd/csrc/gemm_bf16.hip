@@ -523,29 +523,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmParams p) {
 }
 
 // ---- 4-bit B operand (NT products with 4-bit block weights) ---------------
-// The weight panel arrives in LDS as codes and scales and is decoded into the
-// MFMA B fragments as they are read:
+// The weight panel arrives as codes and scales and is decoded in LDS:
 //  * ring stage (24 KB): the A tile (16 KB, as in the dense kernel); the codes
 //    [256 packed rows][16 bytes] (one DMA per wave, lane = row); the fp32
-//    scales of the k-tile's 64-block, one 1 KB slot per wave (64 rows; lanes
+//    scales of the k-tile's 64-block, one 1 KB slot per wave (64 rows, lanes
 //    0-15 carry four rows each, the rest of the slot reads zero).
-//  * a B fragment (tile row R, k-chunk lane >> 4) is one 4-byte code word and
-//    the row's scale, decoded to 8 bf16 by the block rule of the 4-bit
-//    format, w = bf16_rne(q * scale), exact in fp32 before the one rounding
-//    (dq_chunk). Each fragment feeds 8 MFMAs, so the decode (about 30 VALU
-//    instructions per fragment) runs in the shadow of the matrix pipe.
+//  * two decoded B tiles (16 KB each, the dense K-major layout) outside the
+//    ring. During k-tile kt every thread decodes one packed row of tile kt+2
+//    (a row its own wave fetched, so only its own vmcnt wait is needed) into
+//    buffer kt & 1, while the waves read tile kt+1's B fragments from buffer
+//    (kt + 1) & 1; the barrier of tile kt+1 publishes the decoded rows.
+//    Each packed row is decoded once per workgroup (decoding inside the
+//    fragment reads would repeat it in both waves of a B half; measured
+//    about 8% slower at the Llama-3-8B shapes).
 // Packed row order: gate/up tiles hold gate rows j0 .. j0+127 in packed rows
-// 0-127 and the up rows in 128-255 (waves 0-1 fetch gate, 2-3 up); the tile
-// row R the MFMAs see interleaves them every 16 rows as in the dense kernel.
+// 0-127 and the up rows in 128-255 (waves 0-1 fetch gate, 2-3 up); the
+// decoded tile interleaves them every 16 rows as the dense kernel does.
+// Decoding is the block rule of the 4-bit format: w = bf16_rne(q * scale),
+// exact in fp32 before the one rounding (dq_chunk).
 // The adapter segment (dense bf16) follows the 4-bit loop as a short
 // unpipelined tail.
-constexpr int Q4_CODES = TILE_BYTES;          // offset of the codes in a stage
-constexpr int Q4_SCALES = TILE_BYTES + 4096;  // offset of the scale slots
-constexpr int Q4_STAGE = TILE_BYTES + 8192;   // 24 KB
+constexpr int Q4_CODES = TILE_BYTES;             // offset of the codes in a stage
+constexpr int Q4_SCALES = TILE_BYTES + 4096;     // offset of the scale slots
+constexpr int Q4_STAGE = TILE_BYTES + 8192;      // 24 KB
 constexpr int Q4_STAGES = 5;
-constexpr int Q4_RING = Q4_STAGES * Q4_STAGE;  // 120 KB
-// the epilogue stages through the same LDS after the loop
-constexpr int Q4_LDS = Q4_RING > EP_LDS_BYTES ? Q4_RING : EP_LDS_BYTES;
+constexpr int Q4_DEC = Q4_STAGES * Q4_STAGE;     // decoded B tiles start here
+constexpr int Q4_LDS0 = Q4_DEC + 2 * TILE_BYTES;  // 152 KB
+constexpr int Q4_LDS = Q4_LDS0 > EP_LDS_BYTES ? Q4_LDS0 : EP_LDS_BYTES;
 
 struct Q4Dma {
   rsrc_t rA;            // activation panel of this tile row block
@@ -588,8 +592,8 @@ __device__ __forceinline__ void q4_dma_issue(const Q4Dma& d, int j, char* st, in
     const rsrc_t r = make_rsrc(d.codes, (live ? d.qrows : 0u) * d.ldq_b);
     dma16(r, st + Q4_CODES + t.wave * 1024, static_cast<uint32_t>(t.lane) * d.ldq_b, d.k0 / 2);
   } else {
-    // one descriptor per 64-block row, so the range check covers exactly
-    // this wave's 64 scales
+    // the 64-block of this k-tile: one descriptor per block row, so the
+    // range check covers exactly this wave's 64 scales
     const rsrc_t r = make_rsrc(d.scales + static_cast<int64_t>(d.k0 / 64) * d.ld_sc_b, live ? d.qrows * 4 : 0u);
     dma16(r, st + Q4_SCALES + t.wave * 1024, t.lane < 16 ? static_cast<uint32_t>(t.lane) * 16 : OOB, 0);
   }
@@ -600,55 +604,43 @@ __device__ __forceinline__ void q4_dma_advance(Q4Dma& d) {
   d.k0 += BK;
 }
 
-// Lane-constant parts of a 4-bit fragment read: packed row of tile row
-// R = wn*128 + 16b + (lane & 15) and its k-chunk lane >> 4. With the gate/up
-// interleave, R's packed row is (R >> 4 & 1) * 128 + (R >> 5) * 16 + (R & 15);
-// for b = 2q + h that is h*128 + wn*64 + 16q + (lane & 15).
-struct Q4Read {
-  uint32_t code0;  // byte offset of fragment b = 0's code word in a stage
-  uint32_t sc0;    // byte offset of fragment b = 0's scale in a stage
-};
-
+// decoded-tile row of packed row pr (gate/up: interleave the two panels)
 template <int EPI>
-__device__ __forceinline__ Q4Read q4_read_ctx(int wn, int lane) {
-  const int lrow = lane & 15, lgrp = lane >> 4;
-  const int pr = EPI == EPI_SWIGLU_FWD ? wn * 64 + lrow : wn * 128 + lrow;
-  Q4Read q;
-  q.code0 = static_cast<uint32_t>(Q4_CODES + pr * 16 + lgrp * 4);
-  q.sc0 = static_cast<uint32_t>(Q4_SCALES + (pr >> 6) * 1024 + (pr & 63) * 4);
-  return q;
+__device__ __forceinline__ int q4_dense_row(int pr) {
+  if (EPI != EPI_SWIGLU_FWD) return pr;
+  const int panel = pr >> 7, r = pr & 127;
+  return (r >> 4) * 32 + panel * 16 + (r & 15);
 }
 
-// packed-row offset of fragment b relative to fragment 0
+// decode chunk c (8 codes) of this thread's packed row into the decoded tile
 template <int EPI>
-__device__ __forceinline__ int q4_frag_row(int b) {
-  return EPI == EPI_SWIGLU_FWD ? (b & 1) * 128 + (b >> 1) * 16 : b * 16;
+__device__ __forceinline__ void q4_decode_chunk(char* dec, int c, uint32_t codes, float sc, int drow) {
+  *reinterpret_cast<uint4*>(dec + drow * 64 + ((c ^ ((drow >> 2) & 3)) << 4)) = dq_chunk(codes, sc);
 }
 
-template <int EPI>
-__device__ __forceinline__ uint4 read_bq(const Q4Read& q, const char* st, int b) {
-  const int dr = q4_frag_row<EPI>(b);
-  const uint32_t codes = *reinterpret_cast<const uint32_t*>(st + q.code0 + dr * 16);
-  // the scale slot of packed row pr + dr: rows never cross a 64-row slot
-  // within one fragment set (dr keeps pr's position inside its 16-row group)
-  const float sc = *reinterpret_cast<const float*>(st + q.sc0 + (dr >> 6) * 1024 + (dr & 63) * 4);
-  return dq_chunk(codes, sc);
+__device__ __forceinline__ uint4 read_bq(const ReadCtx& rc, const char* dec, int b) {
+  return *reinterpret_cast<const uint4*>(dec + rc.rdB + b * 1024);
 }
 
-// One 4-bit k-tile: the dense pipeline with 6 DMA instructions per wave and
-// decoded B fragments.
+// One 4-bit k-tile kt (stage st_cur, decoded B fragments already in fb).
 template <int EPI>
 __device__ __forceinline__ void q4_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[8], const uint4 (&fb)[8],
                                         uint4 (&fbn)[8], Q4Dma& d, int& st_cur, char* smem, const ReadCtx& rc,
-                                        const Q4Read& qr, const TileCtx& t, int nkq) {
+                                        const TileCtx& t, int nkq, int kt) {
   const int st_nxt = st_cur + 1 == Q4_STAGES ? 0 : st_cur + 1;
   const int st_dma = st_cur == 0 ? Q4_STAGES - 1 : st_cur - 1;  // tile kt-1's stage
+  const int st_dec = st_nxt + 1 == Q4_STAGES ? 0 : st_nxt + 1;  // tile kt+2's stage
   const char* nxt = smem + st_nxt * Q4_STAGE;
   char* dbuf = smem + st_dma * Q4_STAGE;
+  char* dec_w = smem + Q4_DEC + (kt & 1) * TILE_BYTES;              // tile kt+2, decoded now
+  const char* dec_r = smem + Q4_DEC + ((kt + 1) & 1) * TILE_BYTES;  // tile kt+1
   mfma_group(acc, 0, fa, fb);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<6 * (Q4_STAGES - 3)>();  // DMA of tile kt+1 landed (this wave)
+  wait_vmcnt<6>();  // tiles kt+1 and kt+2 landed (this wave); kt+3 may fly
   __syncthreads();
+  const int pr = 64 * t.wave + t.lane;
+  const char* qsrc = smem + st_dec * Q4_STAGE + Q4_CODES + pr * 16;
+  const char* ssrc = smem + st_dec * Q4_STAGE + Q4_SCALES + t.wave * 1024 + t.lane * 4;
 #pragma unroll
   for (int g = 1; g < 8; ++g) {
     mfma_group(acc, g, fa, fb);
@@ -656,9 +648,12 @@ __device__ __forceinline__ void q4_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[8], co
     if (g <= 6) q4_dma_issue(d, g - 1, dbuf, nkq, t);
     fa[g - 1] = read_a(rc, nxt, g - 1);
     if (g <= 4) {
-      fbn[2 * g - 2] = read_bq<EPI>(qr, nxt, 2 * g - 2);
-      fbn[2 * g - 1] = read_bq<EPI>(qr, nxt, 2 * g - 1);
+      fbn[2 * g - 2] = read_bq(rc, dec_r, 2 * g - 2);
+      fbn[2 * g - 1] = read_bq(rc, dec_r, 2 * g - 1);
     }
+    if (g >= 2 && g <= 5)
+      q4_decode_chunk<EPI>(dec_w, g - 2, *reinterpret_cast<const uint32_t*>(qsrc + 4 * (g - 2)),
+                           *reinterpret_cast<const float*>(ssrc), q4_dense_row<EPI>(pr));
     __builtin_amdgcn_sched_barrier(0);
   }
   q4_dma_advance(d);
@@ -679,7 +674,7 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
   const int wn = t.wave & 1;
   select_tile<EPI>(p, t);
 
-  const int nkq = static_cast<int>(p.seg[0].K / BK);  // K is a multiple of 64
+  const int nkq = static_cast<int>(p.seg[0].K / BK);  // K is a multiple of 64: an even count
 
   f32x4_t acc[8][8];
 #pragma unroll
@@ -694,9 +689,8 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
   rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
   rc.nsw = 0;
   rc.rdN = 0;
-  const Q4Read qr = q4_read_ctx<EPI>(wn, t.lane);
 
-  // ---- prologue: DMA of tiles 0 .. Q4_STAGES-2, then tile 0's fragments
+  // ---- prologue: DMA of tiles 0-3, decode of tiles 0 and 1
   Q4Dma d;
   q4_dma_init<EPI>(d, p, t);
 #pragma unroll
@@ -705,11 +699,25 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
     for (int j = 0; j < 6; ++j) q4_dma_issue(d, j, smem + s * Q4_STAGE, nkq, t);
     q4_dma_advance(d);
   }
-  wait_vmcnt<6 * (Q4_STAGES - 2)>();  // tile 0 landed (this wave)
+  wait_vmcnt<6>();  // tiles 0-2 landed (this wave)
+  {
+    const int pr = 64 * t.wave + t.lane;
+    const int drow = q4_dense_row<EPI>(pr);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 codes = *reinterpret_cast<const uint4*>(smem + s * Q4_STAGE + Q4_CODES + pr * 16);
+      const float sc = *reinterpret_cast<const float*>(smem + s * Q4_STAGE + Q4_SCALES + t.wave * 1024 + t.lane * 4);
+      char* dec = smem + Q4_DEC + s * TILE_BYTES;
+      q4_decode_chunk<EPI>(dec, 0, codes.x, sc, drow);
+      q4_decode_chunk<EPI>(dec, 1, codes.y, sc, drow);
+      q4_decode_chunk<EPI>(dec, 2, codes.z, sc, drow);
+      q4_decode_chunk<EPI>(dec, 3, codes.w, sc, drow);
+    }
+  }
   __syncthreads();
   uint4 fa[8], fbA[8], fbB[8];
 #pragma unroll
-  for (int b = 0; b < 8; ++b) fbA[b] = read_bq<EPI>(qr, smem, b);
+  for (int b = 0; b < 8; ++b) fbA[b] = read_bq(rc, smem + Q4_DEC, b);
 #pragma unroll
   for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, a);
 
@@ -718,7 +726,7 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
   // makes the register allocator shuffle the accumulators every trip; the
   // copy of the next B fragments (32 moves) is the cheaper price
   for (int kt = 0; kt < nkq; ++kt) {
-    q4_tile<EPI>(acc, fa, fbA, fbB, d, st_cur, smem, rc, qr, t, nkq);
+    q4_tile<EPI>(acc, fa, fbA, fbB, d, st_cur, smem, rc, t, nkq, kt);
 #pragma unroll
     for (int b = 0; b < 8; ++b) fbA[b] = fbB[b];
   }

@@ -49,6 +49,7 @@ struct Dims {
   int64_t T, H, I, r, r16;
   float s;
   bool bf16, int4, consume;
+  bool q4_inkernel;  // forward decodes 4-bit codes inside the GEMM staging
   int eb;  // element bytes
 };
 
@@ -63,7 +64,7 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   if (!std::isfinite(d->scale)) return fail(LMLP_ERR_INVALID_ARG, "scale is not finite");
   if (d->dtype != LMLP_F32 && d->dtype != LMLP_BF16) return fail(LMLP_ERR_INVALID_ARG, "unknown dtype");
   if (d->wfmt != LMLP_W_DENSE && d->wfmt != LMLP_W_INT4_B64) return fail(LMLP_ERR_INVALID_ARG, "unknown wfmt");
-  if (d->flags & ~LMLP_CONSUME_SAVED) return fail(LMLP_ERR_INVALID_ARG, "unknown flag bits");
+  if (d->flags & ~(LMLP_CONSUME_SAVED | LMLP_INT4_INKERNEL)) return fail(LMLP_ERR_INVALID_ARG, "unknown flag bits");
   if (d->rank > 256) return fail(LMLP_ERR_UNSUPPORTED, "rank > 256");
   const int ch = d->dtype == LMLP_BF16 ? 8 : 4;
   if (d->hidden % ch || d->inter % ch)
@@ -86,6 +87,7 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   o.bf16 = d->dtype == LMLP_BF16;
   o.int4 = d->wfmt == LMLP_W_INT4_B64;
   o.consume = (d->flags & LMLP_CONSUME_SAVED) != 0;
+  o.q4_inkernel = o.int4 && (d->flags & LMLP_INT4_INKERNEL) != 0;
   o.eb = o.bf16 ? 2 : 4;
   return LMLP_OK;
 }
@@ -146,7 +148,8 @@ int64_t colproj_tr(int64_t T, int ntb) {
 int64_t ld_tok(const Dims& d) { return (d.T + 63) / 64 * 64; }  // token-contiguous rows
 
 struct FwdLayout {
-  size_t z, aext_gu, aext_d, agu_pad, ad_pad, bext_g, bext_u, bext_d, rp_part, sc_g, sc_u, sc_d, total;
+  size_t z, aext_gu, aext_d, agu_pad, ad_pad, bext_g, bext_u, bext_d, rp_part, sc_g, sc_u, sc_d;
+  size_t wq_g, wq_u, wq_d, total;
 };
 FwdLayout fwd_layout(const Dims& d) {
   Carver c;
@@ -160,10 +163,15 @@ FwdLayout fwd_layout(const Dims& d) {
   L.bext_u = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.bext_d = c.take(size_t(d.H) * d.r16 * d.eb);
   L.rp_part = c.take(std::max(rp_part_bytes(d, d.H, int(2 * d.r16)), rp_part_bytes(d, d.I, int(d.r16))));
-  // 4-bit weights: block scales as fp32, block-major ([in/64][out])
-  L.sc_g = d.int4 ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
-  L.sc_u = d.int4 ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
-  L.sc_d = d.int4 ? c.take(size_t(d.I / 64) * d.H * 4 + 16) : 0;
+  // 4-bit weights decoded in the GEMMs: block scales as fp32, block-major
+  // ([in/64][out]); otherwise bf16 copies of the weights
+  const bool ink = d.q4_inkernel, cp = d.int4 && !d.q4_inkernel;
+  L.sc_g = ink ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
+  L.sc_u = ink ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
+  L.sc_d = ink ? c.take(size_t(d.I / 64) * d.H * 4 + 16) : 0;
+  L.wq_g = cp ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.wq_u = cp ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.wq_d = cp ? c.take(size_t(d.H) * d.I * 2) : 0;
   L.total = c.off;
   return L;
 }
@@ -329,9 +337,8 @@ struct ProfScope {
 
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
-// bf16 products take the LDS-DMA kernels (4-bit NT weights: the decoding
-// variant); fp32 products the general kernel. The NN products of 4-bit
-// weights run on bf16 copies decoded once per backward call.
+// bf16 products take the LDS-DMA kernels (4-bit weights decoded in the
+// staging: the decoding variant); fp32 products the general kernel.
 hipError_t run_gemm(const GemmParams& p, const Dims& d, int nn, int epi, hipStream_t st) {
   if (!d.bf16) return launch_gemm(p, 0, nn, epi, st);
   if (p.seg[0].bint4) return launch_gemm_q4(p, epi, st);
@@ -519,10 +526,24 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   pk.job[6] = pack_job(bext_d, r16, H, r16, b_down, r, H, r, false);
   pk.njobs = 7;
   LMLP_LAUNCH("pack(fwd)", launch_pack(pk, eb, st));
-  float* sc_g = d.int4 ? reinterpret_cast<float*>(at(workspace, FL.sc_g)) : nullptr;
-  float* sc_u = d.int4 ? reinterpret_cast<float*>(at(workspace, FL.sc_u)) : nullptr;
-  float* sc_d = d.int4 ? reinterpret_cast<float*>(at(workspace, FL.sc_d)) : nullptr;
-  if (d.int4) {
+  float* sc_g = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_g)) : nullptr;
+  float* sc_u = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_u)) : nullptr;
+  float* sc_d = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_d)) : nullptr;
+  const void* wg = w_gate;
+  const void* wu = w_up;
+  const void* wd = w_down;
+  if (d.int4 && !d.q4_inkernel) {
+    char* wq_g = at(workspace, FL.wq_g);
+    char* wq_u = at(workspace, FL.wq_u);
+    char* wq_d = at(workspace, FL.wq_d);
+    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_gate, w_gate_scales, I, H, wq_g, st));
+    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_up, w_up_scales, I, H, wq_u, st));
+    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_down, w_down_scales, H, I, wq_d, st));
+    wg = wq_g;
+    wu = wq_u;
+    wd = wq_d;
+  }
+  if (d.q4_inkernel) {
     ScalePackParams sp{};
     sp.job[0] = {static_cast<const __half*>(w_gate_scales), sc_g, I, H / 64, I};
     sp.job[1] = {static_cast<const __half*>(w_up_scales), sc_u, I, H / 64, I};
@@ -546,7 +567,7 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
 
   GemmParams gp{};
   gp.nseg = 2;
-  gp.seg[0] = seg(x, H, w_gate, w_up, H, H, d.int4, sc_g, sc_u);
+  gp.seg[0] = seg(x, H, wg, wu, H, H, d.q4_inkernel, sc_g, sc_u);
   gp.seg[1] = seg(aext_gu, 2 * r16, bext_g, bext_u, 2 * r16, 2 * r16);
   gp.M = T;
   gp.N = I;
@@ -564,7 +585,7 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
 
   GemmParams gd{};
   gd.nseg = 2;
-  gd.seg[0] = seg(Z, I, w_down, nullptr, I, I, d.int4, sc_d, nullptr);
+  gd.seg[0] = seg(Z, I, wd, nullptr, I, I, d.q4_inkernel, sc_d, nullptr);
   gd.seg[1] = seg(aext_d, r16, bext_d, nullptr, r16, r16);
   gd.M = T;
   gd.N = H;

@@ -11,20 +11,25 @@ import numpy as np
 import pytest
 
 import oracle
+from lora_swiglu_mlp_amd import abi
 from lora_swiglu_mlp_amd import inputs as I
 from lmlp_testutil import TOL, compare, oracle_inputs, run_hip
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["llama3_8b", "llama3_8b_int4", "tinyllama_long", "qwen2_7b"])
+@pytest.mark.parametrize("name", ["llama3_8b", "llama3_8b_int4", "llama3_8b_int4_inkernel", "tinyllama_long",
+                                  "qwen2_7b"])
 def test_fullsize_parity(name):
+    flags = 0
+    if name.endswith("_inkernel"):  # 4-bit codes decoded inside the forward GEMM staging
+        name, flags = name[: -len("_inkernel")], abi.LMLP_INT4_INKERNEL
     wl = I.WORKLOADS[name]
     print(f"[case] {name} T={wl.tokens} H={wl.hidden} I={wl.inter} r={wl.rank} s={wl.scale} "
           f"{wl.dtype} {wl.wfmt}", flush=True)
     t0 = time.time()
     inp = I.make_inputs(wl)
-    got, _ = run_hip(inp, wl)
+    got, _ = run_hip(inp, wl, flags=flags)
     t1 = time.time()
     ref = oracle.forward_backward(oracle_inputs(inp, wl), wl.scale, row_chunk=2048)
     t2 = time.time()

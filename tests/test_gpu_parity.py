@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+from lora_swiglu_mlp_amd import abi
 from lora_swiglu_mlp_amd import inputs as I
 from lmlp_testutil import OUT_KEYS, TOL, compare, oracle_inputs, run_hip
 
@@ -137,6 +138,28 @@ def _dequant_gpu(packed, scales, out, inn):
     abi.lora_mlp_dequant_int4(p, s, out, inn, w)
     torch.cuda.synchronize()
     return w.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name", ["int4_small", "int4_ragged"])
+def test_int4_inkernel_decode_parity(name):
+    """4-bit weights decoded inside the forward GEMMs' operand staging."""
+    wl = workload(name)
+    print(f"[case] {name} in-kernel decode", flush=True)
+    inp = I.make_inputs(wl)
+    got, _ = run_hip(inp, wl, flags=abi.LMLP_INT4_INKERNEL)
+    ref = oracle.forward_backward(oracle_inputs(inp, wl), wl.scale)
+    compare(got, ref, TOL["bf16"], name + "_inkernel")
+
+
+def test_int4_decode_modes_bitwise_equal():
+    """Decoding in the staging and decoding to bf16 copies first give the same
+    weights, fed to the same MFMA sequence in the same k order."""
+    wl = workload("int4_ragged")
+    inp = I.make_inputs(wl)
+    a, _ = run_hip(inp, wl)
+    b, _ = run_hip(inp, wl, flags=abi.LMLP_INT4_INKERNEL)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
 
 
 def test_int4_dequant_bit_exact_random():
