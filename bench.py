@@ -17,8 +17,10 @@ Also reported:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -49,6 +51,50 @@ def kernel_bytes(name: str, T: int, H: int, I: int, r: int, eb: int) -> int:
         "rowproj(dG B_g, dU B_u)": 2 * T * I * eb + 2 * T * r * (4 + eb),
         "colproj": (3 * T * I + 2 * T * H) * eb,
     }.get(name, 0)
+
+
+# sources of the bf16 GEMM kernels: a measured HBM traffic figure applies only
+# while these are unchanged
+GEMM_SOURCES = ("lora_swiglu_mlp_amd/csrc/gemm_bf16.hip", "lora_swiglu_mlp_amd/csrc/lds_dma.h",
+                "lora_swiglu_mlp_amd/csrc/common.h", "lora_swiglu_mlp_amd/csrc/kernels.h")
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the counter summary in profiles/
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when
+    there is none for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    want = gemm_source_hash()
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^traffic_json: (\{.*\})\s*$", line)
+            if m:
+                rec = json.loads(m.group(1))
+                if rec.get("kernel") == kernel and rec.get("source_sha256_16") == want:
+                    return float(rec["bytes_per_launch"])
+    return None
+
+
+def copy_probe(mib: int):
+    """A plain elementwise pass over `mib` MiB (reads and writes that many
+    bytes): the reference reading for the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def cpu_baseline(inp, wl, seconds: float):
@@ -98,6 +144,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -113,6 +161,8 @@ def main():
     wl = I.WORKLOADS[args.workload]
     T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
     inp = I.make_inputs(wl)
     m, x, dy = mlp.from_inputs(inp, wl, "cuda:0")
     saved = m.new_saved()
@@ -174,7 +224,8 @@ def main():
                   key=lambda n: kern[n]["ms"] * kern[n]["launches_per_step"])
         achieved = kern[dom]["tflops"]
         out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                           "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
+                           "unit": "TFLOP/s", "frac": achieved / peak,
+                           "traffic": measured_traffic(dom, wl.name)}
         out["fwd_kernel_ms"] = sum(kern[n]["ms"] * kern[n]["launches_per_step"]
                                    for n in kern if n in fwd_names)
         out["bwd_kernel_ms"] = out["kernel_ms_per_step"] - out["fwd_kernel_ms"]
