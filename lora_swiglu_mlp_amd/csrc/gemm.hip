@@ -1,4 +1,6 @@
-// MFMA GEMM with appended adapter K-steps and fused SwiGLU epilogues.
+// fp32 MFMA GEMM with appended adapter K-steps and fused SwiGLU epilogues.
+// (bf16 products run on the LDS-DMA kernels of gemm_bf16.hip; this
+// register-staged kernel serves the fp32 dtype.)
 //
 // One kernel template serves the four large products of the fused LoRA MLP
 // ("Unsloth 深度分析报告", section 创新之处):
@@ -90,38 +92,6 @@ struct Gemm {
     const GemmSeg& sg = p.seg[it.seg];
     const int c = tid & 7;
     const int r = tid >> 3;
-    if (CH == 8 && sg.bint4) {
-      // packed [rows][K/2] bytes, one fp16 scale per 64 codes: chunk c of a
-      // row is 8 codes = 4 bytes, and a 128-byte LDS row (64 bf16) is exactly
-      // one scale block.
-      const int64_t kc = it.k0 + c * CH;
-      const bool kval = kc < sg.K;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rl = r + 32 * i;
-        int64_t row;
-        const uint8_t* Bp;
-        const __half* Sp;
-        if (EPI == EPI_SWIGLU_FWD) {
-          const int q = rl >> 4;
-          row = (n0 >> 1) + (q >> 1) * 16 + (rl & 15);
-          Bp = static_cast<const uint8_t*>((q & 1) ? sg.b1 : sg.b0);
-          Sp = static_cast<const __half*>((q & 1) ? sg.bs1 : sg.bs0);
-        } else {
-          row = n0 + rl;
-          Bp = static_cast<const uint8_t*>(sg.b0);
-          Sp = static_cast<const __half*>(sg.bs0);
-        }
-        if (kval && row < p.N) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(Bp + row * (sg.ldb >> 1) + (kc >> 1));
-          const float sc = __half2float(Sp[row * (sg.ldb >> 6) + (kc >> 6)]);
-          st.b[i] = dq_chunk(w, sc);
-        } else {
-          st.b[i] = zero4();
-        }
-      }
-      return;
-    }
     const T* B0 = static_cast<const T*>(sg.b0);
     const T* B1 = static_cast<const T*>(sg.b1);
     const int64_t kc = it.k0 + c * CH;
@@ -154,31 +124,6 @@ struct Gemm {
     const GemmSeg& sg = p.seg[it.seg];
     constexpr int NB = BN / CH;          // column blocks per tile
     constexpr int BPT = (ROWCH * NB) / NTHREADS;  // blocks per thread
-    if (CH == 8 && sg.bint4) {
-      // packed [K rows][N/2] bytes, scales [K rows][N/64]; a block is CH=8
-      // rows x 8 columns = 8 x 4 bytes.
-      const uint8_t* Bp = static_cast<const uint8_t*>(sg.b0);
-      const __half* Sp = static_cast<const __half*>(sg.bs0);
-#pragma unroll
-      for (int bi = 0; bi < BPT; ++bi) {
-        const int q = tid + NTHREADS * bi;
-        const int nb = q % NB;
-        const int kb = q / NB;
-        const int64_t n = n0 + nb * CH;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          const int64_t k = it.k0 + kb * CH + i;
-          if (k < sg.K && n < p.N) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(Bp + k * (sg.ldb >> 1) + (n >> 1));
-            const float sc = __half2float(Sp[k * (sg.ldb >> 6) + (n >> 6)]);
-            st.b[bi * CH + i] = dq_chunk(w, sc);
-          } else {
-            st.b[bi * CH + i] = zero4();
-          }
-        }
-      }
-      return;
-    }
     const T* B = static_cast<const T*>(sg.b0);
 #pragma unroll
     for (int bi = 0; bi < BPT; ++bi) {
@@ -374,18 +319,11 @@ static hipError_t launch_t(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmParams& p, int dtype_bf16, int nn, int epi, hipStream_t stream) {
-#define LMLP_DISPATCH(TT)                                                                   \
-  if (!nn && epi == EPI_STORE) return launch_t<TT, false, EPI_STORE>(p, stream);            \
-  if (!nn && epi == EPI_SWIGLU_FWD) return launch_t<TT, false, EPI_SWIGLU_FWD>(p, stream);  \
-  if (nn && epi == EPI_STORE) return launch_t<TT, true, EPI_STORE>(p, stream);              \
-  if (nn && epi == EPI_SWIGLU_BWD) return launch_t<TT, true, EPI_SWIGLU_BWD>(p, stream);
-  if (dtype_bf16) {
-    LMLP_DISPATCH(bf16_t)
-  } else {
-    LMLP_DISPATCH(float)
-  }
-#undef LMLP_DISPATCH
+hipError_t launch_gemm_f32(const GemmParams& p, int nn, int epi, hipStream_t stream) {
+  if (!nn && epi == EPI_STORE) return launch_t<float, false, EPI_STORE>(p, stream);
+  if (!nn && epi == EPI_SWIGLU_FWD) return launch_t<float, false, EPI_SWIGLU_FWD>(p, stream);
+  if (nn && epi == EPI_STORE) return launch_t<float, true, EPI_STORE>(p, stream);
+  if (nn && epi == EPI_SWIGLU_BWD) return launch_t<float, true, EPI_SWIGLU_BWD>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -37,7 +37,8 @@ struct GemmParams {
   const void* u_in; // SWIGLU_BWD: saved U
 };
 
-hipError_t launch_gemm(const GemmParams& p, int dtype_bf16, int nn, int epi, hipStream_t stream);
+// fp32 products (register-staged general kernel)
+hipError_t launch_gemm_f32(const GemmParams& p, int nn, int epi, hipStream_t stream);
 // dense bf16 operands only (LDS-DMA staging); needs every row stride * 256 < 2^31 bytes
 hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t stream);
 // NT products whose segment-0 B operand is 4-bit: seg[0].b0/b1 hold the codes

@@ -340,7 +340,7 @@ char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 // bf16 products take the LDS-DMA kernels (4-bit weights decoded in the
 // staging: the decoding variant); fp32 products the general kernel.
 hipError_t run_gemm(const GemmParams& p, const Dims& d, int nn, int epi, hipStream_t st) {
-  if (!d.bf16) return launch_gemm(p, 0, nn, epi, st);
+  if (!d.bf16) return launch_gemm_f32(p, nn, epi, st);
   if (p.seg[0].bint4) return launch_gemm_q4(p, epi, st);
   return launch_gemm_bf16(p, nn, epi, st);
 }
