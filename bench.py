@@ -56,7 +56,7 @@ def kernel_bytes(name: str, T: int, H: int, I: int, r: int, eb: int) -> int:
 # sources of the bf16 GEMM kernels: a measured HBM traffic figure applies only
 # while these are unchanged
 GEMM_SOURCES = ("lora_swiglu_mlp_amd/csrc/gemm_bf16.hip", "lora_swiglu_mlp_amd/csrc/lds_dma.h",
-                "lora_swiglu_mlp_amd/csrc/common.h", "lora_swiglu_mlp_amd/csrc/kernels.h")
+                "lora_swiglu_mlp_amd/csrc/common.h")
 
 
 def gemm_source_hash() -> str:
