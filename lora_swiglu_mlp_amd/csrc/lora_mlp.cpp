@@ -116,15 +116,15 @@ SavedLayout saved_layout(const Dims& d) {
 }
 
 // Split-K plan of a row projection over a [T, K] activation with n1p output
-// columns: about 1024 workgroups of 64 rows, at least 256 elements per slice.
+// columns: about 768 workgroups of 256 rows, at least 256 elements per slice.
 struct RpPlan {
   int ks;
   int64_t kb;
 };
 RpPlan rp_plan(const Dims& d, int64_t K, int n1p) {
   const int64_t unit = 4 * (d.bf16 ? 32 : 16);  // one load batch: four MFMA k-steps
-  const int64_t work = std::max<int64_t>(1, (d.T + 63) / 64 * ((n1p + 63) / 64));
-  int64_t ks = (1024 + work - 1) / work;
+  const int64_t work = std::max<int64_t>(1, (d.T + 255) / 256 * ((n1p + 63) / 64));
+  int64_t ks = (768 + work - 1) / work;
   ks = std::min(std::max<int64_t>(ks, 1), std::max<int64_t>(1, K / 256));
   int64_t kb = (K + ks - 1) / ks;
   kb = (kb + unit - 1) / unit * unit;

@@ -19,13 +19,14 @@ namespace lmlp {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Row projection, split along K. Workgroup = 64 token rows (16 per wave) x one
-// K slice x up to 64 output columns (four MFMA column tiles). Each wave issues
-// the loads of four k-steps (its activation chunks and the matching factor
-// chunks) before their MFMAs, and many workgroups share a CU, so enough loads
-// are in flight to stream the activation at HBM rate; the factor (a few
-// hundred KB) stays in L2. The slice partials are summed in fixed order by
-// proj_finish_kernel.
+// Row projection, split along K. Workgroup = 256 token rows (64 per wave, four
+// MFMA row tiles) x one K slice x up to 64 output columns (four MFMA column
+// tiles). Each wave issues the loads of four k-steps (16 activation chunks,
+// 16 KB per wave, and the matching factor chunks) before their MFMAs; each
+// factor chunk feeds four row tiles. Enough loads are in flight to stream the
+// activation at HBM rate; the factor (a few hundred KB) stays in L2. The slice
+// partials are summed in fixed order by proj_finish_kernel.
+constexpr int RP_ROWS = 256;  // token rows per workgroup
 template <typename T>
 __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
   constexpr int CH = elem<T>::CH;
@@ -37,23 +38,32 @@ __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lrow = lane & 15, lch = lane >> 4;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16 + lrow;
-  const bool rval = row < p.T;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * RP_ROWS + wave * 64 + lrow;  // row tile 0 of this lane
   const int64_t k0 = static_cast<int64_t>(blockIdx.y) * jb.kb;
   const int64_t k1 = min(jb.K, k0 + jb.kb);
-  const T* X = static_cast<const T*>(jb.x) + (rval ? row : 0) * jb.ldx;
+  const T* X[4];
+  bool rval[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t row = row0 + 16 * r;
+    rval[r] = row < p.T;
+    X[r] = static_cast<const T*>(jb.x) + (rval[r] ? row : 0) * jb.ldx;
+  }
   const T* W = static_cast<const T*>(jb.w) + static_cast<int64_t>(n_base + lrow) * jb.ldw;
 
-  f32x4_t acc[4];
+  f32x4_t acc[4][4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[r][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int64_t kk = k0; kk < k1; kk += 4 * KSTEP) {
-    uint4 a[4], b[4][4];
+    uint4 a[4][4], b[4][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int64_t c = kk + s * KSTEP + lch * CH;  // first element of this lane's chunk
       const bool cval = c < k1;
-      a[s] = (rval && cval) ? *reinterpret_cast<const uint4*>(X + c) : zero4();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[s][r] = (rval[r] && cval) ? *reinterpret_cast<const uint4*>(X[r] + c) : zero4();
 #pragma unroll
       for (int f = 0; f < 4; ++f)
         b[s][f] = (f < nfr && cval) ? *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(f) * 16 * jb.ldw + c)
@@ -62,15 +72,21 @@ __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        if (f < nfr) acc[f] = mma<T>::step(b[s][f], a[s], acc[f]);
-  }
-  if (!rval) return;
-  // lane holds columns n_base + 16f + 4*lch .. +3 of token row `row`
-  float* out = jb.part + (static_cast<int64_t>(blockIdx.y) * p.T + row) * jb.n1p + n_base + 4 * lch;
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
-    if (f < nfr) *reinterpret_cast<float4*>(out + f * 16) = make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
+        for (int f = 0; f < 4; ++f)
+          if (f < nfr) acc[r][f] = mma<T>::step(b[s][f], a[s][r], acc[r][f]);
+  }
+  // lane holds columns n_base + 16f + 4*lch .. +3 of token row row0 + 16r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (!rval[r]) continue;
+    float* out = jb.part + (static_cast<int64_t>(blockIdx.y) * p.T + row0 + 16 * r) * jb.n1p + n_base + 4 * lch;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      if (f < nfr)
+        *reinterpret_cast<float4*>(out + f * 16) = make_float4(acc[r][f][0], acc[r][f][1], acc[r][f][2], acc[r][f][3]);
+  }
 }
 
 // Finish of a split-K row projection: v(t, n) = sum of the slice partials in
@@ -388,26 +404,44 @@ __global__ __launch_bounds__(256, 2) void colproj_bf16_kernel(ColProjParams p) {
 // ---------------------------------------------------------------------------
 // Fixed-order sum of partials: v(i, j) = scale * sum_c src[c][i][col_off + j]
 // for i < rows, j < cols, written to dst[i][j] or, with transpose, dst[j][i],
-// in fp32 or bf16. Workgroup = a 64 x 64 source tile; reads are 16 bytes per
-// lane along source rows, and the transposed case goes through LDS so that
-// its writes also run along destination rows. nchunk = 0 writes zeros.
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
+// in fp32 or bf16. Workgroup = one wave on a 16 x 64 source tile; reads are 16
+// bytes per lane along source rows with eight partials in flight (summed in
+// partial order), and the transposed case goes through LDS so that its writes
+// also run along destination rows. nchunk = 0 writes zeros.
+__global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   const ReduceJob& jb = p.job[blockIdx.z];
-  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t j0 = static_cast<int64_t>(blockIdx.y) * 64;
   if (i0 >= jb.rows || j0 >= jb.cols) return;
-  __shared__ float tile[64][65];
-  const int tid = threadIdx.x, c4 = tid & 15, rr = tid >> 4;
+  __shared__ float tile[64][17];
+  const int lane = threadIdx.x;
+  const int64_t ncols = min<int64_t>(64, jb.cols - j0);
+  const int cpr = static_cast<int>((ncols + 3) / 4);  // float4 items per source row
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int il = 16 * q + rr;
+    const int it = lane + 64 * q;
+    if (it >= 16 * cpr) break;
+    const int il = it / cpr, c = it % cpr;
     const int64_t i = i0 + il;
-    const int64_t j = j0 + 4 * c4;
+    const int64_t j = j0 + 4 * c;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (i < jb.rows && j < jb.cols) {
+    if (i < jb.rows) {
       const float* s = jb.src + i * jb.ld_src + jb.col_off + j;
-      for (int c = 0; c < jb.nchunk; ++c) {
-        const float4 x = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(c) * jb.chunk_stride);
+      int k = 0;
+      for (; k + 8 <= jb.nchunk; k += 8) {
+        float4 x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(k + e) * jb.chunk_stride);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[0] += x[e].x;
+          v[1] += x[e].y;
+          v[2] += x[e].z;
+          v[3] += x[e].w;
+        }
+      }
+      for (; k < jb.nchunk; ++k) {
+        const float4 x = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(k) * jb.chunk_stride);
         v[0] += x.x;
         v[1] += x.y;
         v[2] += x.z;
@@ -428,26 +462,25 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile[4 * c4 + e][il] = v[e];
+      for (int e = 0; e < 4; ++e) tile[4 * c + e][il] = v[e];
     }
   }
   if (!jb.transpose) return;  // uniform over the workgroup
   __syncthreads();
-  const int jl = tid >> 2, iq = tid & 3;
-  const int64_t j = j0 + jl;
-  if (j >= jb.cols) return;
+  const int64_t j = j0 + lane;
+  if (lane >= ncols) return;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int64_t i = i0 + 16 * iq + e;
+    const int64_t i = i0 + e;
     if (i >= jb.rows) break;
     const int64_t o = j * jb.ld_dst + i;
-    const float v = tile[jl][16 * iq + e];
-    if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(v);
-    else static_cast<float*>(jb.dst)[o] = v;
+    if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(tile[lane][e]);
+    else static_cast<float*>(jb.dst)[o] = tile[lane][e];
   }
 }
 
 // ---------------------------------------------------------------------------
+// Zero-padded copy of an adapter factor (flat index over the destination).
 template <typename E>
 __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   const PackJob& jb = p.job[blockIdx.y];
@@ -508,7 +541,7 @@ hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t st
   }
   q.nsl = (maxn + 63) / 64;
   if (q.nsl == 0 || maxks == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((q.T + 63) / 64), maxks, q.njobs * q.nsl);
+  dim3 grid(static_cast<unsigned>((q.T + RP_ROWS - 1) / RP_ROWS), maxks, q.njobs * q.nsl);
   if (dtype_bf16) hipLaunchKernelGGL(rowproj_kernel<bf16_t>, grid, dim3(256), 0, stream, q);
   else hipLaunchKernelGGL(rowproj_kernel<float>, grid, dim3(256), 0, stream, q);
   return hipGetLastError();
@@ -556,8 +589,8 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream) {
     maxc = p.job[i].cols > maxc ? p.job[i].cols : maxc;
   }
   if (maxr == 0 || maxc == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((maxr + 63) / 64), static_cast<unsigned>((maxc + 63) / 64), p.njobs);
-  hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, p);
+  dim3 grid(static_cast<unsigned>((maxr + 15) / 16), static_cast<unsigned>((maxc + 63) / 64), p.njobs);
+  hipLaunchKernelGGL(reduce_kernel, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
