@@ -18,8 +18,10 @@
 //    range), so nothing branches.
 //  * K-major tiles (A always, B in the NT products) sit in LDS as
 //    [256 rows][64 bytes]; chunk c of row r is stored at position
-//    c ^ ((r >> 2) & 3), so the 16 rows of one operand read hit 16 distinct
-//    bank groups. Operand reads are ds_read_b128.
+//    c ^ ((r >> 1) & 3). A ds_read_b128 is served eight lanes at a time, and
+//    eight consecutive rows of one chunk then cover all 32 banks once (with
+//    (r >> 2) the even and the odd rows collided pairwise: every operand read
+//    took twice its time, counted as half of all LDS cycles).
 //  * N-major B tiles (the NN products dZ = dY W_d and dX = dG W_g + dU W_u)
 //    sit in LDS as in memory, [32 k][256 n], and are transposed on the way to
 //    registers by ds_read_b64_tr_b16: in each 16-lane group, lane j names 4
@@ -88,7 +90,7 @@ struct TileCtx {
   int64_t m0, n0, j0;  // j0: first gate/up column (n0 / 2)
   uint32_t m_rows, n_rows;
   int64_t N;
-  int wave, lane, c1;  // c1 = (lane & 3) ^ ((lane >> 4) & 3)
+  int wave, lane, c1;  // c1 = (lane & 3) ^ ((lane >> 3) & 3)
 };
 
 // DMA state of the next k-tile to fetch
@@ -102,7 +104,7 @@ struct Dma {
 // Per-lane offsets of the DMA pattern for segment S.
 // K-major tiles: instruction i of this wave fills tile rows
 // 64*wave + 16*i + (lane >> 2), chunk position lane & 3; that position holds
-// logical chunk (lane & 3) ^ ((row >> 2) & 3) = c1 for every i.
+// logical chunk (lane & 3) ^ ((row >> 1) & 3) = c1 for every i.
 // Gate/up B operand: tile rows alternate gate/up every 16, so instruction i
 // reads weight row (2*wave + i/2)*16 + lane/4 of the gate (i even) or up panel.
 // N-major B tiles: instruction i fills rows k = 2*(4*wave + i) + (lane >> 5),
@@ -176,7 +178,7 @@ __device__ __forceinline__ void dma_advance(Dma& d, int nseg, const Seg& s0, con
 
 // Lane-constant parts of the fragment read addresses.
 // K-major tile, fragment row r = w*128 + a*16 + (lane & 15), chunk lane >> 4:
-// position (lane >> 4) ^ ((r >> 2) & 3) = (lane >> 4) ^ ((lane >> 2) & 3), so
+// position (lane >> 4) ^ ((r >> 1) & 3) = (lane >> 4) ^ ((lane >> 1) & 3), so
 // the address is a per-lane base plus the immediate a*1024.
 // N-major tile: k = hh*4 + (lane >> 4)*8 + (lrow >> 2), n = wn*128 + b*16 +
 // 4*(lrow & 3): nn_swz(k) depends on the lane only and the chunk is
@@ -459,7 +461,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   TileCtx t;
   t.lane = threadIdx.x & 63;
   t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  t.c1 = (t.lane & 3) ^ ((t.lane >> 4) & 3);
+  t.c1 = (t.lane & 3) ^ ((t.lane >> 3) & 3);
   const int wm = t.wave >> 1;
   const int wn = t.wave & 1;
 
@@ -478,8 +480,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   const int lrow = t.lane & 15;
   const int lgrp = t.lane >> 4;
   ReadCtx rc;
-  rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
-  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
+  rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
+  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
   rc.nsw = 2 * ((lrow >> 2) | ((lgrp & 1) << 2));
   rc.rdN = static_cast<uint32_t>((lgrp * 8 + (lrow >> 2)) * 512 + (wn * 16 + ((lrow & 3) >> 1)) * 16 +
                                  8 * (lrow & 1));
@@ -615,7 +617,7 @@ __device__ __forceinline__ int q4_dense_row(int pr) {
 // decode chunk c (8 codes) of this thread's packed row into the decoded tile
 template <int EPI>
 __device__ __forceinline__ void q4_decode_chunk(char* dec, int c, uint32_t codes, float sc, int drow) {
-  *reinterpret_cast<uint4*>(dec + drow * 64 + ((c ^ ((drow >> 2) & 3)) << 4)) = dq_chunk(codes, sc);
+  *reinterpret_cast<uint4*>(dec + drow * 64 + ((c ^ ((drow >> 1) & 3)) << 4)) = dq_chunk(codes, sc);
 }
 
 __device__ __forceinline__ uint4 read_bq(const ReadCtx& rc, const char* dec, int b) {
@@ -669,7 +671,7 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
   TileCtx t;
   t.lane = threadIdx.x & 63;
   t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  t.c1 = (t.lane & 3) ^ ((t.lane >> 4) & 3);
+  t.c1 = (t.lane & 3) ^ ((t.lane >> 3) & 3);
   const int wm = t.wave >> 1;
   const int wn = t.wave & 1;
   select_tile<EPI>(p, t);
@@ -685,8 +687,8 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
   const int lrow = t.lane & 15;
   const int lgrp = t.lane >> 4;
   ReadCtx rc;
-  rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
-  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 2) & 3)) << 4));
+  rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
+  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
   rc.nsw = 0;
   rc.rdN = 0;
 
