@@ -268,6 +268,7 @@ constexpr int EP_LDS_BYTES = 256 * EP_PITCH_C > 2 * 256 * EP_PITCH_GU
                                  : (2 * 256 * EP_PITCH_GU > 128 * EP_PITCH_DZ ? 2 * 256 * EP_PITCH_GU
                                                                              : 128 * EP_PITCH_DZ);
 static_assert(STAGES * STAGE_BYTES >= EP_LDS_BYTES, "the dense ring must hold the epilogue staging");
+static_assert(STAGES * STAGE_BYTES >= 128 * EP_PITCH_DZ + 32 * 512, "dZ half plus the B^T rows");
 
 __device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -302,7 +303,15 @@ __device__ __forceinline__ void lds_rows_to_global(const char* lds, int pitch, i
   }
 }
 
-template <int EPI>
+// Workgroup barrier that orders LDS accesses only: global loads and stores
+// issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int EPI, int QRB = 0>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)[8][8], const TileCtx& t,
                                              int wm, int wn, char* smem) {
   const int lrow = t.lane & 15;
@@ -360,7 +369,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       }
     __syncthreads();
     lds_rows_to_global<16>(gbuf, EP_PITCH_GU, 256, static_cast<bf16_t*>(p.c2) + base, p.ldc, t.m_rows, ncols);
-  } else {  // EPI_SWIGLU_BWD: acc = dZ; reload G, U; recompute the gate
+  } else if (QRB == 0) {  // EPI_SWIGLU_BWD: acc = dZ; reload G, U; recompute the gate
     const bf16_t* Gp = static_cast<const bf16_t*>(p.g_in) + t.m0 * p.ldc + t.n0;
     const bf16_t* Up = static_cast<const bf16_t*>(p.u_in) + t.m0 * p.ldc + t.n0;
     bf16_t* dGp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
@@ -426,6 +435,129 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       }
       if (h == 0) __syncthreads();  // the second half overwrites the staging area
     }
+  } else {  // EPI_SWIGLU_BWD, and the rank-16 row projections dG B_g and dU B_u
+    const bf16_t* Gp = static_cast<const bf16_t*>(p.g_in) + t.m0 * p.ldc + t.n0;
+    const bf16_t* Up = static_cast<const bf16_t*>(p.u_in) + t.m0 * p.ldc + t.n0;
+    bf16_t* dGp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
+    bf16_t* dUp = static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.n0;
+    bf16_t* Zp = p.c2 ? static_cast<bf16_t*>(p.c2) + t.m0 * p.ldc + t.n0 : nullptr;
+    // thread -> 8 consecutive columns (chunk) of rows rsub, rsub + 8, ... of a half
+    const int tid = threadIdx.x;
+    const int chunk = tid & 31;
+    const int rsub = tid >> 5;
+    const bool cval = t.n0 + chunk * 8 < p.N;
+    // G and U of one half-tile (16 rows per thread), fetched before they are
+    // needed; invalid positions read element 0 and are never stored
+    uint4 gv[16], uv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * i + rsub;
+      const int64_t off = (cval && static_cast<uint32_t>(r) < t.m_rows) ? r * p.ldc + chunk * 8 : 0;
+      gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
+      uv[i] = *reinterpret_cast<const uint4*>(Up + off);
+    }
+    lds_barrier();  // every wave is done with the ring
+    // B_g^T (LDS rows 0-15) and B_u^T (16-31) over the tile's columns, 512
+    // bytes a row, chunk c of row n at position c ^ (n & 7); by LDS DMA, two
+    // rows per instruction, waves 0-1 fetching B_g^T and 2-3 B_u^T. Columns
+    // past N read zero.
+    char* bt = smem + 128 * EP_PITCH_DZ;
+    {
+      const rsrc_t rb = make_rsrc(t.wave < 2 ? p.qb0 : p.qb1, static_cast<uint32_t>(16 * p.ldqb * 2));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 8 * t.wave + 2 * j + (t.lane >> 5);  // LDS row, 0..31
+        const int col = ((t.lane & 31) ^ (row & 7)) * 8;
+        const uint32_t voff = static_cast<uint32_t>(col) < t.n_rows
+                                  ? static_cast<uint32_t>(((row & 15) * p.ldqb + t.n0 + col) * 2)
+                                  : OOB;
+        dma16(rb, bt + (8 * t.wave + 2 * j) * 512, voff, 0);
+      }
+    }
+    const int lch = t.lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            *reinterpret_cast<f32x4_t*>(smem + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 128 + b * 16 + lcol) * 4) =
+                acc[a][b];
+      }
+      // h = 0: the B^T rows (and the G, U loads issued before them) have landed
+      if (h == 0) wait_vmcnt<0>();
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = 8 * i + rsub;  // row within the half
+        const int r = h * 128 + rl;   // row within the tile
+        const float4 d0 = *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + chunk * 32);
+        const float4 d1 = *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + chunk * 32 + 16);
+        const float dz[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        float g[8], u[8], dg[8], du[8], z[8];
+        bf16x8_to_f32(gv[i], g);
+        bf16x8_to_f32(uv[i], u);
+        if (h == 0) {  // this slot is free: fetch the same position of the second half
+          const int r2 = 128 + rl;
+          const int64_t off = (cval && static_cast<uint32_t>(r2) < t.m_rows) ? r2 * p.ldc + chunk * 8 : 0;
+          gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
+          uv[i] = *reinterpret_cast<const uint4*>(Up + off);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = sigmoidf_fast(g[e]);
+          const float act = g[e] * sg;
+          dg[e] = dz[e] * u[e] * sg * (1.0f + g[e] * (1.0f - sg));
+          du[e] = dz[e] * act;
+          z[e] = act * u[e];
+        }
+        const bool ok = cval && static_cast<uint32_t>(r) < t.m_rows;
+        const uint4 dgb = ok ? f32x8_to_bf16(dg) : zero4();
+        const uint4 dub = ok ? f32x8_to_bf16(du) : zero4();
+        if (ok) {
+          const int64_t off = r * p.ldc + chunk * 8;
+          *reinterpret_cast<uint4*>(dGp + off) = dgb;
+          *reinterpret_cast<uint4*>(dUp + off) = dub;
+          if (Zp) *reinterpret_cast<uint4*>(Zp + off) = f32x8_to_bf16(z);
+        }
+        // the 32 bytes of dZ just read now hold the bf16 dG and dU chunks
+        *reinterpret_cast<uint4*>(smem + rl * EP_PITCH_DZ + chunk * 32) = dgb;
+        *reinterpret_cast<uint4*>(smem + rl * EP_PITCH_DZ + chunk * 32 + 16) = dub;
+      }
+      lds_barrier();
+      // Q_g[token][n] = sum over the tile's columns of dG * B_g (B_g^T row n =
+      // l & 15), likewise Q_u: wave w takes token blocks 2w, 2w+1 of the half;
+      // the A operand is the staged dG chunk (row l & 15, chunk 4 ks + l / 16).
+      f32x4_t qg[2], qu[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) qg[i] = qu[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int ch = ks * 4 + lch;
+        const int bpos = (ch ^ (lrow & 7)) << 4;
+        const uint4 bg = *reinterpret_cast<const uint4*>(bt + lrow * 512 + bpos);
+        const uint4 bu = *reinterpret_cast<const uint4*>(bt + (16 + lrow) * 512 + bpos);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const char* src = smem + ((2 * t.wave + i) * 16 + lrow) * EP_PITCH_DZ + ch * 32;
+          qg[i] = mma<bf16_t>::step(bg, *reinterpret_cast<const uint4*>(src), qg[i]);
+          qu[i] = mma<bf16_t>::step(bu, *reinterpret_cast<const uint4*>(src + 16), qu[i]);
+        }
+      }
+      // lane l holds Q[token = tb*16 + (l & 15)][n = 4*(l >> 4) .. +3] summed
+      // over the tile's columns: one slice of the split-K partials
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = h * 128 + (2 * t.wave + i) * 16 + lrow;
+        if (static_cast<uint32_t>(r) < t.m_rows) {
+          const int64_t base = ((t.n0 / BN) * p.qT + t.m0 + r) * 16 + 4 * lch;
+          *reinterpret_cast<f32x4_t*>(p.qpart0 + base) = qg[i];
+          *reinterpret_cast<f32x4_t*>(p.qpart1 + base) = qu[i];
+        }
+      }
+      if (h == 0) lds_barrier();  // the second half overwrites the staging area
+    }
   }
 }
 
@@ -454,7 +586,7 @@ __device__ __forceinline__ void select_tile(const GemmParams& p, TileCtx& t) {
 
 }
 
-template <bool NN, int EPI>
+template <bool NN, int EPI, int QRB>
 __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
@@ -516,12 +648,12 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   // workgroup can exit and hand its LDS to another workgroup
   wait_vmcnt<0>();
 
-  epilogue_lds<EPI>(p, acc, t, wm, wn, smem);
+  epilogue_lds<EPI, QRB>(p, acc, t, wm, wn, smem);
 }
 
-template <bool NN, int EPI>
+template <bool NN, int EPI, int QRB>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmParams p) {
-  gemm_bf16_body<NN, EPI>(p);
+  gemm_bf16_body<NN, EPI, QRB>(p);
 }
 
 // ---- 4-bit B operand (NT products with 4-bit block weights) ---------------
@@ -768,7 +900,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_q4_kernel(GemmParams p) {
 
 }  // namespace
 
-template <bool NN, int EPI>
+template <bool NN, int EPI, int QRB = 0>
 static hipError_t launch_t(GemmParams p, hipStream_t stream) {
   p.tiles_m = static_cast<int>((p.M + BM - 1) / BM);
   p.tiles_n = EPI == EPI_SWIGLU_FWD ? static_cast<int>((p.N + BN / 2 - 1) / (BN / 2))
@@ -777,7 +909,7 @@ static hipError_t launch_t(GemmParams p, hipStream_t stream) {
   if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
   const int nblk = p.tiles_m * p.tiles_n;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<NN, EPI>), dim3(nblk), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -804,7 +936,11 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t st
   if (!nn && epi == EPI_STORE) return launch_t<false, EPI_STORE>(p, stream);
   if (!nn && epi == EPI_SWIGLU_FWD) return launch_t<false, EPI_SWIGLU_FWD>(p, stream);
   if (nn && epi == EPI_STORE) return launch_t<true, EPI_STORE>(p, stream);
-  if (nn && epi == EPI_SWIGLU_BWD) return launch_t<true, EPI_SWIGLU_BWD>(p, stream);
+  if (nn && epi == EPI_SWIGLU_BWD) {
+    if (p.qpart0 == nullptr) return launch_t<true, EPI_SWIGLU_BWD, 0>(p, stream);
+    if (p.qr16 == 16) return launch_t<true, EPI_SWIGLU_BWD, 1>(p, stream);
+    return hipErrorInvalidValue;
+  }
   return hipErrorInvalidValue;
 }
 

@@ -35,6 +35,16 @@ struct GemmParams {
   void* c2;         // Z (forward: input of the down product; backward: optional)
   const void* g_in; // SWIGLU_BWD: saved G
   const void* u_in; // SWIGLU_BWD: saved U
+  // SWIGLU_BWD, optional (bf16 kernel, qpart0 != nullptr, rank <= 16): per-tile
+  // partials of the row projections dG B_g and dU B_u over the tile's 256
+  // columns. qb0 / qb1: B_g^T and B_u^T as bf16 [16][ldqb]; qpart0 / qpart1:
+  // fp32 [ceil(N / 256)][qT][16] (slice = tile column, qT = tokens); qr16 = 16.
+  const void* qb0;
+  const void* qb1;
+  float* qpart0;
+  float* qpart1;
+  int64_t ldqb, qT;
+  int32_t qr16;
 };
 
 // fp32 products (register-staged general kernel)

@@ -134,6 +134,14 @@ size_t rp_part_bytes(const Dims& d, int64_t K, int n1p) {
   return size_t(rp_plan(d, K, n1p).ks) * size_t(d.T) * size_t(n1p) * 4;
 }
 
+// bf16 with r <= 16: the dZ GEMM's epilogue also forms the row projections
+// dG B_g and dU B_u, one split-K slice per 256-column tile of I.
+bool fused_q(const Dims& d) { return d.bf16 && d.r16 == 16; }
+int64_t q_slices(const Dims& d) { return (d.I + 255) / 256; }
+size_t q_part_bytes(const Dims& d) {
+  return fused_q(d) ? size_t(q_slices(d)) * size_t(d.T) * size_t(d.r16) * 4 : 0;
+}
+
 // token blocks of the column projections (partial sums over tokens)
 int colproj_ntb(const Dims& d) {
   if (d.T <= 0) return 0;
@@ -201,8 +209,8 @@ BwdLayout bwd_layout(const Dims& d) {
   L.buT = c.take(size_t(d.r16) * d.I * d.eb);
   L.ad_pad = c.take(size_t(d.r16) * d.I * d.eb);
   L.agu_pad = c.take(size_t(2 * d.r16) * d.H * d.eb);
-  L.rp_a = c.take(std::max(rp_part_bytes(d, d.H, int(d.r16)), rp_part_bytes(d, d.I, int(d.r16))));
-  L.rp_b = c.take(rp_part_bytes(d, d.I, int(d.r16)));
+  L.rp_a = c.take(std::max({rp_part_bytes(d, d.H, int(d.r16)), rp_part_bytes(d, d.I, int(d.r16)), q_part_bytes(d)}));
+  L.rp_b = c.take(std::max(rp_part_bytes(d, d.I, int(d.r16)), q_part_bytes(d)));
   // transposed, token-contiguous copies of the [T, r] operands of the column
   // projections (bf16 path only)
   const size_t trow = d.bf16 ? size_t(ld_tok(d)) * d.eb : 0;
@@ -729,15 +737,29 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   gz.g_in = G;
   gz.u_in = U;
   gz.group_m = 8;
+  int q_parts = 0;
+  if (fused_q(d)) {  // Q_g, Q_u partials from the dZ epilogue
+    gz.qb0 = bgT;
+    gz.qb1 = buT;
+    gz.qpart0 = rpa;
+    gz.qpart1 = rpb;
+    gz.ldqb = I;
+    gz.qT = T;
+    gz.qr16 = int(r16);
+    q_parts = int(q_slices(d));
+  }
   LMLP_LAUNCH("gemm(dZ)", run_gemm(gz, d, 1, EPI_SWIGLU_BWD, st));
 
-  rp.njobs = 2;
-  rp.job[0] = rp_job(d, dG, I, I, bgT, I, int(r16), rpa);
-  rp.job[1] = rp_job(d, dU, I, I, buT, I, int(r16), rpb);
-  LMLP_LAUNCH("rowproj(dG B_g, dU B_u)", launch_rowproj(rp, d.bf16, st));
+  if (!fused_q(d)) {
+    rp.njobs = 2;
+    rp.job[0] = rp_job(d, dG, I, I, bgT, I, int(r16), rpa);
+    rp.job[1] = rp_job(d, dU, I, I, buT, I, int(r16), rpb);
+    LMLP_LAUNCH("rowproj(dG B_g, dU B_u)", launch_rowproj(rp, d.bf16, st));
+    q_parts = rp.job[0].kslices;
+  }
   fp.njobs = 2;
-  fp.job[0] = fin_job(rpa, rp.job[0].kslices, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT, 0);
-  fp.job[1] = fin_job(rpb, rp.job[1].kslices, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT,
+  fp.job[0] = fin_job(rpa, q_parts, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT, 0);
+  fp.job[1] = fin_job(rpb, q_parts, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT,
                       int(r16));
   LMLP_LAUNCH("finish(Q_gu)", launch_proj_finish(fp, d.bf16, st));
 
