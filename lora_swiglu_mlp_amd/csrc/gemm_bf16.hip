@@ -463,13 +463,13 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     // past N read zero.
     char* bt = smem + 128 * EP_PITCH_DZ;
     {
-      const rsrc_t rb = make_rsrc(t.wave < 2 ? p.qb0 : p.qb1, static_cast<uint32_t>(16 * p.ldqb * 2));
+      const rsrc_t rb = make_rsrc(t.wave < 2 ? p.pj_b0 : p.pj_b1, static_cast<uint32_t>(16 * p.pj_ldb * 2));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 8 * t.wave + 2 * j + (t.lane >> 5);  // LDS row, 0..31
         const int col = ((t.lane & 31) ^ (row & 7)) * 8;
         const uint32_t voff = static_cast<uint32_t>(col) < t.n_rows
-                                  ? static_cast<uint32_t>(((row & 15) * p.ldqb + t.n0 + col) * 2)
+                                  ? static_cast<uint32_t>(((row & 15) * p.pj_ldb + t.n0 + col) * 2)
                                   : OOB;
         dma16(rb, bt + (8 * t.wave + 2 * j) * 512, voff, 0);
       }
@@ -551,9 +551,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       for (int i = 0; i < 2; ++i) {
         const int r = h * 128 + (2 * t.wave + i) * 16 + lrow;
         if (static_cast<uint32_t>(r) < t.m_rows) {
-          const int64_t base = ((t.n0 / BN) * p.qT + t.m0 + r) * 16 + 4 * lch;
-          *reinterpret_cast<f32x4_t*>(p.qpart0 + base) = qg[i];
-          *reinterpret_cast<f32x4_t*>(p.qpart1 + base) = qu[i];
+          const int64_t base = ((t.n0 / BN) * p.pj_T + t.m0 + r) * 16 + 4 * lch;
+          *reinterpret_cast<f32x4_t*>(p.pj_part0 + base) = qg[i];
+          *reinterpret_cast<f32x4_t*>(p.pj_part1 + base) = qu[i];
         }
       }
       if (h == 0) lds_barrier();  // the second half overwrites the staging area
@@ -937,8 +937,8 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t st
   if (!nn && epi == EPI_SWIGLU_FWD) return launch_t<false, EPI_SWIGLU_FWD>(p, stream);
   if (nn && epi == EPI_STORE) return launch_t<true, EPI_STORE>(p, stream);
   if (nn && epi == EPI_SWIGLU_BWD) {
-    if (p.qpart0 == nullptr) return launch_t<true, EPI_SWIGLU_BWD, 0>(p, stream);
-    if (p.qr16 == 16) return launch_t<true, EPI_SWIGLU_BWD, 1>(p, stream);
+    if (p.pj_part0 == nullptr) return launch_t<true, EPI_SWIGLU_BWD, 0>(p, stream);
+    if (p.pj_r16 == 16) return launch_t<true, EPI_SWIGLU_BWD, 1>(p, stream);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

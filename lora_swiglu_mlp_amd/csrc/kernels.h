@@ -35,16 +35,16 @@ struct GemmParams {
   void* c2;         // Z (forward: input of the down product; backward: optional)
   const void* g_in; // SWIGLU_BWD: saved G
   const void* u_in; // SWIGLU_BWD: saved U
-  // SWIGLU_BWD, optional (bf16 kernel, qpart0 != nullptr, rank <= 16): per-tile
-  // partials of the row projections dG B_g and dU B_u over the tile's 256
-  // columns. qb0 / qb1: B_g^T and B_u^T as bf16 [16][ldqb]; qpart0 / qpart1:
-  // fp32 [ceil(N / 256)][qT][16] (slice = tile column, qT = tokens); qr16 = 16.
-  const void* qb0;
-  const void* qb1;
-  float* qpart0;
-  float* qpart1;
-  int64_t ldqb, qT;
-  int32_t qr16;
+  // SWIGLU_BWD, optional (bf16 kernel, pj_part0 != nullptr, pj_r16 = 16): the
+  // rank-16 row projections dG B_g (into pj_part0) and dU B_u (pj_part1), one
+  // split-K partial slice per 256-column tile: fp32 [tiles_n][pj_T][16] with
+  // pj_T = tokens. pj_b0 / pj_b1: B_g^T / B_u^T as bf16 [16][pj_ldb].
+  const void* pj_b0;
+  const void* pj_b1;
+  float* pj_part0;
+  float* pj_part1;
+  int64_t pj_ldb, pj_T;
+  int32_t pj_r16;
 };
 
 // fp32 products (register-staged general kernel)

@@ -739,13 +739,13 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   gz.group_m = 8;
   int q_parts = 0;
   if (fused_q(d)) {  // Q_g, Q_u partials from the dZ epilogue
-    gz.qb0 = bgT;
-    gz.qb1 = buT;
-    gz.qpart0 = rpa;
-    gz.qpart1 = rpb;
-    gz.ldqb = I;
-    gz.qT = T;
-    gz.qr16 = int(r16);
+    gz.pj_b0 = bgT;
+    gz.pj_b1 = buT;
+    gz.pj_part0 = rpa;
+    gz.pj_part1 = rpb;
+    gz.pj_ldb = I;
+    gz.pj_T = T;
+    gz.pj_r16 = int(r16);
     q_parts = int(q_slices(d));
   }
   LMLP_LAUNCH("gemm(dZ)", run_gemm(gz, d, 1, EPI_SWIGLU_BWD, st));
