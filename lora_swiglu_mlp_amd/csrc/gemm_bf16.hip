@@ -204,6 +204,19 @@ __device__ __forceinline__ uint4 read_b(const ReadCtx& rc, const char* buf, int 
   return make_uint4(u0.x, u0.y, u1.x, u1.y);
 }
 
+// MFMA source chunk of a [k rows][n] bf16 tile read transposed: lane l
+// passes the address of its 4 columns (4 * (l & 3) onward, relative to the
+// lane's 16-column block) in k-row (l >> 4) * 8 + (l & 15) / 4 and receives 8
+// consecutive k of column l & 15 (two ds_read_b64_tr_b16, the second `kstep4`
+// bytes = 4 rows further).
+__device__ __forceinline__ uint4 read_tr16x2(const char* p, int kstep4) {
+  const v4i16_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
+  const v4i16_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p + kstep4));
+  const uint2 u0 = __builtin_bit_cast(uint2, t0);
+  const uint2 u1 = __builtin_bit_cast(uint2, t1);
+  return make_uint4(u0.x, u0.y, u1.x, u1.y);
+}
+
 __device__ __forceinline__ void mfma_group(f32x4_t (&acc)[8][8], int a, const uint4 (&fa)[8], const uint4 (&fb)[8]) {
 #pragma unroll
   for (int b = 0; b < 8; ++b) acc[a][b] = mma<bf16_t>::step(fb[b], fa[a], acc[a][b]);
@@ -261,14 +274,16 @@ __device__ __forceinline__ void pipeline_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[
 // dG = dZ U sig (1 + G (1 - sig)), dU = dZ SiLU(G).
 constexpr int EP_PITCH_C = 256 * 2 + 16;   // bf16 [256 rows][256]
 constexpr int EP_PITCH_GU = 128 * 2 + 16;  // bf16 [256 rows][128], G and U side by side
-constexpr int EP_PITCH_DZ = 256 * 4 + 16;  // fp32 [128 rows][256], one half of dZ at a time
+constexpr int EP_PITCH_DZ = 256 * 4 + 16;  // fp32 [128 rows][256], one half (or quarter) of dZ at a time
+constexpr int EP_PITCH_ZQ = 256 * 2 + 16;  // bf16 [64 rows][256]: Z of one quarter
 // LDS the staging needs: a kernel's shared array must be at least this large
 constexpr int EP_LDS_BYTES = 256 * EP_PITCH_C > 2 * 256 * EP_PITCH_GU
                                  ? (256 * EP_PITCH_C > 128 * EP_PITCH_DZ ? 256 * EP_PITCH_C : 128 * EP_PITCH_DZ)
                                  : (2 * 256 * EP_PITCH_GU > 128 * EP_PITCH_DZ ? 2 * 256 * EP_PITCH_GU
                                                                              : 128 * EP_PITCH_DZ);
 static_assert(STAGES * STAGE_BYTES >= EP_LDS_BYTES, "the dense ring must hold the epilogue staging");
-static_assert(STAGES * STAGE_BYTES >= 128 * EP_PITCH_DZ + 32 * 512, "dZ half plus the B^T rows");
+static_assert(STAGES * STAGE_BYTES >= 64 * (EP_PITCH_DZ + EP_PITCH_ZQ) + 80 * 512,
+              "dZ and Z quarters plus the rank rows");
 
 __device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -435,71 +450,90 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       }
       if (h == 0) __syncthreads();  // the second half overwrites the staging area
     }
-  } else {  // EPI_SWIGLU_BWD, and the rank-16 row projections dG B_g and dU B_u
+  } else {  // EPI_SWIGLU_BWD with the rank-16 products of dG, dU and Z (see above)
     const bf16_t* Gp = static_cast<const bf16_t*>(p.g_in) + t.m0 * p.ldc + t.n0;
     const bf16_t* Up = static_cast<const bf16_t*>(p.u_in) + t.m0 * p.ldc + t.n0;
     bf16_t* dGp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
     bf16_t* dUp = static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.n0;
-    bf16_t* Zp = p.c2 ? static_cast<bf16_t*>(p.c2) + t.m0 * p.ldc + t.n0 : nullptr;
-    // thread -> 8 consecutive columns (chunk) of rows rsub, rsub + 8, ... of a half
+    // LDS: one 64-row quarter of the tile at a time
+    char* dzs = smem;                        // dZ fp32 [64][EP_PITCH_DZ]; then dG | dU bf16 chunks in place
+    char* zs = smem + 64 * EP_PITCH_DZ;      // Z bf16 [64][EP_PITCH_ZQ]
+    char* bt = zs + 64 * EP_PITCH_ZQ;        // B_g^T, B_u^T rows [32][512 B] over the tile's columns
+    char* pt = bt + 32 * 512;                // P_g^T, P_u^T, Q_d^T rows [48][512 B] over the tile's tokens
+    // thread -> 8 consecutive columns (chunk) of rows rsub, rsub + 8, ... of a quarter
     const int tid = threadIdx.x;
     const int chunk = tid & 31;
     const int rsub = tid >> 5;
-    const bool cval = t.n0 + chunk * 8 < p.N;
-    // G and U of one half-tile (16 rows per thread), fetched before they are
-    // needed; invalid positions read element 0 and are never stored
-    uint4 gv[16], uv[16];
+    const int lch = t.lane >> 4;
+    const bool cval = static_cast<uint32_t>(chunk * 8) < t.n_rows;
+    // G and U of the first quarter, fetched before they are needed; invalid
+    // positions read element 0 and are never stored
+    uint4 gv[8], uv[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int r = 8 * i + rsub;
       const int64_t off = (cval && static_cast<uint32_t>(r) < t.m_rows) ? r * p.ldc + chunk * 8 : 0;
       gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
       uv[i] = *reinterpret_cast<const uint4*>(Up + off);
     }
     lds_barrier();  // every wave is done with the ring
-    // B_g^T (LDS rows 0-15) and B_u^T (16-31) over the tile's columns, 512
-    // bytes a row, chunk c of row n at position c ^ (n & 7); by LDS DMA, two
-    // rows per instruction, waves 0-1 fetching B_g^T and 2-3 B_u^T. Columns
-    // past N read zero.
-    char* bt = smem + 128 * EP_PITCH_DZ;
+    // Rank rows by LDS DMA, two 512-byte rows per instruction, chunk c of row n
+    // at position c ^ (n & 7); what lies past N (columns) or T (tokens) reads
+    // zero. bt: waves 0-1 fetch B_g^T, 2-3 B_u^T (4 instructions each). pt:
+    // rows 0-31 from P^T (P_g then P_u), 32-47 from Q_d^T (6 per wave).
     {
       const rsrc_t rb = make_rsrc(t.wave < 2 ? p.pj_b0 : p.pj_b1, static_cast<uint32_t>(16 * p.pj_ldb * 2));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = 8 * t.wave + 2 * j + (t.lane >> 5);  // LDS row, 0..31
+        const int row = 8 * t.wave + 2 * j + (t.lane >> 5);  // 0..31
         const int col = ((t.lane & 31) ^ (row & 7)) * 8;
         const uint32_t voff = static_cast<uint32_t>(col) < t.n_rows
                                   ? static_cast<uint32_t>(((row & 15) * p.pj_ldb + t.n0 + col) * 2)
                                   : OOB;
         dma16(rb, bt + (8 * t.wave + 2 * j) * 512, voff, 0);
       }
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        const int row0 = 12 * t.wave + 2 * j;  // first of the two rows, uniform
+        const bool isq = row0 >= 32;
+        const rsrc_t rp = make_rsrc(isq ? p.pj_qdT : p.pj_pguT, static_cast<uint32_t>((isq ? 16 : 32) * p.pj_ldt * 2));
+        const int row = row0 + (t.lane >> 5);
+        const int tok = ((t.lane & 31) ^ (row & 7)) * 8;
+        const uint32_t voff = static_cast<uint32_t>(tok) < t.m_rows
+                                  ? static_cast<uint32_t>(((row - (isq ? 32 : 0)) * p.pj_ldt + t.m0 + tok) * 2)
+                                  : OOB;
+        dma16(rp, pt + row0 * 512, voff, 0);
+      }
     }
-    const int lch = t.lane >> 4;
+    // column products, summed over the tile's tokens: wave w owns columns
+    // 64w .. 64w+63 (16-column blocks ib = 4w + j)
+    f32x4_t cg[4], cu[4], cz[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (wm == h) {
+    for (int j = 0; j < 4; ++j) cg[j] = cu[j] = cz[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int a = 0; a < 8; ++a)
+    for (int qt = 0; qt < 4; ++qt) {
+      if (wm == (qt >> 1)) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
           for (int b = 0; b < 8; ++b)
-            *reinterpret_cast<f32x4_t*>(smem + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 128 + b * 16 + lcol) * 4) =
-                acc[a][b];
+            *reinterpret_cast<f32x4_t*>(dzs + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 128 + b * 16 + lcol) * 4) =
+                acc[4 * (qt & 1) + a][b];
       }
-      // h = 0: the B^T rows (and the G, U loads issued before them) have landed
-      if (h == 0) wait_vmcnt<0>();
+      if (qt == 0) wait_vmcnt<0>();  // the rank rows (and G, U of the quarter) have landed
       lds_barrier();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rl = 8 * i + rsub;  // row within the half
-        const int r = h * 128 + rl;   // row within the tile
-        const float4 d0 = *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + chunk * 32);
-        const float4 d1 = *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + chunk * 32 + 16);
+      for (int i = 0; i < 8; ++i) {
+        const int rl = 8 * i + rsub;   // row within the quarter
+        const int r = qt * 64 + rl;    // row within the tile
+        const float4 d0 = *reinterpret_cast<const float4*>(dzs + rl * EP_PITCH_DZ + chunk * 32);
+        const float4 d1 = *reinterpret_cast<const float4*>(dzs + rl * EP_PITCH_DZ + chunk * 32 + 16);
         const float dz[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
         float g[8], u[8], dg[8], du[8], z[8];
         bf16x8_to_f32(gv[i], g);
         bf16x8_to_f32(uv[i], u);
-        if (h == 0) {  // this slot is free: fetch the same position of the second half
-          const int r2 = 128 + rl;
+        if (qt < 3) {  // this slot is free: fetch the same position of the next quarter
+          const int r2 = r + 64;
           const int64_t off = (cval && static_cast<uint32_t>(r2) < t.m_rows) ? r2 * p.ldc + chunk * 8 : 0;
           gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
           uv[i] = *reinterpret_cast<const uint4*>(Up + off);
@@ -519,44 +553,78 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
           const int64_t off = r * p.ldc + chunk * 8;
           *reinterpret_cast<uint4*>(dGp + off) = dgb;
           *reinterpret_cast<uint4*>(dUp + off) = dub;
-          if (Zp) *reinterpret_cast<uint4*>(Zp + off) = f32x8_to_bf16(z);
         }
         // the 32 bytes of dZ just read now hold the bf16 dG and dU chunks
-        *reinterpret_cast<uint4*>(smem + rl * EP_PITCH_DZ + chunk * 32) = dgb;
-        *reinterpret_cast<uint4*>(smem + rl * EP_PITCH_DZ + chunk * 32 + 16) = dub;
+        *reinterpret_cast<uint4*>(dzs + rl * EP_PITCH_DZ + chunk * 32) = dgb;
+        *reinterpret_cast<uint4*>(dzs + rl * EP_PITCH_DZ + chunk * 32 + 16) = dub;
+        *reinterpret_cast<uint4*>(zs + rl * EP_PITCH_ZQ + chunk * 16) = ok ? f32x8_to_bf16(z) : zero4();
       }
       lds_barrier();
-      // Q_g[token][n] = sum over the tile's columns of dG * B_g (B_g^T row n =
-      // l & 15), likewise Q_u: wave w takes token blocks 2w, 2w+1 of the half;
-      // the A operand is the staged dG chunk (row l & 15, chunk 4 ks + l / 16).
-      f32x4_t qg[2], qu[2];
+      // Row products: Q_g[token][n] = sum over the tile's columns of dG * B_g
+      // (B_g^T row n = l & 15), likewise Q_u; wave w takes token block w of the
+      // quarter, whose staged dG chunk (row l & 15, chunk 4 ks + l / 16) is the
+      // MFMA source as it stands.
+      {
+        f32x4_t qg = f32x4_t{0.f, 0.f, 0.f, 0.f}, qu = qg;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) qg[i] = qu[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int ch = ks * 4 + lch;
-        const int bpos = (ch ^ (lrow & 7)) << 4;
-        const uint4 bg = *reinterpret_cast<const uint4*>(bt + lrow * 512 + bpos);
-        const uint4 bu = *reinterpret_cast<const uint4*>(bt + (16 + lrow) * 512 + bpos);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const char* src = smem + ((2 * t.wave + i) * 16 + lrow) * EP_PITCH_DZ + ch * 32;
-          qg[i] = mma<bf16_t>::step(bg, *reinterpret_cast<const uint4*>(src), qg[i]);
-          qu[i] = mma<bf16_t>::step(bu, *reinterpret_cast<const uint4*>(src + 16), qu[i]);
+        for (int ks = 0; ks < 8; ++ks) {
+          const int ch = ks * 4 + lch;
+          const int bpos = (ch ^ (lrow & 7)) << 4;
+          const uint4 bg = *reinterpret_cast<const uint4*>(bt + lrow * 512 + bpos);
+          const uint4 bu = *reinterpret_cast<const uint4*>(bt + (16 + lrow) * 512 + bpos);
+          const char* src = dzs + (t.wave * 16 + lrow) * EP_PITCH_DZ + ch * 32;
+          qg = mma<bf16_t>::step(bg, *reinterpret_cast<const uint4*>(src), qg);
+          qu = mma<bf16_t>::step(bu, *reinterpret_cast<const uint4*>(src + 16), qu);
         }
-      }
-      // lane l holds Q[token = tb*16 + (l & 15)][n = 4*(l >> 4) .. +3] summed
-      // over the tile's columns: one slice of the split-K partials
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = h * 128 + (2 * t.wave + i) * 16 + lrow;
+        // lane l holds Q[token = 16w + (l & 15)][n = 4*(l >> 4) .. +3]: one
+        // split-K slice (this tile column)
+        const int r = qt * 64 + t.wave * 16 + lrow;
         if (static_cast<uint32_t>(r) < t.m_rows) {
           const int64_t base = ((t.n0 / BN) * p.pj_T + t.m0 + r) * 16 + 4 * lch;
-          *reinterpret_cast<f32x4_t*>(p.pj_part0 + base) = qg[i];
-          *reinterpret_cast<f32x4_t*>(p.pj_part1 + base) = qu[i];
+          *reinterpret_cast<f32x4_t*>(p.pj_part0 + base) = qg;
+          *reinterpret_cast<f32x4_t*>(p.pj_part1 + base) = qu;
         }
       }
-      if (h == 0) lds_barrier();  // the second half overwrites the staging area
+      // Column products over this quarter's 64 tokens (two k-steps):
+      // dB_g^T[n][col] += sum over tokens of P_g^T[n][t] dG[t][col], likewise
+      // dB_u^T with dU and dA_d[n][col] with Q_d^T and Z. The column operand is
+      // read transposed (ds_read_b64_tr_b16): lane l gets column 16 ib + (l & 15)
+      // and tokens 8 (l >> 4) .. +7 of the k-step.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kc = (qt * 2 + ks) * 4 + lch;  // token chunk within the tile
+        const int ppos = (kc ^ (lrow & 7)) << 4;
+        const uint4 pg = *reinterpret_cast<const uint4*>(pt + lrow * 512 + ppos);
+        const uint4 pu = *reinterpret_cast<const uint4*>(pt + (16 + lrow) * 512 + ppos);
+        const uint4 pq = *reinterpret_cast<const uint4*>(pt + (32 + lrow) * 512 + ppos);
+        const int krow = ks * 32 + lch * 8 + (lrow >> 2);  // token row of the first transposed read
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c0 = (4 * t.wave + j) * 16 + 4 * (lrow & 3);  // first of this lane's 4 columns
+          const char* sg = dzs + krow * EP_PITCH_DZ + (c0 >> 3) * 32 + (c0 & 7) * 2;
+          const char* sz = zs + krow * EP_PITCH_ZQ + c0 * 2;
+          const uint4 tg = read_tr16x2(sg, 4 * EP_PITCH_DZ);
+          const uint4 tu = read_tr16x2(sg + 16, 4 * EP_PITCH_DZ);
+          const uint4 tz = read_tr16x2(sz, 4 * EP_PITCH_ZQ);
+          cg[j] = mma<bf16_t>::step(pg, tg, cg[j]);
+          cu[j] = mma<bf16_t>::step(pu, tu, cu[j]);
+          cz[j] = mma<bf16_t>::step(pq, tz, cz[j]);
+        }
+      }
+      if (qt < 3) lds_barrier();  // the next quarter overwrites the staging
+    }
+    // lane l holds [n = 4*(l >> 4) .. +3][col = 16 ib + (l & 15)] summed over
+    // the tile's tokens: one slice (this tile row) of each [col][16] partial
+    const int64_t mt = t.m0 / BM;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = (4 * t.wave + j) * 16 + lrow;
+      if (static_cast<uint32_t>(col) < t.n_rows) {
+        const int64_t off = (mt * p.N + t.n0 + col) * 16 + 4 * lch;
+        *reinterpret_cast<f32x4_t*>(p.pj_cdg + off) = cg[j];
+        *reinterpret_cast<f32x4_t*>(p.pj_cdu + off) = cu[j];
+        *reinterpret_cast<f32x4_t*>(p.pj_cz + off) = cz[j];
+      }
     }
   }
 }

@@ -36,15 +36,27 @@ struct GemmParams {
   const void* g_in; // SWIGLU_BWD: saved G
   const void* u_in; // SWIGLU_BWD: saved U
   // SWIGLU_BWD, optional (bf16 kernel, pj_part0 != nullptr, pj_r16 = 16): the
-  // rank-16 row projections dG B_g (into pj_part0) and dU B_u (pj_part1), one
-  // split-K partial slice per 256-column tile: fp32 [tiles_n][pj_T][16] with
-  // pj_T = tokens. pj_b0 / pj_b1: B_g^T / B_u^T as bf16 [16][pj_ldb].
+  // epilogue also forms the rank-16 products of dG, dU and Z (Z is then not
+  // written):
+  //  * row products dG B_g (into pj_part0) and dU B_u (pj_part1), one split-K
+  //    slice per 256-column tile: fp32 [tiles_n][pj_T][16], pj_T = tokens;
+  //    pj_b0 / pj_b1 = B_g^T / B_u^T as bf16 [16][pj_ldb];
+  //  * column products P_g^T dG, P_u^T dU, Q_d^T Z (into pj_cdg, pj_cdu, pj_cz),
+  //    one slice per 256-row tile: fp32 [tiles_m][N][16] (column-major in the
+  //    rank); pj_pguT = [P_g^T; P_u^T] as bf16 [32][pj_ldt], pj_qdT = Q_d^T as
+  //    bf16 [16][pj_ldt], zero past T.
   const void* pj_b0;
   const void* pj_b1;
   float* pj_part0;
   float* pj_part1;
   int64_t pj_ldb, pj_T;
   int32_t pj_r16;
+  const void* pj_pguT;
+  const void* pj_qdT;
+  int64_t pj_ldt;
+  float* pj_cdg;
+  float* pj_cdu;
+  float* pj_cz;
 };
 
 // fp32 products (register-staged general kernel)

@@ -135,9 +135,11 @@ size_t rp_part_bytes(const Dims& d, int64_t K, int n1p) {
 }
 
 // bf16 with r <= 16: the dZ GEMM's epilogue also forms the row projections
-// dG B_g and dU B_u, one split-K slice per 256-column tile of I.
+// dG B_g and dU B_u (one split-K slice per 256-column tile of I) and the
+// column products P_g^T dG, P_u^T dU and Q_d^T Z (one slice per 256-row tile).
 bool fused_q(const Dims& d) { return d.bf16 && d.r16 == 16; }
 int64_t q_slices(const Dims& d) { return (d.I + 255) / 256; }
+int64_t col_slices(const Dims& d) { return (d.T + 255) / 256; }
 size_t q_part_bytes(const Dims& d) {
   return fused_q(d) ? size_t(q_slices(d)) * size_t(d.T) * size_t(d.r16) * 4 : 0;
 }
@@ -222,9 +224,10 @@ BwdLayout bwd_layout(const Dims& d) {
   L.wq_g = d.int4 ? c.take(size_t(d.I) * d.H * 2) : 0;
   L.wq_u = d.int4 ? c.take(size_t(d.I) * d.H * 2) : 0;
   L.wq_d = d.int4 ? c.take(size_t(d.H) * d.I * 2) : 0;
-  L.part_dg = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
-  L.part_du = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
-  L.part_z = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
+  const size_t nsl_i = fused_q(d) ? size_t(col_slices(d)) : size_t(L.ntb);
+  L.part_dg = c.take(nsl_i * d.I * d.r16 * 4);
+  L.part_du = c.take(nsl_i * d.I * d.r16 * 4);
+  L.part_z = c.take(nsl_i * d.I * d.r16 * 4);
   L.part_x = c.take(size_t(L.ntb) * d.H * 2 * d.r16 * 4);
   L.part_dy = c.take(size_t(L.ntb) * d.H * d.r16 * 4);
   L.total = c.off;
@@ -746,6 +749,13 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
     gz.pj_ldb = I;
     gz.pj_T = T;
     gz.pj_r16 = int(r16);
+    gz.pj_pguT = pguT;
+    gz.pj_qdT = qdT;
+    gz.pj_ldt = ldT;
+    gz.pj_cdg = part_dg;
+    gz.pj_cdu = part_du;
+    gz.pj_cz = part_z;
+    gz.c2 = nullptr;  // Z is only needed for Q_d^T Z, formed here
     q_parts = int(q_slices(d));
   }
   LMLP_LAUNCH("gemm(dZ)", run_gemm(gz, d, 1, EPI_SWIGLU_BWD, st));
@@ -779,19 +789,24 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   const int64_t tr = BL.tr;
   ColProjParams cp{};
   cp.T = T;
-  cp.njobs = 5;
   const size_t trow = size_t(ldT) * eb;  // bytes of one transposed row
-  cp.job[0] = cp_job(d, dG, I, I, Pgu, 2 * r16, pguT, ldT, int(r16), part_dg, ntb, tr);
-  cp.job[1] = cp_job(d, dU, I, I, Pgu + r16, 2 * r16, pguT ? pguT + r16 * trow : nullptr, ldT, int(r16), part_du,
-                     ntb, tr);
-  cp.job[2] = cp_job(d, Z, I, I, Qd, r16, qdT, ldT, int(r16), part_z, ntb, tr);
-  cp.job[3] = cp_job(d, x, H, H, Qgu, 2 * r16, qguT, ldT, int(2 * r16), part_x, ntb, tr);
-  cp.job[4] = cp_job(d, dy, H, H, Pd, r16, pdT, ldT, int(r16), part_dy, ntb, tr);
+  cp.job[0] = cp_job(d, x, H, H, Qgu, 2 * r16, qguT, ldT, int(2 * r16), part_x, ntb, tr);
+  cp.job[1] = cp_job(d, dy, H, H, Pd, r16, pdT, ldT, int(r16), part_dy, ntb, tr);
+  cp.njobs = 2;
+  int nsl_i = int(col_slices(d));  // slices of the [I]-side partials
+  if (!fused_q(d)) {
+    cp.job[2] = cp_job(d, dG, I, I, Pgu, 2 * r16, pguT, ldT, int(r16), part_dg, ntb, tr);
+    cp.job[3] = cp_job(d, dU, I, I, Pgu + r16, 2 * r16, pguT ? pguT + r16 * trow : nullptr, ldT, int(r16), part_du,
+                       ntb, tr);
+    cp.job[4] = cp_job(d, Z, I, I, Qd, r16, qdT, ldT, int(r16), part_z, ntb, tr);
+    cp.njobs = 5;
+    nsl_i = ntb;
+  }
   LMLP_LAUNCH("colproj", launch_colproj(cp, d.bf16, st));
 
-  rd.job[0] = rd_job(part_dg, I * r16, ntb, r16, 0, I, r, db_gate, r, false, s, d.bf16);
-  rd.job[1] = rd_job(part_du, I * r16, ntb, r16, 0, I, r, db_up, r, false, s, d.bf16);
-  rd.job[2] = rd_job(part_z, I * r16, ntb, r16, 0, I, r, da_down, I, true, s, d.bf16);
+  rd.job[0] = rd_job(part_dg, I * r16, nsl_i, r16, 0, I, r, db_gate, r, false, s, d.bf16);
+  rd.job[1] = rd_job(part_du, I * r16, nsl_i, r16, 0, I, r, db_up, r, false, s, d.bf16);
+  rd.job[2] = rd_job(part_z, I * r16, nsl_i, r16, 0, I, r, da_down, I, true, s, d.bf16);
   rd.job[3] = rd_job(part_x, H * 2 * r16, ntb, 2 * r16, 0, H, r, da_gate, H, true, s, d.bf16);
   rd.job[4] = rd_job(part_x, H * 2 * r16, ntb, 2 * r16, int(r16), H, r, da_up, H, true, s, d.bf16);
   rd.job[5] = rd_job(part_dy, H * r16, ntb, r16, 0, H, r, db_down, r, false, s, d.bf16);
