@@ -116,13 +116,24 @@ SavedLayout saved_layout(const Dims& d) {
 }
 
 // Split-K plan of a row projection over a [T, K] activation with n1p output
-// columns: about 768 workgroups of 256 rows, at least 256 elements per slice.
+// columns. bf16 (LDS-streamed kernel, 128-row workgroups of up to 32 or 64
+// columns, two per CU): about 512 workgroups, slices in whole 64-element
+// stages. fp32: about 768
+// workgroups of 256 rows, at least 256 elements per slice.
 struct RpPlan {
   int ks;
   int64_t kb;
 };
 RpPlan rp_plan(const Dims& d, int64_t K, int n1p) {
-  const int64_t unit = 4 * (d.bf16 ? 32 : 16);  // one load batch: four MFMA k-steps
+  if (d.bf16) {
+    const int64_t work = std::max<int64_t>(1, (d.T + 127) / 128 * (n1p > 32 ? (n1p + 63) / 64 : 1));
+    int64_t ks = (512 + work - 1) / work;
+    ks = std::min(std::max<int64_t>(ks, 1), std::max<int64_t>(1, K / 128));
+    int64_t kb = (K + ks - 1) / ks;
+    kb = (kb + 63) / 64 * 64;
+    return {static_cast<int>((K + kb - 1) / kb), kb};
+  }
+  const int64_t unit = 4 * 16;  // one load batch: four MFMA k-steps
   const int64_t work = std::max<int64_t>(1, (d.T + 255) / 256 * ((n1p + 63) / 64));
   int64_t ks = (768 + work - 1) / work;
   ks = std::min(std::max<int64_t>(ks, 1), std::max<int64_t>(1, K / 256));

@@ -19,13 +19,12 @@ namespace lmlp {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Row projection, split along K. Workgroup = 256 token rows (64 per wave, four
-// MFMA row tiles) x one K slice x up to 64 output columns (four MFMA column
-// tiles). Each wave issues the loads of four k-steps (16 activation chunks,
-// 16 KB per wave, and the matching factor chunks) before their MFMAs; each
-// factor chunk feeds four row tiles. Enough loads are in flight to stream the
-// activation at HBM rate; the factor (a few hundred KB) stays in L2. The slice
-// partials are summed in fixed order by proj_finish_kernel.
+// Row projection, fp32, split along K. Workgroup = 256 token rows (64 per
+// wave, four MFMA row tiles) x one K slice x up to 64 output columns (four
+// MFMA column tiles). Each wave issues the loads of four k-steps (16
+// activation chunks and the matching factor chunks) before their MFMAs; each
+// factor chunk feeds four row tiles. The slice partials are summed in fixed
+// order by proj_finish_kernel. (bf16 uses rowproj_dma_kernel below.)
 constexpr int RP_ROWS = 256;  // token rows per workgroup
 template <typename T>
 __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
@@ -529,6 +528,124 @@ int grid_for(int64_t n) {
   return static_cast<int>(g);
 }
 
+// ---------------------------------------------------------------------------
+// Row projection, bf16, streamed through LDS by DMA. Workgroup = 128 token
+// rows (32 per wave, two MFMA row tiles) x one K slice x up to 16*NF output
+// columns (NF column tiles, 2 or 4). A ring of NS stages holds, per 64
+// elements of K, the activation tile [128 rows][128 bytes] and the factor
+// tile [16*NF rows][128 bytes], chunk c of row n at position c ^ (n & 7)
+// (whole 128-byte lines per row, conflict-free fragment reads). Each wave
+// issues 4 + NF/2 DMA instructions of 1 KB per stage, so NS-1 stages are in
+// flight per workgroup with no registers held; two workgroups share a CU.
+// Rows past T and K past the slice read zero.
+constexpr int RPD_ROWS = 128;
+constexpr int RPD_BK = 64;               // K elements per stage
+constexpr int RPD_XT = RPD_ROWS * 128;   // activation tile bytes
+
+template <int NF, int NS>
+__global__ __launch_bounds__(256, 2) void rowproj_dma_kernel(RowProjParams p) {
+  constexpr int STAGE = RPD_XT + 16 * NF * 128;
+  constexpr int NW = NF / 2;  // factor DMA instructions per wave and stage
+  const RowProjJob& jb = p.job[blockIdx.z / p.nsl];
+  const int n_base = (blockIdx.z % p.nsl) * 16 * NF;
+  if (n_base >= jb.n1p || static_cast<int>(blockIdx.y) >= jb.kslices) return;
+  const int nfr = min(NF, (jb.n1p - n_base) / 16);
+  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * jb.kb;
+  const int64_t k1 = min(jb.K, k0 + jb.kb);
+  if (k0 >= k1) return;
+  const int nst = static_cast<int>((k1 - k0 + RPD_BK - 1) / RPD_BK);
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * RPD_ROWS;
+
+  __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 15, lch = lane >> 4;
+
+  // DMA pattern: activation instruction i of this wave fills rows
+  // 32*wave + 8*i + lane/8, factor instruction j rows 8*(NW*wave + j) + lane/8;
+  // position lane & 7 holds chunk (lane & 7) ^ (row & 7)
+  const uint32_t ldx_b = static_cast<uint32_t>(jb.ldx * 2), ldw_b = static_cast<uint32_t>(jb.ldw * 2);
+  const rsrc_t rx = make_rsrc(static_cast<const char*>(jb.x) + r0 * ldx_b,
+                              static_cast<uint32_t>(min<int64_t>(RPD_ROWS, p.T - r0)) * ldx_b);
+  const rsrc_t rw = make_rsrc(static_cast<const char*>(jb.w) + static_cast<int64_t>(n_base) * ldw_b,
+                              static_cast<uint32_t>(16 * nfr) * ldw_b);
+  uint32_t xo[4], wo[NW];
+  int xc[4], wc[NW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + (lane >> 3);
+    xc[i] = (lane & 7) ^ (row & 7);
+    xo[i] = r0 + row < p.T ? static_cast<uint32_t>(row) * ldx_b + xc[i] * 16 : DMA_OOB;
+  }
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int row = 8 * (NW * wave + j) + (lane >> 3);
+    wc[j] = (lane & 7) ^ (row & 7);
+    wo[j] = row < 16 * nfr ? static_cast<uint32_t>(row) * ldw_b + wc[j] * 16 : DMA_OOB;
+  }
+  // stage s of the slice (past the last one: all lanes out of range, so the
+  // wait counts stay uniform)
+  auto issue = [&](int s) {
+    char* st = ring + (s % NS) * STAGE;
+    const int64_t k = k0 + static_cast<int64_t>(s) * RPD_BK;
+    const bool live = s < nst;
+    const uint32_t soff = live ? static_cast<uint32_t>(k * 2) : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma16(rx, st + (32 * wave + 8 * i) * 128, (live && k + xc[i] * 8 < k1) ? xo[i] : DMA_OOB, soff);
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+      dma16(rw, st + RPD_XT + 8 * (NW * wave + j) * 128, (live && k + wc[j] * 8 < k1) ? wo[j] : DMA_OOB, soff);
+  };
+
+  f32x4_t acc[2][NF];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[r][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  for (int s = 0; s < nst; ++s) {
+    wait_vmcnt<(4 + NW) * (NS - 2)>();  // stage s landed (this wave)
+    __syncthreads();                    // ... everywhere; stage s-1 is free
+    issue(s + NS - 1);
+    const char* st = ring + (s % NS) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = 4 * ks + lch;
+      uint4 xf[2], wf[NF];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = 32 * wave + 16 * r + lrow;
+        xf[r] = *reinterpret_cast<const uint4*>(st + row * 128 + ((ch ^ (row & 7)) << 4));
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int row = 16 * f + lrow;
+        if (f < nfr) wf[f] = *reinterpret_cast<const uint4*>(st + RPD_XT + row * 128 + ((ch ^ (row & 7)) << 4));
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          if (f < nfr) acc[r][f] = mma<bf16_t>::step(wf[f], xf[r], acc[r][f]);
+    }
+  }
+  wait_vmcnt<0>();  // the stages issued past the last one
+  // lane holds columns n_base + 16f + 4*lch .. +3 of token row r0 + 32*wave + 16r + lrow
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int64_t row = r0 + 32 * wave + 16 * r + lrow;
+    if (row >= p.T) continue;
+    float* out = jb.part + (static_cast<int64_t>(blockIdx.y) * p.T + row) * jb.n1p + n_base + 4 * lch;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      if (f < nfr)
+        *reinterpret_cast<float4*>(out + f * 16) = make_float4(acc[r][f][0], acc[r][f][1], acc[r][f][2], acc[r][f][3]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream) {
@@ -539,11 +656,18 @@ hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t st
     maxn = q.job[i].n1p > maxn ? q.job[i].n1p : maxn;
     maxks = q.job[i].kslices > maxks ? q.job[i].kslices : maxks;
   }
-  q.nsl = (maxn + 63) / 64;
-  if (q.nsl == 0 || maxks == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((q.T + RP_ROWS - 1) / RP_ROWS), maxks, q.njobs * q.nsl);
-  if (dtype_bf16) hipLaunchKernelGGL(rowproj_kernel<bf16_t>, grid, dim3(256), 0, stream, q);
-  else hipLaunchKernelGGL(rowproj_kernel<float>, grid, dim3(256), 0, stream, q);
+  if (maxks == 0 || maxn == 0) return hipSuccess;
+  if (dtype_bf16) {
+    const bool wide = maxn > 32;  // 64 columns a pass (4 stages of 24 KB would not fit twice)
+    q.nsl = wide ? (maxn + 63) / 64 : (maxn + 31) / 32;
+    dim3 grid(static_cast<unsigned>((q.T + RPD_ROWS - 1) / RPD_ROWS), maxks, q.njobs * q.nsl);
+    if (wide) hipLaunchKernelGGL((rowproj_dma_kernel<4, 3>), grid, dim3(256), 0, stream, q);
+    else hipLaunchKernelGGL((rowproj_dma_kernel<2, 4>), grid, dim3(256), 0, stream, q);
+  } else {
+    q.nsl = (maxn + 63) / 64;
+    dim3 grid(static_cast<unsigned>((q.T + RP_ROWS - 1) / RP_ROWS), maxks, q.njobs * q.nsl);
+    hipLaunchKernelGGL(rowproj_kernel<float>, grid, dim3(256), 0, stream, q);
+  }
   return hipGetLastError();
 }
 
