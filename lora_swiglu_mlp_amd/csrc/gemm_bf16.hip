@@ -186,17 +186,21 @@ __device__ __forceinline__ void dma_advance(Dma& d, int nseg, const Seg& s0, con
 struct ReadCtx {
   uint32_t rdA, rdB, rdN;
   int nsw;
+  int wc;  // N-major reads of 128-wide tiles: the wave's first column chunk (wn * 8)
 };
 
 __device__ __forceinline__ uint4 read_a(const ReadCtx& rc, const char* buf, int a) {
   return *reinterpret_cast<const uint4*>(buf + rc.rdA + a * 1024);
 }
 
-template <bool NN>
+template <bool NN, int NB = 8>
 __device__ __forceinline__ uint4 read_b(const ReadCtx& rc, const char* buf, int b) {
   const char* bbuf = buf + TILE_BYTES;
   if (!NN) return *reinterpret_cast<const uint4*>(bbuf + rc.rdB + b * 1024);
-  const uint32_t base = rc.rdN + ((((2 * b) ^ rc.nsw) & 15) << 4);
+  // 256-wide tiles: the wave's first chunk (wn * 16) is a multiple of 16 and
+  // sits in rdN; 128-wide ones (wn * 8): the swizzle has to see it
+  const uint32_t base = NB == 8 ? rc.rdN + ((((2 * b) ^ rc.nsw) & 15) << 4)
+                                : rc.rdN + (((rc.wc + 2 * b) ^ rc.nsw) << 4);
   const v4i16_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(bbuf + base));
   const v4i16_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(bbuf + base + 4 * 512));
   const uint2 u0 = __builtin_bit_cast(uint2, t0);
@@ -217,9 +221,10 @@ __device__ __forceinline__ uint4 read_tr16x2(const char* p, int kstep4) {
   return make_uint4(u0.x, u0.y, u1.x, u1.y);
 }
 
-__device__ __forceinline__ void mfma_group(f32x4_t (&acc)[8][8], int a, const uint4 (&fa)[8], const uint4 (&fb)[8]) {
+template <int NB>
+__device__ __forceinline__ void mfma_group(f32x4_t (&acc)[8][NB], int a, const uint4 (&fa)[8], const uint4 (&fb)[8]) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) acc[a][b] = mma<bf16_t>::step(fb[b], fa[a], acc[a][b]);
+  for (int b = 0; b < NB; ++b) acc[a][b] = mma<bf16_t>::step(fb[b], fa[a], acc[a][b]);
 }
 
 
@@ -230,8 +235,8 @@ __device__ __forceinline__ void mfma_group(f32x4_t (&acc)[8][8], int a, const ui
 // per group. After group 0 each wave waits for its DMA of tile kt+1 and the
 // workgroup meets at a barrier: tile kt+1 is then in LDS for every wave and
 // every read of tile kt-1 has retired.
-template <bool NN, int EPI>
-__device__ __forceinline__ void pipeline_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[8], const uint4 (&fb)[8],
+template <bool NN, int EPI, int NB>
+__device__ __forceinline__ void pipeline_tile(f32x4_t (&acc)[8][NB], uint4 (&fa)[8], const uint4 (&fb)[8],
                                               uint4 (&fbn)[8], Dma& d, int& st_cur, char* smem,
                                               const ReadCtx& rc, const TileCtx& t, int nk, int nseg,
                                               const Seg& s0, const Seg& s1, const Seg& s2) {
@@ -239,19 +244,19 @@ __device__ __forceinline__ void pipeline_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[
   const int st_dma = st_cur == 0 ? STAGES - 1 : st_cur - 1;  // tile kt-1's stage
   const char* nxt = smem + st_nxt * STAGE_BYTES;
   char* dbuf = smem + st_dma * STAGE_BYTES;
-  mfma_group(acc, 0, fa, fb);
+  mfma_group<NB>(acc, 0, fa, fb);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<8 * (STAGES - 3)>();  // DMA of tile kt+1 landed (this wave)
   __syncthreads();
 #pragma unroll
   for (int g = 1; g < 8; ++g) {
-    mfma_group(acc, g, fa, fb);
+    mfma_group<NB>(acc, g, fa, fb);
     __builtin_amdgcn_sched_barrier(0);
     dma_issue<NN, EPI>(d, g - 1, dbuf, nk, t);
     fa[g - 1] = read_a(rc, nxt, g - 1);
-    if (g <= 4) {
-      fbn[2 * g - 2] = read_b<NN>(rc, nxt, 2 * g - 2);
-      fbn[2 * g - 1] = read_b<NN>(rc, nxt, 2 * g - 1);
+    if (2 * g <= NB) {
+      fbn[2 * g - 2] = read_b<NN, NB>(rc, nxt, 2 * g - 2);
+      fbn[2 * g - 1] = read_b<NN, NB>(rc, nxt, 2 * g - 1);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -326,9 +331,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int EPI, int QRB = 0>
-__device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)[8][8], const TileCtx& t,
+// NB: 16-column blocks per wave (8: 256-wide tiles; 4: 128-wide, the plain
+// and backward epilogues only, with the upper half of the staging left idle).
+template <int EPI, int QRB = 0, int NB = 8>
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)[8][NB], const TileCtx& t,
                                              int wm, int wn, char* smem) {
+  static_assert(NB == 8 || EPI != EPI_SWIGLU_FWD, "gate/up tiles are 256 wide");
   const int lrow = t.lane & 15;
   const int lcol = 4 * (t.lane >> 4);
   if (EPI == EPI_STORE) {
@@ -336,15 +344,15 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < NB; ++b) {
         const int r = wm * 128 + a * 16 + lrow;
-        const int c = wn * 128 + b * 16 + lcol;
+        const int c = wn * 16 * NB + b * 16 + lcol;
         *reinterpret_cast<uint2*>(smem + r * EP_PITCH_C + c * 2) =
             make_uint2(pack_bf16x2(acc[a][b][0], acc[a][b][1]), pack_bf16x2(acc[a][b][2], acc[a][b][3]));
       }
     __syncthreads();
     bf16_t* C = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
-    lds_rows_to_global<32>(smem, EP_PITCH_C, 256, C, p.ldc, t.m_rows, p.N - t.n0);
+    lds_rows_to_global<32>(smem, EP_PITCH_C, 256, C, p.ldc, t.m_rows, t.n_rows);
   } else if (EPI == EPI_SWIGLU_FWD) {
     // tiles (a, 2q) hold G and (a, 2q+1) hold U of gate/up columns
     // j0 + wn*64 + 16q + lcol .. +3
@@ -394,7 +402,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     const int tid = threadIdx.x;
     const int chunk = tid & 31;
     const int rsub = tid >> 5;
-    const bool cval = t.n0 + chunk * 8 < p.N;
+    const bool cval = static_cast<uint32_t>(chunk * 8) < t.n_rows;
     // G and U of one half-tile (16 rows per thread), fetched before they are
     // needed; invalid positions read element 0 and are never stored
     uint4 gv[16], uv[16];
@@ -412,8 +420,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
 #pragma unroll
         for (int a = 0; a < 8; ++a)
 #pragma unroll
-          for (int b = 0; b < 8; ++b)
-            *reinterpret_cast<f32x4_t*>(smem + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 128 + b * 16 + lcol) * 4) =
+          for (int b = 0; b < NB; ++b)
+            *reinterpret_cast<f32x4_t*>(smem + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 16 * NB + b * 16 + lcol) * 4) =
                 acc[a][b];
       }
       __syncthreads();
@@ -516,8 +524,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int b = 0; b < 8; ++b)
-            *reinterpret_cast<f32x4_t*>(dzs + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 128 + b * 16 + lcol) * 4) =
+          for (int b = 0; b < NB; ++b)
+            *reinterpret_cast<f32x4_t*>(dzs + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 16 * NB + b * 16 + lcol) * 4) =
                 acc[4 * (qt & 1) + a][b];
       }
       if (qt == 0) wait_vmcnt<0>();  // the rank rows (and G, U of the quarter) have landed
@@ -580,7 +588,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
         // split-K slice (this tile column)
         const int r = qt * 64 + t.wave * 16 + lrow;
         if (static_cast<uint32_t>(r) < t.m_rows) {
-          const int64_t base = ((t.n0 / BN) * p.pj_T + t.m0 + r) * 16 + 4 * lch;
+          const int64_t base = ((p.pj_slice0 + t.n0 / (32 * NB)) * p.pj_T + t.m0 + r) * 16 + 4 * lch;
           *reinterpret_cast<f32x4_t*>(p.pj_part0 + base) = qg;
           *reinterpret_cast<f32x4_t*>(p.pj_part1 + base) = qu;
         }
@@ -620,7 +628,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     for (int j = 0; j < 4; ++j) {
       const int col = (4 * t.wave + j) * 16 + lrow;
       if (static_cast<uint32_t>(col) < t.n_rows) {
-        const int64_t off = (mt * p.N + t.n0 + col) * 16 + 4 * lch;
+        const int64_t off = (mt * p.pj_ncol + t.n0 + col) * 16 + 4 * lch;
         *reinterpret_cast<f32x4_t*>(p.pj_cdg + off) = cg[j];
         *reinterpret_cast<f32x4_t*>(p.pj_cdu + off) = cu[j];
         *reinterpret_cast<f32x4_t*>(p.pj_cz + off) = cz[j];
@@ -631,8 +639,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
 
 // Output tile of this workgroup: XCD-aware (block b runs on XCD b % 8), each
 // XCD sweeping bands of group_m tiles along M so that its L2 reuses B panels.
-template <int EPI>
+template <int EPI, int NB = 8>
 __device__ __forceinline__ void select_tile(const GemmParams& p, TileCtx& t) {
+  constexpr int TN = 32 * NB;  // tile width (gate/up: interleaved gate and up columns)
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
   const int per = nblk / 8, rem = nblk % 8, x = bid % 8;
@@ -645,16 +654,16 @@ __device__ __forceinline__ void select_tile(const GemmParams& p, TileCtx& t) {
   const int tm = first_m + (logical % width) % gsize;
   const int tn = (logical % width) / gsize;
   t.m0 = static_cast<int64_t>(tm) * BM;
-  t.n0 = static_cast<int64_t>(tn) * BN;  // gate/up: twice the first column j0
+  t.n0 = static_cast<int64_t>(tn) * TN;  // gate/up: twice the first column j0
   t.j0 = t.n0 >> 1;
-  t.N = p.N;
+  t.N = EPI == EPI_SWIGLU_FWD ? p.N : min<int64_t>(p.N, t.n0 + TN);  // end of this tile's columns
   t.m_rows = static_cast<uint32_t>(min<int64_t>(BM, p.M - t.m0));
-  t.n_rows = static_cast<uint32_t>(EPI == EPI_SWIGLU_FWD ? min<int64_t>(BN / 2, p.N - t.j0)
-                                                         : min<int64_t>(BN, p.N - t.n0));
+  t.n_rows = static_cast<uint32_t>(EPI == EPI_SWIGLU_FWD ? min<int64_t>(TN / 2, p.N - t.j0)
+                                                         : min<int64_t>(TN, p.N - t.n0));
 
 }
 
-template <bool NN, int EPI, int QRB>
+template <bool NN, int EPI, int QRB, int NB>
 __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
@@ -665,25 +674,26 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   const int wm = t.wave >> 1;
   const int wn = t.wave & 1;
 
-  select_tile<EPI>(p, t);
+  select_tile<EPI, NB>(p, t);
 
   const Seg s0 = seg_at(p, 0), s1 = seg_at(p, 1), s2 = seg_at(p, 2);
   int nk = (s0.K + BK - 1) / BK + (s1.K + BK - 1) / BK + (s2.K + BK - 1) / BK;
   nk += nk & 1;  // the loop runs k-tiles in pairs; an odd count gets one empty tile
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[8][NB];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int lrow = t.lane & 15;
   const int lgrp = t.lane >> 4;
   ReadCtx rc;
   rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
-  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
+  rc.rdB = static_cast<uint32_t>((wn * 16 * NB + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
   rc.nsw = 2 * ((lrow >> 2) | ((lgrp & 1) << 2));
-  rc.rdN = static_cast<uint32_t>((lgrp * 8 + (lrow >> 2)) * 512 + (wn * 16 + ((lrow & 3) >> 1)) * 16 +
+  rc.wc = wn * 2 * NB;
+  rc.rdN = static_cast<uint32_t>((lgrp * 8 + (lrow >> 2)) * 512 + ((NB == 8 ? wn * 16 : 0) + ((lrow & 3) >> 1)) * 16 +
                                  8 * (lrow & 1));
 
   // ---- prologue: DMA of tiles 0 .. STAGES-2, then tile 0's fragments
@@ -702,26 +712,26 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   wait_vmcnt<8 * (STAGES - 2)>();  // tile 0 landed (this wave)
   __syncthreads();
 #pragma unroll
-  for (int b = 0; b < 8; ++b) fbA[b] = read_b<NN>(rc, smem, b);
+  for (int b = 0; b < NB; ++b) fbA[b] = read_b<NN, NB>(rc, smem, b);
 #pragma unroll
   for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, a);
 
   int st_cur = 0;
   for (int kt = 0; kt < nk; kt += 2) {
-    pipeline_tile<NN, EPI>(acc, fa, fbA, fbB, d, st_cur, smem, rc, t, nk, p.nseg, s0, s1, s2);
-    pipeline_tile<NN, EPI>(acc, fa, fbB, fbA, d, st_cur, smem, rc, t, nk, p.nseg, s0, s1, s2);
+    pipeline_tile<NN, EPI, NB>(acc, fa, fbA, fbB, d, st_cur, smem, rc, t, nk, p.nseg, s0, s1, s2);
+    pipeline_tile<NN, EPI, NB>(acc, fa, fbB, fbA, d, st_cur, smem, rc, t, nk, p.nseg, s0, s1, s2);
   }
 
   // the last tiles prefetched empty k-tiles: let that DMA retire before the
   // workgroup can exit and hand its LDS to another workgroup
   wait_vmcnt<0>();
 
-  epilogue_lds<EPI, QRB>(p, acc, t, wm, wn, smem);
+  epilogue_lds<EPI, QRB, NB>(p, acc, t, wm, wn, smem);
 }
 
-template <bool NN, int EPI, int QRB>
+template <bool NN, int EPI, int QRB, int NB>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmParams p) {
-  gemm_bf16_body<NN, EPI, QRB>(p);
+  gemm_bf16_body<NN, EPI, QRB, NB>(p);
 }
 
 // ---- 4-bit B operand (NT products with 4-bit block weights) ---------------
@@ -836,7 +846,7 @@ __device__ __forceinline__ void q4_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[8], co
   char* dbuf = smem + st_dma * Q4_STAGE;
   char* dec_w = smem + Q4_DEC + (kt & 1) * TILE_BYTES;              // tile kt+2, decoded now
   const char* dec_r = smem + Q4_DEC + ((kt + 1) & 1) * TILE_BYTES;  // tile kt+1
-  mfma_group(acc, 0, fa, fb);
+  mfma_group<8>(acc, 0, fa, fb);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<6>();  // tiles kt+1 and kt+2 landed (this wave); kt+3 may fly
   __syncthreads();
@@ -845,7 +855,7 @@ __device__ __forceinline__ void q4_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[8], co
   const char* ssrc = smem + st_dec * Q4_STAGE + Q4_SCALES + t.wave * 1024 + t.lane * 4;
 #pragma unroll
   for (int g = 1; g < 8; ++g) {
-    mfma_group(acc, g, fa, fb);
+    mfma_group<8>(acc, g, fa, fb);
     __builtin_amdgcn_sched_barrier(0);
     if (g <= 6) q4_dma_issue(d, g - 1, dbuf, nkq, t);
     fa[g - 1] = read_a(rc, nxt, g - 1);
@@ -954,7 +964,7 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
 #pragma unroll
       for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, a);
 #pragma unroll
-      for (int g = 0; g < 8; ++g) mfma_group(acc, g, fa, fbA);
+      for (int g = 0; g < 8; ++g) mfma_group<8>(acc, g, fa, fbA);
     }
   }
 
@@ -968,16 +978,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_q4_kernel(GemmParams p) {
 
 }  // namespace
 
-template <bool NN, int EPI, int QRB = 0>
+template <bool NN, int EPI, int QRB = 0, int NB = 8>
 static hipError_t launch_t(GemmParams p, hipStream_t stream) {
+  constexpr int TN = 32 * NB;
   p.tiles_m = static_cast<int>((p.M + BM - 1) / BM);
-  p.tiles_n = EPI == EPI_SWIGLU_FWD ? static_cast<int>((p.N + BN / 2 - 1) / (BN / 2))
-                                    : static_cast<int>((p.N + BN - 1) / BN);
+  p.tiles_n = EPI == EPI_SWIGLU_FWD ? static_cast<int>((p.N + TN / 2 - 1) / (TN / 2))
+                                    : static_cast<int>((p.N + TN - 1) / TN);
   if (p.group_m <= 0) p.group_m = 8;
   if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
   const int nblk = p.tiles_m * p.tiles_n;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1005,8 +1016,12 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t st
   if (!nn && epi == EPI_SWIGLU_FWD) return launch_t<false, EPI_SWIGLU_FWD>(p, stream);
   if (nn && epi == EPI_STORE) return launch_t<true, EPI_STORE>(p, stream);
   if (nn && epi == EPI_SWIGLU_BWD) {
-    if (p.pj_part0 == nullptr) return launch_t<true, EPI_SWIGLU_BWD, 0>(p, stream);
-    if (p.pj_r16 == 16) return launch_t<true, EPI_SWIGLU_BWD, 1>(p, stream);
+    const bool narrow = p.tile_n == 128;
+    if (p.tile_n != 0 && p.tile_n != 128 && p.tile_n != 256) return hipErrorInvalidValue;
+    if (p.pj_part0 == nullptr)
+      return narrow ? launch_t<true, EPI_SWIGLU_BWD, 0, 4>(p, stream) : launch_t<true, EPI_SWIGLU_BWD, 0, 8>(p, stream);
+    if (p.pj_r16 == 16)
+      return narrow ? launch_t<true, EPI_SWIGLU_BWD, 1, 4>(p, stream) : launch_t<true, EPI_SWIGLU_BWD, 1, 8>(p, stream);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

@@ -39,12 +39,13 @@ struct GemmParams {
   // epilogue also forms the rank-16 products of dG, dU and Z (Z is then not
   // written):
   //  * row products dG B_g (into pj_part0) and dU B_u (pj_part1), one split-K
-  //    slice per 256-column tile: fp32 [tiles_n][pj_T][16], pj_T = tokens;
+  //    slice per tile column: fp32 [slices][pj_T][16], pj_T = tokens, slice
+  //    pj_slice0 + n0 / tile width;
   //    pj_b0 / pj_b1 = B_g^T / B_u^T as bf16 [16][pj_ldb];
   //  * column products P_g^T dG, P_u^T dU, Q_d^T Z (into pj_cdg, pj_cdu, pj_cz),
-  //    one slice per 256-row tile: fp32 [tiles_m][N][16] (column-major in the
-  //    rank); pj_pguT = [P_g^T; P_u^T] as bf16 [32][pj_ldt], pj_qdT = Q_d^T as
-  //    bf16 [16][pj_ldt], zero past T.
+  //    one slice per 256-row tile: fp32 [tiles_m][pj_ncol][16] (column-major in
+  //    the rank); pj_pguT = [P_g^T; P_u^T] as bf16 [32][pj_ldt], pj_qdT = Q_d^T
+  //    as bf16 [16][pj_ldt], zero past T.
   const void* pj_b0;
   const void* pj_b1;
   float* pj_part0;
@@ -57,6 +58,11 @@ struct GemmParams {
   float* pj_cdg;
   float* pj_cdu;
   float* pj_cz;
+  int64_t pj_ncol;    // row stride (columns) of the column-product partials
+  int32_t pj_slice0;  // first row-product slice of this launch
+  // SWIGLU_BWD: tile width, 256 (0 = default) or 128 (row-product slices are
+  // then per 128 columns)
+  int32_t tile_n;
 };
 
 // fp32 products (register-staged general kernel)

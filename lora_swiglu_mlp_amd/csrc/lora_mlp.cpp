@@ -149,10 +149,35 @@ size_t rp_part_bytes(const Dims& d, int64_t K, int n1p) {
 // dG B_g and dU B_u (one split-K slice per 256-column tile of I) and the
 // column products P_g^T dG, P_u^T dU and Q_d^T Z (one slice per 256-row tile).
 bool fused_q(const Dims& d) { return d.bf16 && d.r16 == 16; }
-int64_t q_slices(const Dims& d) { return (d.I + 255) / 256; }
+// Row-product slices at most (every column in 128-wide tiles); the actual
+// count follows the dZ GEMM's split (dz_split).
+int64_t q_slices(const Dims& d) { return (d.I + 127) / 128; }
 int64_t col_slices(const Dims& d) { return (d.T + 255) / 256; }
 size_t q_part_bytes(const Dims& d) {
   return fused_q(d) ? size_t(q_slices(d)) * size_t(d.T) * size_t(d.r16) * 4 : 0;
+}
+
+// Compute units of the current device.
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 256;
+  return n;
+}
+
+// Columns of the dZ GEMM (bf16) covered by 256-wide tiles; the rest, when the
+// last wave of workgroups would be at most half full, goes to a second launch
+// of 128-wide tiles that fill one wave with twice as many half-size tiles.
+int64_t dz_split(const Dims& d) {
+  if (!d.bf16) return d.I;
+  const int64_t ncu = device_cus();
+  const int64_t tm = (d.T + 255) / 256, tn = (d.I + 255) / 256;
+  const int64_t tiles = tm * tn, rem = tiles % ncu;
+  if (tiles <= ncu || rem == 0 || 2 * rem > ncu) return d.I;
+  const int64_t ntail = (rem + tm - 1) / tm;  // 256-wide tile columns moved to the tail
+  if (ntail >= tn || tm * ntail * 2 > ncu) return d.I;
+  return (tn - ntail) * 256;
 }
 
 // token blocks of the column projections (partial sums over tokens)
@@ -766,10 +791,37 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
     gz.pj_cdg = part_dg;
     gz.pj_cdu = part_du;
     gz.pj_cz = part_z;
+    gz.pj_ncol = I;
     gz.c2 = nullptr;  // Z is only needed for Q_d^T Z, formed here
-    q_parts = int(q_slices(d));
   }
-  LMLP_LAUNCH("gemm(dZ)", run_gemm(gz, d, 1, EPI_SWIGLU_BWD, st));
+  const int64_t n1 = dz_split(d);  // columns in 256-wide tiles
+  if (n1 > 0) {
+    GemmParams g1 = gz;
+    g1.N = n1;
+    LMLP_LAUNCH("gemm(dZ)", run_gemm(g1, d, 1, EPI_SWIGLU_BWD, st));
+  }
+  if (n1 < I) {  // the tail columns in 128-wide tiles
+    GemmParams g2 = gz;
+    g2.N = I - n1;
+    g2.tile_n = 128;
+    g2.seg[0].b0 = static_cast<const char*>(wd) + n1 * eb;
+    g2.seg[1].b0 = ad_pad + n1 * eb;
+    g2.c0 = dG + n1 * eb;
+    g2.c1 = dU + n1 * eb;
+    if (g2.c2) g2.c2 = Z + n1 * eb;
+    g2.g_in = G + n1 * eb;
+    g2.u_in = U + n1 * eb;
+    if (fused_q(d)) {
+      g2.pj_b0 = bgT + n1 * eb;
+      g2.pj_b1 = buT + n1 * eb;
+      g2.pj_cdg = part_dg + n1 * 16;
+      g2.pj_cdu = part_du + n1 * 16;
+      g2.pj_cz = part_z + n1 * 16;
+      g2.pj_slice0 = int(n1 / 256);
+    }
+    LMLP_LAUNCH("gemm(dZ tail)", run_gemm(g2, d, 1, EPI_SWIGLU_BWD, st));
+  }
+  if (fused_q(d)) q_parts = int((n1 + 255) / 256 + (I - n1 + 127) / 128);
 
   if (!fused_q(d)) {
     rp.njobs = 2;
