@@ -33,6 +33,11 @@ CASES = {
     "bf16_min_width": (40, 8, 8, 2, 4.0, "bf16", "dense"),
     "int4_small": (192, 256, 384, 16, 16.0, "bf16", "int4_b64"),
     "int4_ragged": (300, 192, 320, 12, 24.0, "bf16", "int4_b64"),
+    # dZ has 2 x 129 tiles of 256 columns: on 256 CUs the last column goes to
+    # the second launch of 128-wide tiles (ragged: 232 columns), rank 16 with
+    # the fused rank products and rank 32 without
+    "bf16_dz_tail": (512, 64, 33000, 16, 16.0, "bf16", "dense"),
+    "bf16_dz_tail_r32": (512, 64, 33000, 32, 32.0, "bf16", "dense"),
 }
 
 
@@ -55,6 +60,20 @@ def test_parity_against_oracle(name):
         assert np.linalg.norm(got[k]) > 0, k  # gradients flow into every adapter factor
     assert all(np.isfinite(v).all() for v in got.values())
     assert errs
+
+
+def test_dz_tail_launch_taken():
+    """On a 256-CU device the bf16_dz_tail shape runs dZ as two launches (256-
+    and 128-wide tiles); the parity cases above then cover the second one."""
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split point depends on the CU count")
+    wl = workload("bf16_dz_tail")
+    inp = I.make_inputs(wl)
+    abi.lora_mlp_profile_begin()
+    run_hip(inp, wl)
+    names = [n for n, _ in abi.lora_mlp_profile_end()]
+    assert names.count("gemm(dZ)") == 1 and names.count("gemm(dZ tail)") == 1, names
 
 
 def test_empty_token_batch():
