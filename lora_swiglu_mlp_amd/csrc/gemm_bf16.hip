@@ -355,43 +355,46 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     lds_rows_to_global<32>(smem, EP_PITCH_C, 256, C, p.ldc, t.m_rows, t.n_rows);
   } else if (EPI == EPI_SWIGLU_FWD) {
     // tiles (a, 2q) hold G and (a, 2q+1) hold U of gate/up columns
-    // j0 + wn*64 + 16q + lcol .. +3
+    // j0 + wn*64 + 16q + lcol .. +3; both go to LDS rounded to bf16, then one
+    // pass per row chunk stores G and U and forms Z = SiLU(G) U from the same
+    // rounded values
     char* gbuf = smem;
     char* ubuf = smem + 256 * EP_PITCH_GU;
-    uint32_t zp[8][4][2];
     __syncthreads();
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float g[4], u[4], z[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          g[i] = elem<bf16_t>::round(acc[a][2 * q][i]);
-          u[i] = elem<bf16_t>::round(acc[a][2 * q + 1][i]);
-          z[i] = g[i] * sigmoidf_fast(g[i]) * u[i];
-        }
         const int off = (wm * 128 + a * 16 + lrow) * EP_PITCH_GU + (wn * 64 + q * 16 + lcol) * 2;
+        const f32x4_t& g = acc[a][2 * q];
+        const f32x4_t& u = acc[a][2 * q + 1];
         *reinterpret_cast<uint2*>(gbuf + off) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
         *reinterpret_cast<uint2*>(ubuf + off) = make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
-        zp[a][q][0] = pack_bf16x2(z[0], z[1]);
-        zp[a][q][1] = pack_bf16x2(z[2], z[3]);
       }
     __syncthreads();
-    const int64_t base = t.m0 * p.ldc + t.j0;
-    const int64_t ncols = p.N - t.j0;
-    lds_rows_to_global<16>(gbuf, EP_PITCH_GU, 256, static_cast<bf16_t*>(p.c0) + base, p.ldc, t.m_rows, ncols);
-    lds_rows_to_global<16>(ubuf, EP_PITCH_GU, 256, static_cast<bf16_t*>(p.c1) + base, p.ldc, t.m_rows, ncols);
-    __syncthreads();
+    const int tid = threadIdx.x;
+    const int chunk = tid & 15;  // 8 columns of a 128-column row
+    const int rsub = tid >> 4;
+    const bool cval = static_cast<uint32_t>(chunk * 8) < t.n_rows;
+    bf16_t* Gp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.j0 + chunk * 8;
+    bf16_t* Up = static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.j0 + chunk * 8;
+    bf16_t* Zp = static_cast<bf16_t*>(p.c2) + t.m0 * p.ldc + t.j0 + chunk * 8;
+#pragma unroll 4
+    for (int r = rsub; r < 256; r += NTHREADS / 16) {
+      const uint4 gv = *reinterpret_cast<const uint4*>(gbuf + r * EP_PITCH_GU + chunk * 16);
+      const uint4 uv = *reinterpret_cast<const uint4*>(ubuf + r * EP_PITCH_GU + chunk * 16);
+      if (cval && static_cast<uint32_t>(r) < t.m_rows) {
+        float g[8], u[8], z[8];
+        bf16x8_to_f32(gv, g);
+        bf16x8_to_f32(uv, u);
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int off = (wm * 128 + a * 16 + lrow) * EP_PITCH_GU + (wn * 64 + q * 16 + lcol) * 2;
-        *reinterpret_cast<uint2*>(gbuf + off) = make_uint2(zp[a][q][0], zp[a][q][1]);
+        for (int e = 0; e < 8; ++e) z[e] = g[e] * sigmoidf_fast(g[e]) * u[e];
+        const int64_t off = r * p.ldc;
+        *reinterpret_cast<uint4*>(Gp + off) = gv;
+        *reinterpret_cast<uint4*>(Up + off) = uv;
+        *reinterpret_cast<uint4*>(Zp + off) = f32x8_to_bf16(z);
       }
-    __syncthreads();
-    lds_rows_to_global<16>(gbuf, EP_PITCH_GU, 256, static_cast<bf16_t*>(p.c2) + base, p.ldc, t.m_rows, ncols);
+    }
   } else if (QRB == 0) {  // EPI_SWIGLU_BWD: acc = dZ; reload G, U; recompute the gate
     const bf16_t* Gp = static_cast<const bf16_t*>(p.g_in) + t.m0 * p.ldc + t.n0;
     const bf16_t* Up = static_cast<const bf16_t*>(p.u_in) + t.m0 * p.ldc + t.n0;
