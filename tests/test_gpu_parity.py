@@ -62,6 +62,33 @@ def test_parity_against_oracle(name):
     assert errs
 
 
+def _random_shapes(n, seed=20261203):
+    """Seeded random shapes: ragged M, N and K at every tile size the kernels
+    use, ranks 1..64, both dtypes (fp32 smaller)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        f32 = i % 4 == 3
+        T = int(rng.integers(1, 700 if not f32 else 200))
+        H = 8 * int(rng.integers(1, 90 if not f32 else 20))
+        Iw = 8 * int(rng.integers(1, 150 if not f32 else 30))
+        r = int(rng.choice([1, 3, 8, 13, 16, 16, 24, 32, 48, 64]))
+        out.append((f"rand{i}", T, H, Iw, r, float(2 * r), "f32" if f32 else "bf16"))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_shapes(12), ids=lambda c: c[0])
+def test_parity_random_shapes(case):
+    name, T, H, Iw, r, alpha, dt = case
+    base = I.WORKLOADS["tiny_fp32"] if dt == "f32" else I.WORKLOADS["llama3_8b"]
+    wl = base.replace(name=name, tokens=T, hidden=H, inter=Iw, rank=r, alpha=alpha, dtype=dt, wfmt="dense")
+    print(f"[case] {case}", flush=True)
+    inp = I.make_inputs(wl)
+    got, _ = run_hip(inp, wl)
+    ref = oracle.forward_backward(oracle_inputs(inp, wl), wl.scale)
+    compare(got, ref, TOL[dt], name)
+
+
 def test_dz_tail_launch_taken():
     """On a 256-CU device the bf16_dz_tail shape runs dZ as two launches (256-
     and 128-wide tiles); the parity cases above then cover the second one."""
