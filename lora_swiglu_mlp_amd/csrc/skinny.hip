@@ -479,18 +479,29 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Zero-padded copy of an adapter factor (flat index over the destination).
+// Zero-padded copy of an adapter factor (flat index over the destination),
+// four consecutive destination elements of one row per thread, 32-bit index
+// arithmetic (every factor has far fewer than 2^31 elements).
 template <typename E>
 __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   const PackJob& jb = p.job[blockIdx.y];
-  const int64_t n = jb.rows * jb.cols;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < n;
-       idx += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t i = idx / jb.cols, j = idx % jb.cols;
-    const int64_t si = jb.transpose ? j : i, sj = jb.transpose ? i : j;
-    E v = 0;
-    if (jb.src && si < jb.srows && sj < jb.scols) v = static_cast<const E*>(jb.src)[si * jb.ld_src + sj];
-    static_cast<E*>(jb.dst)[i * jb.ld_dst + j] = v;
+  const uint32_t cols = static_cast<uint32_t>(jb.cols);
+  const uint32_t cq = (cols + 3) / 4;  // groups of four per destination row
+  const uint32_t n = static_cast<uint32_t>(jb.rows) * cq;
+  const uint32_t srows = static_cast<uint32_t>(jb.srows), scols = static_cast<uint32_t>(jb.scols);
+  const E* src = static_cast<const E*>(jb.src);
+  E* dst = static_cast<E*>(jb.dst);
+  for (uint32_t idx = blockIdx.x * 256 + threadIdx.x; idx < n; idx += gridDim.x * 256) {
+    const uint32_t i = idx / cq, j0 = (idx % cq) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t j = j0 + e;
+      if (j >= cols) break;
+      const uint32_t si = jb.transpose ? j : i, sj = jb.transpose ? i : j;
+      E v = 0;
+      if (src && si < srows && sj < scols) v = src[static_cast<int64_t>(si) * jb.ld_src + sj];
+      dst[static_cast<int64_t>(i) * jb.ld_dst + j] = v;
+    }
   }
 }
 
@@ -723,7 +734,7 @@ hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream) 
   int64_t maxn = 0;
   for (int i = 0; i < p.njobs; ++i) maxn = p.job[i].rows * p.job[i].cols > maxn ? p.job[i].rows * p.job[i].cols : maxn;
   if (maxn == 0) return hipSuccess;
-  dim3 grid(grid_for(maxn), p.njobs);
+  dim3 grid(grid_for((maxn + 3) / 4), p.njobs);
   if (elem_bytes == 2) hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(pack_kernel<uint32_t>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
