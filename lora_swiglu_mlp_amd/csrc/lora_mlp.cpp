@@ -117,9 +117,9 @@ SavedLayout saved_layout(const Dims& d) {
 
 // Split-K plan of a row projection over a [T, K] activation with n1p output
 // columns. bf16 (LDS-streamed kernel, 128-row workgroups of up to 32 or 64
-// columns, two per CU): about 512 workgroups, slices in whole 64-element
-// stages. fp32: about 768
-// workgroups of 256 rows, at least 256 elements per slice.
+// columns, two per CU): about 256 workgroups (measured a little faster than
+// 512), slices in whole 64-element stages. fp32: about 768 workgroups of 256
+// rows, at least 256 elements per slice.
 struct RpPlan {
   int ks;
   int64_t kb;
@@ -127,7 +127,7 @@ struct RpPlan {
 RpPlan rp_plan(const Dims& d, int64_t K, int n1p) {
   if (d.bf16) {
     const int64_t work = std::max<int64_t>(1, (d.T + 127) / 128 * (n1p > 32 ? (n1p + 63) / 64 : 1));
-    int64_t ks = (512 + work - 1) / work;
+    int64_t ks = (256 + work - 1) / work;
     ks = std::min(std::max<int64_t>(ks, 1), std::max<int64_t>(1, K / 128));
     int64_t kb = (K + ks - 1) / ks;
     kb = (kb + 63) / 64 * 64;
