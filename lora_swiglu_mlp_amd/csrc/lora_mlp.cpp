@@ -10,10 +10,13 @@
 // Backward:
 //   pack, rowproj Q_d = dY B_d
 //   gemm     dZ = [dY | sQ_d] [W_d ; A_d], epilogue: reload G, U, recompute
-//            sigmoid(G), SiLU(G), Z; dG = dZ U sig (1 + G (1 - sig)), dU = dZ SiLU(G)
-//   rowproj  Q_g = dG B_g, Q_u = dU B_u
+//            sigmoid(G), SiLU(G), Z; dG = dZ U sig (1 + G (1 - sig)), dU = dZ SiLU(G);
+//            at rank <= 16 also the partials of Q_g = dG B_g, Q_u = dU B_u and of
+//            dG^T P_g, dU^T P_u, Z^T Q_d (the last dZ tile columns may run as a
+//            second launch of 128-wide tiles)
+//   rowproj  Q_g = dG B_g, Q_u = dU B_u (rank > 16)
 //   gemm     dX = [dG | dU | sQ_g | sQ_u] [W_g ; W_u ; A_g ; A_u]
-//   colproj  dG^T P_g, dU^T P_u, Z^T Q_d, X^T Q_gu, dY^T Pd (per token block)
+//   colproj  X^T Q_gu, dY^T Pd (rank > 16 also dG^T P_g, dU^T P_u, Z^T Q_d), per token block
 //   reduce   fixed-order sums, times s -> dB_g, dB_u, dA_d, dA_g, dA_u, dB_d
 // This is the hand-derived backward of the fused LoRA MLP ("Unsloth 深度分析报告",
 // section 创新之处) with the gate activations recomputed rather than stored
@@ -180,10 +183,12 @@ int64_t dz_split(const Dims& d) {
   return (tn - ntail) * 256;
 }
 
-// token blocks of the column projections (partial sums over tokens)
+// token blocks of the column projections (partial sums over tokens). bf16:
+// at most 8; more blocks measured slower at 8K and 32K tokens (more partials
+// to write and reduce, no gain in streaming rate).
 int colproj_ntb(const Dims& d) {
   if (d.T <= 0) return 0;
-  if (d.bf16) return static_cast<int>(std::min<int64_t>(32, std::max<int64_t>(1, (d.T + 511) / 512)));
+  if (d.bf16) return static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(1, (d.T + 511) / 512)));
   return static_cast<int>(std::min<int64_t>(16, (d.T + 255) / 256));
 }
 int64_t colproj_tr(int64_t T, int ntb) {
