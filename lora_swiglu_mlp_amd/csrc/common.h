@@ -43,7 +43,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // The same rounding as pack_bf16x2 as one packed convert (gfx950
-// v_cvt_pk_bf16_f32); used by the 4-bit decode inside the GEMM K loop.
+// v_cvt_pk_bf16_f32). Used where conversions dominate (the 4-bit decode in the
+// GEMM K loop, the SwiGLU backward epilogue); elsewhere the two-convert form
+// is kept because it leaves the GEMM K loops' register allocation as it is
+// (with the packed form the compiler moved accumulators between AGPRs and
+// VGPRs inside the plain, gate/up and dX K loops).
 __device__ __forceinline__ uint32_t pack_bf16x2_pk(float lo, float hi) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

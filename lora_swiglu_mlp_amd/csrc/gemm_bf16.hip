@@ -279,16 +279,17 @@ __device__ __forceinline__ void pipeline_tile(f32x4_t (&acc)[8][NB], uint4 (&fa)
 // dG = dZ U sig (1 + G (1 - sig)), dU = dZ SiLU(G).
 constexpr int EP_PITCH_C = 256 * 2 + 16;   // bf16 [256 rows][256]
 constexpr int EP_PITCH_GU = 128 * 2 + 16;  // bf16 [256 rows][128], G and U side by side
-constexpr int EP_PITCH_DZ = 256 * 4 + 16;  // fp32 [128 rows][256], one half (or quarter) of dZ at a time
-constexpr int EP_PITCH_ZQ = 256 * 2 + 16;  // bf16 [64 rows][256]: Z of one quarter
+constexpr int EP_PITCH_DZ = 256 * 4 + 16;  // fp32 [128 rows][256], one half of dZ at a time
+constexpr int EP_SP = 256 * 2 + 16;        // bf16 [32 rows][256]: dG, dU or Z of one backward pass
+constexpr int EP_SBUF = 3 * 32 * EP_SP;     // dG, dU and Z of one pass
+constexpr int EP_PF = 4;                    // backward passes whose G and U are in flight
 // LDS the staging needs: a kernel's shared array must be at least this large
 constexpr int EP_LDS_BYTES = 256 * EP_PITCH_C > 2 * 256 * EP_PITCH_GU
                                  ? (256 * EP_PITCH_C > 128 * EP_PITCH_DZ ? 256 * EP_PITCH_C : 128 * EP_PITCH_DZ)
                                  : (2 * 256 * EP_PITCH_GU > 128 * EP_PITCH_DZ ? 2 * 256 * EP_PITCH_GU
                                                                              : 128 * EP_PITCH_DZ);
 static_assert(STAGES * STAGE_BYTES >= EP_LDS_BYTES, "the dense ring must hold the epilogue staging");
-static_assert(STAGES * STAGE_BYTES >= 64 * (EP_PITCH_DZ + EP_PITCH_ZQ) + 80 * 512,
-              "dZ and Z quarters plus the rank rows");
+static_assert(STAGES * STAGE_BYTES >= 2 * EP_SBUF + 80 * 512, "two pass buffers plus the rank rows");
 
 __device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -331,11 +332,43 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Epilogue operands that do not depend on the product, fetched before the K
+// loop so that their latency is hidden: the rank rows of the fused backward,
+// 16-byte chunk c of row n (thread tid + 256 j) for the LDS position
+// c ^ (n & 7); what lies past N (columns) or M (tokens) is zero. Rows 0-31:
+// B_g^T, B_u^T over the tile's columns; rows 32-79: P_g^T, P_u^T, Q_d^T over
+// the tile's tokens.
+struct EpiPre {
+  uint4 rk[10];
+};
+
+template <int EPI, int QRB>
+__device__ __forceinline__ void epi_preload(const GemmParams& p, const TileCtx& t, EpiPre& pre) {
+  if (EPI != EPI_SWIGLU_BWD || QRB != 1) return;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 10; ++j) {
+    const int idx = tid + NTHREADS * (j < 4 ? j : j - 4);
+    const int row = idx >> 5, c = idx & 31;
+    const bf16_t* src;
+    bool ok;
+    if (j < 4) {
+      src = static_cast<const bf16_t*>(row < 16 ? p.pj_b0 : p.pj_b1) + (row & 15) * p.pj_ldb + t.n0 + 8 * c;
+      ok = static_cast<uint32_t>(8 * c) < t.n_rows;
+    } else {
+      src = row < 32 ? static_cast<const bf16_t*>(p.pj_pguT) + row * p.pj_ldt + t.m0 + 8 * c
+                     : static_cast<const bf16_t*>(p.pj_qdT) + (row - 32) * p.pj_ldt + t.m0 + 8 * c;
+      ok = static_cast<uint32_t>(8 * c) < t.m_rows;
+    }
+    pre.rk[j] = ok ? *reinterpret_cast<const uint4*>(src) : zero4();
+  }
+}
+
 // NB: 16-column blocks per wave (8: 256-wide tiles; 4: 128-wide, the plain
 // and backward epilogues only, with the upper half of the staging left idle).
 template <int EPI, int QRB = 0, int NB = 8>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)[8][NB], const TileCtx& t,
-                                             int wm, int wn, char* smem) {
+                                             int wm, int wn, char* smem, const EpiPre& pre) {
   static_assert(NB == 8 || EPI != EPI_SWIGLU_FWD, "gate/up tiles are 256 wide");
   const int lrow = t.lane & 15;
   const int lcol = 4 * (t.lane >> 4);
@@ -462,174 +495,170 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       if (h == 0) __syncthreads();  // the second half overwrites the staging area
     }
   } else {  // EPI_SWIGLU_BWD with the rank-16 products of dG, dU and Z (see above)
+    // Eight passes; pass a takes accumulator row block a of every wave, i.e.
+    // tile rows 16a .. 16a+15 (wm = 0) and 128 + 16a .. +15 (wm = 1): 32
+    // staging rows, staging row s = tile row (s >> 4) * 128 + 16a + (s & 15).
+    // G and U come from global memory straight into registers in the
+    // accumulator layout (lane l: row l & 15, columns 4 (l >> 4) .. +3 of each
+    // 16-column block, 8 bytes per block), EP_PF passes ahead, so the gate
+    // arithmetic runs on registers and dZ never goes through LDS. dG, dU and Z
+    // (bf16) go to one of two LDS buffers per pass, from which the rank
+    // products read their operands and the row-contiguous stores of dG and dU
+    // are made.
+    constexpr int JB = NB / 2;  // 16-column blocks of column products per wave
     const bf16_t* Gp = static_cast<const bf16_t*>(p.g_in) + t.m0 * p.ldc + t.n0;
     const bf16_t* Up = static_cast<const bf16_t*>(p.u_in) + t.m0 * p.ldc + t.n0;
     bf16_t* dGp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
     bf16_t* dUp = static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.n0;
-    // LDS: one 64-row quarter of the tile at a time
-    char* dzs = smem;                        // dZ fp32 [64][EP_PITCH_DZ]; then dG | dU bf16 chunks in place
-    char* zs = smem + 64 * EP_PITCH_DZ;      // Z bf16 [64][EP_PITCH_ZQ]
-    char* bt = zs + 64 * EP_PITCH_ZQ;        // B_g^T, B_u^T rows [32][512 B] over the tile's columns
-    char* pt = bt + 32 * 512;                // P_g^T, P_u^T, Q_d^T rows [48][512 B] over the tile's tokens
-    // thread -> 8 consecutive columns (chunk) of rows rsub, rsub + 8, ... of a quarter
+    char* bt = smem + 2 * EP_SBUF;  // B_g^T, B_u^T rows [32][512 B] over the tile's columns
+    char* pt = bt + 32 * 512;       // P_g^T, P_u^T, Q_d^T rows [48][512 B] over the tile's tokens
     const int tid = threadIdx.x;
-    const int chunk = tid & 31;
-    const int rsub = tid >> 5;
     const int lch = t.lane >> 4;
-    const bool cval = static_cast<uint32_t>(chunk * 8) < t.n_rows;
-    // G and U of the first quarter, fetched before they are needed; invalid
-    // positions read element 0 and are never stored
-    uint4 gv[8], uv[8];
+    // G and U of pass a into (g, u) by buffer loads over the tile's rows.
+    // The whole offset is in the lane's VGPR, which the range check covers:
+    // rows past M fall past num_records and read zero, and columns past N get
+    // an offset past it.
+    const int crow = wm * 128 + lrow;         // tile row of the lane in pass 0
+    const int ccol = wn * 16 * NB + 4 * lch;  // tile column of the lane in block 0
+    const int nrec = static_cast<int>(t.m_rows * p.ldc * 2);
+    const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Gp), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rU = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Up), 0, nrec, 0x00020000);
+    const int vb = (crow * static_cast<int>(p.ldc) + ccol) * 2;
+    auto fetch = [&](int a, uint2 (&g)[NB], uint2 (&u)[NB]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * i + rsub;
-      const int64_t off = (cval && static_cast<uint32_t>(r) < t.m_rows) ? r * p.ldc + chunk * 8 : 0;
-      gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
-      uv[i] = *reinterpret_cast<const uint4*>(Up + off);
-    }
+      for (int b = 0; b < NB; ++b) {
+        const bool ok = static_cast<uint32_t>(ccol + 16 * b) < t.n_rows;
+        const int vo = ok ? vb + (16 * a * static_cast<int>(p.ldc) + 16 * b) * 2 : static_cast<int>(OOB);
+        const auto gv = __builtin_amdgcn_raw_buffer_load_b64(rG, vo, 0, 0);
+        const auto uv = __builtin_amdgcn_raw_buffer_load_b64(rU, vo, 0, 0);
+        g[b] = make_uint2(gv[0], gv[1]);
+        u[b] = make_uint2(uv[0], uv[1]);
+      }
+    };
+    // (the last of the first EP_PF passes after the rank rows are written: the
+    // compiler's wait for those, at most 63 newer loads, then waits for none)
+    uint2 pg[EP_PF][NB], pu[EP_PF][NB];
+    static_assert(2 * NB * (EP_PF - 1) <= 63, "vmcnt range");
+#pragma unroll
+    for (int a = 0; a < EP_PF - 1; ++a) fetch(a, pg[a], pu[a]);
     lds_barrier();  // every wave is done with the ring
-    // Rank rows by LDS DMA, two 512-byte rows per instruction, chunk c of row n
-    // at position c ^ (n & 7); what lies past N (columns) or T (tokens) reads
-    // zero. bt: waves 0-1 fetch B_g^T, 2-3 B_u^T (4 instructions each). pt:
-    // rows 0-31 from P^T (P_g then P_u), 32-47 from Q_d^T (6 per wave).
-    {
-      const rsrc_t rb = make_rsrc(t.wave < 2 ? p.pj_b0 : p.pj_b1, static_cast<uint32_t>(16 * p.pj_ldb * 2));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 8 * t.wave + 2 * j + (t.lane >> 5);  // 0..31
-        const int col = ((t.lane & 31) ^ (row & 7)) * 8;
-        const uint32_t voff = static_cast<uint32_t>(col) < t.n_rows
-                                  ? static_cast<uint32_t>(((row & 15) * p.pj_ldb + t.n0 + col) * 2)
-                                  : OOB;
-        dma16(rb, bt + (8 * t.wave + 2 * j) * 512, voff, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 6; ++j) {
-        const int row0 = 12 * t.wave + 2 * j;  // first of the two rows, uniform
-        const bool isq = row0 >= 32;
-        const rsrc_t rp = make_rsrc(isq ? p.pj_qdT : p.pj_pguT, static_cast<uint32_t>((isq ? 16 : 32) * p.pj_ldt * 2));
-        const int row = row0 + (t.lane >> 5);
-        const int tok = ((t.lane & 31) ^ (row & 7)) * 8;
-        const uint32_t voff = static_cast<uint32_t>(tok) < t.m_rows
-                                  ? static_cast<uint32_t>(((row - (isq ? 32 : 0)) * p.pj_ldt + t.m0 + tok) * 2)
-                                  : OOB;
-        dma16(rp, pt + row0 * 512, voff, 0);
-      }
+    for (int j = 0; j < 10; ++j) {
+      const int idx = tid + NTHREADS * (j < 4 ? j : j - 4);
+      const int row = idx >> 5, c = idx & 31;
+      char* dst = (j < 4 ? bt : pt) + row * 512 + ((c ^ (row & 7)) << 4);
+      *reinterpret_cast<uint4*>(dst) = pre.rk[j];
     }
-    // column products, summed over the tile's tokens: wave w owns columns
-    // 64w .. 64w+63 (16-column blocks ib = 4w + j)
-    f32x4_t cg[4], cu[4], cz[4];
+    fetch(EP_PF - 1, pg[EP_PF - 1], pu[EP_PF - 1]);
+    // column products, summed over the tile's tokens: wave w owns the
+    // 16-column blocks JB w .. JB w + JB - 1
+    f32x4_t cg[JB], cu[JB], cz[JB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cg[j] = cu[j] = cz[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < JB; ++j) cg[j] = cu[j] = cz[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int srow = wm * 16 + lrow;  // staging row of the lane's accumulator rows
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      if (wm == (qt >> 1)) {
+    for (int a = 0; a < 8; ++a) {
+      __builtin_amdgcn_sched_barrier(0);
+      char* sgb = smem + (a & 1) * EP_SBUF;  // dG [32][EP_SP]
+      char* sub = sgb + 32 * EP_SP;          // dU
+      char* szb = sub + 32 * EP_SP;          // Z
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+      for (int b = 0; b < NB; ++b) {
+        const uint2 gq = pg[a % EP_PF][b], uq = pu[a % EP_PF][b];
+        const float g[4] = {__uint_as_float(gq.x << 16), __uint_as_float(gq.x & 0xFFFF0000u),
+                            __uint_as_float(gq.y << 16), __uint_as_float(gq.y & 0xFFFF0000u)};
+        const float u[4] = {__uint_as_float(uq.x << 16), __uint_as_float(uq.x & 0xFFFF0000u),
+                            __uint_as_float(uq.y << 16), __uint_as_float(uq.y & 0xFFFF0000u)};
+        float dg[4], du[4], z[4];
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
-            *reinterpret_cast<f32x4_t*>(dzs + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 16 * NB + b * 16 + lcol) * 4) =
-                acc[4 * (qt & 1) + a][b];
-      }
-      if (qt == 0) wait_vmcnt<0>();  // the rank rows (and G, U of the quarter) have landed
-      lds_barrier();
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rl = 8 * i + rsub;   // row within the quarter
-        const int r = qt * 64 + rl;    // row within the tile
-        const float4 d0 = *reinterpret_cast<const float4*>(dzs + rl * EP_PITCH_DZ + chunk * 32);
-        const float4 d1 = *reinterpret_cast<const float4*>(dzs + rl * EP_PITCH_DZ + chunk * 32 + 16);
-        const float dz[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-        float g[8], u[8], dg[8], du[8], z[8];
-        bf16x8_to_f32(gv[i], g);
-        bf16x8_to_f32(uv[i], u);
-        if (qt < 3) {  // this slot is free: fetch the same position of the next quarter
-          const int r2 = r + 64;
-          const int64_t off = (cval && static_cast<uint32_t>(r2) < t.m_rows) ? r2 * p.ldc + chunk * 8 : 0;
-          gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
-          uv[i] = *reinterpret_cast<const uint4*>(Up + off);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
+          const float dz = acc[a][b][e];
           const float sg = sigmoidf_fast(g[e]);
           const float act = g[e] * sg;
-          dg[e] = dz[e] * u[e] * sg * (1.0f + g[e] * (1.0f - sg));
-          du[e] = dz[e] * act;
+          dg[e] = dz * u[e] * sg * (1.0f + g[e] * (1.0f - sg));
+          du[e] = dz * act;
           z[e] = act * u[e];
         }
-        const bool ok = cval && static_cast<uint32_t>(r) < t.m_rows;
-        const uint4 dgb = ok ? f32x8_to_bf16(dg) : zero4();
-        const uint4 dub = ok ? f32x8_to_bf16(du) : zero4();
-        if (ok) {
-          const int64_t off = r * p.ldc + chunk * 8;
-          *reinterpret_cast<uint4*>(dGp + off) = dgb;
-          *reinterpret_cast<uint4*>(dUp + off) = dub;
-        }
-        // the 32 bytes of dZ just read now hold the bf16 dG and dU chunks
-        *reinterpret_cast<uint4*>(dzs + rl * EP_PITCH_DZ + chunk * 32) = dgb;
-        *reinterpret_cast<uint4*>(dzs + rl * EP_PITCH_DZ + chunk * 32 + 16) = dub;
-        *reinterpret_cast<uint4*>(zs + rl * EP_PITCH_ZQ + chunk * 16) = ok ? f32x8_to_bf16(z) : zero4();
+        const int off = srow * EP_SP + (wn * 16 * NB + 16 * b + 4 * lch) * 2;
+        *reinterpret_cast<uint2*>(sgb + off) = make_uint2(pack_bf16x2_pk(dg[0], dg[1]), pack_bf16x2_pk(dg[2], dg[3]));
+        *reinterpret_cast<uint2*>(sub + off) = make_uint2(pack_bf16x2_pk(du[0], du[1]), pack_bf16x2_pk(du[2], du[3]));
+        *reinterpret_cast<uint2*>(szb + off) = make_uint2(pack_bf16x2_pk(z[0], z[1]), pack_bf16x2_pk(z[2], z[3]));
+        __builtin_amdgcn_sched_barrier(0);
       }
-      lds_barrier();
+      if (a + EP_PF < 8) fetch(a + EP_PF, pg[a % EP_PF], pu[a % EP_PF]);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();  // the pass's staging (and, at pass 0, the rank rows) complete
+      __builtin_amdgcn_sched_barrier(0);
       // Row products: Q_g[token][n] = sum over the tile's columns of dG * B_g
-      // (B_g^T row n = l & 15), likewise Q_u; wave w takes token block w of the
-      // quarter, whose staged dG chunk (row l & 15, chunk 4 ks + l / 16) is the
-      // MFMA source as it stands.
+      // (B_g^T row n = l & 15), likewise Q_u: wave w takes token block w & 1 of
+      // the pass and product w >> 1; the staged chunk (row l & 15, chunk
+      // 4 ks + l / 16) is the MFMA source as it stands.
       {
-        f32x4_t qg = f32x4_t{0.f, 0.f, 0.f, 0.f}, qu = qg;
+        const int tb = t.wave & 1;
+        const int pr = t.wave >> 1;
+        const char* src = (pr ? sub : sgb) + (tb * 16 + lrow) * EP_SP;
+        const char* brow = bt + (pr * 16 + lrow) * 512;
+        f32x4_t q = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < NB; ++ks) {
           const int ch = ks * 4 + lch;
-          const int bpos = (ch ^ (lrow & 7)) << 4;
-          const uint4 bg = *reinterpret_cast<const uint4*>(bt + lrow * 512 + bpos);
-          const uint4 bu = *reinterpret_cast<const uint4*>(bt + (16 + lrow) * 512 + bpos);
-          const char* src = dzs + (t.wave * 16 + lrow) * EP_PITCH_DZ + ch * 32;
-          qg = mma<bf16_t>::step(bg, *reinterpret_cast<const uint4*>(src), qg);
-          qu = mma<bf16_t>::step(bu, *reinterpret_cast<const uint4*>(src + 16), qu);
+          const uint4 bv = *reinterpret_cast<const uint4*>(brow + ((ch ^ (lrow & 7)) << 4));
+          q = mma<bf16_t>::step(bv, *reinterpret_cast<const uint4*>(src + ch * 16), q);
         }
-        // lane l holds Q[token = 16w + (l & 15)][n = 4*(l >> 4) .. +3]: one
-        // split-K slice (this tile column)
-        const int r = qt * 64 + t.wave * 16 + lrow;
+        // lane l holds Q[token = staging row 16 tb + (l & 15)][n = 4 (l >> 4) .. +3]:
+        // one split-K slice (this tile column)
+        const int r = tb * 128 + 16 * a + lrow;
         if (static_cast<uint32_t>(r) < t.m_rows) {
           const int64_t base = ((p.pj_slice0 + t.n0 / (32 * NB)) * p.pj_T + t.m0 + r) * 16 + 4 * lch;
-          *reinterpret_cast<f32x4_t*>(p.pj_part0 + base) = qg;
-          *reinterpret_cast<f32x4_t*>(p.pj_part1 + base) = qu;
+          *reinterpret_cast<f32x4_t*>((pr ? p.pj_part1 : p.pj_part0) + base) = q;
         }
       }
-      // Column products over this quarter's 64 tokens (two k-steps):
+      // Column products over the pass's 32 tokens (one k-step):
       // dB_g^T[n][col] += sum over tokens of P_g^T[n][t] dG[t][col], likewise
-      // dB_u^T with dU and dA_d[n][col] with Q_d^T and Z. The column operand is
-      // read transposed (ds_read_b64_tr_b16): lane l gets column 16 ib + (l & 15)
-      // and tokens 8 (l >> 4) .. +7 of the k-step.
+      // dB_u^T with dU and dA_d[n][col] with Q_d^T and Z. Lane l supplies k
+      // slots 8 (l >> 4) .. +7 = staging rows, i.e. tokens tok0 .. tok0 + 7;
+      // the column operand is read transposed (ds_read_b64_tr_b16): column
+      // 16 ib + (l & 15) of those staging rows.
+      {
+        const int tok0 = (lch >> 1) * 128 + 16 * a + 8 * (lch & 1);
+        const int ppos = (((tok0 >> 3) ^ (lrow & 7)) << 4);
+        const uint4 pgv = *reinterpret_cast<const uint4*>(pt + lrow * 512 + ppos);
+        const uint4 puv = *reinterpret_cast<const uint4*>(pt + (16 + lrow) * 512 + ppos);
+        const uint4 pqv = *reinterpret_cast<const uint4*>(pt + (32 + lrow) * 512 + ppos);
+        const int krow = lch * 8 + (lrow >> 2);  // staging row of the first transposed read
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int kc = (qt * 2 + ks) * 4 + lch;  // token chunk within the tile
-        const int ppos = (kc ^ (lrow & 7)) << 4;
-        const uint4 pg = *reinterpret_cast<const uint4*>(pt + lrow * 512 + ppos);
-        const uint4 pu = *reinterpret_cast<const uint4*>(pt + (16 + lrow) * 512 + ppos);
-        const uint4 pq = *reinterpret_cast<const uint4*>(pt + (32 + lrow) * 512 + ppos);
-        const int krow = ks * 32 + lch * 8 + (lrow >> 2);  // token row of the first transposed read
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c0 = (4 * t.wave + j) * 16 + 4 * (lrow & 3);  // first of this lane's 4 columns
-          const char* sg = dzs + krow * EP_PITCH_DZ + (c0 >> 3) * 32 + (c0 & 7) * 2;
-          const char* sz = zs + krow * EP_PITCH_ZQ + c0 * 2;
-          const uint4 tg = read_tr16x2(sg, 4 * EP_PITCH_DZ);
-          const uint4 tu = read_tr16x2(sg + 16, 4 * EP_PITCH_DZ);
-          const uint4 tz = read_tr16x2(sz, 4 * EP_PITCH_ZQ);
-          cg[j] = mma<bf16_t>::step(pg, tg, cg[j]);
-          cu[j] = mma<bf16_t>::step(pu, tu, cu[j]);
-          cz[j] = mma<bf16_t>::step(pq, tz, cz[j]);
+        for (int j = 0; j < JB; ++j) {
+          const int c0 = (JB * t.wave + j) * 16 + 4 * (lrow & 3);  // first of this lane's 4 columns
+          const int o = krow * EP_SP + c0 * 2;
+          cg[j] = mma<bf16_t>::step(pgv, read_tr16x2(sgb + o, 4 * EP_SP), cg[j]);
+          cu[j] = mma<bf16_t>::step(puv, read_tr16x2(sub + o, 4 * EP_SP), cu[j]);
+          cz[j] = mma<bf16_t>::step(pqv, read_tr16x2(szb + o, 4 * EP_SP), cz[j]);
         }
       }
-      if (qt < 3) lds_barrier();  // the next quarter overwrites the staging
+      // dG and dU of the pass, row-contiguous from the staging
+      {
+        constexpr int CH = 4 * NB;         // 16-byte chunks of a staging row
+        constexpr int RS = NTHREADS / CH;  // staging rows per step
+        const int chunk = tid % CH;
+        const bool cv = static_cast<uint32_t>(chunk * 8) < t.n_rows;
+#pragma unroll
+        for (int s = tid / CH; s < 32; s += RS) {
+          const int r = (s >> 4) * 128 + 16 * a + (s & 15);
+          const uint4 vg = *reinterpret_cast<const uint4*>(sgb + s * EP_SP + chunk * 16);
+          const uint4 vu = *reinterpret_cast<const uint4*>(sub + s * EP_SP + chunk * 16);
+          if (cv && static_cast<uint32_t>(r) < t.m_rows) {
+            *reinterpret_cast<uint4*>(dGp + r * p.ldc + chunk * 8) = vg;
+            *reinterpret_cast<uint4*>(dUp + r * p.ldc + chunk * 8) = vu;
+          }
+        }
+      }
     }
-    // lane l holds [n = 4*(l >> 4) .. +3][col = 16 ib + (l & 15)] summed over
+    // lane l holds [n = 4 (l >> 4) .. +3][col = 16 ib + (l & 15)] summed over
     // the tile's tokens: one slice (this tile row) of each [col][16] partial
     const int64_t mt = t.m0 / BM;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = (4 * t.wave + j) * 16 + lrow;
+    for (int j = 0; j < JB; ++j) {
+      const int col = (JB * t.wave + j) * 16 + lrow;
       if (static_cast<uint32_t>(col) < t.n_rows) {
         const int64_t off = (mt * p.pj_ncol + t.n0 + col) * 16 + 4 * lch;
         *reinterpret_cast<f32x4_t*>(p.pj_cdg + off) = cg[j];
@@ -643,10 +672,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
 // Output tile of this workgroup: XCD-aware (block b runs on XCD b % 8), each
 // XCD sweeping bands of group_m tiles along M so that its L2 reuses B panels.
 template <int EPI, int NB = 8>
-__device__ __forceinline__ void select_tile(const GemmParams& p, TileCtx& t) {
+__device__ __forceinline__ void select_tile(const GemmParams& p, TileCtx& t, int bid, int nblk) {
   constexpr int TN = 32 * NB;  // tile width (gate/up: interleaved gate and up columns)
-  const int nblk = gridDim.x;
-  const int bid = blockIdx.x;
   const int per = nblk / 8, rem = nblk % 8, x = bid % 8;
   const int logical = x * per + (x < rem ? x : rem) + bid / 8;
   const int gm = p.group_m;
@@ -666,10 +693,10 @@ __device__ __forceinline__ void select_tile(const GemmParams& p, TileCtx& t) {
 
 }
 
+// One output tile: workgroup `bid` of `nblk` that share the tile sequence of p
+// (bid % 8 must be the XCD the workgroup runs on for the XCD-aware order).
 template <bool NN, int EPI, int QRB, int NB>
-__device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
-
+__device__ __forceinline__ void gemm_bf16_body(const GemmParams& p, int bid, int nblk, char* smem) {
   TileCtx t;
   t.lane = threadIdx.x & 63;
   t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -677,7 +704,9 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   const int wm = t.wave >> 1;
   const int wn = t.wave & 1;
 
-  select_tile<EPI, NB>(p, t);
+  select_tile<EPI, NB>(p, t, bid, nblk);
+  EpiPre pre;
+  epi_preload<EPI, QRB>(p, t, pre);
 
   const Seg s0 = seg_at(p, 0), s1 = seg_at(p, 1), s2 = seg_at(p, 2);
   int nk = (s0.K + BK - 1) / BK + (s1.K + BK - 1) / BK + (s2.K + BK - 1) / BK;
@@ -729,12 +758,13 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p) {
   // workgroup can exit and hand its LDS to another workgroup
   wait_vmcnt<0>();
 
-  epilogue_lds<EPI, QRB, NB>(p, acc, t, wm, wn, smem);
+  epilogue_lds<EPI, QRB, NB>(p, acc, t, wm, wn, smem, pre);
 }
 
 template <bool NN, int EPI, int QRB, int NB>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmParams p) {
-  gemm_bf16_body<NN, EPI, QRB, NB>(p);
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  gemm_bf16_body<NN, EPI, QRB, NB>(p, blockIdx.x, gridDim.x, smem);
 }
 
 // ---- 4-bit B operand (NT products with 4-bit block weights) ---------------
@@ -887,7 +917,7 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
   t.c1 = (t.lane & 3) ^ ((t.lane >> 3) & 3);
   const int wm = t.wave >> 1;
   const int wn = t.wave & 1;
-  select_tile<EPI>(p, t);
+  select_tile<EPI>(p, t, blockIdx.x, gridDim.x);
 
   const int nkq = static_cast<int>(p.seg[0].K / BK);  // K is a multiple of 64: an even count
 
@@ -971,7 +1001,8 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
     }
   }
 
-  epilogue_lds<EPI>(p, acc, t, wm, wn, smem);
+  const EpiPre none{};
+  epilogue_lds<EPI>(p, acc, t, wm, wn, smem, none);
 }
 
 template <int EPI>

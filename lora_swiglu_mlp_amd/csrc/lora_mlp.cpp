@@ -151,7 +151,9 @@ size_t rp_part_bytes(const Dims& d, int64_t K, int n1p) {
 // bf16 with r <= 16: the dZ GEMM's epilogue also forms the row projections
 // dG B_g and dU B_u (one split-K slice per 256-column tile of I) and the
 // column products P_g^T dG, P_u^T dU and Q_d^T Z (one slice per 256-row tile).
-bool fused_q(const Dims& d) { return d.bf16 && d.r16 == 16; }
+// The fused epilogue addresses a 256-row tile of G and U with 32-bit byte
+// offsets (256 * I * 2 bytes must stay below 2^31).
+bool fused_q(const Dims& d) { return d.bf16 && d.r16 == 16 && d.I < (int64_t(1) << 22); }
 // Row-product slices at most (every column in 128-wide tiles); the actual
 // count follows the dZ GEMM's split (dz_split).
 int64_t q_slices(const Dims& d) { return (d.I + 127) / 128; }
