@@ -514,31 +514,46 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     char* pt = bt + 32 * 512;       // P_g^T, P_u^T, Q_d^T rows [48][512 B] over the tile's tokens
     const int tid = threadIdx.x;
     const int lch = t.lane >> 4;
-    // G and U of pass a into (g, u) by buffer loads over the tile's rows.
-    // The whole offset is in the lane's VGPR, which the range check covers:
-    // rows past M fall past num_records and read zero, and columns past N get
-    // an offset past it.
+    // G and U of pass a into (g, u), by buffer loads over the tile's rows: 16
+    // bytes per lane, lane l reading row l & 15 at columns 8 (l >> 4) .. +7 of
+    // each 32-column pair of accumulator blocks (an instruction covers 16 rows
+    // x 64 bytes; 8-byte loads in the accumulator layout itself, 16 rows x 32
+    // bytes, fetch at half the rate per compute unit). Two permlane16 and two
+    // permlane32 swaps then give every lane its accumulator-layout columns
+    // 4 (l >> 4) .. +3 of both blocks. The whole offset is in the lane's VGPR,
+    // which the range check covers: rows past M fall past num_records and read
+    // zero, and chunks past N (a multiple of 8) get an offset past it.
     const int crow = wm * 128 + lrow;         // tile row of the lane in pass 0
-    const int ccol = wn * 16 * NB + 4 * lch;  // tile column of the lane in block 0
+    const int ccol = wn * 16 * NB + 8 * lch;  // first column of the lane's chunk in pair 0
     const int nrec = static_cast<int>(t.m_rows * p.ldc * 2);
     const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Gp), 0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t rU = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Up), 0, nrec, 0x00020000);
     const int vb = (crow * static_cast<int>(p.ldc) + ccol) * 2;
-    auto fetch = [&](int a, uint2 (&g)[NB], uint2 (&u)[NB]) {
+    // dwords d0..d3 of the lanes' chunks -> accumulator-layout pairs of blocks
+    // 2j (x) and 2j + 1 (y): with D_g the chunk of lane group g (= l >> 4),
+    // group g needs D_{g>>1} dwords 2(g&1), +1 for block 2j and D_{2+(g>>1)}
+    // for block 2j + 1
+    auto to_acc_layout = [](const uint4& d, uint2& x, uint2& y) {
+      const auto s0 = __builtin_amdgcn_permlane16_swap(d.x, d.z, false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(d.y, d.w, false, false);
+      const auto t0 = __builtin_amdgcn_permlane32_swap(s0[0], s0[1], false, false);
+      const auto t1 = __builtin_amdgcn_permlane32_swap(s1[0], s1[1], false, false);
+      x = make_uint2(t0[0], t1[0]);
+      y = make_uint2(t0[1], t1[1]);
+    };
+    auto fetch = [&](int a, uint4 (&g)[NB / 2], uint4 (&u)[NB / 2]) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const bool ok = static_cast<uint32_t>(ccol + 16 * b) < t.n_rows;
-        const int vo = ok ? vb + (16 * a * static_cast<int>(p.ldc) + 16 * b) * 2 : static_cast<int>(OOB);
-        const auto gv = __builtin_amdgcn_raw_buffer_load_b64(rG, vo, 0, 0);
-        const auto uv = __builtin_amdgcn_raw_buffer_load_b64(rU, vo, 0, 0);
-        g[b] = make_uint2(gv[0], gv[1]);
-        u[b] = make_uint2(uv[0], uv[1]);
+      for (int j = 0; j < NB / 2; ++j) {
+        const bool ok = static_cast<uint32_t>(ccol + 32 * j) < t.n_rows;
+        const int vo = ok ? vb + (16 * a * static_cast<int>(p.ldc) + 32 * j) * 2 : static_cast<int>(OOB);
+        g[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rG, vo, 0, 0));
+        u[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rU, vo, 0, 0));
       }
     };
     // (the last of the first EP_PF passes after the rank rows are written: the
     // compiler's wait for those, at most 63 newer loads, then waits for none)
-    uint2 pg[EP_PF][NB], pu[EP_PF][NB];
-    static_assert(2 * NB * (EP_PF - 1) <= 63, "vmcnt range");
+    uint4 pg[EP_PF][NB / 2], pu[EP_PF][NB / 2];
+    static_assert(NB * (EP_PF - 1) <= 63, "vmcnt range");
 #pragma unroll
     for (int a = 0; a < EP_PF - 1; ++a) fetch(a, pg[a], pu[a]);
     lds_barrier();  // every wave is done with the ring
@@ -562,9 +577,15 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       char* sgb = smem + (a & 1) * EP_SBUF;  // dG [32][EP_SP]
       char* sub = sgb + 32 * EP_SP;          // dU
       char* szb = sub + 32 * EP_SP;          // Z
+      uint2 gl[NB], ul[NB];
+#pragma unroll
+      for (int j = 0; j < NB / 2; ++j) {
+        to_acc_layout(pg[a % EP_PF][j], gl[2 * j], gl[2 * j + 1]);
+        to_acc_layout(pu[a % EP_PF][j], ul[2 * j], ul[2 * j + 1]);
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const uint2 gq = pg[a % EP_PF][b], uq = pu[a % EP_PF][b];
+        const uint2 gq = gl[b], uq = ul[b];
         const float g[4] = {__uint_as_float(gq.x << 16), __uint_as_float(gq.x & 0xFFFF0000u),
                             __uint_as_float(gq.y << 16), __uint_as_float(gq.y & 0xFFFF0000u)};
         const float u[4] = {__uint_as_float(uq.x << 16), __uint_as_float(uq.x & 0xFFFF0000u),
