@@ -282,7 +282,7 @@ constexpr int EP_PITCH_GU = 128 * 2 + 16;  // bf16 [256 rows][128], G and U side
 constexpr int EP_PITCH_DZ = 256 * 4 + 16;  // fp32 [128 rows][256], one half of dZ at a time
 constexpr int EP_SP = 256 * 2 + 16;        // bf16 [32 rows][256]: dG, dU or Z of one backward pass
 constexpr int EP_SBUF = 3 * 32 * EP_SP;     // dG, dU and Z of one pass
-constexpr int EP_PF = 4;                    // backward passes whose G and U are in flight
+constexpr int EP_PF = 2;                    // backward passes whose G and U are in flight
 // LDS the staging needs: a kernel's shared array must be at least this large
 constexpr int EP_LDS_BYTES = 256 * EP_PITCH_C > 2 * 256 * EP_PITCH_GU
                                  ? (256 * EP_PITCH_C > 128 * EP_PITCH_DZ ? 256 * EP_PITCH_C : 128 * EP_PITCH_DZ)
@@ -541,13 +541,17 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       x = make_uint2(t0[0], t1[0]);
       y = make_uint2(t0[1], t1[1]);
     };
+    // chunk j (0 .. NB/2 - 1) of G (up false) or U of pass a
+    auto load_one = [&](int a, int j, bool up) {
+      const bool ok = static_cast<uint32_t>(ccol + 32 * j) < t.n_rows;
+      const int vo = ok ? vb + (16 * a * static_cast<int>(p.ldc) + 32 * j) * 2 : static_cast<int>(OOB);
+      return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(up ? rU : rG, vo, 0, 0));
+    };
     auto fetch = [&](int a, uint4 (&g)[NB / 2], uint4 (&u)[NB / 2]) {
 #pragma unroll
       for (int j = 0; j < NB / 2; ++j) {
-        const bool ok = static_cast<uint32_t>(ccol + 32 * j) < t.n_rows;
-        const int vo = ok ? vb + (16 * a * static_cast<int>(p.ldc) + 32 * j) * 2 : static_cast<int>(OOB);
-        g[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rG, vo, 0, 0));
-        u[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rU, vo, 0, 0));
+        g[j] = load_one(a, j, false);
+        u[j] = load_one(a, j, true);
       }
     };
     // (the last of the first EP_PF passes after the rank rows are written: the
@@ -570,6 +574,21 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     f32x4_t cg[JB], cu[JB], cz[JB];
 #pragma unroll
     for (int j = 0; j < JB; ++j) cg[j] = cu[j] = cz[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // store k (0 .. NB-1) of pass a's dG (k even) or dU (k odd), row-contiguous
+    // from the staging: staging row tid / CH + RS (k >> 1), 16-byte chunk tid % CH
+    constexpr int CH = 4 * NB;         // 16-byte chunks of a staging row
+    constexpr int RS = NTHREADS / CH;  // staging rows per step
+    static_assert(2 * (32 / RS) == NB, "one store per accumulator block");
+    const int chunk = tid % CH;
+    const bool cv = static_cast<uint32_t>(chunk * 8) < t.n_rows;
+    auto store_one = [&](int a, int k) {
+      const char* src = smem + (a & 1) * EP_SBUF + (k & 1) * 32 * EP_SP;
+      const int sr = tid / CH + RS * (k >> 1);
+      const int r = (sr >> 4) * 128 + 16 * a + (sr & 15);
+      const uint4 v = *reinterpret_cast<const uint4*>(src + sr * EP_SP + chunk * 16);
+      if (cv && static_cast<uint32_t>(r) < t.m_rows)
+        *reinterpret_cast<uint4*>(((k & 1) ? dUp : dGp) + r * p.ldc + chunk * 8) = v;
+    };
     const int srow = wm * 16 + lrow;  // staging row of the lane's accumulator rows
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
@@ -604,9 +623,17 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
         *reinterpret_cast<uint2*>(sgb + off) = make_uint2(pack_bf16x2_pk(dg[0], dg[1]), pack_bf16x2_pk(dg[2], dg[3]));
         *reinterpret_cast<uint2*>(sub + off) = make_uint2(pack_bf16x2_pk(du[0], du[1]), pack_bf16x2_pk(du[2], du[3]));
         *reinterpret_cast<uint2*>(szb + off) = make_uint2(pack_bf16x2_pk(z[0], z[1]), pack_bf16x2_pk(z[2], z[3]));
+        // one load of pass a + EP_PF (into the registers this pass has just
+        // converted) and one store of pass a - 1 per block: spread through
+        // the arithmetic, the vector memory instructions find the queue
+        // drained instead of stalling in a burst behind each other
+        if (a + EP_PF < 8) {
+          if (b & 1) pu[a % EP_PF][b >> 1] = load_one(a + EP_PF, b >> 1, true);
+          else pg[a % EP_PF][b >> 1] = load_one(a + EP_PF, b >> 1, false);
+        }
+        if (a > 0) store_one(a - 1, b);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (a + EP_PF < 8) fetch(a + EP_PF, pg[a % EP_PF], pu[a % EP_PF]);
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();  // the pass's staging (and, at pass 0, the rank rows) complete
       __builtin_amdgcn_sched_barrier(0);
@@ -656,24 +683,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
           cz[j] = mma<bf16_t>::step(pqv, read_tr16x2(szb + o, 4 * EP_SP), cz[j]);
         }
       }
-      // dG and dU of the pass, row-contiguous from the staging
-      {
-        constexpr int CH = 4 * NB;         // 16-byte chunks of a staging row
-        constexpr int RS = NTHREADS / CH;  // staging rows per step
-        const int chunk = tid % CH;
-        const bool cv = static_cast<uint32_t>(chunk * 8) < t.n_rows;
-#pragma unroll
-        for (int s = tid / CH; s < 32; s += RS) {
-          const int r = (s >> 4) * 128 + 16 * a + (s & 15);
-          const uint4 vg = *reinterpret_cast<const uint4*>(sgb + s * EP_SP + chunk * 16);
-          const uint4 vu = *reinterpret_cast<const uint4*>(sub + s * EP_SP + chunk * 16);
-          if (cv && static_cast<uint32_t>(r) < t.m_rows) {
-            *reinterpret_cast<uint4*>(dGp + r * p.ldc + chunk * 8) = vg;
-            *reinterpret_cast<uint4*>(dUp + r * p.ldc + chunk * 8) = vu;
-          }
-        }
-      }
     }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) store_one(7, k);
     // lane l holds [n = 4 (l >> 4) .. +3][col = 16 ib + (l & 15)] summed over
     // the tile's tokens: one slice (this tile row) of each [col][16] partial
     const int64_t mt = t.m0 / BM;
