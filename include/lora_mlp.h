@@ -81,8 +81,10 @@ typedef struct {
 } lmlp_dims;
 
 /* Bytes of the forward->backward `saved` buffer: the gate and up
- * pre-activations G, U (2*T*I elements of dtype) plus the three rank-r
- * projections X A_gate^T, X A_up^T and Z A_down^T in fp32, padded.
+ * pre-activations G, U (2*T*I elements of dtype), the three rank-r
+ * projections X A_gate^T, X A_up^T and Z A_down^T in fp32, and the adapter
+ * factors in the padded operand layouts both passes use (about
+ * 16*(3H + 3I) elements of dtype at rank <= 16), padded.
  * Returns 0 if dims is invalid. */
 size_t lora_mlp_saved_bytes(const lmlp_dims* dims);
 

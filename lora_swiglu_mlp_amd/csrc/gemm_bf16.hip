@@ -425,7 +425,9 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
         const int64_t off = r * p.ldc;
         *reinterpret_cast<uint4*>(Gp + off) = gv;
         *reinterpret_cast<uint4*>(Up + off) = uv;
-        *reinterpret_cast<uint4*>(Zp + off) = f32x8_to_bf16(z);
+        *reinterpret_cast<uint4*>(Zp + off) =
+            make_uint4(pack_bf16x2_pk(z[0], z[1]), pack_bf16x2_pk(z[2], z[3]), pack_bf16x2_pk(z[4], z[5]),
+                       pack_bf16x2_pk(z[6], z[7]));
       }
     }
   } else if (QRB == 0) {  // EPI_SWIGLU_BWD: acc = dZ; reload G, U; recompute the gate

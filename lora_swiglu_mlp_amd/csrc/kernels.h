@@ -179,7 +179,7 @@ struct PackJob {
   int32_t pad_;
 };
 struct PackParams {
-  PackJob job[8];
+  PackJob job[12];
   int32_t njobs;
   int32_t pad_;
 };

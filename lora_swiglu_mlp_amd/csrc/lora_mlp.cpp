@@ -2,13 +2,14 @@
 // launch sequence. See include/lora_mlp.h for the contract.
 //
 // Forward (all on the caller's stream, no host synchronisation):
-//   pack     adapter factors -> zero-padded operand layouts
+//   pack     adapter factors -> zero-padded operand layouts (those the backward
+//            uses too go to `saved`)
 //   rowproj  P_gu = X [A_g; A_u]^T            (fp32 -> saved; s*P_gu -> GEMM operand)
 //   gemm     [G|U] = [X | sP_gu] [W|B]^T, epilogue G, U -> saved, Z = SiLU(G) U
 //   rowproj  Pd = Z A_d^T                     (fp32 -> saved; s*Pd -> GEMM operand)
 //   gemm     Y = [Z | sPd] [W_d | B_d]^T
 // Backward:
-//   pack, rowproj Q_d = dY B_d
+//   rowproj  Q_d = dY B_d
 //   gemm     dZ = [dY | sQ_d] [W_d ; A_d], epilogue: reload G, U, recompute
 //            sigmoid(G), SiLU(G), Z; dG = dZ U sig (1 + G (1 - sig)), dU = dZ SiLU(G);
 //            at rank <= 16 also the partials of Q_g = dG B_g, Q_u = dU B_u and of
@@ -104,8 +105,11 @@ struct Carver {
   }
 };
 
+// The adapter factors in the operand layouts both passes use are packed once,
+// by the forward, next to the activations (the backward gets the same
+// weights).
 struct SavedLayout {
-  size_t g, u, pgu, pd, total;
+  size_t g, u, pgu, pd, agu_pad, ad_pad, bdT, bgT, buT, total;
 };
 SavedLayout saved_layout(const Dims& d) {
   Carver c;
@@ -114,6 +118,11 @@ SavedLayout saved_layout(const Dims& d) {
   L.u = c.take(size_t(d.T) * d.I * d.eb);
   L.pgu = c.take(size_t(d.T) * 2 * d.r16 * 4);
   L.pd = c.take(size_t(d.T) * d.r16 * 4);
+  L.agu_pad = c.take(size_t(2 * d.r16) * d.H * d.eb);  // [A_g; A_u], rank rows zero-padded
+  L.ad_pad = c.take(size_t(d.r16) * d.I * d.eb);       // A_d
+  L.bdT = c.take(size_t(d.r16) * d.H * d.eb);          // B_d^T
+  L.bgT = c.take(size_t(d.r16) * d.I * d.eb);          // B_g^T
+  L.buT = c.take(size_t(d.r16) * d.I * d.eb);          // B_u^T
   L.total = c.off;
   return L;
 }
@@ -201,7 +210,7 @@ int64_t colproj_tr(int64_t T, int ntb) {
 int64_t ld_tok(const Dims& d) { return (d.T + 63) / 64 * 64; }  // token-contiguous rows
 
 struct FwdLayout {
-  size_t z, aext_gu, aext_d, agu_pad, ad_pad, bext_g, bext_u, bext_d, rp_part, sc_g, sc_u, sc_d;
+  size_t z, aext_gu, aext_d, bext_g, bext_u, bext_d, rp_part, sc_g, sc_u, sc_d;
   size_t wq_g, wq_u, wq_d, total;
 };
 FwdLayout fwd_layout(const Dims& d) {
@@ -210,8 +219,6 @@ FwdLayout fwd_layout(const Dims& d) {
   L.z = c.take(size_t(d.T) * d.I * d.eb);
   L.aext_gu = c.take(size_t(d.T) * 2 * d.r16 * d.eb);
   L.aext_d = c.take(size_t(d.T) * d.r16 * d.eb);
-  L.agu_pad = c.take(size_t(2 * d.r16) * d.H * d.eb);
-  L.ad_pad = c.take(size_t(d.r16) * d.I * d.eb);
   L.bext_g = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.bext_u = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.bext_d = c.take(size_t(d.H) * d.r16 * d.eb);
@@ -230,7 +237,7 @@ FwdLayout fwd_layout(const Dims& d) {
 }
 
 struct BwdLayout {
-  size_t dg, du, z, qd, aext_d, qgu, aext_gu, bdT, bgT, buT, ad_pad, agu_pad;
+  size_t dg, du, z, qd, aext_d, qgu, aext_gu;
   size_t rp_a, rp_b, pguT, pdT, qdT, qguT, wq_g, wq_u, wq_d;
   size_t part_dg, part_du, part_z, part_x, part_dy, total;
   int ntb;
@@ -249,11 +256,6 @@ BwdLayout bwd_layout(const Dims& d) {
   L.aext_d = c.take(size_t(d.T) * d.r16 * d.eb);
   L.qgu = c.take(size_t(d.T) * 2 * d.r16 * 4);
   L.aext_gu = c.take(size_t(d.T) * 2 * d.r16 * d.eb);
-  L.bdT = c.take(size_t(d.r16) * d.H * d.eb);
-  L.bgT = c.take(size_t(d.r16) * d.I * d.eb);
-  L.buT = c.take(size_t(d.r16) * d.I * d.eb);
-  L.ad_pad = c.take(size_t(d.r16) * d.I * d.eb);
-  L.agu_pad = c.take(size_t(2 * d.r16) * d.H * d.eb);
   L.rp_a = c.take(std::max({rp_part_bytes(d, d.H, int(d.r16)), rp_part_bytes(d, d.I, int(d.r16)), q_part_bytes(d)}));
   L.rp_b = c.take(std::max(rp_part_bytes(d, d.I, int(d.r16)), q_part_bytes(d)));
   // transposed, token-contiguous copies of the [T, r] operands of the column
@@ -563,8 +565,8 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   char* Z = at(workspace, FL.z);
   char* aext_gu = at(workspace, FL.aext_gu);
   char* aext_d = at(workspace, FL.aext_d);
-  char* agu_pad = at(workspace, FL.agu_pad);
-  char* ad_pad = at(workspace, FL.ad_pad);
+  char* agu_pad = at(saved, SL.agu_pad);
+  char* ad_pad = at(saved, SL.ad_pad);
   char* bext_g = at(workspace, FL.bext_g);
   char* bext_u = at(workspace, FL.bext_u);
   char* bext_d = at(workspace, FL.bext_d);
@@ -578,7 +580,11 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   pk.job[4] = pack_job(bext_u, 2 * r16, I, r16, nullptr, 0, 0, 0, false);
   pk.job[5] = pack_job(bext_u + size_t(r16) * eb, 2 * r16, I, r16, b_up, r, I, r, false);
   pk.job[6] = pack_job(bext_d, r16, H, r16, b_down, r, H, r, false);
-  pk.njobs = 7;
+  // for the backward
+  pk.job[7] = pack_job(at(saved, SL.bdT), H, r16, H, b_down, r, H, r, true);  // B_d^T
+  pk.job[8] = pack_job(at(saved, SL.bgT), I, r16, I, b_gate, r, I, r, true);  // B_g^T
+  pk.job[9] = pack_job(at(saved, SL.buT), I, r16, I, b_up, r, I, r, true);    // B_u^T
+  pk.njobs = 10;
   LMLP_LAUNCH("pack(fwd)", launch_pack(pk, eb, st));
   float* sc_g = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_g)) : nullptr;
   float* sc_u = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_u)) : nullptr;
@@ -711,11 +717,12 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   char* aext_d = at(workspace, BL.aext_d);
   float* Qgu = reinterpret_cast<float*>(at(workspace, BL.qgu));
   char* aext_gu = at(workspace, BL.aext_gu);
-  char* bdT = at(workspace, BL.bdT);
-  char* bgT = at(workspace, BL.bgT);
-  char* buT = at(workspace, BL.buT);
-  char* ad_pad = at(workspace, BL.ad_pad);
-  char* agu_pad = at(workspace, BL.agu_pad);
+  // adapter factors packed by the forward
+  const char* bdT = at(saved, SL.bdT);
+  const char* bgT = at(saved, SL.bgT);
+  const char* buT = at(saved, SL.buT);
+  const char* ad_pad = at(saved, SL.ad_pad);
+  const char* agu_pad = at(saved, SL.agu_pad);
   float* rpa = reinterpret_cast<float*>(at(workspace, BL.rp_a));
   float* rpb = reinterpret_cast<float*>(at(workspace, BL.rp_b));
   const int64_t ldT = ld_tok(d);
@@ -729,15 +736,6 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   float* part_x = reinterpret_cast<float*>(at(workspace, BL.part_x));
   float* part_dy = reinterpret_cast<float*>(at(workspace, BL.part_dy));
 
-  PackParams pk{};
-  pk.job[0] = pack_job(bdT, H, r16, H, b_down, r, H, r, true);   // B_d^T
-  pk.job[1] = pack_job(bgT, I, r16, I, b_gate, r, I, r, true);   // B_g^T
-  pk.job[2] = pack_job(buT, I, r16, I, b_up, r, I, r, true);     // B_u^T
-  pk.job[3] = pack_job(ad_pad, I, r16, I, a_down, I, r, I, false);
-  pk.job[4] = pack_job(agu_pad, H, r16, H, a_gate, H, r, H, false);
-  pk.job[5] = pack_job(agu_pad + size_t(r16) * H * eb, H, r16, H, a_up, H, r, H, false);
-  pk.njobs = 6;
-  LMLP_LAUNCH("pack(bwd)", launch_pack(pk, eb, st));
   const void* wg = w_gate;
   const void* wu = w_up;
   const void* wd = w_down;

@@ -51,10 +51,13 @@ def align(n):
 def test_saved_bytes_formula(T, H, I, r, dt):
     eb = 2 if dt == "bf16" else 4
     r16 = (r + 15) // 16 * 16
-    want = 2 * align(T * I * eb) + align(T * 2 * r16 * 4) + align(T * r16 * 4)
+    # G, U; P_gu, P_d (fp32); the adapter factors packed for both passes:
+    # [A_g; A_u], A_d, B_d^T, B_g^T, B_u^T (rank rows padded to r16)
+    packed = align(2 * r16 * H * eb) + align(r16 * I * eb) + align(r16 * H * eb) + 2 * align(r16 * I * eb)
+    want = 2 * align(T * I * eb) + align(T * 2 * r16 * 4) + align(T * r16 * 4) + packed
     assert abi.lora_mlp_saved_bytes(dims(tokens=T, hidden=H, inter=I, rank=r, dtype=dt)) == want
     # only the gate/up pre-activations are kept at activation size: no SiLU(G), no Z
-    assert want <= 2 * T * I * eb + 3 * T * r16 * 4 + 4 * 256
+    assert want <= 2 * T * I * eb + 3 * T * r16 * 4 + 3 * r16 * (H + I) * eb + 9 * 256
 
 
 def test_workspace_sizes_positive_and_consume_flag_saves_memory():
