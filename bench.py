@@ -43,13 +43,16 @@ def kernel_flops(name: str, T: int, H: int, I: int, r: int) -> int:
 
 
 def kernel_bytes(name: str, T: int, H: int, I: int, r: int, eb: int) -> int:
-    """Algorithmic HBM bytes of one launch of the rank-r side kernels."""
+    """Algorithmic HBM bytes of one launch of the rank-r side kernels. bf16 at
+    rank <= 16 forms the products of dG, dU and Z in the dZ epilogue, and the
+    column projection then reads only X and dY."""
+    fused = eb == 2 and r <= 16
     return {
         "rowproj(X A^T)": T * H * eb + T * 2 * r * (4 + eb),
         "rowproj(Z A_d^T)": T * I * eb + T * r * (4 + eb),
         "rowproj(dY B_d)": T * H * eb + T * r * (4 + eb),
         "rowproj(dG B_g, dU B_u)": 2 * T * I * eb + 2 * T * r * (4 + eb),
-        "colproj": (3 * T * I + 2 * T * H) * eb,
+        "colproj": (2 * T * H if fused else 3 * T * I + 2 * T * H) * eb,
     }.get(name, 0)
 
 
