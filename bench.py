@@ -36,6 +36,7 @@ def kernel_flops(name: str, T: int, H: int, I: int, r: int) -> int:
     """Algorithmic FLOPs of one launch (2mnk per product, real rank, no padding)."""
     return {
         "gemm(gate/up)": 4 * T * H * I + 4 * T * I * r,
+        "gemm(gate/up, recompute)": 4 * T * H * I + 4 * T * I * r,
         "gemm(down)": 2 * T * I * H + 2 * T * H * r,
         "gemm(dZ)": 2 * T * H * I + 2 * T * r * I,
         "gemm(dX)": 4 * T * I * H + 4 * T * r * H,
@@ -147,6 +148,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="full-recompute mode: G, U are not saved, the backward recomputes them "
+                         "(its FLOPs are not counted in the metric)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -167,7 +171,8 @@ def main():
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
     inp = I.make_inputs(wl)
-    m, x, dy = mlp.from_inputs(inp, wl, "cuda:0")
+    flags = abi.LMLP_RECOMPUTE_GU if args.recompute else 0
+    m, x, dy = mlp.from_inputs(inp, wl, "cuda:0", flags)
     saved = m.new_saved()
     y = torch.empty((T, H), dtype=m.tdtype, device="cuda:0")
     grads = m.new_grads(x.device)
@@ -195,7 +200,8 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": wl.dtype, "data": "synthetic (seeded normal draws; random-init weights)",
            "config": {"workload": wl.name, "tokens": T, "hidden": H, "inter": Iw, "rank": r,
-                      "alpha": wl.alpha, "weights": wl.wfmt, "parallelism": "single-gpu"},
+                      "alpha": wl.alpha, "weights": wl.wfmt, "parallelism": "single-gpu",
+                      "saved": "recompute G, U" if args.recompute else "G, U"},
            "tflops": tflops, "pct_of_peak": 100.0 * tflops / peak}
 
     if not args.no_profile:

@@ -68,6 +68,14 @@ typedef enum { LMLP_W_DENSE = 0, LMLP_W_INT4_B64 = 1 } lmlp_wfmt;
  * instead (no bf16 copies in the forward workspace; slower). Backward always
  * uses the bf16 copies for its two products with the transposed weights. */
 #define LMLP_INT4_INKERNEL 0x2u
+/* Full recompute (the gradient-checkpointing variant of the fused MLP): the
+ * forward keeps only the rank-r projections and the packed adapter factors
+ * in `saved` (no G, U: `saved` shrinks by 2*T*I elements of dtype and the
+ * forward writes 2*T*I elements less), and the backward recomputes G and U
+ * with the forward's gate/up product (4*T*H*I more FLOPs) into its workspace,
+ * where dG and dU then overwrite them. Outputs are bitwise equal to the
+ * default mode. LMLP_CONSUME_SAVED has no effect with it. */
+#define LMLP_RECOMPUTE_GU 0x4u
 
 typedef struct {
   int64_t tokens;  /* T >= 0 (T == 0: forward is a no-op, backward writes zero adapter gradients) */
@@ -77,11 +85,12 @@ typedef struct {
   float scale;     /* s = alpha / r, finite */
   int32_t dtype;   /* lmlp_dtype */
   int32_t wfmt;    /* lmlp_wfmt */
-  uint32_t flags;  /* bitwise OR of LMLP_CONSUME_SAVED, LMLP_INT4_INKERNEL, or 0 */
+  uint32_t flags;  /* bitwise OR of LMLP_CONSUME_SAVED, LMLP_INT4_INKERNEL, LMLP_RECOMPUTE_GU, or 0 */
 } lmlp_dims;
 
 /* Bytes of the forward->backward `saved` buffer: the gate and up
- * pre-activations G, U (2*T*I elements of dtype), the three rank-r
+ * pre-activations G, U (2*T*I elements of dtype; none with
+ * LMLP_RECOMPUTE_GU), the three rank-r
  * projections X A_gate^T, X A_up^T and Z A_down^T in fp32, and the adapter
  * factors in the padded operand layouts both passes use (about
  * 16*(3H + 3I) elements of dtype at rank <= 16), padded.

@@ -22,6 +22,7 @@ LMLP_F32, LMLP_BF16 = 0, 1
 LMLP_W_DENSE, LMLP_W_INT4_B64 = 0, 1
 LMLP_CONSUME_SAVED = 0x1
 LMLP_INT4_INKERNEL = 0x2
+LMLP_RECOMPUTE_GU = 0x4
 
 
 class lmlp_dims(ctypes.Structure):

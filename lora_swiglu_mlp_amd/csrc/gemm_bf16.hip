@@ -409,25 +409,29 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     const int chunk = tid & 15;  // 8 columns of a 128-column row
     const int rsub = tid >> 4;
     const bool cval = static_cast<uint32_t>(chunk * 8) < t.n_rows;
-    bf16_t* Gp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.j0 + chunk * 8;
-    bf16_t* Up = static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.j0 + chunk * 8;
-    bf16_t* Zp = static_cast<bf16_t*>(p.c2) + t.m0 * p.ldc + t.j0 + chunk * 8;
+    // outputs are optional (uniform branches): the backward's recompute of G
+    // and U has no Z, the forward of the recompute mode no G, U
+    bf16_t* Gp = p.c0 ? static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.j0 + chunk * 8 : nullptr;
+    bf16_t* Up = p.c1 ? static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.j0 + chunk * 8 : nullptr;
+    bf16_t* Zp = p.c2 ? static_cast<bf16_t*>(p.c2) + t.m0 * p.ldc + t.j0 + chunk * 8 : nullptr;
 #pragma unroll 4
     for (int r = rsub; r < 256; r += NTHREADS / 16) {
       const uint4 gv = *reinterpret_cast<const uint4*>(gbuf + r * EP_PITCH_GU + chunk * 16);
       const uint4 uv = *reinterpret_cast<const uint4*>(ubuf + r * EP_PITCH_GU + chunk * 16);
       if (cval && static_cast<uint32_t>(r) < t.m_rows) {
-        float g[8], u[8], z[8];
-        bf16x8_to_f32(gv, g);
-        bf16x8_to_f32(uv, u);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = g[e] * sigmoidf_fast(g[e]) * u[e];
         const int64_t off = r * p.ldc;
-        *reinterpret_cast<uint4*>(Gp + off) = gv;
-        *reinterpret_cast<uint4*>(Up + off) = uv;
-        *reinterpret_cast<uint4*>(Zp + off) =
-            make_uint4(pack_bf16x2_pk(z[0], z[1]), pack_bf16x2_pk(z[2], z[3]), pack_bf16x2_pk(z[4], z[5]),
-                       pack_bf16x2_pk(z[6], z[7]));
+        if (Gp) *reinterpret_cast<uint4*>(Gp + off) = gv;
+        if (Up) *reinterpret_cast<uint4*>(Up + off) = uv;
+        if (Zp) {
+          float g[8], u[8], z[8];
+          bf16x8_to_f32(gv, g);
+          bf16x8_to_f32(uv, u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[e] = g[e] * sigmoidf_fast(g[e]) * u[e];
+          *reinterpret_cast<uint4*>(Zp + off) =
+              make_uint4(pack_bf16x2_pk(z[0], z[1]), pack_bf16x2_pk(z[2], z[3]), pack_bf16x2_pk(z[4], z[5]),
+                         pack_bf16x2_pk(z[6], z[7]));
+        }
       }
     }
   } else if (QRB == 0) {  // EPI_SWIGLU_BWD: acc = dZ; reload G, U; recompute the gate

@@ -59,9 +59,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x4_t (&acc
           z[i] = g[i] * sigmoidf_fast(g[i]) * u[i];
         }
         const int64_t off = m * p.ldc + j;
-        store4(Gp + off, g[0], g[1], g[2], g[3]);
-        store4(Up + off, u[0], u[1], u[2], u[3]);
-        store4(Zp + off, z[0], z[1], z[2], z[3]);
+        // optional outputs (uniform): no Z in the backward's recompute of G,
+        // U; no G, U in the forward of the recompute mode
+        if (Gp) store4(Gp + off, g[0], g[1], g[2], g[3]);
+        if (Up) store4(Up + off, u[0], u[1], u[2], u[3]);
+        if (Zp) store4(Zp + off, z[0], z[1], z[2], z[3]);
       }
     }
   } else {  // EPI_SWIGLU_BWD: acc = dZ; reload G, U; recompute the gate

@@ -53,6 +53,7 @@ struct Dims {
   int64_t T, H, I, r, r16;
   float s;
   bool bf16, int4, consume;
+  bool recompute;    // G, U not saved: the backward recomputes them
   bool q4_inkernel;  // forward decodes 4-bit codes inside the GEMM staging
   int eb;  // element bytes
 };
@@ -68,7 +69,8 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   if (!std::isfinite(d->scale)) return fail(LMLP_ERR_INVALID_ARG, "scale is not finite");
   if (d->dtype != LMLP_F32 && d->dtype != LMLP_BF16) return fail(LMLP_ERR_INVALID_ARG, "unknown dtype");
   if (d->wfmt != LMLP_W_DENSE && d->wfmt != LMLP_W_INT4_B64) return fail(LMLP_ERR_INVALID_ARG, "unknown wfmt");
-  if (d->flags & ~(LMLP_CONSUME_SAVED | LMLP_INT4_INKERNEL)) return fail(LMLP_ERR_INVALID_ARG, "unknown flag bits");
+  if (d->flags & ~(LMLP_CONSUME_SAVED | LMLP_INT4_INKERNEL | LMLP_RECOMPUTE_GU))
+    return fail(LMLP_ERR_INVALID_ARG, "unknown flag bits");
   if (d->rank > 256) return fail(LMLP_ERR_UNSUPPORTED, "rank > 256");
   const int ch = d->dtype == LMLP_BF16 ? 8 : 4;
   if (d->hidden % ch || d->inter % ch)
@@ -90,7 +92,8 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   o.s = d->scale;
   o.bf16 = d->dtype == LMLP_BF16;
   o.int4 = d->wfmt == LMLP_W_INT4_B64;
-  o.consume = (d->flags & LMLP_CONSUME_SAVED) != 0;
+  o.recompute = (d->flags & LMLP_RECOMPUTE_GU) != 0;
+  o.consume = !o.recompute && (d->flags & LMLP_CONSUME_SAVED) != 0;
   o.q4_inkernel = o.int4 && (d->flags & LMLP_INT4_INKERNEL) != 0;
   o.eb = o.bf16 ? 2 : 4;
   return LMLP_OK;
@@ -109,13 +112,13 @@ struct Carver {
 // by the forward, next to the activations (the backward gets the same
 // weights).
 struct SavedLayout {
-  size_t g, u, pgu, pd, agu_pad, ad_pad, bdT, bgT, buT, total;
+  size_t g, u, pgu, pd, agu_pad, ad_pad, bdT, bgT, buT, bext_g, bext_u, total;
 };
 SavedLayout saved_layout(const Dims& d) {
   Carver c;
   SavedLayout L;
-  L.g = c.take(size_t(d.T) * d.I * d.eb);
-  L.u = c.take(size_t(d.T) * d.I * d.eb);
+  L.g = d.recompute ? 0 : c.take(size_t(d.T) * d.I * d.eb);
+  L.u = d.recompute ? 0 : c.take(size_t(d.T) * d.I * d.eb);
   L.pgu = c.take(size_t(d.T) * 2 * d.r16 * 4);
   L.pd = c.take(size_t(d.T) * d.r16 * 4);
   L.agu_pad = c.take(size_t(2 * d.r16) * d.H * d.eb);  // [A_g; A_u], rank rows zero-padded
@@ -123,6 +126,10 @@ SavedLayout saved_layout(const Dims& d) {
   L.bdT = c.take(size_t(d.r16) * d.H * d.eb);          // B_d^T
   L.bgT = c.take(size_t(d.r16) * d.I * d.eb);          // B_g^T
   L.buT = c.take(size_t(d.r16) * d.I * d.eb);          // B_u^T
+  // B_g, B_u as [I, 2 r16] (rank along K, padded): the gate/up product's
+  // adapter segment, which the backward reruns with LMLP_RECOMPUTE_GU
+  L.bext_g = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
+  L.bext_u = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.total = c.off;
   return L;
 }
@@ -210,7 +217,7 @@ int64_t colproj_tr(int64_t T, int ntb) {
 int64_t ld_tok(const Dims& d) { return (d.T + 63) / 64 * 64; }  // token-contiguous rows
 
 struct FwdLayout {
-  size_t z, aext_gu, aext_d, bext_g, bext_u, bext_d, rp_part, sc_g, sc_u, sc_d;
+  size_t z, aext_gu, aext_d, bext_d, rp_part, sc_g, sc_u, sc_d;
   size_t wq_g, wq_u, wq_d, total;
 };
 FwdLayout fwd_layout(const Dims& d) {
@@ -219,8 +226,6 @@ FwdLayout fwd_layout(const Dims& d) {
   L.z = c.take(size_t(d.T) * d.I * d.eb);
   L.aext_gu = c.take(size_t(d.T) * 2 * d.r16 * d.eb);
   L.aext_d = c.take(size_t(d.T) * d.r16 * d.eb);
-  L.bext_g = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
-  L.bext_u = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.bext_d = c.take(size_t(d.H) * d.r16 * d.eb);
   L.rp_part = c.take(std::max(rp_part_bytes(d, d.H, int(2 * d.r16)), rp_part_bytes(d, d.I, int(d.r16))));
   // 4-bit weights decoded in the GEMMs: block scales as fp32, block-major
@@ -237,7 +242,7 @@ FwdLayout fwd_layout(const Dims& d) {
 }
 
 struct BwdLayout {
-  size_t dg, du, z, qd, aext_d, qgu, aext_gu;
+  size_t g_rc, u_rc, dg, du, z, qd, aext_d, qgu, aext_gu;
   size_t rp_a, rp_b, pguT, pdT, qdT, qguT, wq_g, wq_u, wq_d;
   size_t part_dg, part_du, part_z, part_x, part_dy, total;
   int ntb;
@@ -249,8 +254,11 @@ BwdLayout bwd_layout(const Dims& d) {
   L.ntb = colproj_ntb(d);
   L.tr = colproj_tr(d.T, L.ntb);
   const size_t act = size_t(d.T) * d.I * d.eb;
-  L.dg = d.consume ? 0 : c.take(act);
-  L.du = d.consume ? 0 : c.take(act);
+  // LMLP_RECOMPUTE_GU: G, U recomputed here; dG, dU overwrite them
+  L.g_rc = d.recompute ? c.take(act) : 0;
+  L.u_rc = d.recompute ? c.take(act) : 0;
+  L.dg = d.consume || d.recompute ? 0 : c.take(act);
+  L.du = d.consume || d.recompute ? 0 : c.take(act);
   L.z = c.take(act);
   L.qd = c.take(size_t(d.T) * d.r16 * 4);
   L.aext_d = c.take(size_t(d.T) * d.r16 * d.eb);
@@ -558,8 +566,9 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t T = d.T, H = d.H, I = d.I, r = d.r, r16 = d.r16;
-  char* G = at(saved, SL.g);
-  char* U = at(saved, SL.u);
+  // with LMLP_RECOMPUTE_GU the gate/up epilogue stores only Z
+  char* G = d.recompute ? nullptr : at(saved, SL.g);
+  char* U = d.recompute ? nullptr : at(saved, SL.u);
   float* Pgu = reinterpret_cast<float*>(at(saved, SL.pgu));
   float* Pd = reinterpret_cast<float*>(at(saved, SL.pd));
   char* Z = at(workspace, FL.z);
@@ -567,8 +576,8 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   char* aext_d = at(workspace, FL.aext_d);
   char* agu_pad = at(saved, SL.agu_pad);
   char* ad_pad = at(saved, SL.ad_pad);
-  char* bext_g = at(workspace, FL.bext_g);
-  char* bext_u = at(workspace, FL.bext_u);
+  char* bext_g = at(saved, SL.bext_g);
+  char* bext_u = at(saved, SL.bext_u);
   char* bext_d = at(workspace, FL.bext_d);
   const int eb = d.eb;
 
@@ -706,12 +715,15 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
     return LMLP_OK;
   }
 
-  const char* G = at(saved, SL.g);
-  const char* U = at(saved, SL.u);
+  char* G_rc = d.recompute ? at(workspace, BL.g_rc) : nullptr;
+  char* U_rc = d.recompute ? at(workspace, BL.u_rc) : nullptr;
+  const char* G = d.recompute ? G_rc : at(saved, SL.g);
+  const char* U = d.recompute ? U_rc : at(saved, SL.u);
   const float* Pgu = reinterpret_cast<const float*>(at(saved, SL.pgu));
   const float* Pd = reinterpret_cast<const float*>(at(saved, SL.pd));
-  char* dG = d.consume ? at(saved, SL.g) : at(workspace, BL.dg);
-  char* dU = d.consume ? at(saved, SL.u) : at(workspace, BL.du);
+  // dG, dU in place of G, U when those are not needed afterwards
+  char* dG = d.recompute ? G_rc : d.consume ? at(saved, SL.g) : at(workspace, BL.dg);
+  char* dU = d.recompute ? U_rc : d.consume ? at(saved, SL.u) : at(workspace, BL.du);
   char* Z = at(workspace, BL.z);
   float* Qd = reinterpret_cast<float*>(at(workspace, BL.qd));
   char* aext_d = at(workspace, BL.aext_d);
@@ -766,7 +778,27 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
     fp.job[2] = fin_job(Pd, 1, 0, r16, int(r16), nullptr, 0, nullptr, 0, 1.f, pdT, ldT, 0);
     fp.njobs = 3;
   }
+  if (d.recompute)  // s P_gu in the compute dtype: the gate/up product's adapter segment
+    fp.job[fp.njobs++] = fin_job(Pgu, 1, 0, 2 * r16, int(2 * r16), nullptr, 0, aext_gu, 2 * r16, s, nullptr, 0, 0);
   LMLP_LAUNCH("finish(Q_d, P^T)", launch_proj_finish(fp, d.bf16, st));
+
+  if (d.recompute) {
+    // G, U again from X: the forward's gate/up product (its adapter segment
+    // from the saved P_gu, bit for bit the forward's), without Z. aext_gu is
+    // free until finish(Q_gu) overwrites it.
+    GemmParams gp{};
+    gp.nseg = 2;
+    gp.seg[0] = seg(x, H, wg, wu, H, H);
+    gp.seg[1] = seg(aext_gu, 2 * r16, at(saved, SL.bext_g), at(saved, SL.bext_u), 2 * r16, 2 * r16);
+    gp.M = T;
+    gp.N = I;
+    gp.ldc = I;
+    gp.c0 = G_rc;
+    gp.c1 = U_rc;
+    gp.c2 = nullptr;
+    gp.group_m = 8;
+    LMLP_LAUNCH("gemm(gate/up, recompute)", run_gemm(gp, d, 0, EPI_SWIGLU_FWD, st));
+  }
 
   GemmParams gz{};
   gz.nseg = 2;

@@ -53,11 +53,16 @@ def test_saved_bytes_formula(T, H, I, r, dt):
     r16 = (r + 15) // 16 * 16
     # G, U; P_gu, P_d (fp32); the adapter factors packed for both passes:
     # [A_g; A_u], A_d, B_d^T, B_g^T, B_u^T (rank rows padded to r16)
-    packed = align(2 * r16 * H * eb) + align(r16 * I * eb) + align(r16 * H * eb) + 2 * align(r16 * I * eb)
+    # and B_g, B_u as [I, 2 r16], the gate/up product's adapter segment
+    packed = (align(2 * r16 * H * eb) + align(r16 * I * eb) + align(r16 * H * eb) + 2 * align(r16 * I * eb)
+              + 2 * align(I * 2 * r16 * eb))
     want = 2 * align(T * I * eb) + align(T * 2 * r16 * 4) + align(T * r16 * 4) + packed
     assert abi.lora_mlp_saved_bytes(dims(tokens=T, hidden=H, inter=I, rank=r, dtype=dt)) == want
     # only the gate/up pre-activations are kept at activation size: no SiLU(G), no Z
-    assert want <= 2 * T * I * eb + 3 * T * r16 * 4 + 3 * r16 * (H + I) * eb + 9 * 256
+    assert want <= 2 * T * I * eb + 3 * T * r16 * 4 + 7 * r16 * (H + I) * eb + 11 * 256
+    # full recompute: no activation-sized tensor at all
+    rc = abi.lora_mlp_saved_bytes(dims(tokens=T, hidden=H, inter=I, rank=r, dtype=dt, flags=abi.LMLP_RECOMPUTE_GU))
+    assert rc == want - 2 * align(T * I * eb)
 
 
 def test_workspace_sizes_positive_and_consume_flag_saves_memory():
@@ -66,6 +71,12 @@ def test_workspace_sizes_positive_and_consume_flag_saves_memory():
     assert fw > 4096 * 14336 * 2 and bw > fw
     dc = dims(tokens=4096, hidden=4096, inter=14336, rank=16, flags=abi.LMLP_CONSUME_SAVED)
     assert abi.lora_mlp_workspace_bytes(dc, True) == bw - 2 * align(4096 * 14336 * 2)
+    # full recompute: G, U come back into the backward workspace and dG, dU
+    # overwrite them, so it is as large as without the flag; the forward's
+    # does not change
+    dr = dims(tokens=4096, hidden=4096, inter=14336, rank=16, flags=abi.LMLP_RECOMPUTE_GU)
+    assert abi.lora_mlp_workspace_bytes(dr, True) == bw
+    assert abi.lora_mlp_workspace_bytes(dr, False) == fw
 
 
 @pytest.mark.parametrize("kw,code", [

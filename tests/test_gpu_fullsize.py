@@ -37,3 +37,16 @@ def test_fullsize_parity(name):
     compare(got, ref, TOL[wl.dtype], name)
     for k in ("da_gate", "db_gate", "da_up", "db_up", "da_down", "db_down"):
         assert np.linalg.norm(got[k]) > 0, k
+
+
+def test_fullsize_recompute_mode_bitwise_equal():
+    """The recompute mode at the Llama-3-8B MLP size, in the bench's launch
+    configuration: bitwise equal to the default mode (checked against the
+    oracle above)."""
+    wl = I.WORKLOADS["llama3_8b"]
+    print(f"[case] llama3_8b recompute", flush=True)
+    inp = I.make_inputs(wl)
+    a, _ = run_hip(inp, wl)
+    b, _ = run_hip(inp, wl, flags=abi.LMLP_RECOMPUTE_GU)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k

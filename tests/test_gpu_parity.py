@@ -208,6 +208,26 @@ def test_int4_decode_modes_bitwise_equal():
         assert np.array_equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("name,flags", [
+    ("tiny_fp32", 0), ("f32_ragged", 0), ("bf16_ragged", 0), ("bf16_multi", 0), ("bf16_rank64", 0),
+    ("bf16_dz_tail", 0), ("bf16_rank8", abi.LMLP_CONSUME_SAVED), ("int4_ragged", 0),
+    ("int4_ragged", abi.LMLP_INT4_INKERNEL)])
+def test_recompute_mode_bitwise_equal(name, flags):
+    """LMLP_RECOMPUTE_GU (the gradient-checkpointing variant): the backward
+    recomputes G and U with the forward's gate/up product from the same
+    operand bits (X, the weights, and s P_gu rounded from the saved fp32
+    P_gu), so every output equals the default mode's bit for bit; the default
+    mode is checked against the oracle above. CONSUME_SAVED has no effect
+    with it."""
+    wl = workload(name)
+    print(f"[case] {name} recompute flags={flags}", flush=True)
+    inp = I.make_inputs(wl)
+    a, _ = run_hip(inp, wl)
+    b, _ = run_hip(inp, wl, flags=flags | abi.LMLP_RECOMPUTE_GU)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
 def test_int4_dequant_bit_exact_random():
     packed, scales = I.draw_int4_codes(5, 384, 1024)
     got = _dequant_gpu(packed, scales, 384, 1024)
