@@ -32,8 +32,11 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}    # MI355X published dense MFMA pe
 HBM_PEAK_GBS = 8000.0
 
 
-def kernel_flops(name: str, T: int, H: int, I: int, r: int) -> int:
-    """Algorithmic FLOPs of one launch (2mnk per product, real rank, no padding)."""
+def kernel_flops(name: str, T: int, H: int, I: int, r: int, linear: bool = False) -> int:
+    """Algorithmic FLOPs of one launch (2mnk per product, real rank, no padding).
+    For the fused LoRA linear, H is the input and I the output width."""
+    if linear:
+        return {"gemm(y)": 2 * T * H * I + 2 * T * r * I, "gemm(dX)": 2 * T * I * H + 2 * T * r * H}.get(name, 0)
     return {
         "gemm(gate/up)": 4 * T * H * I + 4 * T * I * r,
         "gemm(gate/up, recompute)": 4 * T * H * I + 4 * T * I * r,
@@ -139,6 +142,91 @@ def cpu_baseline(inp, wl, seconds: float):
             "gflops": oracle.flops(n, wl.hidden, wl.inter, wl.rank) / t / 1e9}
 
 
+def cpu_baseline_linear(inp, wl, seconds: float):
+    from oracle import lora_linear_oracle as L
+    from lora_swiglu_mlp_amd import inputs as I
+    w = {k: I.to_f64(inp[k], wl.dtype) for k in ("w", "a", "b")}
+    if wl.wfmt == "int4_b64":
+        import oracle
+        w["w"] = oracle.dequant_int4(inp["w"], inp["w_scales"], wl.hidden)
+
+    def run(n):
+        d = dict(w, x=I.to_f64(inp["x"][:n], wl.dtype), dy=I.to_f64(inp["dy"][:n], wl.dtype))
+        t0 = time.perf_counter()
+        L.forward_backward(d, wl.scale)
+        return time.perf_counter() - t0
+
+    n, t = 64, run(64)
+    while t < seconds / 4 and n < wl.tokens:
+        n = min(wl.tokens, n * 2)
+        t = run(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": os.cpu_count() or 1, "kind": "oracle",
+            "sample": f"first {n} of {wl.tokens} tokens of {wl.name}, forward+backward, fp64 numpy, {t:.1f} s"}
+
+
+def bench_linear(args, wl):
+    """The fused LoRA linear (one projection) on a LINEAR_WORKLOADS shape."""
+    import torch
+    from lora_swiglu_mlp_amd import abi, mlp
+    from lora_swiglu_mlp_amd import inputs as I
+    T, n_in, n_out, r = wl.tokens, wl.hidden, wl.inter, wl.rank
+    torch.cuda.set_device(0)
+    inp = I.make_linear_inputs(wl)
+    m, x, dy = mlp.linear_from_inputs(inp, wl, "cuda:0")
+    saved = m.new_saved()
+    y = torch.empty((T, n_out), dtype=m.tdtype, device="cuda:0")
+    grads = m.new_grads(x.device)
+    m.workspace()
+
+    def step():
+        m.forward(x, y, saved)
+        m.backward(dy, x, saved, grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flops = 4 * T * n_in * n_out + 6 * T * r * (n_in + n_out)
+    peak = PEAK_TFLOPS[wl.dtype]
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {"metric": "fused LoRA linear fwd+bwd tokens/sec + TFLOP/s as % of MI355X bf16 peak",
+           "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": wl.dtype, "data": "synthetic (seeded normal draws; random-init weights)",
+           "config": {"workload": wl.name, "tokens": T, "in": n_in, "out": n_out, "rank": r, "alpha": wl.alpha,
+                      "weights": wl.wfmt, "parallelism": "single-gpu"},
+           "tflops": tflops, "pct_of_peak": 100.0 * tflops / peak}
+    if not args.no_profile:
+        nprof = max(1, min(args.steps, 10))
+        abi.lora_mlp_profile_begin()
+        for _ in range(nprof):
+            step()
+        recs = abi.lora_mlp_profile_end()
+        agg = {}
+        for name, t in recs:
+            a = agg.setdefault(name, [0.0, 0])
+            a[0] += t
+            a[1] += 1
+        kern = {}
+        for name, (tot, cnt) in agg.items():
+            e = {"ms": tot / cnt, "launches_per_step": cnt / nprof}
+            f = kernel_flops(name, T, n_in, n_out, r, linear=True)
+            if f:
+                e["tflops"] = f / (e["ms"] * 1e-3) / 1e12
+            kern[name] = e
+        out["kernels"] = kern
+        dom = max((n for n in kern if "tflops" in kern[n]), key=lambda n: kern[n]["ms"])
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"], "peak": peak,
+                           "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / peak, "traffic": None}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_linear(inp, wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +253,9 @@ def main():
     from lora_swiglu_mlp_amd import abi, mlp
     from lora_swiglu_mlp_amd import inputs as I
 
+    if args.workload in I.LINEAR_WORKLOADS:
+        bench_linear(args, I.LINEAR_WORKLOADS[args.workload])
+        return
     wl = I.WORKLOADS[args.workload]
     T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank
     torch.cuda.set_device(0)

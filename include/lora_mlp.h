@@ -135,6 +135,36 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x,
                       void* da_up, void* db_up, void* da_down, void* db_down,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Fused LoRA linear (one projection: q, k, v, o, ...) ----------------
+ * y = x W^T + s (x A^T) B^T and its backward, the matmul-with-LoRA fusion of
+ * "Unsloth 深度分析报告" (section 创新之处): the rank-r adapter rides as r
+ * extra K-steps of the base product, the projections through A and B are one
+ * pass over x (forward) and over dy (backward), and the adapter gradients
+ * come from two column projections. The same kernels as the MLP.
+ *
+ * dims: `hidden` is the input width (in), `inter` the output width (out);
+ * tokens, rank, scale, dtype and wfmt as for the MLP; flags 0 or
+ * LMLP_INT4_INKERNEL. Shapes: x [T,in]; w [out,in] (dense: dtype; INT4_B64:
+ * packed bytes [out,in/2] with w_scales [out,in/64] fp16, else w_scales
+ * NULL); a [r,in]; b [out,r]; y, dy [T,out]; dx [T,in]; da [r,in]; db
+ * [out,r]. Ownership, streams and errors as for the MLP. */
+size_t lora_linear_saved_bytes(const lmlp_dims* dims);
+size_t lora_linear_workspace_bytes(const lmlp_dims* dims, int is_backward);
+
+/* y = x W^T + s (x A^T) B^T. `saved` receives x A^T (fp32) and the adapter
+ * factors in the layouts the backward reads. */
+int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, const void* w_scales,
+                        const void* a, const void* b, void* y, void* saved, size_t saved_bytes,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* dx = dy W + s (dy B) A; da = s (dy B)^T x; db = s dy^T (x A^T), for the
+ * same x, w, a, b as the forward that filled `saved` (left unchanged).
+ * Outputs are overwritten, in dtype, accumulated in fp32. */
+int lora_linear_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* w,
+                         const void* w_scales, const void* a, const void* b, const void* saved,
+                         size_t saved_bytes, void* dx, void* da, void* db, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Dequantise one INT4_B64 weight (packed [out, in/2] bytes, fp16 scales
  * [out, in/64]) to bf16 [out, in] with the same device code the GEMM loaders
  * use. in % 64 == 0. Exposed so the 4-bit decode can be checked bit for bit. */

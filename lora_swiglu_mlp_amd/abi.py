@@ -57,6 +57,11 @@ _SIGS = {
     "lora_mlp_forward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 14 + [_P, _SZ, _P, _SZ, _P]),
     "lora_mlp_backward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 15 + [_SZ] + [_P] * 8
                           + [_SZ, _P]),
+    "lora_linear_saved_bytes": (_SZ, [ctypes.POINTER(lmlp_dims)]),
+    "lora_linear_workspace_bytes": (_SZ, [ctypes.POINTER(lmlp_dims), ctypes.c_int]),
+    "lora_linear_forward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 7 + [_SZ, _P, _SZ, _P]),
+    "lora_linear_backward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 7 + [_SZ] + [_P] * 4
+                             + [_SZ, _P]),
     "lora_mlp_dequant_int4": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     "lora_mlp_profile_begin": (ctypes.c_int, []),
     "lora_mlp_profile_end": (ctypes.c_int, [ctypes.POINTER(lmlp_kernel_time), ctypes.c_int,
@@ -71,7 +76,7 @@ def header_functions() -> list:
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lora_mlp_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lora_(?:mlp|linear)_\w+)\s*\(", text)))
 
 
 def lib() -> ctypes.CDLL:
@@ -164,6 +169,34 @@ def lora_mlp_backward(dims, dy, x, w_gate, w_gate_scales, w_up, w_up_scales, w_d
         _ptr(db_down), _ptr(workspace),
         _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
     _check(rc, "lora_mlp_backward")
+
+
+def lora_linear_saved_bytes(dims: lmlp_dims) -> int:
+    return int(lib().lora_linear_saved_bytes(ctypes.byref(dims)))
+
+
+def lora_linear_workspace_bytes(dims: lmlp_dims, is_backward: bool) -> int:
+    return int(lib().lora_linear_workspace_bytes(ctypes.byref(dims), int(bool(is_backward))))
+
+
+def lora_linear_forward(dims, x, w, w_scales, a, b, y, saved, workspace, stream=None, saved_bytes=None,
+                        workspace_bytes=None):
+    """dims: make_dims(tokens, in, out, rank, scale, ...) (hidden = in, inter = out)."""
+    rc = lib().lora_linear_forward(
+        ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(w_scales), _ptr(a), _ptr(b), _ptr(y), _ptr(saved),
+        _nbytes(saved) if saved_bytes is None else saved_bytes,
+        _ptr(workspace), _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
+    _check(rc, "lora_linear_forward")
+
+
+def lora_linear_backward(dims, dy, x, w, w_scales, a, b, saved, dx, da, db, workspace, stream=None,
+                         saved_bytes=None, workspace_bytes=None):
+    rc = lib().lora_linear_backward(
+        ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(w), _ptr(w_scales), _ptr(a), _ptr(b), _ptr(saved),
+        _nbytes(saved) if saved_bytes is None else saved_bytes,
+        _ptr(dx), _ptr(da), _ptr(db), _ptr(workspace),
+        _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
+    _check(rc, "lora_linear_backward")
 
 
 def lora_mlp_dequant_int4(packed, scales, out: int, inn: int, w_bf16, stream=None):

@@ -99,6 +99,13 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   return LMLP_OK;
 }
 
+// The linear takes the MLP's dims (hidden = in, inter = out); of the flags
+// only LMLP_INT4_INKERNEL applies to it.
+int parse_linear_dims(const lmlp_dims* d, Dims& o) {
+  if (d && (d->flags & ~LMLP_INT4_INKERNEL)) return fail(LMLP_ERR_INVALID_ARG, "flags other than INT4_INKERNEL");
+  return parse_dims(d, o);
+}
+
 struct Carver {
   size_t off = 0;
   size_t take(size_t bytes) {
@@ -283,6 +290,55 @@ BwdLayout bwd_layout(const Dims& d) {
   L.part_z = c.take(nsl_i * d.I * d.r16 * 4);
   L.part_x = c.take(size_t(L.ntb) * d.H * 2 * d.r16 * 4);
   L.part_dy = c.take(size_t(L.ntb) * d.H * d.r16 * 4);
+  L.total = c.off;
+  return L;
+}
+
+// ---- fused LoRA linear: y = x W^T + s (x A^T) B^T, in = H, out = I of Dims
+struct LinSavedLayout {
+  size_t p, pT, a_pad, bext, bT, total;
+};
+LinSavedLayout lin_saved_layout(const Dims& d) {
+  Carver c;
+  LinSavedLayout L;
+  L.p = c.take(size_t(d.T) * d.r16 * 4);                                // x A^T fp32
+  L.pT = d.bf16 ? c.take(size_t(d.r16) * ld_tok(d) * d.eb) : 0;        // its transposed copy
+  L.a_pad = c.take(size_t(d.r16) * d.H * d.eb);                         // A, rank rows padded
+  L.bext = c.take(size_t(d.I) * d.r16 * d.eb);                          // B as [out, r16]
+  L.bT = c.take(size_t(d.r16) * d.I * d.eb);                            // B^T as [r16, out]
+  L.total = c.off;
+  return L;
+}
+struct LinFwdLayout {
+  size_t aext, rp_part, sc, wq, total;
+};
+LinFwdLayout lin_fwd_layout(const Dims& d) {
+  Carver c;
+  LinFwdLayout L;
+  L.aext = c.take(size_t(d.T) * d.r16 * d.eb);  // s x A^T, the product's adapter segment
+  L.rp_part = c.take(rp_part_bytes(d, d.H, int(d.r16)));
+  L.sc = d.q4_inkernel ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
+  L.wq = d.int4 && !d.q4_inkernel ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.total = c.off;
+  return L;
+}
+struct LinBwdLayout {
+  size_t q, aext, qT, rp_part, part_x, part_dy, wq, total;
+  int ntb;
+  int64_t tr;
+};
+LinBwdLayout lin_bwd_layout(const Dims& d) {
+  Carver c;
+  LinBwdLayout L;
+  L.ntb = colproj_ntb(d);
+  L.tr = colproj_tr(d.T, L.ntb);
+  L.q = c.take(size_t(d.T) * d.r16 * 4);                          // dy B fp32
+  L.aext = c.take(size_t(d.T) * d.r16 * d.eb);                    // s dy B, the dX product's segment
+  L.qT = d.bf16 ? c.take(size_t(d.r16) * ld_tok(d) * d.eb) : 0;  // its transposed copy
+  L.rp_part = c.take(rp_part_bytes(d, d.I, int(d.r16)));
+  L.part_x = c.take(size_t(L.ntb) * d.H * d.r16 * 4);
+  L.part_dy = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
+  L.wq = d.int4 ? c.take(size_t(d.I) * d.H * 2) : 0;  // bf16 copy of W for the NN product
   L.total = c.off;
   return L;
 }
@@ -911,6 +967,197 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   rd.job[4] = rd_job(part_x, H * 2 * r16, ntb, 2 * r16, int(r16), H, r, da_up, H, true, s, d.bf16);
   rd.job[5] = rd_job(part_dy, H * r16, ntb, r16, 0, H, r, db_down, r, false, s, d.bf16);
   rd.njobs = 6;
+  LMLP_LAUNCH("reduce", launch_reduce(rd, st));
+  return LMLP_OK;
+}
+
+// ---- fused LoRA linear ----------------------------------------------------
+// Forward: pack A, B; rowproj P = x A^T (split-K) and its finish (P fp32 and
+// its bf16 transpose to saved, s P as the adapter segment); gemm y = [x | sP]
+// [W | B]^T. Backward: rowproj Q = dy B and its finish; gemm dX = [dy | sQ]
+// [W ; A] (NN); colproj x^T Q and dy^T P per token block; reduce to
+// da = s Q^T x, db = s dy^T P. The same kernels as the MLP's F1/F4, B1/B4,
+// B5 and B3 steps.
+
+size_t lora_linear_saved_bytes(const lmlp_dims* dims) {
+  Dims d;
+  if (parse_linear_dims(dims, d) != LMLP_OK) return 0;
+  return lin_saved_layout(d).total;
+}
+
+size_t lora_linear_workspace_bytes(const lmlp_dims* dims, int is_backward) {
+  Dims d;
+  if (parse_linear_dims(dims, d) != LMLP_OK) return 0;
+  return is_backward ? lin_bwd_layout(d).total : lin_fwd_layout(d).total;
+}
+
+int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, const void* w_scales, const void* a,
+                        const void* b, void* y, void* saved, size_t saved_bytes, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Dims d;
+  LMLP_TRY(parse_linear_dims(dims, d));
+  LMLP_TRY(need_ptr(w, "w"));
+  if (d.int4) LMLP_TRY(need_ptr(w_scales, "w_scales"));
+  else if (w_scales) return fail(LMLP_ERR_INVALID_ARG, "w_scales must be NULL for dense weights");
+  LMLP_TRY(need_ptr(a, "a"));
+  LMLP_TRY(need_ptr(b, "b"));
+  const LinSavedLayout SL = lin_saved_layout(d);
+  const LinFwdLayout FL = lin_fwd_layout(d);
+  if (d.T > 0) {
+    LMLP_TRY(need_ptr(x, "x"));
+    LMLP_TRY(need_ptr(y, "y"));
+    LMLP_TRY(need_ptr(saved, "saved"));
+    LMLP_TRY(need_ptr(workspace, "workspace"));
+  }
+  if (saved_bytes < SL.total) return fail(LMLP_ERR_WORKSPACE, "saved buffer smaller than lora_linear_saved_bytes()");
+  if (workspace_bytes < FL.total)
+    return fail(LMLP_ERR_WORKSPACE, "workspace smaller than lora_linear_workspace_bytes(dims, 0)");
+  LMLP_TRY(check_device());
+  if (d.T == 0) return LMLP_OK;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t T = d.T, In = d.H, Out = d.I, r = d.r, r16 = d.r16;
+  const int eb = d.eb;
+  float* P = reinterpret_cast<float*>(at(saved, SL.p));
+  char* pT = d.bf16 ? at(saved, SL.pT) : nullptr;
+  char* a_pad = at(saved, SL.a_pad);
+  char* bext = at(saved, SL.bext);
+  char* aext = at(workspace, FL.aext);
+
+  PackParams pk{};
+  pk.job[0] = pack_job(a_pad, In, r16, In, a, In, r, In, false);
+  pk.job[1] = pack_job(bext, r16, Out, r16, b, r, Out, r, false);
+  pk.job[2] = pack_job(at(saved, SL.bT), Out, r16, Out, b, r, Out, r, true);  // B^T for the backward
+  pk.njobs = 3;
+  LMLP_LAUNCH("pack(linear)", launch_pack(pk, eb, st));
+  const void* wk = w;
+  float* sc = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc)) : nullptr;
+  if (d.int4 && !d.q4_inkernel) {
+    char* wq = at(workspace, FL.wq);
+    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w, w_scales, Out, In, wq, st));
+    wk = wq;
+  }
+  if (d.q4_inkernel) {
+    ScalePackParams sp{};
+    sp.job[0] = {static_cast<const __half*>(w_scales), sc, Out, In / 64, Out};
+    sp.njobs = 1;
+    LMLP_LAUNCH("pack(scales)", launch_scale_pack(sp, st));
+  }
+
+  float* rpp = reinterpret_cast<float*>(at(workspace, FL.rp_part));
+  RowProjParams rp{};
+  rp.T = T;
+  rp.njobs = 1;
+  rp.job[0] = rp_job(d, x, In, In, a_pad, In, int(r16), rpp);
+  LMLP_LAUNCH("rowproj(x A^T)", launch_rowproj(rp, d.bf16, st));
+  ProjFinishParams fp{};
+  fp.T = T;
+  fp.njobs = 1;
+  fp.job[0] = fin_job(rpp, rp.job[0].kslices, T * r16, r16, int(r16), P, r16, aext, r16, d.s, pT, ld_tok(d), 0);
+  LMLP_LAUNCH("finish(P)", launch_proj_finish(fp, d.bf16, st));
+
+  GemmParams gy{};
+  gy.nseg = 2;
+  gy.seg[0] = seg(x, In, wk, nullptr, In, In, d.q4_inkernel, sc, nullptr);
+  gy.seg[1] = seg(aext, r16, bext, nullptr, r16, r16);
+  gy.M = T;
+  gy.N = Out;
+  gy.ldc = Out;
+  gy.c0 = y;
+  gy.group_m = 8;
+  LMLP_LAUNCH("gemm(y)", run_gemm(gy, d, 0, EPI_STORE, st));
+  return LMLP_OK;
+}
+
+int lora_linear_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* w, const void* w_scales,
+                         const void* a, const void* b, const void* saved, size_t saved_bytes, void* dx, void* da,
+                         void* db, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Dims d;
+  LMLP_TRY(parse_linear_dims(dims, d));
+  LMLP_TRY(need_ptr(w, "w"));
+  if (d.int4) LMLP_TRY(need_ptr(w_scales, "w_scales"));
+  else if (w_scales) return fail(LMLP_ERR_INVALID_ARG, "w_scales must be NULL for dense weights");
+  LMLP_TRY(need_ptr(a, "a"));
+  LMLP_TRY(need_ptr(b, "b"));
+  LMLP_TRY(need_ptr(da, "da"));
+  LMLP_TRY(need_ptr(db, "db"));
+  const LinSavedLayout SL = lin_saved_layout(d);
+  const LinBwdLayout BL = lin_bwd_layout(d);
+  if (d.T > 0) {
+    LMLP_TRY(need_ptr(dy, "dy"));
+    LMLP_TRY(need_ptr(x, "x"));
+    LMLP_TRY(need_ptr(dx, "dx"));
+    LMLP_TRY(need_ptr(saved, "saved"));
+    LMLP_TRY(need_ptr(workspace, "workspace"));
+  }
+  if (saved_bytes < SL.total) return fail(LMLP_ERR_WORKSPACE, "saved buffer smaller than lora_linear_saved_bytes()");
+  if (workspace_bytes < BL.total)
+    return fail(LMLP_ERR_WORKSPACE, "workspace smaller than lora_linear_workspace_bytes(dims, 1)");
+  LMLP_TRY(check_device());
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t T = d.T, In = d.H, Out = d.I, r = d.r, r16 = d.r16;
+  const float s = d.s;
+  ReduceParams rd{};
+  if (T == 0) {  // no tokens: the adapter gradients are empty sums
+    rd.job[0] = rd_job(nullptr, 0, 0, 0, 0, In, r, da, In, true, s, d.bf16);
+    rd.job[1] = rd_job(nullptr, 0, 0, 0, 0, Out, r, db, r, false, s, d.bf16);
+    rd.njobs = 2;
+    LMLP_LAUNCH("reduce(zero)", launch_reduce(rd, st));
+    return LMLP_OK;
+  }
+  const float* P = reinterpret_cast<const float*>(static_cast<const char*>(saved) + SL.p);
+  const char* pT = d.bf16 ? static_cast<const char*>(saved) + SL.pT : nullptr;
+  const char* a_pad = static_cast<const char*>(saved) + SL.a_pad;
+  const char* bT = static_cast<const char*>(saved) + SL.bT;
+  float* Q = reinterpret_cast<float*>(at(workspace, BL.q));
+  char* aext = at(workspace, BL.aext);
+  char* qT = d.bf16 ? at(workspace, BL.qT) : nullptr;
+  float* rpa = reinterpret_cast<float*>(at(workspace, BL.rp_part));
+  float* part_x = reinterpret_cast<float*>(at(workspace, BL.part_x));
+  float* part_dy = reinterpret_cast<float*>(at(workspace, BL.part_dy));
+  const int64_t ldT = ld_tok(d);
+
+  const void* wk = w;
+  if (d.int4) {
+    char* wq = at(workspace, BL.wq);
+    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w, w_scales, Out, In, wq, st));
+    wk = wq;
+  }
+  RowProjParams rp{};
+  rp.T = T;
+  rp.njobs = 1;
+  rp.job[0] = rp_job(d, dy, Out, Out, bT, Out, int(r16), rpa);
+  LMLP_LAUNCH("rowproj(dY B)", launch_rowproj(rp, d.bf16, st));
+  ProjFinishParams fp{};
+  fp.T = T;
+  fp.njobs = 1;
+  fp.job[0] = fin_job(rpa, rp.job[0].kslices, T * r16, r16, int(r16), Q, r16, aext, r16, s, qT, ldT, 0);
+  LMLP_LAUNCH("finish(Q)", launch_proj_finish(fp, d.bf16, st));
+
+  GemmParams gx{};
+  gx.nseg = 2;
+  gx.seg[0] = seg(dy, Out, wk, nullptr, In, Out);
+  gx.seg[1] = seg(aext, r16, a_pad, nullptr, In, r16);
+  gx.M = T;
+  gx.N = In;
+  gx.ldc = In;
+  gx.c0 = dx;
+  gx.group_m = 8;
+  LMLP_LAUNCH("gemm(dX)", run_gemm(gx, d, 1, EPI_STORE, st));
+
+  const int ntb = BL.ntb;
+  ColProjParams cp{};
+  cp.T = T;
+  cp.job[0] = cp_job(d, x, In, In, Q, r16, qT, ldT, int(r16), part_x, ntb, BL.tr);
+  cp.job[1] = cp_job(d, dy, Out, Out, P, r16, pT, ldT, int(r16), part_dy, ntb, BL.tr);
+  cp.njobs = 2;
+  LMLP_LAUNCH("colproj", launch_colproj(cp, d.bf16, st));
+  rd.job[0] = rd_job(part_x, In * r16, ntb, r16, 0, In, r, da, In, true, s, d.bf16);
+  rd.job[1] = rd_job(part_dy, Out * r16, ntb, r16, 0, Out, r, db, r, false, s, d.bf16);
+  rd.njobs = 2;
   LMLP_LAUNCH("reduce", launch_reduce(rd, st));
   return LMLP_OK;
 }

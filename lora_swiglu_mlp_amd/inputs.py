@@ -168,6 +168,44 @@ def make_inputs(wl: Workload, seed: int | None = None, with_dy: bool = True) -> 
     return out
 
 
+# Fused LoRA linear workloads: ``hidden`` is the input width, ``inter`` the
+# output width (the single projections of the same models; same draws).
+LINEAR_WORKLOADS: Dict[str, Workload] = {
+    "linear_tiny_fp32": Workload("linear_tiny_fp32", 256, 128, 344, 8, 16.0, "f32", x_std=0.02, w_std=0.02),
+    # Llama-3-8B attention q / o projection (4096 -> 4096), batch 2 x seq 2048
+    "linear_llama3_qo": Workload("linear_llama3_qo", 4096, 4096, 4096, 16, 16.0, "bf16"),
+    # Llama-3-8B k / v projection with 8 key-value heads (4096 -> 1024)
+    "linear_llama3_kv": Workload("linear_llama3_kv", 4096, 4096, 1024, 16, 16.0, "bf16"),
+    # one Llama-3-8B MLP projection (4096 -> 14336) as a plain LoRA linear
+    "linear_llama3_up": Workload("linear_llama3_up", 4096, 4096, 14336, 16, 16.0, "bf16"),
+    "linear_llama3_up_int4": Workload("linear_llama3_up_int4", 4096, 4096, 14336, 16, 16.0, "bf16",
+                                      wfmt="int4_b64"),
+}
+
+
+def make_linear_inputs(wl: Workload, seed: int | None = None, with_dy: bool = True) -> dict:
+    """Draw one linear workload's tensors in a fixed order from
+    ``default_rng(seed)``: x [T, in], W [out, in] (int4: codes then scales),
+    A [r, in], B [out, r], dY [T, out]."""
+    seed = wl.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    T, n_in, n_out, r, dt = wl.tokens, wl.hidden, wl.inter, wl.rank, wl.dtype
+    if wl.wfmt not in ("dense", "int4_b64"):
+        raise ValueError(wl.wfmt)
+    if wl.wfmt == "int4_b64" and dt != "bf16":
+        raise ValueError("int4 weights are defined for bf16 only")
+    out = {"x": _store(_normal(rng, (T, n_in), wl.x_std), dt)}
+    if wl.wfmt == "dense":
+        out["w"] = _store(_normal(rng, (n_out, n_in), wl.w_std), dt)
+    else:
+        out["w"], out["w_scales"] = _draw_int4(rng, n_out, n_in, wl.qscale_std)
+    out["a"] = _store(_normal(rng, (r, n_in), wl.a_std), dt)
+    out["b"] = _store(_normal(rng, (n_out, r), wl.b_std), dt)
+    if with_dy:
+        out["dy"] = _store(_normal(rng, (T, n_out), wl.dy_std), dt)
+    return out
+
+
 def draw_int4_codes(seed: int, out: int, inn: int, qscale_std: float = 0.003):
     """Packed codes and fp16 scales for one weight matrix (dequant tests)."""
     rng = np.random.default_rng(seed)

@@ -97,3 +97,63 @@ def from_inputs(inp: Dict[str, np.ndarray], wl, device="cuda", flags: int = 0):
     tens = {k: tensor_from_storage(v, wl.dtype, device) for k, v in inp.items()}
     m = LoraMLP(tens, wl.tokens, wl.hidden, wl.inter, wl.rank, wl.scale, wl.dtype, wl.wfmt, flags)
     return m, tens["x"], tens.get("dy")
+
+
+class LoraLinear:
+    """One fused LoRA linear y = x W^T + s (x A^T) B^T (frozen W, trainable A/B)
+    bound to device tensors ``w`` [out, in] (or 4-bit codes + ``w_scales``),
+    ``a`` [r, in], ``b`` [out, r]."""
+
+    def __init__(self, tensors: Dict[str, torch.Tensor], tokens: int, inn: int, out: int, rank: int,
+                 scale: float, dtype: str = "bf16", wfmt: str = "dense", flags: int = 0):
+        self.t = tensors
+        self.dtype, self.wfmt = dtype, wfmt
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.inn, self.out, self.rank, self.scale, self.flags = inn, out, rank, scale, flags
+        self.tokens = tokens
+        self.dims = abi.make_dims(tokens, inn, out, rank, scale, dtype, wfmt, flags)
+        self._ws: Optional[torch.Tensor] = None
+
+    def workspace(self) -> torch.Tensor:
+        need = max(abi.lora_linear_workspace_bytes(self.dims, False),
+                   abi.lora_linear_workspace_bytes(self.dims, True))
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.t["a"].device)
+        return self._ws
+
+    def new_saved(self) -> torch.Tensor:
+        n = abi.lora_linear_saved_bytes(self.dims)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.t["a"].device)
+
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                saved: Optional[torch.Tensor] = None, stream=None):
+        t = self.t
+        if y is None:
+            y = torch.empty((self.tokens, self.out), dtype=self.tdtype, device=x.device)
+        if saved is None:
+            saved = self.new_saved()
+        abi.lora_linear_forward(self.dims, x, t["w"], t.get("w_scales") if self.wfmt == "int4_b64" else None,
+                                t["a"], t["b"], y, saved, self.workspace(), stream=stream)
+        return y, saved
+
+    def new_grads(self, device) -> Dict[str, torch.Tensor]:
+        T, r = self.tokens, self.rank
+        shapes = {"dx": (T, self.inn), "da": (r, self.inn), "db": (self.out, r)}
+        return {k: torch.empty(s, dtype=self.tdtype, device=device) for k, s in shapes.items()}
+
+    def backward(self, dy: torch.Tensor, x: torch.Tensor, saved: torch.Tensor,
+                 grads: Optional[Dict[str, torch.Tensor]] = None, stream=None):
+        t = self.t
+        g = grads if grads is not None else self.new_grads(dy.device)
+        abi.lora_linear_backward(self.dims, dy, x, t["w"], t.get("w_scales") if self.wfmt == "int4_b64" else None,
+                                 t["a"], t["b"], saved, g["dx"], g["da"], g["db"], self.workspace(),
+                                 stream=stream)
+        return g
+
+
+def linear_from_inputs(inp: Dict[str, np.ndarray], wl, device="cuda", flags: int = 0):
+    """LoraLinear plus device x, dy from a generated linear workload
+    (inputs.make_linear_inputs; ``hidden`` = in, ``inter`` = out)."""
+    tens = {k: tensor_from_storage(v, wl.dtype, device) for k, v in inp.items()}
+    m = LoraLinear(tens, wl.tokens, wl.hidden, wl.inter, wl.rank, wl.scale, wl.dtype, wl.wfmt, flags)
+    return m, tens["x"], tens.get("dy")

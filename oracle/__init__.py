@@ -1,4 +1,5 @@
-"""CPU oracle for the LoRA SwiGLU MLP (test infrastructure only).
+"""CPU oracles for the LoRA SwiGLU MLP and the fused LoRA linear (test
+infrastructure only).
 
 Only the tests, the smoke check and the bench's CPU-baseline leg may import
 this package. The HIP product path never does.
@@ -7,3 +8,4 @@ from .lora_mlp_oracle import (ADAPTER_KEYS, WEIGHT_KEYS, backward, base_mlp_rows
                               bf16_round, bruteforce, dequant_int4, dequant_int4_bits,
                               flops, forward, forward_backward, merged_reference,
                               sigmoid, silu, unpack_int4)
+from . import lora_linear_oracle as linear  # noqa: F401,E402  (the fused LoRA linear)

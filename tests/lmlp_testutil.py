@@ -23,8 +23,8 @@ def oracle_inputs(inp: dict, wl) -> dict:
     for k, v in inp.items():
         if k.endswith("_scales"):
             continue
-        if wl.wfmt == "int4_b64" and k in ("w_gate", "w_up", "w_down"):
-            inn = wl.inter if k == "w_down" else wl.hidden
+        if wl.wfmt == "int4_b64" and k in ("w_gate", "w_up", "w_down", "w"):
+            inn = wl.inter if k == "w_down" else wl.hidden  # the linear's w is [out, in = hidden]
             d[k] = oracle.dequant_int4(v, inp[k + "_scales"], inn)
         else:
             d[k] = inp_mod.to_f64(v, wl.dtype)
@@ -52,8 +52,25 @@ def relerr(got: np.ndarray, ref: np.ndarray) -> float:
     return num / den
 
 
+LIN_KEYS = ("y", "dx", "da", "db")
+
+
+def run_hip_linear(inp: dict, wl, flags: int = 0, device="cuda"):
+    """Fused LoRA linear forward + backward on the GPU; fp64 numpy outputs."""
+    import torch
+    from lora_swiglu_mlp_amd import mlp
+    m, x, dy = mlp.linear_from_inputs(inp, wl, device, flags)
+    y, saved = m.forward(x)
+    g = m.backward(dy, x, saved)
+    torch.cuda.synchronize()
+    out = {"y": y}
+    out.update(g)
+    return {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}, m
+
+
 def compare(got: dict, ref: dict, tol: float, label: str = "") -> dict:
-    errs = {k: relerr(got[k], ref[k]) for k in OUT_KEYS if k in ref}
+    keys = OUT_KEYS if "da_gate" in ref else LIN_KEYS
+    errs = {k: relerr(got[k], ref[k]) for k in keys if k in ref}
     print(f"[parity] {label} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     sys.stdout.flush()
     bad = {k: v for k, v in errs.items() if not v <= tol}

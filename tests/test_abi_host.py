@@ -25,7 +25,9 @@ def test_library_exports_every_header_symbol():
     names = abi.header_functions()
     assert set(names) == {"lora_mlp_saved_bytes", "lora_mlp_workspace_bytes", "lora_mlp_forward",
                           "lora_mlp_backward", "lora_mlp_dequant_int4", "lora_mlp_status_string",
-                          "lora_mlp_last_error", "lora_mlp_profile_begin", "lora_mlp_profile_end"}
+                          "lora_mlp_last_error", "lora_mlp_profile_begin", "lora_mlp_profile_end",
+                          "lora_linear_saved_bytes", "lora_linear_workspace_bytes", "lora_linear_forward",
+                          "lora_linear_backward"}
     L = abi.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -181,3 +183,23 @@ def test_python_binding_raises():
 def test_profile_session_without_launches():
     abi.lora_mlp_profile_begin()
     assert abi.lora_mlp_profile_end() == []
+
+
+@pytest.mark.parametrize("T,n_in,n_out,r,dt", [(256, 128, 344, 8, "f32"), (4096, 4096, 1024, 16, "bf16"),
+                                               (0, 64, 64, 4, "bf16")])
+def test_linear_saved_bytes_formula(T, n_in, n_out, r, dt):
+    eb = 2 if dt == "bf16" else 4
+    r16 = (r + 15) // 16 * 16
+    ldT = (T + 63) // 64 * 64
+    want = (align(T * r16 * 4) + (align(r16 * ldT * eb) if dt == "bf16" else 0) + align(r16 * n_in * eb)
+            + align(n_out * r16 * eb) + align(r16 * n_out * eb))
+    d = dims(tokens=T, hidden=n_in, inter=n_out, rank=r, dtype=dt)
+    assert abi.lora_linear_saved_bytes(d) == want
+    if T > 0:
+        assert abi.lora_linear_workspace_bytes(d, False) > 0 and abi.lora_linear_workspace_bytes(d, True) > 0
+
+
+def test_linear_rejects_the_mlp_only_flags():
+    for f in (abi.LMLP_CONSUME_SAVED, abi.LMLP_RECOMPUTE_GU):
+        assert abi.lora_linear_saved_bytes(dims(flags=f)) == 0
+    assert abi.lora_linear_saved_bytes(dims(inter=384, wfmt="int4_b64", flags=abi.LMLP_INT4_INKERNEL)) > 0
