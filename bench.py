@@ -57,6 +57,11 @@ def kernel_bytes(name: str, T: int, H: int, I: int, r: int, eb: int) -> int:
         "rowproj(dY B_d)": T * H * eb + T * r * (4 + eb),
         "rowproj(dG B_g, dU B_u)": 2 * T * I * eb + 2 * T * r * (4 + eb),
         "colproj": (2 * T * H if fused else 3 * T * I + 2 * T * H) * eb,
+        # RMSNorm in front of the MLP: x in, xn out (+ the fp32 row statistic);
+        # the backward reads x and g and writes dx
+        "rmsnorm(fwd)": 2 * T * H * eb + 4 * T,
+        "rmsnorm(apply)": 2 * T * H * eb + 4 * T,
+        "rmsnorm(bwd)": 3 * T * H * eb + 4 * T,
     }.get(name, 0)
 
 
@@ -104,7 +109,7 @@ def copy_probe(mib: int):
     del a, b
 
 
-def cpu_baseline(inp, wl, seconds: float):
+def cpu_baseline(inp, wl, seconds: float, norm_eps=None):
     import numpy as np
     import oracle
     from lora_swiglu_mlp_amd import inputs as I
@@ -126,7 +131,10 @@ def cpu_baseline(inp, wl, seconds: float):
         d["x"] = I.to_f64(inp["x"][:n], wl.dtype)
         d["dy"] = I.to_f64(inp["dy"][:n], wl.dtype)
         t0 = time.perf_counter()
-        oracle.forward_backward(d, wl.scale)
+        if norm_eps is None:
+            oracle.forward_backward(d, wl.scale)
+        else:
+            oracle.rmsnorm.norm_mlp_forward_backward(d, I.to_f64(inp["gamma"], wl.dtype), norm_eps, wl.scale)
         return time.perf_counter() - t0
 
     n, t = 32, run(32)
@@ -137,7 +145,8 @@ def cpu_baseline(inp, wl, seconds: float):
         n = min(wl.tokens, max(n, int(n * seconds / max(t, 1e-3))))
         t = run(n)
     return {"value": n / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n} of {wl.tokens} tokens of {wl.name}, forward+backward, "
+            "sample": f"first {n} of {wl.tokens} tokens of {wl.name}, "
+                      f"{'RMSNorm then ' if norm_eps is not None else ''}forward+backward, "
                       f"fp64 numpy (row-local work per token is the full path), {t:.1f} s",
             "gflops": oracle.flops(n, wl.hidden, wl.inter, wl.rank) / t / 1e9}
 
@@ -239,6 +248,8 @@ def main():
     ap.add_argument("--recompute", action="store_true",
                     help="full-recompute mode: G, U are not saved, the backward recomputes them "
                          "(its FLOPs are not counted in the metric)")
+    ap.add_argument("--norm", action="store_true",
+                    help="RMSNorm (eps 1e-5) in front of the MLP: the library's norm entry points")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -262,8 +273,11 @@ def main():
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
     inp = I.make_inputs(wl)
+    norm_eps = I.NORM_EPS if args.norm else None
+    if args.norm:
+        inp["gamma"] = I.make_norm_gamma(wl)
     flags = abi.LMLP_RECOMPUTE_GU if args.recompute else 0
-    m, x, dy = mlp.from_inputs(inp, wl, "cuda:0", flags)
+    m, x, dy = mlp.from_inputs(inp, wl, "cuda:0", flags, norm_eps=norm_eps)
     saved = m.new_saved()
     y = torch.empty((T, H), dtype=m.tdtype, device="cuda:0")
     grads = m.new_grads(x.device)
@@ -282,7 +296,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
-    flops = 12 * T * H * Iw + 18 * T * r * (H + Iw)
+    flops = 12 * T * H * Iw + 18 * T * r * (H + Iw) + (12 * T * H if args.norm else 0)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
 
@@ -292,7 +306,8 @@ def main():
            "dtype": wl.dtype, "data": "synthetic (seeded normal draws; random-init weights)",
            "config": {"workload": wl.name, "tokens": T, "hidden": H, "inter": Iw, "rank": r,
                       "alpha": wl.alpha, "weights": wl.wfmt, "parallelism": "single-gpu",
-                      "saved": "recompute G, U" if args.recompute else "G, U"},
+                      "saved": "recompute G, U" if args.recompute else "G, U",
+                      "norm": f"rmsnorm eps={norm_eps}" if args.norm else "none"},
            "tflops": tflops, "pct_of_peak": 100.0 * tflops / peak}
 
     if not args.no_profile:
@@ -318,7 +333,7 @@ def main():
                 e["gbps"] = b / (avg * 1e-3) / 1e9
             kern[name] = e
         out["kernels"] = kern
-        fwd_names = ("pack(fwd)", "rowproj(X A^T)", "gemm(gate/up)", "rowproj(Z A_d^T)", "gemm(down)")
+        fwd_names = ("rmsnorm(fwd)", "pack(fwd)", "rowproj(X A^T)", "gemm(gate/up)", "rowproj(Z A_d^T)", "gemm(down)")
         out["kernel_ms_per_step"] = sum(v["ms"] * v["launches_per_step"] for v in kern.values())
         dom = max((n for n in kern if kernel_flops(n, T, H, Iw, r)),
                   key=lambda n: kern[n]["ms"] * kern[n]["launches_per_step"])
@@ -331,7 +346,7 @@ def main():
         out["bwd_kernel_ms"] = out["kernel_ms_per_step"] - out["fwd_kernel_ms"]
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds, norm_eps)
 
     print(json.dumps(out), flush=True)
 

@@ -76,6 +76,11 @@ typedef enum { LMLP_W_DENSE = 0, LMLP_W_INT4_B64 = 1 } lmlp_wfmt;
  * where dG and dU then overwrite them. Outputs are bitwise equal to the
  * default mode. LMLP_CONSUME_SAVED has no effect with it. */
 #define LMLP_RECOMPUTE_GU 0x4u
+/* RMSNorm in front of the MLP: set for lora_mlp_norm_forward / _backward and
+ * for their size queries (saved grows by 4*T bytes for the per-row
+ * statistics, each workspace by T*H elements of dtype for the normalised
+ * rows); lora_mlp_forward / _backward and the linear reject it. */
+#define LMLP_RMSNORM 0x8u
 
 typedef struct {
   int64_t tokens;  /* T >= 0 (T == 0: forward is a no-op, backward writes zero adapter gradients) */
@@ -85,7 +90,8 @@ typedef struct {
   float scale;     /* s = alpha / r, finite */
   int32_t dtype;   /* lmlp_dtype */
   int32_t wfmt;    /* lmlp_wfmt */
-  uint32_t flags;  /* bitwise OR of LMLP_CONSUME_SAVED, LMLP_INT4_INKERNEL, LMLP_RECOMPUTE_GU, or 0 */
+  uint32_t flags;  /* bitwise OR of LMLP_CONSUME_SAVED, LMLP_INT4_INKERNEL, LMLP_RECOMPUTE_GU,
+                      LMLP_RMSNORM, or 0 */
 } lmlp_dims;
 
 /* Bytes of the forward->backward `saved` buffer: the gate and up
@@ -134,6 +140,40 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x,
                       void* dx, void* da_gate, void* db_gate,
                       void* da_up, void* db_up, void* da_down, void* db_down,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- RMSNorm then the MLP ------------------------------------------------
+ * y = MLP(RMSNorm(x)) with the MLP above and, per token row t of width H,
+ *   rstd_t = (mean_h x_th^2 + eps)^(-1/2),   xn_th = x_th * rstd_t * gamma_h
+ * (gamma [H] in dtype, frozen: no gradient; xn rounded once to dtype). The
+ * norm is one of the forward+backward kernels of the training path in
+ * "Unsloth 深度分析报告" (section 关键设计决策); as in "Unsloth支持哪些模型？
+ * 主流LLM兼容性一览" (section 4.2) the backward reuses the forward's rstd
+ * (kept in `saved`) instead of recomputing the row statistics. dims.flags
+ * must include LMLP_RMSNORM; every other argument, flag and rule is the
+ * MLP's. Backward returns dx = d/dx of <dy, y> through the norm:
+ *   dx = rstd * (gamma g - xhat * mean_h(gamma g xhat)),  xhat = x rstd,
+ * g the MLP's gradient at xn; the adapter gradients are the MLP's at xn.
+ * x (the un-normalised rows) must be the same in both calls. */
+int lora_mlp_norm_forward(const lmlp_dims* dims, float eps, const void* x, const void* gamma,
+                          const void* w_gate, const void* w_gate_scales,
+                          const void* w_up, const void* w_up_scales,
+                          const void* w_down, const void* w_down_scales,
+                          const void* a_gate, const void* b_gate,
+                          const void* a_up, const void* b_up,
+                          const void* a_down, const void* b_down,
+                          void* y, void* saved, size_t saved_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* gamma,
+                           const void* w_gate, const void* w_gate_scales,
+                           const void* w_up, const void* w_up_scales,
+                           const void* w_down, const void* w_down_scales,
+                           const void* a_gate, const void* b_gate,
+                           const void* a_up, const void* b_up,
+                           const void* a_down, const void* b_down,
+                           void* saved, size_t saved_bytes,
+                           void* dx, void* da_gate, void* db_gate,
+                           void* da_up, void* db_up, void* da_down, void* db_down,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- Fused LoRA linear (one projection: q, k, v, o, ...) ----------------
  * y = x W^T + s (x A^T) B^T and its backward, the matmul-with-LoRA fusion of

@@ -23,6 +23,7 @@ LMLP_W_DENSE, LMLP_W_INT4_B64 = 0, 1
 LMLP_CONSUME_SAVED = 0x1
 LMLP_INT4_INKERNEL = 0x2
 LMLP_RECOMPUTE_GU = 0x4
+LMLP_RMSNORM = 0x8
 
 
 class lmlp_dims(ctypes.Structure):
@@ -57,6 +58,10 @@ _SIGS = {
     "lora_mlp_forward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 14 + [_P, _SZ, _P, _SZ, _P]),
     "lora_mlp_backward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 15 + [_SZ] + [_P] * 8
                           + [_SZ, _P]),
+    "lora_mlp_norm_forward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims), ctypes.c_float] + [_P] * 15
+                              + [_P, _SZ, _P, _SZ, _P]),
+    "lora_mlp_norm_backward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 16 + [_SZ] + [_P] * 8
+                               + [_SZ, _P]),
     "lora_linear_saved_bytes": (_SZ, [ctypes.POINTER(lmlp_dims)]),
     "lora_linear_workspace_bytes": (_SZ, [ctypes.POINTER(lmlp_dims), ctypes.c_int]),
     "lora_linear_forward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 7 + [_SZ, _P, _SZ, _P]),
@@ -169,6 +174,33 @@ def lora_mlp_backward(dims, dy, x, w_gate, w_gate_scales, w_up, w_up_scales, w_d
         _ptr(db_down), _ptr(workspace),
         _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
     _check(rc, "lora_mlp_backward")
+
+
+def lora_mlp_norm_forward(dims, eps, x, gamma, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales,
+                          a_gate, b_gate, a_up, b_up, a_down, b_down, y, saved, workspace, stream=None,
+                          saved_bytes=None, workspace_bytes=None):
+    rc = lib().lora_mlp_norm_forward(
+        ctypes.byref(dims), float(eps), _ptr(x), _ptr(gamma), _ptr(w_gate), _ptr(w_gate_scales), _ptr(w_up),
+        _ptr(w_up_scales), _ptr(w_down), _ptr(w_down_scales), _ptr(a_gate), _ptr(b_gate), _ptr(a_up),
+        _ptr(b_up), _ptr(a_down), _ptr(b_down), _ptr(y), _ptr(saved),
+        _nbytes(saved) if saved_bytes is None else saved_bytes,
+        _ptr(workspace), _nbytes(workspace) if workspace_bytes is None else workspace_bytes,
+        _stream(stream))
+    _check(rc, "lora_mlp_norm_forward")
+
+
+def lora_mlp_norm_backward(dims, dy, x, gamma, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales,
+                           a_gate, b_gate, a_up, b_up, a_down, b_down, saved, dx, da_gate, db_gate, da_up, db_up,
+                           da_down, db_down, workspace, stream=None, saved_bytes=None, workspace_bytes=None):
+    rc = lib().lora_mlp_norm_backward(
+        ctypes.byref(dims), _ptr(dy), _ptr(x), _ptr(gamma), _ptr(w_gate), _ptr(w_gate_scales), _ptr(w_up),
+        _ptr(w_up_scales), _ptr(w_down), _ptr(w_down_scales), _ptr(a_gate), _ptr(b_gate), _ptr(a_up),
+        _ptr(b_up), _ptr(a_down), _ptr(b_down), _ptr(saved),
+        _nbytes(saved) if saved_bytes is None else saved_bytes,
+        _ptr(dx), _ptr(da_gate), _ptr(db_gate), _ptr(da_up), _ptr(db_up), _ptr(da_down),
+        _ptr(db_down), _ptr(workspace),
+        _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
+    _check(rc, "lora_mlp_norm_backward")
 
 
 def lora_linear_saved_bytes(dims: lmlp_dims) -> int:

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblora_mlp.so")
-SOURCES = ["gemm.hip", "gemm_bf16.hip", "skinny.hip", "lora_mlp.cpp"]
+SOURCES = ["gemm.hip", "gemm_bf16.hip", "skinny.hip", "rmsnorm.hip", "lora_mlp.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU ops (kept off on purpose).

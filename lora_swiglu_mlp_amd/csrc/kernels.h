@@ -202,4 +202,24 @@ hipError_t launch_scale_pack(const ScalePackParams& p, hipStream_t stream);
 hipError_t launch_dequant_int4(const void* packed, const void* scales, int64_t out, int64_t in,
                                void* w_bf16, hipStream_t stream);
 
+// RMSNorm of token rows [T][H] with a frozen weight gamma [H] (all in the
+// compute dtype; rstd fp32 [T]):
+//   NORM_FWD    xn = x * rstd * gamma, rstd written
+//   NORM_APPLY  xn from the given rstd
+//   NORM_BWD    dx = rstd * (gamma g - xhat * mean(gamma g xhat)), xhat = x rstd;
+//               g may be the same buffer as dx
+enum { NORM_FWD = 0, NORM_APPLY = 1, NORM_BWD = 2 };
+struct NormParams {
+  const void* x;
+  const void* gamma;
+  void* xn;
+  float* rstd;
+  const void* g;
+  void* dx;
+  int64_t T, H;  // H a multiple of the 16-byte chunk
+  float eps;
+  int32_t mode;
+};
+hipError_t launch_rmsnorm(const NormParams& p, int dtype_bf16, hipStream_t stream);
+
 }  // namespace lmlp

@@ -55,6 +55,7 @@ struct Dims {
   bool bf16, int4, consume;
   bool recompute;    // G, U not saved: the backward recomputes them
   bool q4_inkernel;  // forward decodes 4-bit codes inside the GEMM staging
+  bool norm;         // RMSNorm in front of the MLP (the norm entry points)
   int eb;  // element bytes
 };
 
@@ -69,7 +70,7 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   if (!std::isfinite(d->scale)) return fail(LMLP_ERR_INVALID_ARG, "scale is not finite");
   if (d->dtype != LMLP_F32 && d->dtype != LMLP_BF16) return fail(LMLP_ERR_INVALID_ARG, "unknown dtype");
   if (d->wfmt != LMLP_W_DENSE && d->wfmt != LMLP_W_INT4_B64) return fail(LMLP_ERR_INVALID_ARG, "unknown wfmt");
-  if (d->flags & ~(LMLP_CONSUME_SAVED | LMLP_INT4_INKERNEL | LMLP_RECOMPUTE_GU))
+  if (d->flags & ~(LMLP_CONSUME_SAVED | LMLP_INT4_INKERNEL | LMLP_RECOMPUTE_GU | LMLP_RMSNORM))
     return fail(LMLP_ERR_INVALID_ARG, "unknown flag bits");
   if (d->rank > 256) return fail(LMLP_ERR_UNSUPPORTED, "rank > 256");
   const int ch = d->dtype == LMLP_BF16 ? 8 : 4;
@@ -95,6 +96,7 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   o.recompute = (d->flags & LMLP_RECOMPUTE_GU) != 0;
   o.consume = !o.recompute && (d->flags & LMLP_CONSUME_SAVED) != 0;
   o.q4_inkernel = o.int4 && (d->flags & LMLP_INT4_INKERNEL) != 0;
+  o.norm = (d->flags & LMLP_RMSNORM) != 0;
   o.eb = o.bf16 ? 2 : 4;
   return LMLP_OK;
 }
@@ -119,7 +121,7 @@ struct Carver {
 // by the forward, next to the activations (the backward gets the same
 // weights).
 struct SavedLayout {
-  size_t g, u, pgu, pd, agu_pad, ad_pad, bdT, bgT, buT, bext_g, bext_u, total;
+  size_t g, u, pgu, pd, agu_pad, ad_pad, bdT, bgT, buT, bext_g, bext_u, rstd, total;
 };
 SavedLayout saved_layout(const Dims& d) {
   Carver c;
@@ -137,6 +139,7 @@ SavedLayout saved_layout(const Dims& d) {
   // adapter segment, which the backward reruns with LMLP_RECOMPUTE_GU
   L.bext_g = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
   L.bext_u = c.take(size_t(d.I) * 2 * d.r16 * d.eb);
+  L.rstd = d.norm ? c.take(size_t(d.T) * 4) : 0;  // the norm's statistics, reused by the backward
   L.total = c.off;
   return L;
 }
@@ -225,7 +228,7 @@ int64_t ld_tok(const Dims& d) { return (d.T + 63) / 64 * 64; }  // token-contigu
 
 struct FwdLayout {
   size_t z, aext_gu, aext_d, bext_d, rp_part, sc_g, sc_u, sc_d;
-  size_t wq_g, wq_u, wq_d, total;
+  size_t wq_g, wq_u, wq_d, xn, total;
 };
 FwdLayout fwd_layout(const Dims& d) {
   Carver c;
@@ -244,6 +247,7 @@ FwdLayout fwd_layout(const Dims& d) {
   L.wq_g = cp ? c.take(size_t(d.I) * d.H * 2) : 0;
   L.wq_u = cp ? c.take(size_t(d.I) * d.H * 2) : 0;
   L.wq_d = cp ? c.take(size_t(d.H) * d.I * 2) : 0;
+  L.xn = d.norm ? c.take(size_t(d.T) * d.H * d.eb) : 0;  // the normalised rows
   L.total = c.off;
   return L;
 }
@@ -251,7 +255,7 @@ FwdLayout fwd_layout(const Dims& d) {
 struct BwdLayout {
   size_t g_rc, u_rc, dg, du, z, qd, aext_d, qgu, aext_gu;
   size_t rp_a, rp_b, pguT, pdT, qdT, qguT, wq_g, wq_u, wq_d;
-  size_t part_dg, part_du, part_z, part_x, part_dy, total;
+  size_t part_dg, part_du, part_z, part_x, part_dy, xn, total;
   int ntb;
   int64_t tr;
 };
@@ -290,6 +294,7 @@ BwdLayout bwd_layout(const Dims& d) {
   L.part_z = c.take(nsl_i * d.I * d.r16 * 4);
   L.part_x = c.take(size_t(L.ntb) * d.H * 2 * d.r16 * 4);
   L.part_dy = c.take(size_t(L.ntb) * d.H * d.r16 * 4);
+  L.xn = d.norm ? c.take(size_t(d.T) * d.H * d.eb) : 0;  // the normalised rows, re-applied
   L.total = c.off;
   return L;
 }
@@ -596,14 +601,16 @@ const char* lora_mlp_status_string(int status) {
 
 const char* lora_mlp_last_error(void) { return g_last_error.c_str(); }
 
-int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, const void* w_gate_scales,
-                     const void* w_up, const void* w_up_scales, const void* w_down, const void* w_down_scales,
-                     const void* a_gate, const void* b_gate, const void* a_up, const void* b_up,
-                     const void* a_down, const void* b_down, void* y, void* saved, size_t saved_bytes,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+// The MLP forward; with dims.flags & LMLP_RMSNORM the rows of x are first
+// normalised (gamma, eps) and the MLP runs on the result.
+static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, const void* x, const void* w_gate,
+                        const void* w_gate_scales, const void* w_up, const void* w_up_scales, const void* w_down,
+                        const void* w_down_scales, const void* a_gate, const void* b_gate, const void* a_up,
+                        const void* b_up, const void* a_down, const void* b_down, void* y, void* saved,
+                        size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
   LMLP_TRY(parse_dims(dims, d));
+  if (d.norm) LMLP_TRY(need_ptr(gamma, "gamma"));
   LMLP_TRY(check_weights(d, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales));
   LMLP_TRY(check_adapters(a_gate, b_gate, a_up, b_up, a_down, b_down));
   const SavedLayout SL = saved_layout(d);
@@ -622,6 +629,19 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t T = d.T, H = d.H, I = d.I, r = d.r, r16 = d.r16;
+  if (d.norm) {  // xn = RMSNorm(x); rstd kept for the backward
+    NormParams np{};
+    np.x = x;
+    np.gamma = gamma;
+    np.xn = at(workspace, FL.xn);
+    np.rstd = reinterpret_cast<float*>(at(saved, SL.rstd));
+    np.T = T;
+    np.H = H;
+    np.eps = eps;
+    np.mode = NORM_FWD;
+    LMLP_LAUNCH("rmsnorm(fwd)", launch_rmsnorm(np, d.bf16, st));
+    x = np.xn;
+  }
   // with LMLP_RECOMPUTE_GU the gate/up epilogue stores only Z
   char* G = d.recompute ? nullptr : at(saved, SL.g);
   char* U = d.recompute ? nullptr : at(saved, SL.u);
@@ -721,15 +741,17 @@ int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, c
   return LMLP_OK;
 }
 
-int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* w_gate,
-                      const void* w_gate_scales, const void* w_up, const void* w_up_scales, const void* w_down,
-                      const void* w_down_scales, const void* a_gate, const void* b_gate, const void* a_up,
-                      const void* b_up, const void* a_down, const void* b_down, void* saved, size_t saved_bytes,
-                      void* dx, void* da_gate, void* db_gate, void* da_up, void* db_up, void* da_down,
-                      void* db_down, void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+// The MLP backward; with LMLP_RMSNORM the normalised rows are re-applied from
+// the saved statistics first and dx is carried through the norm at the end.
+static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* dy, const void* x,
+                         const void* w_gate, const void* w_gate_scales, const void* w_up, const void* w_up_scales,
+                         const void* w_down, const void* w_down_scales, const void* a_gate, const void* b_gate,
+                         const void* a_up, const void* b_up, const void* a_down, const void* b_down, void* saved,
+                         size_t saved_bytes, void* dx, void* da_gate, void* db_gate, void* da_up, void* db_up,
+                         void* da_down, void* db_down, void* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
   LMLP_TRY(parse_dims(dims, d));
+  if (d.norm) LMLP_TRY(need_ptr(gamma, "gamma"));
   LMLP_TRY(check_weights(d, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales));
   LMLP_TRY(check_adapters(a_gate, b_gate, a_up, b_up, a_down, b_down));
   LMLP_TRY(need_ptr(da_gate, "da_gate"));
@@ -769,6 +791,20 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
     rd.njobs = 6;
     LMLP_LAUNCH("reduce(zero)", launch_reduce(rd, st));
     return LMLP_OK;
+  }
+
+  const void* x_in = x;
+  NormParams np{};
+  if (d.norm) {  // the forward's normalised rows, from its saved rstd
+    np.x = x;
+    np.gamma = gamma;
+    np.xn = at(workspace, BL.xn);
+    np.rstd = reinterpret_cast<float*>(at(saved, SL.rstd));
+    np.T = T;
+    np.H = H;
+    np.mode = NORM_APPLY;
+    LMLP_LAUNCH("rmsnorm(apply)", launch_rmsnorm(np, d.bf16, st));
+    x = np.xn;
   }
 
   char* G_rc = d.recompute ? at(workspace, BL.g_rc) : nullptr;
@@ -968,7 +1004,68 @@ int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, cons
   rd.job[5] = rd_job(part_dy, H * r16, ntb, r16, 0, H, r, db_down, r, false, s, d.bf16);
   rd.njobs = 6;
   LMLP_LAUNCH("reduce", launch_reduce(rd, st));
+  if (d.norm) {  // dx (so far the gradient of the normalised rows) through the norm, in place
+    np.x = x_in;
+    np.g = dx;
+    np.dx = dx;
+    np.mode = NORM_BWD;
+    LMLP_LAUNCH("rmsnorm(bwd)", launch_rmsnorm(np, d.bf16, st));
+  }
   return LMLP_OK;
+}
+
+int lora_mlp_forward(const lmlp_dims* dims, const void* x, const void* w_gate, const void* w_gate_scales,
+                     const void* w_up, const void* w_up_scales, const void* w_down, const void* w_down_scales,
+                     const void* a_gate, const void* b_gate, const void* a_up, const void* b_up,
+                     const void* a_down, const void* b_down, void* y, void* saved, size_t saved_bytes,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (dims && (dims->flags & LMLP_RMSNORM))
+    return fail(LMLP_ERR_INVALID_ARG, "LMLP_RMSNORM is for lora_mlp_norm_forward");
+  return forward_impl(dims, nullptr, 0.f, x, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales,
+                      a_gate, b_gate, a_up, b_up, a_down, b_down, y, saved, saved_bytes, workspace, workspace_bytes,
+                      stream);
+}
+
+int lora_mlp_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* w_gate,
+                      const void* w_gate_scales, const void* w_up, const void* w_up_scales, const void* w_down,
+                      const void* w_down_scales, const void* a_gate, const void* b_gate, const void* a_up,
+                      const void* b_up, const void* a_down, const void* b_down, void* saved, size_t saved_bytes,
+                      void* dx, void* da_gate, void* db_gate, void* da_up, void* db_up, void* da_down,
+                      void* db_down, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (dims && (dims->flags & LMLP_RMSNORM))
+    return fail(LMLP_ERR_INVALID_ARG, "LMLP_RMSNORM is for lora_mlp_norm_backward");
+  return backward_impl(dims, nullptr, dy, x, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales,
+                       a_gate, b_gate, a_up, b_up, a_down, b_down, saved, saved_bytes, dx, da_gate, db_gate, da_up,
+                       db_up, da_down, db_down, workspace, workspace_bytes, stream);
+}
+
+int lora_mlp_norm_forward(const lmlp_dims* dims, float eps, const void* x, const void* gamma, const void* w_gate,
+                          const void* w_gate_scales, const void* w_up, const void* w_up_scales, const void* w_down,
+                          const void* w_down_scales, const void* a_gate, const void* b_gate, const void* a_up,
+                          const void* b_up, const void* a_down, const void* b_down, void* y, void* saved,
+                          size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (dims && !(dims->flags & LMLP_RMSNORM))
+    return fail(LMLP_ERR_INVALID_ARG, "lora_mlp_norm_forward needs LMLP_RMSNORM in dims.flags");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(LMLP_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return forward_impl(dims, gamma, eps, x, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales, a_gate,
+                      b_gate, a_up, b_up, a_down, b_down, y, saved, saved_bytes, workspace, workspace_bytes, stream);
+}
+
+int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* gamma,
+                           const void* w_gate, const void* w_gate_scales, const void* w_up, const void* w_up_scales,
+                           const void* w_down, const void* w_down_scales, const void* a_gate, const void* b_gate,
+                           const void* a_up, const void* b_up, const void* a_down, const void* b_down, void* saved,
+                           size_t saved_bytes, void* dx, void* da_gate, void* db_gate, void* da_up, void* db_up,
+                           void* da_down, void* db_down, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (dims && !(dims->flags & LMLP_RMSNORM))
+    return fail(LMLP_ERR_INVALID_ARG, "lora_mlp_norm_backward needs LMLP_RMSNORM in dims.flags");
+  return backward_impl(dims, gamma, dy, x, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales, a_gate,
+                       b_gate, a_up, b_up, a_down, b_down, saved, saved_bytes, dx, da_gate, db_gate, da_up, db_up,
+                       da_down, db_down, workspace, workspace_bytes, stream);
 }
 
 // ---- fused LoRA linear ----------------------------------------------------

@@ -168,6 +168,20 @@ def make_inputs(wl: Workload, seed: int | None = None, with_dy: bool = True) -> 
     return out
 
 
+# RMSNorm in front of the MLP (the same workloads with the norm switched on):
+# eps as the pages' model table gives it for one family (1e-5, which is also
+# Llama-3's), the weight drawn from its own seeded stream so the MLP's draws
+# are unchanged.
+NORM_EPS = 1e-5
+
+
+def make_norm_gamma(wl: Workload, seed: int | None = None) -> np.ndarray:
+    """RMSNorm weight [H] in the workload's storage, uniform in [0.5, 1.5)."""
+    seed = wl.seed if seed is None else seed
+    rng = np.random.default_rng([seed, 7])
+    return _store((0.5 + rng.random(wl.hidden, dtype=np.float32)).astype(np.float32), wl.dtype)
+
+
 # Fused LoRA linear workloads: ``hidden`` is the input width, ``inter`` the
 # output width (the single projections of the same models; same draws).
 LINEAR_WORKLOADS: Dict[str, Workload] = {

@@ -28,11 +28,18 @@ def tensor_from_storage(a: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 class LoraMLP:
-    """One LoRA SwiGLU MLP (frozen W, trainable A/B) bound to device tensors."""
+    """One LoRA SwiGLU MLP (frozen W, trainable A/B) bound to device tensors.
+
+    With ``norm_eps`` set, an RMSNorm with the frozen weight ``tensors["gamma"]``
+    runs in front of the MLP (the library's norm entry points)."""
 
     def __init__(self, tensors: Dict[str, torch.Tensor], tokens: int, hidden: int, inter: int,
-                 rank: int, scale: float, dtype: str = "bf16", wfmt: str = "dense", flags: int = 0):
+                 rank: int, scale: float, dtype: str = "bf16", wfmt: str = "dense", flags: int = 0,
+                 norm_eps: Optional[float] = None):
         self.t = tensors
+        self.norm_eps = norm_eps
+        if norm_eps is not None:
+            flags |= abi.LMLP_RMSNORM
         self.dtype, self.wfmt = dtype, wfmt
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.hidden, self.inter, self.rank, self.scale, self.flags = hidden, inter, rank, scale, flags
@@ -65,10 +72,14 @@ class LoraMLP:
             y = torch.empty((self.tokens, self.hidden), dtype=self.tdtype, device=x.device)
         if saved is None:
             saved = self.new_saved()
-        abi.lora_mlp_forward(self.dims, x, t["w_gate"], self._scale_ptr("w_gate"), t["w_up"],
-                             self._scale_ptr("w_up"), t["w_down"], self._scale_ptr("w_down"),
-                             t["a_gate"], t["b_gate"], t["a_up"], t["b_up"], t["a_down"], t["b_down"],
-                             y, saved, self.workspace(False), stream=stream)
+        w = (t["w_gate"], self._scale_ptr("w_gate"), t["w_up"], self._scale_ptr("w_up"), t["w_down"],
+             self._scale_ptr("w_down"), t["a_gate"], t["b_gate"], t["a_up"], t["b_up"], t["a_down"],
+             t["b_down"])
+        if self.norm_eps is None:
+            abi.lora_mlp_forward(self.dims, x, *w, y, saved, self.workspace(False), stream=stream)
+        else:
+            abi.lora_mlp_norm_forward(self.dims, self.norm_eps, x, t["gamma"], *w, y, saved,
+                                      self.workspace(False), stream=stream)
         return y, saved
 
     def new_grads(self, device) -> Dict[str, torch.Tensor]:
@@ -83,19 +94,24 @@ class LoraMLP:
         if grads is None:
             grads = self.new_grads(dy.device)
         g = grads
-        abi.lora_mlp_backward(self.dims, dy, x, t["w_gate"], self._scale_ptr("w_gate"), t["w_up"],
-                              self._scale_ptr("w_up"), t["w_down"], self._scale_ptr("w_down"),
-                              t["a_gate"], t["b_gate"], t["a_up"], t["b_up"], t["a_down"],
-                              t["b_down"], saved, g["dx"], g["da_gate"], g["db_gate"], g["da_up"],
-                              g["db_up"], g["da_down"], g["db_down"], self.workspace(True),
-                              stream=stream)
+        w = (t["w_gate"], self._scale_ptr("w_gate"), t["w_up"], self._scale_ptr("w_up"), t["w_down"],
+             self._scale_ptr("w_down"), t["a_gate"], t["b_gate"], t["a_up"], t["b_up"], t["a_down"],
+             t["b_down"])
+        outs = (g["dx"], g["da_gate"], g["db_gate"], g["da_up"], g["db_up"], g["da_down"], g["db_down"])
+        if self.norm_eps is None:
+            abi.lora_mlp_backward(self.dims, dy, x, *w, saved, *outs, self.workspace(True), stream=stream)
+        else:
+            abi.lora_mlp_norm_backward(self.dims, dy, x, t["gamma"], *w, saved, *outs, self.workspace(True),
+                                       stream=stream)
         return grads
 
 
-def from_inputs(inp: Dict[str, np.ndarray], wl, device="cuda", flags: int = 0):
-    """LoraMLP plus device x, dy from a generated workload (see inputs.make_inputs)."""
+def from_inputs(inp: Dict[str, np.ndarray], wl, device="cuda", flags: int = 0,
+                norm_eps: Optional[float] = None):
+    """LoraMLP plus device x, dy from a generated workload (see inputs.make_inputs;
+    with ``norm_eps``, ``inp["gamma"]`` from inputs.make_norm_gamma)."""
     tens = {k: tensor_from_storage(v, wl.dtype, device) for k, v in inp.items()}
-    m = LoraMLP(tens, wl.tokens, wl.hidden, wl.inter, wl.rank, wl.scale, wl.dtype, wl.wfmt, flags)
+    m = LoraMLP(tens, wl.tokens, wl.hidden, wl.inter, wl.rank, wl.scale, wl.dtype, wl.wfmt, flags, norm_eps)
     return m, tens["x"], tens.get("dy")
 
 

@@ -44,6 +44,26 @@ def run_hip(inp: dict, wl, flags: int = 0, device="cuda"):
     return {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}, m
 
 
+def run_hip_norm(inp: dict, wl, eps: float, flags: int = 0, device="cuda"):
+    """RMSNorm then the MLP, forward + backward on the GPU (inp holds "gamma")."""
+    import torch
+    from lora_swiglu_mlp_amd import mlp
+    m, x, dy = mlp.from_inputs(inp, wl, device, flags, norm_eps=eps)
+    y, saved = m.forward(x)
+    g = m.backward(dy, x, saved)
+    torch.cuda.synchronize()
+    out = {"y": y}
+    out.update(g)
+    return {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}, m
+
+
+def norm_oracle(inp: dict, wl, eps: float, row_chunk: int = 2048) -> dict:
+    """The fp64 oracle of RMSNorm then the MLP on the same stored inputs."""
+    d = oracle_inputs(inp, wl)
+    gamma = d.pop("gamma")
+    return oracle.rmsnorm.norm_mlp_forward_backward(d, gamma, eps, wl.scale, row_chunk=row_chunk)
+
+
 def relerr(got: np.ndarray, ref: np.ndarray) -> float:
     den = float(np.max(np.abs(ref))) if ref.size else 0.0
     num = float(np.max(np.abs(got - ref))) if ref.size else 0.0

@@ -27,7 +27,7 @@ def test_library_exports_every_header_symbol():
                           "lora_mlp_backward", "lora_mlp_dequant_int4", "lora_mlp_status_string",
                           "lora_mlp_last_error", "lora_mlp_profile_begin", "lora_mlp_profile_end",
                           "lora_linear_saved_bytes", "lora_linear_workspace_bytes", "lora_linear_forward",
-                          "lora_linear_backward"}
+                          "lora_linear_backward", "lora_mlp_norm_forward", "lora_mlp_norm_backward"}
     L = abi.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -90,6 +90,7 @@ def test_workspace_sizes_positive_and_consume_flag_saves_memory():
     (dict(dtype=7), abi.LMLP_ERR_INVALID_ARG),
     (dict(wfmt=3), abi.LMLP_ERR_INVALID_ARG),
     (dict(flags=0x10), abi.LMLP_ERR_INVALID_ARG),
+    (dict(flags=0x8), abi.LMLP_ERR_INVALID_ARG),  # the norm flag on the plain entry point
     (dict(rank=257), abi.LMLP_ERR_UNSUPPORTED),
     (dict(hidden=132), abi.LMLP_ERR_UNSUPPORTED),          # not a multiple of 8 for bf16
     (dict(inter=346, dtype="f32"), abi.LMLP_ERR_UNSUPPORTED),  # not a multiple of 4
@@ -98,8 +99,9 @@ def test_workspace_sizes_positive_and_consume_flag_saves_memory():
 ])
 def test_invalid_dims_rejected(kw, code):
     d = dims(**kw)
-    assert abi.lora_mlp_saved_bytes(d) == 0
-    assert abi.lora_mlp_workspace_bytes(d, True) == 0
+    if kw.get("flags") != abi.LMLP_RMSNORM:  # valid dims, wrong entry point
+        assert abi.lora_mlp_saved_bytes(d) == 0
+        assert abi.lora_mlp_workspace_bytes(d, True) == 0
     rc = _forward_raw(d, saved_bytes=1 << 40, workspace_bytes=1 << 40)
     assert rc == code, abi.lora_mlp_last_error()
     assert abi.lora_mlp_last_error()
@@ -203,3 +205,43 @@ def test_linear_rejects_the_mlp_only_flags():
     for f in (abi.LMLP_CONSUME_SAVED, abi.LMLP_RECOMPUTE_GU):
         assert abi.lora_linear_saved_bytes(dims(flags=f)) == 0
     assert abi.lora_linear_saved_bytes(dims(inter=384, wfmt="int4_b64", flags=abi.LMLP_INT4_INKERNEL)) > 0
+
+
+def _norm_forward_raw(d, eps=1e-5, gamma=FAKE, saved_bytes=1 << 40, workspace_bytes=1 << 40):
+    return abi.lib().lora_mlp_norm_forward(
+        ctypes.byref(d), eps, FAKE, gamma, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        FAKE, FAKE, saved_bytes, FAKE, workspace_bytes, None)
+
+
+def _norm_backward_raw(d, gamma=FAKE, saved_bytes=1 << 40, workspace_bytes=1 << 40):
+    return abi.lib().lora_mlp_norm_backward(
+        ctypes.byref(d), FAKE, FAKE, gamma, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+        FAKE, FAKE, saved_bytes, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, workspace_bytes, None)
+
+
+@pytest.mark.parametrize("T,H,I,r,dt", [(256, 128, 344, 8, "f32"), (4096, 4096, 14336, 16, "bf16"), (0, 64, 64, 4, "bf16")])
+def test_norm_sizes(T, H, I, r, dt):
+    eb = 2 if dt == "bf16" else 4
+    base = dims(tokens=T, hidden=H, inter=I, rank=r, dtype=dt)
+    nd = dims(tokens=T, hidden=H, inter=I, rank=r, dtype=dt, flags=abi.LMLP_RMSNORM)
+    # saved: one fp32 statistic per token row; each workspace: the normalised rows
+    assert abi.lora_mlp_saved_bytes(nd) == abi.lora_mlp_saved_bytes(base) + align(4 * T)
+    for bwd in (False, True):
+        assert abi.lora_mlp_workspace_bytes(nd, bwd) == abi.lora_mlp_workspace_bytes(base, bwd) + align(T * H * eb)
+
+
+def test_norm_entry_point_argument_checks():
+    nd = dims(flags=abi.LMLP_RMSNORM)
+    plain = dims()
+    assert _norm_forward_raw(plain) == abi.LMLP_ERR_INVALID_ARG      # flag missing
+    assert "LMLP_RMSNORM" in abi.lora_mlp_last_error()
+    assert _norm_backward_raw(plain) == abi.LMLP_ERR_INVALID_ARG
+    for eps in (float("nan"), float("inf"), -1e-6):
+        assert _norm_forward_raw(nd, eps=eps) == abi.LMLP_ERR_INVALID_ARG
+    assert _norm_forward_raw(nd, gamma=None) == abi.LMLP_ERR_INVALID_ARG
+    assert _norm_forward_raw(nd, gamma=FAKE + 4) == abi.LMLP_ERR_INVALID_ARG
+    assert _norm_backward_raw(nd, gamma=None) == abi.LMLP_ERR_INVALID_ARG
+    assert _norm_forward_raw(nd, saved_bytes=16) == abi.LMLP_ERR_WORKSPACE
+    assert _norm_backward_raw(nd, workspace_bytes=16) == abi.LMLP_ERR_WORKSPACE
+    assert _backward_raw(nd, saved_bytes=1 << 40, workspace_bytes=1 << 40) == abi.LMLP_ERR_INVALID_ARG
+    assert abi.lora_linear_saved_bytes(dims(flags=abi.LMLP_RMSNORM)) == 0
