@@ -1,5 +1,5 @@
-"""CPU oracles for the LoRA SwiGLU MLP, the fused LoRA linear and the RMSNorm
-in front of the MLP (test infrastructure only).
+"""CPU oracles for the LoRA SwiGLU MLP, the fused LoRA linear, the RMSNorm in
+front of the MLP and the grouped (MoE) MLP (test infrastructure only).
 
 Only the tests, the smoke check and the bench's CPU-baseline leg may import
 this package. The HIP product path never does.
@@ -10,3 +10,4 @@ from .lora_mlp_oracle import (ADAPTER_KEYS, WEIGHT_KEYS, backward, base_mlp_rows
                               sigmoid, silu, unpack_int4)
 from . import lora_linear_oracle as linear  # noqa: F401,E402  (the fused LoRA linear)
 from . import rmsnorm_oracle as rmsnorm  # noqa: F401,E402  (RMSNorm, and RMSNorm then the MLP)
+from . import moe_oracle as moe  # noqa: F401,E402  (one LoRA MLP per expert over grouped rows)
