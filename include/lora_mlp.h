@@ -175,6 +175,48 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
                            void* da_up, void* db_up, void* da_down, void* db_down,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Grouped (mixture-of-experts) LoRA MLP --------------------------------
+ * E experts, each the MLP above with its own frozen weights and adapters,
+ * applied to the token rows routed to it: the MoE form of the fused MLP that
+ * "Unsloth 深度分析报告" (section 创新之处, the grouped GEMM over experts)
+ * accelerates. Routing, the top-k choice and the weighted combine of expert
+ * outputs stay with the caller: rows arrive grouped by expert, rows
+ * offsets[e] .. offsets[e+1]-1 of x (and of y, dy, dx) belonging to expert e.
+ * `offsets` is a HOST array of n_experts + 1 int64 values, rising from 0 to
+ * dims.tokens (the number of routed rows); 1 <= n_experts <= 65536.
+ * Per-expert tensors are stacked along a leading axis: w_gate, w_up
+ * [E,I,H] and w_down [E,H,I] (INT4_B64: [E,I,H/2] and [E,H,I/2] bytes with
+ * scales [E,I,H/64] and [E,H,I/64]), a_gate, a_up [E,r,H], b_gate, b_up
+ * [E,I,r], a_down [E,r,I], b_down [E,H,r], and the adapter gradients in the
+ * same shapes. dims.flags as for the MLP except LMLP_RMSNORM. An expert
+ * with no rows gets zero adapter gradients. Ownership, streams, determinism
+ * and errors as for the MLP: every argument is checked for every expert
+ * before anything is enqueued. */
+size_t lora_moe_saved_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets);
+size_t lora_moe_workspace_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets,
+                                int is_backward);
+int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets, const void* x,
+                     const void* w_gate, const void* w_gate_scales,
+                     const void* w_up, const void* w_up_scales,
+                     const void* w_down, const void* w_down_scales,
+                     const void* a_gate, const void* b_gate,
+                     const void* a_up, const void* b_up,
+                     const void* a_down, const void* b_down,
+                     void* y, void* saved, size_t saved_bytes,
+                     void* workspace, size_t workspace_bytes, void* stream);
+int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets,
+                      const void* dy, const void* x,
+                      const void* w_gate, const void* w_gate_scales,
+                      const void* w_up, const void* w_up_scales,
+                      const void* w_down, const void* w_down_scales,
+                      const void* a_gate, const void* b_gate,
+                      const void* a_up, const void* b_up,
+                      const void* a_down, const void* b_down,
+                      void* saved, size_t saved_bytes,
+                      void* dx, void* da_gate, void* db_gate,
+                      void* da_up, void* db_up, void* da_down, void* db_down,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Fused LoRA linear (one projection: q, k, v, o, ...) ----------------
  * y = x W^T + s (x A^T) B^T and its backward, the matmul-with-LoRA fusion of
  * "Unsloth 深度分析报告" (section 创新之处): the rank-r adapter rides as r

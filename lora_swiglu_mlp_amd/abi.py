@@ -62,6 +62,12 @@ _SIGS = {
                               + [_P, _SZ, _P, _SZ, _P]),
     "lora_mlp_norm_backward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 16 + [_SZ] + [_P] * 8
                                + [_SZ, _P]),
+    "lora_moe_saved_bytes": (_SZ, [ctypes.POINTER(lmlp_dims), ctypes.c_int64, _P]),
+    "lora_moe_workspace_bytes": (_SZ, [ctypes.POINTER(lmlp_dims), ctypes.c_int64, _P, ctypes.c_int]),
+    "lora_moe_forward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims), ctypes.c_int64, _P] + [_P] * 14
+                         + [_P, _SZ, _P, _SZ, _P]),
+    "lora_moe_backward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims), ctypes.c_int64, _P] + [_P] * 15 + [_SZ]
+                          + [_P] * 8 + [_SZ, _P]),
     "lora_linear_saved_bytes": (_SZ, [ctypes.POINTER(lmlp_dims)]),
     "lora_linear_workspace_bytes": (_SZ, [ctypes.POINTER(lmlp_dims), ctypes.c_int]),
     "lora_linear_forward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 7 + [_SZ, _P, _SZ, _P]),
@@ -81,7 +87,7 @@ def header_functions() -> list:
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lora_(?:mlp|linear)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lora_(?:mlp|linear|moe)_\w+)\s*\(", text)))
 
 
 def lib() -> ctypes.CDLL:
@@ -201,6 +207,50 @@ def lora_mlp_norm_backward(dims, dy, x, gamma, w_gate, w_gate_scales, w_up, w_up
         _ptr(db_down), _ptr(workspace),
         _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
     _check(rc, "lora_mlp_norm_backward")
+
+
+def offsets_array(offsets) -> "ctypes.Array":
+    """Host int64 array of the expert row offsets (n_experts + 1 values)."""
+    vals = [int(v) for v in offsets]
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def lora_moe_saved_bytes(dims: lmlp_dims, offsets) -> int:
+    off = offsets_array(offsets)
+    return int(lib().lora_moe_saved_bytes(ctypes.byref(dims), len(off) - 1, off))
+
+
+def lora_moe_workspace_bytes(dims: lmlp_dims, offsets, is_backward: bool) -> int:
+    off = offsets_array(offsets)
+    return int(lib().lora_moe_workspace_bytes(ctypes.byref(dims), len(off) - 1, off, int(bool(is_backward))))
+
+
+def lora_moe_forward(dims, offsets, x, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales,
+                     a_gate, b_gate, a_up, b_up, a_down, b_down, y, saved, workspace, stream=None,
+                     saved_bytes=None, workspace_bytes=None):
+    """offsets: n_experts + 1 host ints (rows of expert e: offsets[e] .. offsets[e+1]-1)."""
+    off = offsets_array(offsets)
+    rc = lib().lora_moe_forward(
+        ctypes.byref(dims), len(off) - 1, off, _ptr(x), _ptr(w_gate), _ptr(w_gate_scales), _ptr(w_up),
+        _ptr(w_up_scales), _ptr(w_down), _ptr(w_down_scales), _ptr(a_gate), _ptr(b_gate), _ptr(a_up),
+        _ptr(b_up), _ptr(a_down), _ptr(b_down), _ptr(y), _ptr(saved),
+        _nbytes(saved) if saved_bytes is None else saved_bytes,
+        _ptr(workspace), _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
+    _check(rc, "lora_moe_forward")
+
+
+def lora_moe_backward(dims, offsets, dy, x, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales,
+                      a_gate, b_gate, a_up, b_up, a_down, b_down, saved, dx, da_gate, db_gate, da_up, db_up,
+                      da_down, db_down, workspace, stream=None, saved_bytes=None, workspace_bytes=None):
+    off = offsets_array(offsets)
+    rc = lib().lora_moe_backward(
+        ctypes.byref(dims), len(off) - 1, off, _ptr(dy), _ptr(x), _ptr(w_gate), _ptr(w_gate_scales),
+        _ptr(w_up), _ptr(w_up_scales), _ptr(w_down), _ptr(w_down_scales), _ptr(a_gate), _ptr(b_gate),
+        _ptr(a_up), _ptr(b_up), _ptr(a_down), _ptr(b_down), _ptr(saved),
+        _nbytes(saved) if saved_bytes is None else saved_bytes,
+        _ptr(dx), _ptr(da_gate), _ptr(db_gate), _ptr(da_up), _ptr(db_up), _ptr(da_down), _ptr(db_down),
+        _ptr(workspace), _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
+    _check(rc, "lora_moe_backward")
 
 
 def lora_linear_saved_bytes(dims: lmlp_dims) -> int:

@@ -1068,6 +1068,170 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
                        da_down, db_down, workspace, workspace_bytes, stream);
 }
 
+// ---- grouped (MoE) LoRA MLP -------------------------------------------------
+// Rows grouped by expert (host offsets); per-expert tensors stacked along a
+// leading axis. Every argument is checked for all experts before anything is
+// enqueued; then each expert with rows runs the fused MLP above on its rows
+// and its slices of the stacked tensors, in expert order on the caller's
+// stream. The experts share one workspace (stream order makes the reuse
+// safe); `saved` holds one region per expert, in expert order. An expert
+// without rows gets zero adapter gradients.
+
+struct MoePlan {
+  std::vector<lmlp_dims> dims;  // per expert: tokens = its rows
+  std::vector<int64_t> row0;
+  std::vector<size_t> soff, ssize;
+  size_t saved_total = 0, ws_fwd = 0, ws_bwd = 0;
+  Dims d;  // the whole call
+};
+
+static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePlan& P) {
+  LMLP_TRY(parse_dims(dims, P.d));
+  if (P.d.norm) return fail(LMLP_ERR_INVALID_ARG, "LMLP_RMSNORM is not supported by the grouped MLP");
+  if (E < 1 || E > 65536) return fail(LMLP_ERR_INVALID_ARG, "n_experts must be in [1, 65536]");
+  if (!off) return fail(LMLP_ERR_INVALID_ARG, "offsets is NULL");
+  if (off[0] != 0 || off[E] != P.d.T) return fail(LMLP_ERR_INVALID_ARG, "offsets must run from 0 to dims.tokens");
+  P.dims.resize(E);
+  P.row0.resize(E);
+  P.soff.resize(E);
+  P.ssize.resize(E);
+  for (int64_t e = 0; e < E; ++e) {
+    if (off[e + 1] < off[e]) return fail(LMLP_ERR_INVALID_ARG, "offsets must not decrease");
+    lmlp_dims de = *dims;
+    de.tokens = off[e + 1] - off[e];
+    Dims dd;
+    LMLP_TRY(parse_dims(&de, dd));
+    P.dims[e] = de;
+    P.row0[e] = off[e];
+    P.soff[e] = P.saved_total;
+    P.ssize[e] = saved_layout(dd).total;
+    P.saved_total += P.ssize[e];
+    P.ws_fwd = std::max(P.ws_fwd, fwd_layout(dd).total);
+    P.ws_bwd = std::max(P.ws_bwd, bwd_layout(dd).total);
+  }
+  return LMLP_OK;
+}
+
+// bytes between consecutive experts of each stacked tensor
+struct MoeStrides {
+  size_t wgu, wgu_s, wd, wd_s, agu, bgu, ad, bd, rows;
+};
+static MoeStrides moe_strides(const Dims& d) {
+  MoeStrides S;
+  const size_t H = size_t(d.H), I = size_t(d.I), r = size_t(d.r), eb = size_t(d.eb);
+  S.wgu = d.int4 ? I * H / 2 : I * H * eb;
+  S.wgu_s = d.int4 ? I * (H / 64) * 2 : 0;
+  S.wd = d.int4 ? H * I / 2 : H * I * eb;
+  S.wd_s = d.int4 ? H * (I / 64) * 2 : 0;
+  S.agu = r * H * eb;
+  S.bgu = I * r * eb;
+  S.ad = r * I * eb;
+  S.bd = H * r * eb;
+  S.rows = H * eb;  // one token row of x, y, dy, dx
+  return S;
+}
+
+// item e of a stacked tensor (NULL stays NULL)
+static const void* slice(const void* base, int64_t e, size_t stride) {
+  return base ? static_cast<const char*>(base) + size_t(e) * stride : nullptr;
+}
+static void* slice(void* base, int64_t e, size_t stride) {
+  return base ? static_cast<char*>(base) + size_t(e) * stride : nullptr;
+}
+
+size_t lora_moe_saved_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets) {
+  MoePlan P;
+  if (moe_plan(dims, n_experts, offsets, P) != LMLP_OK) return 0;
+  return P.saved_total;
+}
+
+size_t lora_moe_workspace_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets,
+                                int is_backward) {
+  MoePlan P;
+  if (moe_plan(dims, n_experts, offsets, P) != LMLP_OK) return 0;
+  return is_backward ? P.ws_bwd : P.ws_fwd;
+}
+
+int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets, const void* x,
+                     const void* w_gate, const void* w_gate_scales, const void* w_up, const void* w_up_scales,
+                     const void* w_down, const void* w_down_scales, const void* a_gate, const void* b_gate,
+                     const void* a_up, const void* b_up, const void* a_down, const void* b_down, void* y,
+                     void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  MoePlan P;
+  LMLP_TRY(moe_plan(dims, n_experts, offsets, P));
+  const Dims& d = P.d;
+  LMLP_TRY(check_weights(d, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales));
+  LMLP_TRY(check_adapters(a_gate, b_gate, a_up, b_up, a_down, b_down));
+  if (d.T > 0) {
+    LMLP_TRY(need_ptr(x, "x"));
+    LMLP_TRY(need_ptr(y, "y"));
+    LMLP_TRY(need_ptr(saved, "saved"));
+    LMLP_TRY(need_ptr(workspace, "workspace"));
+  }
+  if (saved_bytes < P.saved_total) return fail(LMLP_ERR_WORKSPACE, "saved buffer smaller than lora_moe_saved_bytes()");
+  if (workspace_bytes < P.ws_fwd)
+    return fail(LMLP_ERR_WORKSPACE, "workspace smaller than lora_moe_workspace_bytes(dims, ..., 0)");
+  LMLP_TRY(check_device());
+  const MoeStrides S = moe_strides(d);
+  for (int64_t e = 0; e < n_experts; ++e) {
+    if (P.dims[e].tokens == 0) continue;
+    LMLP_TRY(forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
+                          slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu), slice(w_up_scales, e, S.wgu_s),
+                          slice(w_down, e, S.wd), slice(w_down_scales, e, S.wd_s), slice(a_gate, e, S.agu),
+                          slice(b_gate, e, S.bgu), slice(a_up, e, S.agu), slice(b_up, e, S.bgu),
+                          slice(a_down, e, S.ad), slice(b_down, e, S.bd), slice(y, P.row0[e], S.rows),
+                          at(saved, P.soff[e]), P.ssize[e], workspace, workspace_bytes, stream));
+  }
+  return LMLP_OK;
+}
+
+int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets, const void* dy,
+                      const void* x, const void* w_gate, const void* w_gate_scales, const void* w_up,
+                      const void* w_up_scales, const void* w_down, const void* w_down_scales, const void* a_gate,
+                      const void* b_gate, const void* a_up, const void* b_up, const void* a_down,
+                      const void* b_down, void* saved, size_t saved_bytes, void* dx, void* da_gate, void* db_gate,
+                      void* da_up, void* db_up, void* da_down, void* db_down, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  MoePlan P;
+  LMLP_TRY(moe_plan(dims, n_experts, offsets, P));
+  const Dims& d = P.d;
+  LMLP_TRY(check_weights(d, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales));
+  LMLP_TRY(check_adapters(a_gate, b_gate, a_up, b_up, a_down, b_down));
+  LMLP_TRY(need_ptr(da_gate, "da_gate"));
+  LMLP_TRY(need_ptr(db_gate, "db_gate"));
+  LMLP_TRY(need_ptr(da_up, "da_up"));
+  LMLP_TRY(need_ptr(db_up, "db_up"));
+  LMLP_TRY(need_ptr(da_down, "da_down"));
+  LMLP_TRY(need_ptr(db_down, "db_down"));
+  if (d.T > 0) {
+    LMLP_TRY(need_ptr(dy, "dy"));
+    LMLP_TRY(need_ptr(x, "x"));
+    LMLP_TRY(need_ptr(dx, "dx"));
+    LMLP_TRY(need_ptr(saved, "saved"));
+    LMLP_TRY(need_ptr(workspace, "workspace"));
+  }
+  if (saved_bytes < P.saved_total) return fail(LMLP_ERR_WORKSPACE, "saved buffer smaller than lora_moe_saved_bytes()");
+  if (workspace_bytes < P.ws_bwd)
+    return fail(LMLP_ERR_WORKSPACE, "workspace smaller than lora_moe_workspace_bytes(dims, ..., 1)");
+  LMLP_TRY(check_device());
+  const MoeStrides S = moe_strides(d);
+  for (int64_t e = 0; e < n_experts; ++e) {  // an expert without rows: its gradients are zero
+    const bool any = P.dims[e].tokens > 0;
+    LMLP_TRY(backward_impl(
+        &P.dims[e], nullptr, any ? slice(dy, P.row0[e], S.rows) : nullptr, any ? slice(x, P.row0[e], S.rows) : nullptr,
+        slice(w_gate, e, S.wgu), slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu),
+        slice(w_up_scales, e, S.wgu_s), slice(w_down, e, S.wd), slice(w_down_scales, e, S.wd_s),
+        slice(a_gate, e, S.agu), slice(b_gate, e, S.bgu), slice(a_up, e, S.agu), slice(b_up, e, S.bgu),
+        slice(a_down, e, S.ad), slice(b_down, e, S.bd), any ? at(saved, P.soff[e]) : nullptr, P.ssize[e],
+        any ? slice(dx, P.row0[e], S.rows) : nullptr, slice(da_gate, e, S.agu), slice(db_gate, e, S.bgu),
+        slice(da_up, e, S.agu), slice(db_up, e, S.bgu), slice(da_down, e, S.ad), slice(db_down, e, S.bd),
+        any ? workspace : nullptr, workspace_bytes, stream));
+  }
+  return LMLP_OK;
+}
+
 // ---- fused LoRA linear ----------------------------------------------------
 // Forward: pack A, B; rowproj P = x A^T (split-K) and its finish (P fp32 and
 // its bf16 transpose to saved, s P as the adapter segment); gemm y = [x | sP]

@@ -43,6 +43,8 @@ class Workload:
     dy_std: float = 1.0
     qscale_std: float = 0.003
     seed: int = 0
+    experts: int = 0      # grouped (MoE) workloads: number of experts
+    top_k: int = 0        # ... and experts per token (routed rows = tokens * top_k)
 
     @property
     def scale(self) -> float:
@@ -218,6 +220,66 @@ def make_linear_inputs(wl: Workload, seed: int | None = None, with_dy: bool = Tr
     if with_dy:
         out["dy"] = _store(_normal(rng, (T, n_out), wl.dy_std), dt)
     return out
+
+
+# Grouped (MoE) workloads: ``tokens`` tokens each routed to ``top_k`` of
+# ``experts`` experts, every expert a LoRA SwiGLU MLP of width ``inter``.
+# The shapes are the public MoE MLP shapes of model families the pages name
+# (Mistral's 8-expert top-2 Mixtral-8x7B; Qwen's 128-expert top-8 30B-A3B).
+MOE_WORKLOADS: Dict[str, Workload] = {
+    "moe_tiny_fp32": Workload("moe_tiny_fp32", 96, 128, 344, 8, 16.0, "f32", x_std=0.02, w_std=0.02,
+                              experts=4, top_k=2),
+    "moe_mixtral": Workload("moe_mixtral", 4096, 4096, 14336, 16, 16.0, "bf16", experts=8, top_k=2),
+    "moe_qwen3": Workload("moe_qwen3", 4096, 2048, 768, 16, 16.0, "bf16", experts=128, top_k=8),
+}
+
+
+def route_counts(rng: np.random.Generator, tokens: int, experts: int, top_k: int):
+    """Synthetic router: logits N(0, 1) plus a per-expert popularity bias
+    N(0, 0.5); each token takes its top_k experts. Returns, per routed row in
+    expert-grouped order, the token it came from, and the expert offsets."""
+    bias = _normal(rng, (experts,), 0.5)
+    logits = _normal(rng, (tokens, experts), 1.0) + bias[None, :]
+    choice = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]     # [tokens, top_k]
+    expert = choice.reshape(-1)
+    token = np.repeat(np.arange(tokens), top_k)
+    order = np.argsort(expert, kind="stable")
+    counts = np.bincount(expert, minlength=experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return token[order], offsets
+
+
+def make_moe_inputs(wl: Workload, seed: int | None = None, with_dy: bool = True):
+    """(inputs, offsets) of a grouped workload, drawn in a fixed order from
+    ``default_rng(seed)``: the router, x [tokens, H] (gathered into the routed
+    rows), the stacked weights W_gate, W_up [E, I, H], W_down [E, H, I] (int4:
+    codes then scales per expert), A_gate, B_gate, A_up, B_up, A_down, B_down
+    stacked [E, ...], and dY [rows, H]."""
+    seed = wl.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    E, H, I, r, dt = wl.experts, wl.hidden, wl.inter, wl.rank, wl.dtype
+    if E < 1 or wl.top_k < 1 or wl.top_k > E:
+        raise ValueError("a grouped workload needs 1 <= top_k <= experts")
+    tok, offsets = route_counts(rng, wl.tokens, E, wl.top_k)
+    x = _normal(rng, (wl.tokens, H), wl.x_std)
+    out = {"x": _store(np.ascontiguousarray(x[tok]), dt)}
+    del x
+    for name, (o, i) in (("w_gate", (I, H)), ("w_up", (I, H)), ("w_down", (H, I))):
+        if wl.wfmt == "dense":
+            out[name] = _store(_normal(rng, (E, o, i), wl.w_std), dt)
+        else:
+            qs = [_draw_int4(rng, o, i, wl.qscale_std) for _ in range(E)]
+            out[name] = np.stack([q for q, _ in qs])
+            out[name + "_scales"] = np.stack([s for _, s in qs])
+    out["a_gate"] = _store(_normal(rng, (E, r, H), wl.a_std), dt)
+    out["b_gate"] = _store(_normal(rng, (E, I, r), wl.b_std), dt)
+    out["a_up"] = _store(_normal(rng, (E, r, H), wl.a_std), dt)
+    out["b_up"] = _store(_normal(rng, (E, I, r), wl.b_std), dt)
+    out["a_down"] = _store(_normal(rng, (E, r, I), wl.a_std), dt)
+    out["b_down"] = _store(_normal(rng, (E, H, r), wl.b_std), dt)
+    if with_dy:
+        out["dy"] = _store(_normal(rng, (int(offsets[-1]), H), wl.dy_std), dt)
+    return out, offsets
 
 
 def draw_int4_codes(seed: int, out: int, inn: int, qscale_std: float = 0.003):

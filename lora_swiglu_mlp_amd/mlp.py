@@ -115,6 +115,70 @@ def from_inputs(inp: Dict[str, np.ndarray], wl, device="cuda", flags: int = 0,
     return m, tens["x"], tens.get("dy")
 
 
+class LoraMoE:
+    """E LoRA SwiGLU MLP experts (stacked tensors [E, ...]) over token rows
+    grouped by expert: rows offsets[e] .. offsets[e+1]-1 belong to expert e."""
+
+    def __init__(self, tensors: Dict[str, torch.Tensor], offsets, hidden: int, inter: int, rank: int,
+                 scale: float, dtype: str = "bf16", wfmt: str = "dense", flags: int = 0):
+        self.t = tensors
+        self.offsets = [int(v) for v in offsets]
+        self.experts = len(self.offsets) - 1
+        self.dtype, self.wfmt = dtype, wfmt
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.rows, self.hidden, self.inter, self.rank = self.offsets[-1], hidden, inter, rank
+        self.dims = abi.make_dims(self.rows, hidden, inter, rank, scale, dtype, wfmt, flags)
+        self._ws: Optional[torch.Tensor] = None
+
+    def _scale_ptr(self, name):
+        return self.t.get(name + "_scales") if self.wfmt == "int4_b64" else None
+
+    def _w(self):
+        t = self.t
+        return (t["w_gate"], self._scale_ptr("w_gate"), t["w_up"], self._scale_ptr("w_up"), t["w_down"],
+                self._scale_ptr("w_down"), t["a_gate"], t["b_gate"], t["a_up"], t["b_up"], t["a_down"],
+                t["b_down"])
+
+    def workspace(self) -> torch.Tensor:
+        need = max(abi.lora_moe_workspace_bytes(self.dims, self.offsets, False),
+                   abi.lora_moe_workspace_bytes(self.dims, self.offsets, True))
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.t["a_gate"].device)
+        return self._ws
+
+    def new_saved(self) -> torch.Tensor:
+        n = abi.lora_moe_saved_bytes(self.dims, self.offsets)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.t["a_gate"].device)
+
+    def forward(self, x, y=None, saved=None, stream=None):
+        if y is None:
+            y = torch.empty((self.rows, self.hidden), dtype=self.tdtype, device=x.device)
+        if saved is None:
+            saved = self.new_saved()
+        abi.lora_moe_forward(self.dims, self.offsets, x, *self._w(), y, saved, self.workspace(), stream=stream)
+        return y, saved
+
+    def new_grads(self, device) -> Dict[str, torch.Tensor]:
+        E, T, H, I, r = self.experts, self.rows, self.hidden, self.inter, self.rank
+        shapes = {"dx": (T, H), "da_gate": (E, r, H), "db_gate": (E, I, r), "da_up": (E, r, H),
+                  "db_up": (E, I, r), "da_down": (E, r, I), "db_down": (E, H, r)}
+        return {k: torch.empty(s, dtype=self.tdtype, device=device) for k, s in shapes.items()}
+
+    def backward(self, dy, x, saved, grads=None, stream=None):
+        g = self.new_grads(dy.device) if grads is None else grads
+        abi.lora_moe_backward(self.dims, self.offsets, dy, x, *self._w(), saved, g["dx"], g["da_gate"],
+                              g["db_gate"], g["da_up"], g["db_up"], g["da_down"], g["db_down"], self.workspace(),
+                              stream=stream)
+        return g
+
+
+def moe_from_inputs(inp: Dict[str, np.ndarray], offsets, wl, device="cuda", flags: int = 0):
+    """LoraMoE plus device x, dy from inputs.make_moe_inputs."""
+    tens = {k: tensor_from_storage(v, wl.dtype, device) for k, v in inp.items()}
+    m = LoraMoE(tens, offsets, wl.hidden, wl.inter, wl.rank, wl.scale, wl.dtype, wl.wfmt, flags)
+    return m, tens["x"], tens.get("dy")
+
+
 class LoraLinear:
     """One fused LoRA linear y = x W^T + s (x A^T) B^T (frozen W, trainable A/B)
     bound to device tensors ``w`` [out, in] (or 4-bit codes + ``w_scales``),

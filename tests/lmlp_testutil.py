@@ -64,6 +64,33 @@ def norm_oracle(inp: dict, wl, eps: float, row_chunk: int = 2048) -> dict:
     return oracle.rmsnorm.norm_mlp_forward_backward(d, gamma, eps, wl.scale, row_chunk=row_chunk)
 
 
+def run_hip_moe(inp: dict, offsets, wl, flags: int = 0, device="cuda"):
+    """Grouped (MoE) forward + backward on the GPU; fp64 numpy outputs."""
+    import torch
+    from lora_swiglu_mlp_amd import mlp
+    m, x, dy = mlp.moe_from_inputs(inp, offsets, wl, device, flags)
+    y, saved = m.forward(x)
+    g = m.backward(dy, x, saved)
+    torch.cuda.synchronize()
+    out = {"y": y}
+    out.update(g)
+    return {k: v.float().cpu().numpy().astype(np.float64) for k, v in out.items()}, m
+
+
+def moe_oracle_inputs(inp: dict, wl) -> dict:
+    """fp64 copies of stacked MoE inputs (4-bit weights decoded expert by expert)."""
+    d = {}
+    for k, v in inp.items():
+        if k.endswith("_scales"):
+            continue
+        if wl.wfmt == "int4_b64" and k in ("w_gate", "w_up", "w_down"):
+            inn = wl.inter if k == "w_down" else wl.hidden
+            d[k] = np.stack([oracle.dequant_int4(v[e], inp[k + "_scales"][e], inn) for e in range(v.shape[0])])
+        else:
+            d[k] = inp_mod.to_f64(v, wl.dtype)
+    return d
+
+
 def relerr(got: np.ndarray, ref: np.ndarray) -> float:
     den = float(np.max(np.abs(ref))) if ref.size else 0.0
     num = float(np.max(np.abs(got - ref))) if ref.size else 0.0

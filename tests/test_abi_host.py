@@ -8,6 +8,7 @@ import ctypes
 import os
 import subprocess
 
+import numpy as np
 import pytest
 
 from lora_swiglu_mlp_amd import abi
@@ -27,7 +28,9 @@ def test_library_exports_every_header_symbol():
                           "lora_mlp_backward", "lora_mlp_dequant_int4", "lora_mlp_status_string",
                           "lora_mlp_last_error", "lora_mlp_profile_begin", "lora_mlp_profile_end",
                           "lora_linear_saved_bytes", "lora_linear_workspace_bytes", "lora_linear_forward",
-                          "lora_linear_backward", "lora_mlp_norm_forward", "lora_mlp_norm_backward"}
+                          "lora_linear_backward", "lora_mlp_norm_forward", "lora_mlp_norm_backward",
+                          "lora_moe_saved_bytes", "lora_moe_workspace_bytes", "lora_moe_forward",
+                          "lora_moe_backward"}
     L = abi.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -245,3 +248,50 @@ def test_norm_entry_point_argument_checks():
     assert _norm_backward_raw(nd, workspace_bytes=16) == abi.LMLP_ERR_WORKSPACE
     assert _backward_raw(nd, saved_bytes=1 << 40, workspace_bytes=1 << 40) == abi.LMLP_ERR_INVALID_ARG
     assert abi.lora_linear_saved_bytes(dims(flags=abi.LMLP_RMSNORM)) == 0
+
+
+def _moe_forward_raw(d, offsets, saved_bytes=1 << 40, workspace_bytes=1 << 40):
+    off = abi.offsets_array(offsets) if offsets is not None else None
+    n = len(offsets) - 1 if offsets is not None else 1
+    return abi.lib().lora_moe_forward(
+        ctypes.byref(d), n, off, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        FAKE, FAKE, saved_bytes, FAKE, workspace_bytes, None)
+
+
+@pytest.mark.parametrize("counts,dt", [((3, 0, 5, 1), "bf16"), ((4096, 2048, 2048, 0), "bf16"), ((7, 9), "f32")])
+def test_moe_sizes(counts, dt):
+    T = sum(counts)
+    off = [0] + list(np.cumsum(counts))
+    d = dims(tokens=T, hidden=256, inter=512, rank=16, dtype=dt)
+    per = [dims(tokens=c, hidden=256, inter=512, rank=16, dtype=dt) for c in counts]
+    # one saved region per expert; one workspace, as large as the largest expert's
+    assert abi.lora_moe_saved_bytes(d, off) == sum(abi.lora_mlp_saved_bytes(p) for p in per)
+    for bwd in (False, True):
+        assert abi.lora_moe_workspace_bytes(d, off, bwd) == max(abi.lora_mlp_workspace_bytes(p, bwd) for p in per)
+
+
+def test_moe_argument_checks():
+    d = dims(tokens=10)
+    good = [0, 4, 10]
+    assert abi.lora_moe_saved_bytes(d, good) > 0
+    for bad in ([0, 5, 4, 10], [1, 4, 10], [0, 4, 9], [0, 4, 11]):
+        assert abi.lora_moe_saved_bytes(d, bad) == 0
+        assert _moe_forward_raw(d, bad) == abi.LMLP_ERR_INVALID_ARG
+    assert _moe_forward_raw(d, None) == abi.LMLP_ERR_INVALID_ARG  # offsets NULL
+    assert "offsets" in abi.lora_mlp_last_error()
+    assert abi.lib().lora_moe_saved_bytes(ctypes.byref(d), 0, abi.offsets_array([0])) == 0  # no experts
+    assert abi.lora_moe_saved_bytes(dims(tokens=10, flags=abi.LMLP_RMSNORM), good) == 0
+    assert _moe_forward_raw(d, good, saved_bytes=16) == abi.LMLP_ERR_WORKSPACE
+    assert _moe_forward_raw(d, good, workspace_bytes=16) == abi.LMLP_ERR_WORKSPACE
+
+
+def test_binding_argument_counts_match_the_header():
+    """Every ctypes signature has as many arguments as the header prototype."""
+    import re
+    with open(abi.HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    for name, (_, args) in abi._SIGS.items():
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), (name, len(params), len(args))
