@@ -173,6 +173,98 @@ def cpu_baseline_linear(inp, wl, seconds: float):
             "sample": f"first {n} of {wl.tokens} tokens of {wl.name}, forward+backward, fp64 numpy, {t:.1f} s"}
 
 
+def cpu_baseline_moe(inp, offsets, wl, seconds: float):
+    """The MoE oracle on the first experts (all their rows) until about
+    `seconds` of CPU work; reported per input token (routed rows / top_k)."""
+    from oracle import moe_oracle as MO
+    from lora_swiglu_mlp_amd import inputs as I
+    keys = ("w_gate", "w_up", "w_down", "a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
+    rows = t = 0.0
+    e = 0
+    while e < wl.experts and t < seconds:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        d = {k: I.to_f64(inp[k][e:e + 1], wl.dtype) for k in keys}
+        d["x"] = I.to_f64(inp["x"][lo:hi], wl.dtype)
+        d["dy"] = I.to_f64(inp["dy"][lo:hi], wl.dtype)
+        t0 = time.perf_counter()
+        MO.forward_backward(d, [0, hi - lo], wl.scale)
+        t += time.perf_counter() - t0
+        rows += hi - lo
+        e += 1
+    return {"value": rows / wl.top_k / t, "unit": "tokens/s", "cores": os.cpu_count() or 1, "kind": "oracle",
+            "sample": f"experts 0..{e - 1} of {wl.experts} with all their rows ({int(rows)} of "
+                      f"{int(offsets[-1])} routed rows) of {wl.name}, forward+backward, fp64 numpy, {t:.1f} s"}
+
+
+def bench_moe(args, wl):
+    """The grouped (MoE) LoRA MLP on a MOE_WORKLOADS shape."""
+    import torch
+    from lora_swiglu_mlp_amd import abi, mlp
+    from lora_swiglu_mlp_amd import inputs as I
+    H, Iw, r = wl.hidden, wl.inter, wl.rank
+    torch.cuda.set_device(0)
+    inp, offsets = I.make_moe_inputs(wl)
+    rows = int(offsets[-1])
+    m, x, dy = mlp.moe_from_inputs(inp, offsets, wl, "cuda:0")
+    saved = m.new_saved()
+    y = torch.empty((rows, H), dtype=m.tdtype, device="cuda:0")
+    grads = m.new_grads(x.device)
+    m.workspace()
+
+    def step():
+        m.forward(x, y, saved)
+        m.backward(dy, x, saved, grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flops = 12 * rows * H * Iw + 18 * rows * r * (H + Iw)
+    peak = PEAK_TFLOPS[wl.dtype]
+    tflops = flops / (ms * 1e-3) / 1e12
+    counts = [int(c) for c in (offsets[1:] - offsets[:-1])]
+    out = {"metric": "grouped (MoE) LoRA-SwiGLU MLP fwd+bwd tokens/sec + TFLOP/s as % of MI355X bf16 peak",
+           "value": wl.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": wl.dtype,
+           "data": "synthetic (seeded normal draws; random-init weights; synthetic top-k router)",
+           "config": {"workload": wl.name, "tokens": wl.tokens, "experts": wl.experts, "top_k": wl.top_k,
+                      "routed_rows": rows, "rows_per_expert_min_max": [min(counts), max(counts)],
+                      "hidden": H, "inter": Iw, "rank": r, "alpha": wl.alpha, "weights": wl.wfmt,
+                      "parallelism": "single-gpu"},
+           "tflops": tflops, "pct_of_peak": 100.0 * tflops / peak}
+    if not args.no_profile:
+        nprof = max(1, min(args.steps, 5))
+        abi.lora_mlp_profile_begin()
+        for _ in range(nprof):
+            step()
+        recs = abi.lora_mlp_profile_end()
+        agg = {}
+        for name, t in recs:
+            a = agg.setdefault(name, [0.0, 0])
+            a[0] += t
+            a[1] += 1
+        # per kernel: time per step summed over the experts' launches; FLOPs over all routed rows
+        kern = {name: {"ms_per_step": tot / nprof, "launches_per_step": cnt / nprof}
+                for name, (tot, cnt) in agg.items()}
+        for name, e in kern.items():
+            f = kernel_flops(name, rows, H, Iw, r)
+            if f:
+                e["tflops"] = f / (e["ms_per_step"] * 1e-3) / 1e12
+        out["kernels"] = kern
+        out["kernel_ms_per_step"] = sum(e["ms_per_step"] for e in kern.values())
+        dom = max((n for n in kern if "tflops" in kern[n]), key=lambda n: kern[n]["ms_per_step"])
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"], "peak": peak,
+                           "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / peak, "traffic": None}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_moe(inp, offsets, wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def bench_linear(args, wl):
     """The fused LoRA linear (one projection) on a LINEAR_WORKLOADS shape."""
     import torch
@@ -266,6 +358,9 @@ def main():
 
     if args.workload in I.LINEAR_WORKLOADS:
         bench_linear(args, I.LINEAR_WORKLOADS[args.workload])
+        return
+    if args.workload in I.MOE_WORKLOADS:
+        bench_moe(args, I.MOE_WORKLOADS[args.workload])
         return
     wl = I.WORKLOADS[args.workload]
     T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank

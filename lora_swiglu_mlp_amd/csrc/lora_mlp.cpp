@@ -33,6 +33,9 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1072,18 +1075,76 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
 // Rows grouped by expert (host offsets); per-expert tensors stacked along a
 // leading axis. Every argument is checked for all experts before anything is
 // enqueued; then each expert with rows runs the fused MLP above on its rows
-// and its slices of the stacked tensors, in expert order on the caller's
-// stream. The experts share one workspace (stream order makes the reuse
-// safe); `saved` holds one region per expert, in expert order. An expert
-// without rows gets zero adapter gradients.
+// and its slices of the stacked tensors. One expert's GEMMs are small (a few
+// hundred to a few thousand rows: tens of tiles for 256 CUs), so the experts
+// run concurrently on kMoeStreams worker streams (default priority,
+// non-blocking, created once per device), expert e on stream e % kMoeStreams
+// with workspace slot e % kMoeStreams; the workers start after the work
+// already on the caller's stream and the caller's stream continues after all
+// of them (events). `saved` holds one region per expert, in expert order. An
+// expert without rows gets zero adapter gradients. Each expert's arithmetic
+// does not depend on the stream it runs on, so results are bitwise
+// reproducible.
+
+constexpr int kMoeStreams = 4;
 
 struct MoePlan {
   std::vector<lmlp_dims> dims;  // per expert: tokens = its rows
   std::vector<int64_t> row0;
   std::vector<size_t> soff, ssize;
-  size_t saved_total = 0, ws_fwd = 0, ws_bwd = 0;
+  size_t saved_total = 0, ws_fwd = 0, ws_bwd = 0;  // workspace: `slots` slots of slot_fwd / slot_bwd bytes
+  size_t slot_fwd = 0, slot_bwd = 0;
+  int slots = 1;
   Dims d;  // the whole call
 };
+
+// The worker streams and fork/join events of one device. Enqueueing a grouped
+// call holds g_moe_mu, so calls from several host threads do not interleave
+// their event records.
+struct MoeStreams {
+  hipStream_t s[kMoeStreams];
+  hipEvent_t fork, join[kMoeStreams];
+};
+static std::mutex g_moe_mu;
+static std::map<int, MoeStreams> g_moe_streams;
+
+static int moe_streams(MoeStreams*& out) {  // call with g_moe_mu held
+  int dev = 0;
+  LMLP_TRY(hip_rc(hipGetDevice(&dev), "hipGetDevice"));
+  auto it = g_moe_streams.find(dev);
+  if (it == g_moe_streams.end()) {
+    MoeStreams m{};
+    for (int i = 0; i < kMoeStreams; ++i) {
+      LMLP_TRY(hip_rc(hipStreamCreateWithFlags(&m.s[i], hipStreamNonBlocking), "hipStreamCreateWithFlags"));
+      LMLP_TRY(hip_rc(hipEventCreateWithFlags(&m.join[i], hipEventDisableTiming), "hipEventCreateWithFlags"));
+    }
+    LMLP_TRY(hip_rc(hipEventCreateWithFlags(&m.fork, hipEventDisableTiming), "hipEventCreateWithFlags"));
+    it = g_moe_streams.emplace(dev, m).first;
+  }
+  out = &it->second;
+  return LMLP_OK;
+}
+
+// Run body(e, worker stream, workspace slot) for the experts in `order`,
+// forked from and joined back to the caller's stream.
+static int moe_run(hipStream_t caller, const std::vector<int64_t>& order, int slots,
+                   const std::function<int(int64_t, hipStream_t, int)>& body) {
+  std::lock_guard<std::mutex> lock(g_moe_mu);
+  MoeStreams* ms = nullptr;
+  LMLP_TRY(moe_streams(ms));
+  const int nw = std::min<int>(slots, kMoeStreams);
+  LMLP_TRY(hip_rc(hipEventRecord(ms->fork, caller), "hipEventRecord"));
+  for (int i = 0; i < nw; ++i) LMLP_TRY(hip_rc(hipStreamWaitEvent(ms->s[i], ms->fork, 0), "hipStreamWaitEvent"));
+  for (size_t k = 0; k < order.size(); ++k) {
+    const int w = int(k % size_t(nw));
+    LMLP_TRY(body(order[k], ms->s[w], w));
+  }
+  for (int i = 0; i < nw; ++i) {
+    LMLP_TRY(hip_rc(hipEventRecord(ms->join[i], ms->s[i]), "hipEventRecord"));
+    LMLP_TRY(hip_rc(hipStreamWaitEvent(caller, ms->join[i], 0), "hipStreamWaitEvent"));
+  }
+  return LMLP_OK;
+}
 
 static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePlan& P) {
   LMLP_TRY(parse_dims(dims, P.d));
@@ -1106,9 +1167,12 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
     P.soff[e] = P.saved_total;
     P.ssize[e] = saved_layout(dd).total;
     P.saved_total += P.ssize[e];
-    P.ws_fwd = std::max(P.ws_fwd, fwd_layout(dd).total);
-    P.ws_bwd = std::max(P.ws_bwd, bwd_layout(dd).total);
+    P.slot_fwd = std::max(P.slot_fwd, fwd_layout(dd).total);
+    P.slot_bwd = std::max(P.slot_bwd, bwd_layout(dd).total);
   }
+  P.slots = int(std::min<int64_t>(E, kMoeStreams));
+  P.ws_fwd = P.slot_fwd * P.slots;
+  P.ws_bwd = P.slot_bwd * P.slots;
   return LMLP_OK;
 }
 
@@ -1174,16 +1238,18 @@ int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* of
     return fail(LMLP_ERR_WORKSPACE, "workspace smaller than lora_moe_workspace_bytes(dims, ..., 0)");
   LMLP_TRY(check_device());
   const MoeStrides S = moe_strides(d);
-  for (int64_t e = 0; e < n_experts; ++e) {
-    if (P.dims[e].tokens == 0) continue;
-    LMLP_TRY(forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
-                          slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu), slice(w_up_scales, e, S.wgu_s),
-                          slice(w_down, e, S.wd), slice(w_down_scales, e, S.wd_s), slice(a_gate, e, S.agu),
-                          slice(b_gate, e, S.bgu), slice(a_up, e, S.agu), slice(b_up, e, S.bgu),
-                          slice(a_down, e, S.ad), slice(b_down, e, S.bd), slice(y, P.row0[e], S.rows),
-                          at(saved, P.soff[e]), P.ssize[e], workspace, workspace_bytes, stream));
-  }
-  return LMLP_OK;
+  std::vector<int64_t> order;  // experts with rows
+  for (int64_t e = 0; e < n_experts; ++e)
+    if (P.dims[e].tokens > 0) order.push_back(e);
+  if (order.empty()) return LMLP_OK;
+  return moe_run(static_cast<hipStream_t>(stream), order, P.slots, [&](int64_t e, hipStream_t ws, int slot) {
+    return forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
+                        slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu), slice(w_up_scales, e, S.wgu_s),
+                        slice(w_down, e, S.wd), slice(w_down_scales, e, S.wd_s), slice(a_gate, e, S.agu),
+                        slice(b_gate, e, S.bgu), slice(a_up, e, S.agu), slice(b_up, e, S.bgu), slice(a_down, e, S.ad),
+                        slice(b_down, e, S.bd), slice(y, P.row0[e], S.rows), at(saved, P.soff[e]), P.ssize[e],
+                        at(workspace, size_t(slot) * P.slot_fwd), P.slot_fwd, ws);
+  });
 }
 
 int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets, const void* dy,
@@ -1217,9 +1283,11 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
     return fail(LMLP_ERR_WORKSPACE, "workspace smaller than lora_moe_workspace_bytes(dims, ..., 1)");
   LMLP_TRY(check_device());
   const MoeStrides S = moe_strides(d);
-  for (int64_t e = 0; e < n_experts; ++e) {  // an expert without rows: its gradients are zero
+  std::vector<int64_t> order(n_experts);  // every expert: one without rows gets zero gradients
+  for (int64_t e = 0; e < n_experts; ++e) order[e] = e;
+  return moe_run(static_cast<hipStream_t>(stream), order, P.slots, [&](int64_t e, hipStream_t ws, int slot) {
     const bool any = P.dims[e].tokens > 0;
-    LMLP_TRY(backward_impl(
+    return backward_impl(
         &P.dims[e], nullptr, any ? slice(dy, P.row0[e], S.rows) : nullptr, any ? slice(x, P.row0[e], S.rows) : nullptr,
         slice(w_gate, e, S.wgu), slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu),
         slice(w_up_scales, e, S.wgu_s), slice(w_down, e, S.wd), slice(w_down_scales, e, S.wd_s),
@@ -1227,9 +1295,8 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
         slice(a_down, e, S.ad), slice(b_down, e, S.bd), any ? at(saved, P.soff[e]) : nullptr, P.ssize[e],
         any ? slice(dx, P.row0[e], S.rows) : nullptr, slice(da_gate, e, S.agu), slice(db_gate, e, S.bgu),
         slice(da_up, e, S.agu), slice(db_up, e, S.bgu), slice(da_down, e, S.ad), slice(db_down, e, S.bd),
-        any ? workspace : nullptr, workspace_bytes, stream));
-  }
-  return LMLP_OK;
+        any ? at(workspace, size_t(slot) * P.slot_bwd) : nullptr, P.slot_bwd, ws);
+  });
 }
 
 // ---- fused LoRA linear ----------------------------------------------------
@@ -1451,9 +1518,13 @@ int lora_mlp_profile_end(lmlp_kernel_time* out, int capacity, int* count) {
   g_prof.on = false;
   int rc = LMLP_OK;
   int n = 0;
-  if (!g_prof.recs.empty()) {
-    hipError_t e = hipEventSynchronize(g_prof.recs.back().e);
-    if (e != hipSuccess) rc = fail(LMLP_ERR_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+  // every end event: the grouped MLP records on several streams
+  for (const ProfRec& r : g_prof.recs) {
+    hipError_t e = hipEventSynchronize(r.e);
+    if (e != hipSuccess) {
+      rc = fail(LMLP_ERR_HIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+      break;
+    }
   }
   if (rc == LMLP_OK) {
     for (const ProfRec& r : g_prof.recs) {
