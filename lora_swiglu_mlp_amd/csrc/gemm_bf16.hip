@@ -806,6 +806,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmParams p) {
   gemm_bf16_body<NN, EPI, QRB, NB>(p, blockIdx.x, gridDim.x, smem);
 }
 
+// Several independent products of one kind in one launch (the experts of a
+// grouped MLP): group g owns workgroups start[g] .. start[g+1]-1, of which the
+// first tiles(g) compute its tiles in its own XCD-aware order; start[g] is a
+// multiple of 8 so that a workgroup's position in its group keeps the XCD it
+// runs on, and the padding workgroups exit at once.
+template <bool NN, int EPI, int QRB, int NB>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_grouped_kernel(GemmGroups gg) {
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  const int bid = blockIdx.x;
+  int g = 0;
+  while (g + 1 < gg.n && bid >= gg.start[g + 1]) ++g;
+  const GemmParams& p = gg.p[g];
+  const int local = bid - gg.start[g];
+  const int tiles = p.tiles_m * p.tiles_n;
+  if (local >= tiles) return;
+  gemm_bf16_body<NN, EPI, QRB, NB>(p, local, tiles, smem);
+}
+
 // ---- 4-bit B operand (NT products with 4-bit block weights) ---------------
 // The weight panel arrives as codes and scales and is decoded in LDS:
 //  * ring stage (24 KB): the A tile (16 KB, as in the dense kernel); the codes
@@ -1065,6 +1083,41 @@ static hipError_t launch_t(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// tile counts and band height of one product, as launch_t sets them
+template <int EPI, int NB>
+static void set_tiles(GemmParams& p) {
+  constexpr int TN = 32 * NB;
+  p.tiles_m = static_cast<int>((p.M + BM - 1) / BM);
+  p.tiles_n = EPI == EPI_SWIGLU_FWD ? static_cast<int>((p.N + TN / 2 - 1) / (TN / 2))
+                                    : static_cast<int>((p.N + TN - 1) / TN);
+  if (p.group_m <= 0) p.group_m = 8;
+  if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
+}
+
+template <bool NN, int EPI, int QRB = 0, int NB = 8>
+static hipError_t launch_grouped_t(const GemmParams* ps, int n, hipStream_t stream) {
+  for (int i0 = 0; i0 < n; i0 += kMaxGemmGroups) {
+    GemmGroups gg{};
+    int nblk = 0;
+    for (int i = i0; i < n && gg.n < kMaxGemmGroups; ++i) {
+      GemmParams q = ps[i];
+      set_tiles<EPI, NB>(q);
+      const int tiles = q.tiles_m * q.tiles_n;
+      if (tiles == 0) continue;
+      gg.p[gg.n] = q;
+      gg.start[gg.n] = nblk;
+      nblk += (tiles + 7) / 8 * 8;
+      ++gg.n;
+    }
+    gg.start[gg.n] = nblk;
+    if (gg.n == 0) continue;
+    hipLaunchKernelGGL((gemm_bf16_grouped_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream, gg);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int EPI>
 static hipError_t launch_q4(GemmParams p, hipStream_t stream) {
   p.tiles_m = static_cast<int>((p.M + BM - 1) / BM);
@@ -1095,6 +1148,26 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t st
       return narrow ? launch_t<true, EPI_SWIGLU_BWD, 0, 4>(p, stream) : launch_t<true, EPI_SWIGLU_BWD, 0, 8>(p, stream);
     if (p.pj_r16 == 16)
       return narrow ? launch_t<true, EPI_SWIGLU_BWD, 1, 4>(p, stream) : launch_t<true, EPI_SWIGLU_BWD, 1, 8>(p, stream);
+    return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const GemmParams& p = ps[0];  // every product of one call is of one kind
+  if (!nn && epi == EPI_STORE) return launch_grouped_t<false, EPI_STORE>(ps, n, stream);
+  if (!nn && epi == EPI_SWIGLU_FWD) return launch_grouped_t<false, EPI_SWIGLU_FWD>(ps, n, stream);
+  if (nn && epi == EPI_STORE) return launch_grouped_t<true, EPI_STORE>(ps, n, stream);
+  if (nn && epi == EPI_SWIGLU_BWD) {
+    const bool narrow = p.tile_n == 128;
+    if (p.tile_n != 0 && p.tile_n != 128 && p.tile_n != 256) return hipErrorInvalidValue;
+    if (p.pj_part0 == nullptr)
+      return narrow ? launch_grouped_t<true, EPI_SWIGLU_BWD, 0, 4>(ps, n, stream)
+                    : launch_grouped_t<true, EPI_SWIGLU_BWD, 0, 8>(ps, n, stream);
+    if (p.pj_r16 == 16)
+      return narrow ? launch_grouped_t<true, EPI_SWIGLU_BWD, 1, 4>(ps, n, stream)
+                    : launch_grouped_t<true, EPI_SWIGLU_BWD, 1, 8>(ps, n, stream);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

@@ -65,10 +65,22 @@ struct GemmParams {
   int32_t tile_n;
 };
 
+// Up to kMaxGemmGroups products of one kind (same NN / epilogue / tile
+// width) in one launch; set by the grouped launcher.
+constexpr int kMaxGemmGroups = 8;
+struct GemmGroups {
+  GemmParams p[kMaxGemmGroups];
+  int32_t start[kMaxGemmGroups + 1];  // first workgroup of each group (multiples of 8), then the total
+  int32_t n;
+};
+
 // fp32 products (register-staged general kernel)
 hipError_t launch_gemm_f32(const GemmParams& p, int nn, int epi, hipStream_t stream);
 // dense bf16 operands only (LDS-DMA staging); needs every row stride * 256 < 2^31 bytes
 hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t stream);
+// The same products, n of them of one kind (grouped MLP experts), in
+// launches of up to kMaxGemmGroups products each.
+hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi, hipStream_t stream);
 // NT products whose segment-0 B operand is 4-bit: seg[0].b0/b1 hold the codes
 // ([N][K/2] bytes, seg[0].ldb = K codes per row), seg[0].bs0/bs1 the block
 // scales as fp32 [K/64][N]; K and N multiples of 64. Segment 1 (the

@@ -463,6 +463,44 @@ struct ProfScope {
     ps_.done();                                  \
   } while (0)
 
+// Phase control of one forward or backward pass, for the grouped MLP: the
+// pass is cut at its GEMMs. phase < 0: everything runs (the plain entry
+// points). phase k: only the side kernels between GEMM k-1 and GEMM k are
+// launched, and GEMM k is handed back in `gp` instead of being launched (the
+// pass returns there); a pass with no GEMM left hands back nothing. Running
+// phases 0, 1, ... in order launches the same work in the same order.
+struct Exec {
+  int phase = -1;
+  int seg = 0;  // GEMMs passed so far
+  bool sunk = false;
+  const char* name = nullptr;
+  GemmParams gp{};
+  int nn = 0, epi = 0;
+  bool groupable = false;  // a dense bf16 product (the grouped launcher takes it)
+  bool side() const { return phase < 0 || seg == phase; }
+};
+
+#define LMLP_SIDE(name, expr)                  \
+  do {                                         \
+    if (ex.side()) LMLP_LAUNCH(name, expr);    \
+  } while (0)
+
+#define LMLP_GEMM(name_, gp_, nn_, epi_)                                          \
+  do {                                                                             \
+    if (ex.phase < 0) {                                                            \
+      LMLP_LAUNCH(name_, run_gemm(gp_, d, nn_, epi_, st));                         \
+    } else if (ex.seg == ex.phase) {                                               \
+      ex.sunk = true;                                                              \
+      ex.name = name_;                                                             \
+      ex.gp = gp_;                                                                 \
+      ex.nn = nn_;                                                                 \
+      ex.epi = epi_;                                                               \
+      ex.groupable = d.bf16 && !(gp_).seg[0].bint4;                                \
+      return LMLP_OK;                                                              \
+    }                                                                              \
+    ++ex.seg;                                                                      \
+  } while (0)
+
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
 // bf16 products take the LDS-DMA kernels (4-bit weights decoded in the
@@ -610,7 +648,10 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
                         const void* w_gate_scales, const void* w_up, const void* w_up_scales, const void* w_down,
                         const void* w_down_scales, const void* a_gate, const void* b_gate, const void* a_up,
                         const void* b_up, const void* a_down, const void* b_down, void* y, void* saved,
-                        size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+                        size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                        Exec* exec = nullptr) {
+  Exec local_exec;
+  Exec& ex = exec ? *exec : local_exec;
   Dims d;
   LMLP_TRY(parse_dims(dims, d));
   if (d.norm) LMLP_TRY(need_ptr(gamma, "gamma"));
@@ -642,7 +683,7 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
     np.H = H;
     np.eps = eps;
     np.mode = NORM_FWD;
-    LMLP_LAUNCH("rmsnorm(fwd)", launch_rmsnorm(np, d.bf16, st));
+    LMLP_SIDE("rmsnorm(fwd)", launch_rmsnorm(np, d.bf16, st));
     x = np.xn;
   }
   // with LMLP_RECOMPUTE_GU the gate/up epilogue stores only Z
@@ -673,7 +714,7 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   pk.job[8] = pack_job(at(saved, SL.bgT), I, r16, I, b_gate, r, I, r, true);  // B_g^T
   pk.job[9] = pack_job(at(saved, SL.buT), I, r16, I, b_up, r, I, r, true);    // B_u^T
   pk.njobs = 10;
-  LMLP_LAUNCH("pack(fwd)", launch_pack(pk, eb, st));
+  LMLP_SIDE("pack(fwd)", launch_pack(pk, eb, st));
   float* sc_g = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_g)) : nullptr;
   float* sc_u = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_u)) : nullptr;
   float* sc_d = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_d)) : nullptr;
@@ -684,9 +725,9 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
     char* wq_g = at(workspace, FL.wq_g);
     char* wq_u = at(workspace, FL.wq_u);
     char* wq_d = at(workspace, FL.wq_d);
-    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_gate, w_gate_scales, I, H, wq_g, st));
-    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_up, w_up_scales, I, H, wq_u, st));
-    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_down, w_down_scales, H, I, wq_d, st));
+    LMLP_SIDE("dequant(W)", launch_dequant_int4(w_gate, w_gate_scales, I, H, wq_g, st));
+    LMLP_SIDE("dequant(W)", launch_dequant_int4(w_up, w_up_scales, I, H, wq_u, st));
+    LMLP_SIDE("dequant(W)", launch_dequant_int4(w_down, w_down_scales, H, I, wq_d, st));
     wg = wq_g;
     wu = wq_u;
     wd = wq_d;
@@ -697,7 +738,7 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
     sp.job[1] = {static_cast<const __half*>(w_up_scales), sc_u, I, H / 64, I};
     sp.job[2] = {static_cast<const __half*>(w_down_scales), sc_d, H, I / 64, H};
     sp.njobs = 3;
-    LMLP_LAUNCH("pack(scales)", launch_scale_pack(sp, st));
+    LMLP_SIDE("pack(scales)", launch_scale_pack(sp, st));
   }
 
   float* rpp = reinterpret_cast<float*>(at(workspace, FL.rp_part));
@@ -705,13 +746,13 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   rp.T = T;
   rp.njobs = 1;
   rp.job[0] = rp_job(d, x, H, H, agu_pad, H, int(2 * r16), rpp);
-  LMLP_LAUNCH("rowproj(X A^T)", launch_rowproj(rp, d.bf16, st));
+  LMLP_SIDE("rowproj(X A^T)", launch_rowproj(rp, d.bf16, st));
   ProjFinishParams fp{};
   fp.T = T;
   fp.njobs = 1;
   fp.job[0] = fin_job(rpp, rp.job[0].kslices, T * 2 * r16, 2 * r16, int(2 * r16), Pgu, 2 * r16, aext_gu, 2 * r16,
                       d.s, nullptr, 0, 0);
-  LMLP_LAUNCH("finish(P_gu)", launch_proj_finish(fp, d.bf16, st));
+  LMLP_SIDE("finish(P_gu)", launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gp{};
   gp.nseg = 2;
@@ -724,12 +765,12 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   gp.c1 = U;
   gp.c2 = Z;
   gp.group_m = 8;
-  LMLP_LAUNCH("gemm(gate/up)", run_gemm(gp, d, 0, EPI_SWIGLU_FWD, st));
+  LMLP_GEMM("gemm(gate/up)", gp, 0, EPI_SWIGLU_FWD);
 
   rp.job[0] = rp_job(d, Z, I, I, ad_pad, I, int(r16), rpp);
-  LMLP_LAUNCH("rowproj(Z A_d^T)", launch_rowproj(rp, d.bf16, st));
+  LMLP_SIDE("rowproj(Z A_d^T)", launch_rowproj(rp, d.bf16, st));
   fp.job[0] = fin_job(rpp, rp.job[0].kslices, T * r16, r16, int(r16), Pd, r16, aext_d, r16, d.s, nullptr, 0, 0);
-  LMLP_LAUNCH("finish(Pd)", launch_proj_finish(fp, d.bf16, st));
+  LMLP_SIDE("finish(Pd)", launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gd{};
   gd.nseg = 2;
@@ -740,7 +781,7 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   gd.ldc = H;
   gd.c0 = y;
   gd.group_m = 8;
-  LMLP_LAUNCH("gemm(down)", run_gemm(gd, d, 0, EPI_STORE, st));
+  LMLP_GEMM("gemm(down)", gd, 0, EPI_STORE);
   return LMLP_OK;
 }
 
@@ -751,7 +792,10 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
                          const void* w_down, const void* w_down_scales, const void* a_gate, const void* b_gate,
                          const void* a_up, const void* b_up, const void* a_down, const void* b_down, void* saved,
                          size_t saved_bytes, void* dx, void* da_gate, void* db_gate, void* da_up, void* db_up,
-                         void* da_down, void* db_down, void* workspace, size_t workspace_bytes, void* stream) {
+                         void* da_down, void* db_down, void* workspace, size_t workspace_bytes, void* stream,
+                         Exec* exec = nullptr) {
+  Exec local_exec;
+  Exec& ex = exec ? *exec : local_exec;
   Dims d;
   LMLP_TRY(parse_dims(dims, d));
   if (d.norm) LMLP_TRY(need_ptr(gamma, "gamma"));
@@ -792,7 +836,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     rd.job[4] = rd_job(nullptr, 0, 0, 0, 0, r, H, da_up, H, false, s, d.bf16);
     rd.job[5] = rd_job(nullptr, 0, 0, 0, 0, H, r, db_down, r, false, s, d.bf16);
     rd.njobs = 6;
-    LMLP_LAUNCH("reduce(zero)", launch_reduce(rd, st));
+    LMLP_SIDE("reduce(zero)", launch_reduce(rd, st));
     return LMLP_OK;
   }
 
@@ -806,7 +850,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     np.T = T;
     np.H = H;
     np.mode = NORM_APPLY;
-    LMLP_LAUNCH("rmsnorm(apply)", launch_rmsnorm(np, d.bf16, st));
+    LMLP_SIDE("rmsnorm(apply)", launch_rmsnorm(np, d.bf16, st));
     x = np.xn;
   }
 
@@ -850,9 +894,9 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     char* wq_g = at(workspace, BL.wq_g);
     char* wq_u = at(workspace, BL.wq_u);
     char* wq_d = at(workspace, BL.wq_d);
-    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_gate, w_gate_scales, I, H, wq_g, st));
-    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_up, w_up_scales, I, H, wq_u, st));
-    LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w_down, w_down_scales, H, I, wq_d, st));
+    LMLP_SIDE("dequant(W)", launch_dequant_int4(w_gate, w_gate_scales, I, H, wq_g, st));
+    LMLP_SIDE("dequant(W)", launch_dequant_int4(w_up, w_up_scales, I, H, wq_u, st));
+    LMLP_SIDE("dequant(W)", launch_dequant_int4(w_down, w_down_scales, H, I, wq_d, st));
     wg = wq_g;
     wu = wq_u;
     wd = wq_d;
@@ -862,7 +906,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   rp.T = T;
   rp.njobs = 1;
   rp.job[0] = rp_job(d, dy, H, H, bdT, H, int(r16), rpa);
-  LMLP_LAUNCH("rowproj(dY B_d)", launch_rowproj(rp, d.bf16, st));
+  LMLP_SIDE("rowproj(dY B_d)", launch_rowproj(rp, d.bf16, st));
   // Q_d, and (bf16) the transposed copies the column projections read
   ProjFinishParams fp{};
   fp.T = T;
@@ -875,7 +919,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   }
   if (d.recompute)  // s P_gu in the compute dtype: the gate/up product's adapter segment
     fp.job[fp.njobs++] = fin_job(Pgu, 1, 0, 2 * r16, int(2 * r16), nullptr, 0, aext_gu, 2 * r16, s, nullptr, 0, 0);
-  LMLP_LAUNCH("finish(Q_d, P^T)", launch_proj_finish(fp, d.bf16, st));
+  LMLP_SIDE("finish(Q_d, P^T)", launch_proj_finish(fp, d.bf16, st));
 
   if (d.recompute) {
     // G, U again from X: the forward's gate/up product (its adapter segment
@@ -892,7 +936,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     gp.c1 = U_rc;
     gp.c2 = nullptr;
     gp.group_m = 8;
-    LMLP_LAUNCH("gemm(gate/up, recompute)", run_gemm(gp, d, 0, EPI_SWIGLU_FWD, st));
+    LMLP_GEMM("gemm(gate/up, recompute)", gp, 0, EPI_SWIGLU_FWD);
   }
 
   GemmParams gz{};
@@ -930,7 +974,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   if (n1 > 0) {
     GemmParams g1 = gz;
     g1.N = n1;
-    LMLP_LAUNCH("gemm(dZ)", run_gemm(g1, d, 1, EPI_SWIGLU_BWD, st));
+    LMLP_GEMM("gemm(dZ)", g1, 1, EPI_SWIGLU_BWD);
   }
   if (n1 < I) {  // the tail columns in 128-wide tiles
     GemmParams g2 = gz;
@@ -951,7 +995,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
       g2.pj_cz = part_z + n1 * 16;
       g2.pj_slice0 = int(n1 / 256);
     }
-    LMLP_LAUNCH("gemm(dZ tail)", run_gemm(g2, d, 1, EPI_SWIGLU_BWD, st));
+    LMLP_GEMM("gemm(dZ tail)", g2, 1, EPI_SWIGLU_BWD);
   }
   if (fused_q(d)) q_parts = int((n1 + 255) / 256 + (I - n1 + 127) / 128);
 
@@ -959,14 +1003,14 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     rp.njobs = 2;
     rp.job[0] = rp_job(d, dG, I, I, bgT, I, int(r16), rpa);
     rp.job[1] = rp_job(d, dU, I, I, buT, I, int(r16), rpb);
-    LMLP_LAUNCH("rowproj(dG B_g, dU B_u)", launch_rowproj(rp, d.bf16, st));
+    LMLP_SIDE("rowproj(dG B_g, dU B_u)", launch_rowproj(rp, d.bf16, st));
     q_parts = rp.job[0].kslices;
   }
   fp.njobs = 2;
   fp.job[0] = fin_job(rpa, q_parts, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT, 0);
   fp.job[1] = fin_job(rpb, q_parts, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT,
                       int(r16));
-  LMLP_LAUNCH("finish(Q_gu)", launch_proj_finish(fp, d.bf16, st));
+  LMLP_SIDE("finish(Q_gu)", launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gx{};
   gx.nseg = 3;
@@ -978,7 +1022,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   gx.ldc = H;
   gx.c0 = dx;
   gx.group_m = 8;
-  LMLP_LAUNCH("gemm(dX)", run_gemm(gx, d, 1, EPI_STORE, st));
+  LMLP_GEMM("gemm(dX)", gx, 1, EPI_STORE);
 
   const int ntb = BL.ntb;
   const int64_t tr = BL.tr;
@@ -997,7 +1041,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     cp.njobs = 5;
     nsl_i = ntb;
   }
-  LMLP_LAUNCH("colproj", launch_colproj(cp, d.bf16, st));
+  LMLP_SIDE("colproj", launch_colproj(cp, d.bf16, st));
 
   rd.job[0] = rd_job(part_dg, I * r16, nsl_i, r16, 0, I, r, db_gate, r, false, s, d.bf16);
   rd.job[1] = rd_job(part_du, I * r16, nsl_i, r16, 0, I, r, db_up, r, false, s, d.bf16);
@@ -1006,13 +1050,13 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   rd.job[4] = rd_job(part_x, H * 2 * r16, ntb, 2 * r16, int(r16), H, r, da_up, H, true, s, d.bf16);
   rd.job[5] = rd_job(part_dy, H * r16, ntb, r16, 0, H, r, db_down, r, false, s, d.bf16);
   rd.njobs = 6;
-  LMLP_LAUNCH("reduce", launch_reduce(rd, st));
+  LMLP_SIDE("reduce", launch_reduce(rd, st));
   if (d.norm) {  // dx (so far the gradient of the normalised rows) through the norm, in place
     np.x = x_in;
     np.g = dx;
     np.dx = dx;
     np.mode = NORM_BWD;
-    LMLP_LAUNCH("rmsnorm(bwd)", launch_rmsnorm(np, d.bf16, st));
+    LMLP_SIDE("rmsnorm(bwd)", launch_rmsnorm(np, d.bf16, st));
   }
   return LMLP_OK;
 }
@@ -1074,27 +1118,27 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
 // ---- grouped (MoE) LoRA MLP -------------------------------------------------
 // Rows grouped by expert (host offsets); per-expert tensors stacked along a
 // leading axis. Every argument is checked for all experts before anything is
-// enqueued; then each expert with rows runs the fused MLP above on its rows
-// and its slices of the stacked tensors. One expert's GEMMs are small (a few
-// hundred to a few thousand rows: tens of tiles for 256 CUs), so the experts
-// run concurrently on kMoeStreams worker streams (default priority,
-// non-blocking, created once per device), expert e on stream e % kMoeStreams
-// with workspace slot e % kMoeStreams; the workers start after the work
-// already on the caller's stream and the caller's stream continues after all
-// of them (events). `saved` holds one region per expert, in expert order. An
-// expert without rows gets zero adapter gradients. Each expert's arithmetic
-// does not depend on the stream it runs on, so results are bitwise
-// reproducible.
+// enqueued; then each expert runs the fused MLP above on its rows and its
+// slices of the stacked tensors, in phases cut at the GEMMs (Exec): in each
+// phase every expert's side kernels run, spread over kMoeStreams worker
+// streams (default priority, non-blocking, created once per device, forked
+// from and joined back to the caller's stream with events), and then the
+// GEMMs they lead to run as one grouped launch per kind over all experts'
+// tiles on the caller's stream (a few hundred rows per expert are only tens
+// of tiles for 256 CUs). `saved` and the workspace hold one region per
+// expert, in expert order, so every expert's intermediates stay resident
+// across the phases. An expert without rows gets zero adapter gradients.
+// Each expert's arithmetic is that of the plain entry point, so results are
+// bitwise reproducible.
 
 constexpr int kMoeStreams = 4;
 
 struct MoePlan {
   std::vector<lmlp_dims> dims;  // per expert: tokens = its rows
   std::vector<int64_t> row0;
-  std::vector<size_t> soff, ssize;
-  size_t saved_total = 0, ws_fwd = 0, ws_bwd = 0;  // workspace: `slots` slots of slot_fwd / slot_bwd bytes
-  size_t slot_fwd = 0, slot_bwd = 0;
-  int slots = 1;
+  std::vector<size_t> soff, ssize;          // saved region of each expert
+  std::vector<size_t> wfoff, wfsize, wboff, wbsize;  // forward / backward workspace regions
+  size_t saved_total = 0, ws_fwd = 0, ws_bwd = 0;
   Dims d;  // the whole call
 };
 
@@ -1125,23 +1169,55 @@ static int moe_streams(MoeStreams*& out) {  // call with g_moe_mu held
   return LMLP_OK;
 }
 
-// Run body(e, worker stream, workspace slot) for the experts in `order`,
-// forked from and joined back to the caller's stream.
-static int moe_run(hipStream_t caller, const std::vector<int64_t>& order, int slots,
-                   const std::function<int(int64_t, hipStream_t, int)>& body) {
+// Run the passes body(e, exec, stream) of the experts in `order` phase by
+// phase: each phase's side kernels on the worker streams (expert k of the
+// order on stream k % kMoeStreams), then the GEMMs handed back, grouped by
+// kind, on the caller's stream; until no expert hands back a GEMM.
+static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order,
+                      const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
   std::lock_guard<std::mutex> lock(g_moe_mu);
   MoeStreams* ms = nullptr;
   LMLP_TRY(moe_streams(ms));
-  const int nw = std::min<int>(slots, kMoeStreams);
-  LMLP_TRY(hip_rc(hipEventRecord(ms->fork, caller), "hipEventRecord"));
-  for (int i = 0; i < nw; ++i) LMLP_TRY(hip_rc(hipStreamWaitEvent(ms->s[i], ms->fork, 0), "hipStreamWaitEvent"));
-  for (size_t k = 0; k < order.size(); ++k) {
-    const int w = int(k % size_t(nw));
-    LMLP_TRY(body(order[k], ms->s[w], w));
-  }
-  for (int i = 0; i < nw; ++i) {
-    LMLP_TRY(hip_rc(hipEventRecord(ms->join[i], ms->s[i]), "hipEventRecord"));
-    LMLP_TRY(hip_rc(hipStreamWaitEvent(caller, ms->join[i], 0), "hipStreamWaitEvent"));
+  const int nw = int(std::min<size_t>(order.size(), kMoeStreams));
+  std::vector<Exec> ex(order.size());
+  for (int phase = 0;; ++phase) {
+    LMLP_TRY(hip_rc(hipEventRecord(ms->fork, caller), "hipEventRecord"));
+    for (int i = 0; i < nw; ++i) LMLP_TRY(hip_rc(hipStreamWaitEvent(ms->s[i], ms->fork, 0), "hipStreamWaitEvent"));
+    for (size_t k = 0; k < order.size(); ++k) {
+      ex[k] = Exec{};
+      ex[k].phase = phase;
+      LMLP_TRY(body(order[k], &ex[k], ms->s[k % size_t(nw)]));
+    }
+    for (int i = 0; i < nw; ++i) {
+      LMLP_TRY(hip_rc(hipEventRecord(ms->join[i], ms->s[i]), "hipEventRecord"));
+      LMLP_TRY(hip_rc(hipStreamWaitEvent(caller, ms->join[i], 0), "hipStreamWaitEvent"));
+    }
+    // the GEMMs of this phase: dense bf16 ones grouped by kind, the rest one by one
+    bool any = false;
+    std::vector<bool> done(order.size(), false);
+    hipStream_t st = caller;
+    for (size_t k = 0; k < order.size(); ++k) {
+      if (!ex[k].sunk || done[k]) continue;
+      any = true;
+      if (!ex[k].groupable) {
+        LMLP_LAUNCH(ex[k].name, ex[k].gp.seg[0].bint4 ? launch_gemm_q4(ex[k].gp, ex[k].epi, st)
+                                                      : launch_gemm_f32(ex[k].gp, ex[k].nn, ex[k].epi, st));
+        done[k] = true;
+        continue;
+      }
+      std::vector<GemmParams> grp;
+      for (size_t j = k; j < order.size(); ++j) {
+        const Exec& a = ex[k];
+        const Exec& b = ex[j];
+        if (done[j] || !b.sunk || !b.groupable || std::strcmp(a.name, b.name) != 0 || a.nn != b.nn ||
+            a.epi != b.epi || a.gp.tile_n != b.gp.tile_n || (a.gp.pj_part0 == nullptr) != (b.gp.pj_part0 == nullptr))
+          continue;
+        grp.push_back(b.gp);
+        done[j] = true;
+      }
+      LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped(grp.data(), int(grp.size()), ex[k].nn, ex[k].epi, st));
+    }
+    if (!any) break;
   }
   return LMLP_OK;
 }
@@ -1156,6 +1232,10 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
   P.row0.resize(E);
   P.soff.resize(E);
   P.ssize.resize(E);
+  P.wfoff.resize(E);
+  P.wfsize.resize(E);
+  P.wboff.resize(E);
+  P.wbsize.resize(E);
   for (int64_t e = 0; e < E; ++e) {
     if (off[e + 1] < off[e]) return fail(LMLP_ERR_INVALID_ARG, "offsets must not decrease");
     lmlp_dims de = *dims;
@@ -1167,12 +1247,15 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
     P.soff[e] = P.saved_total;
     P.ssize[e] = saved_layout(dd).total;
     P.saved_total += P.ssize[e];
-    P.slot_fwd = std::max(P.slot_fwd, fwd_layout(dd).total);
-    P.slot_bwd = std::max(P.slot_bwd, bwd_layout(dd).total);
+    P.wfoff[e] = P.ws_fwd;
+    P.wfsize[e] = dd.T > 0 ? fwd_layout(dd).total : 0;  // no forward work without rows
+    P.ws_fwd += P.wfsize[e];
+    // an expert without rows only writes zero gradients: it gets no region
+    // (its pass is handed the size it checks, and no pointer)
+    P.wboff[e] = P.ws_bwd;
+    P.wbsize[e] = bwd_layout(dd).total;
+    P.ws_bwd += dd.T > 0 ? P.wbsize[e] : 0;
   }
-  P.slots = int(std::min<int64_t>(E, kMoeStreams));
-  P.ws_fwd = P.slot_fwd * P.slots;
-  P.ws_bwd = P.slot_bwd * P.slots;
   return LMLP_OK;
 }
 
@@ -1242,13 +1325,13 @@ int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* of
   for (int64_t e = 0; e < n_experts; ++e)
     if (P.dims[e].tokens > 0) order.push_back(e);
   if (order.empty()) return LMLP_OK;
-  return moe_run(static_cast<hipStream_t>(stream), order, P.slots, [&](int64_t e, hipStream_t ws, int slot) {
+  return moe_phased(static_cast<hipStream_t>(stream), order, [&](int64_t e, Exec* ex, hipStream_t ws) {
     return forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
                         slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu), slice(w_up_scales, e, S.wgu_s),
                         slice(w_down, e, S.wd), slice(w_down_scales, e, S.wd_s), slice(a_gate, e, S.agu),
                         slice(b_gate, e, S.bgu), slice(a_up, e, S.agu), slice(b_up, e, S.bgu), slice(a_down, e, S.ad),
                         slice(b_down, e, S.bd), slice(y, P.row0[e], S.rows), at(saved, P.soff[e]), P.ssize[e],
-                        at(workspace, size_t(slot) * P.slot_fwd), P.slot_fwd, ws);
+                        at(workspace, P.wfoff[e]), P.wfsize[e], ws, ex);
   });
 }
 
@@ -1285,7 +1368,7 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
   const MoeStrides S = moe_strides(d);
   std::vector<int64_t> order(n_experts);  // every expert: one without rows gets zero gradients
   for (int64_t e = 0; e < n_experts; ++e) order[e] = e;
-  return moe_run(static_cast<hipStream_t>(stream), order, P.slots, [&](int64_t e, hipStream_t ws, int slot) {
+  return moe_phased(static_cast<hipStream_t>(stream), order, [&](int64_t e, Exec* ex, hipStream_t ws) {
     const bool any = P.dims[e].tokens > 0;
     return backward_impl(
         &P.dims[e], nullptr, any ? slice(dy, P.row0[e], S.rows) : nullptr, any ? slice(x, P.row0[e], S.rows) : nullptr,
@@ -1295,7 +1378,7 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
         slice(a_down, e, S.ad), slice(b_down, e, S.bd), any ? at(saved, P.soff[e]) : nullptr, P.ssize[e],
         any ? slice(dx, P.row0[e], S.rows) : nullptr, slice(da_gate, e, S.agu), slice(db_gate, e, S.bgu),
         slice(da_up, e, S.agu), slice(db_up, e, S.bgu), slice(da_down, e, S.ad), slice(db_down, e, S.bd),
-        any ? at(workspace, size_t(slot) * P.slot_bwd) : nullptr, P.slot_bwd, ws);
+        any ? at(workspace, P.wboff[e]) : nullptr, P.wbsize[e], ws, ex);
   });
 }
 

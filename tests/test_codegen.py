@@ -74,11 +74,12 @@ def test_wide_tile_k_loops_keep_accumulators_in_place(gemm_asm):
         nmfma, seg = loop
         # 256-wide tiles: 8 x 8 MFMAs per wave and k-tile, two k-tiles per
         # iteration; the 4-bit kernels: one k-tile per iteration
-        if nmfma not in (64, 128) or ("gemm_bf16_kernel" in name and nmfma != 128):
+        if nmfma not in (64, 128) or ("gemm_bf16" in name and nmfma != 128):
             continue
         ops = collections.Counter(i.split()[0] for i in seg)
         bad = {o: c for o, c in ops.items() if o.startswith(MOVES)}
         assert not bad, f"{name}: {bad}"
         checked += 1
-    # plain NT, gate/up, plain NN, dZ (both epilogues) and the two 4-bit kernels
-    assert checked >= 7, checked
+    # plain NT, gate/up, plain NN, dZ (both epilogues) and the two 4-bit
+    # kernels, and the grouped forms of the five 256-wide bf16 kernels
+    assert checked >= 12, checked
