@@ -1138,9 +1138,13 @@ hipError_t launch_gemm_q4(const GemmParams& p, int epi, hipStream_t stream) {
 }
 
 hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t stream) {
-  if (!nn && epi == EPI_STORE) return launch_t<false, EPI_STORE>(p, stream);
+  if (epi == EPI_STORE && p.tile_n != 0 && p.tile_n != 128 && p.tile_n != 256) return hipErrorInvalidValue;
+  const bool narrow_store = epi == EPI_STORE && p.tile_n == 128;  // 256 x 128 tiles for narrow products
+  if (!nn && epi == EPI_STORE)
+    return narrow_store ? launch_t<false, EPI_STORE, 0, 4>(p, stream) : launch_t<false, EPI_STORE>(p, stream);
   if (!nn && epi == EPI_SWIGLU_FWD) return launch_t<false, EPI_SWIGLU_FWD>(p, stream);
-  if (nn && epi == EPI_STORE) return launch_t<true, EPI_STORE>(p, stream);
+  if (nn && epi == EPI_STORE)
+    return narrow_store ? launch_t<true, EPI_STORE, 0, 4>(p, stream) : launch_t<true, EPI_STORE>(p, stream);
   if (nn && epi == EPI_SWIGLU_BWD) {
     const bool narrow = p.tile_n == 128;
     if (p.tile_n != 0 && p.tile_n != 128 && p.tile_n != 256) return hipErrorInvalidValue;

@@ -60,8 +60,8 @@ struct GemmParams {
   float* pj_cz;
   int64_t pj_ncol;    // row stride (columns) of the column-product partials
   int32_t pj_slice0;  // first row-product slice of this launch
-  // SWIGLU_BWD: tile width, 256 (0 = default) or 128 (row-product slices are
-  // then per 128 columns)
+  // STORE and SWIGLU_BWD: tile width, 256 (0 = default) or 128 (SWIGLU_BWD:
+  // row-product slices are then per 128 columns)
   int32_t tile_n;
 };
 

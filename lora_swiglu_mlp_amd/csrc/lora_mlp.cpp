@@ -200,6 +200,15 @@ int device_cus() {
   return n;
 }
 
+// Tile width of a bf16 product with the plain store epilogue: 256 x 128 tiles
+// when 256 x 256 ones would not fill one wave of the device (narrow outputs,
+// few tokens), else the default 256 x 256.
+int store_tile_n(const Dims& d, int64_t M, int64_t N) {
+  if (!d.bf16) return 0;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return tiles < device_cus() ? 128 : 0;
+}
+
 // Columns of the dZ GEMM (bf16) covered by 256-wide tiles; the rest, when the
 // last wave of workgroups would be at most half full, goes to a second launch
 // of 128-wide tiles that fill one wave with twice as many half-size tiles.
@@ -781,6 +790,7 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   gd.ldc = H;
   gd.c0 = y;
   gd.group_m = 8;
+  if (ex.phase < 0) gd.tile_n = store_tile_n(d, T, H);  // grouped launches keep one tile shape
   LMLP_GEMM("gemm(down)", gd, 0, EPI_STORE);
   return LMLP_OK;
 }
@@ -1022,6 +1032,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   gx.ldc = H;
   gx.c0 = dx;
   gx.group_m = 8;
+  if (ex.phase < 0) gx.tile_n = store_tile_n(d, T, H);
   LMLP_GEMM("gemm(dX)", gx, 1, EPI_STORE);
 
   const int ntb = BL.ntb;
@@ -1477,6 +1488,7 @@ int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, con
   gy.ldc = Out;
   gy.c0 = y;
   gy.group_m = 8;
+  gy.tile_n = store_tile_n(d, T, Out);
   LMLP_LAUNCH("gemm(y)", run_gemm(gy, d, 0, EPI_STORE, st));
   return LMLP_OK;
 }
@@ -1557,6 +1569,7 @@ int lora_linear_backward(const lmlp_dims* dims, const void* dy, const void* x, c
   gx.ldc = In;
   gx.c0 = dx;
   gx.group_m = 8;
+  gx.tile_n = store_tile_n(d, T, In);
   LMLP_LAUNCH("gemm(dX)", run_gemm(gx, d, 1, EPI_STORE, st));
 
   const int ntb = BL.ntb;
