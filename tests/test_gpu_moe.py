@@ -107,3 +107,16 @@ def test_moe_fullsize_parity(name):
     ref = _oracle(inp, off, wl)
     print(f"[time] inputs+gpu {t1 - t0:.1f}s oracle {time.time() - t1:.1f}s", flush=True)
     compare(got, ref, TOL[wl.dtype], name)
+
+
+def test_moe_int4_inkernel_mode_bitwise_equal():
+    """4-bit weights decoded inside the forward products' staging (those
+    products are launched expert by expert, not grouped) give the outputs of
+    the decoded-copy mode bit for bit; that mode is checked against the
+    oracle above."""
+    wl = workload("int4_routed")
+    inp, off = I.make_moe_inputs(wl)
+    a, _ = run_hip_moe(inp, off, wl)
+    b, _ = run_hip_moe(inp, off, wl, flags=abi.LMLP_INT4_INKERNEL)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
