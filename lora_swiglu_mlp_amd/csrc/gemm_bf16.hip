@@ -1083,6 +1083,46 @@ static hipError_t launch_t(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Groups whose parameter blocks sit in device memory (more groups than the
+// kernel arguments hold): the same workgroup -> (group, tile) map, with the
+// group starts in the arguments.
+struct GroupStarts {
+  int32_t start[kMaxTableGroups + 1];
+  int32_t n;
+};
+
+template <bool NN, int EPI, int QRB, int NB>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_table_kernel(const GemmParams* __restrict__ table,
+                                                                     GroupStarts gs) {
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  const int bid = blockIdx.x;
+  int lo = 0, hi = gs.n - 1;  // the last group whose start is <= bid
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gs.start[mid] <= bid) lo = mid;
+    else hi = mid - 1;
+  }
+  const GemmParams& p = table[lo];
+  const int local = bid - gs.start[lo];
+  const int tiles = p.tiles_m * p.tiles_n;
+  if (local >= tiles) return;
+  gemm_bf16_body<NN, EPI, QRB, NB>(p, local, tiles, smem);
+}
+
+// copy of up to kMaxGemmGroups parameter blocks into a device table
+struct TableChunk {
+  GemmParams p[kMaxGemmGroups];
+  GemmParams* dst;
+  int32_t n;
+};
+__global__ __launch_bounds__(256) void write_table_kernel(TableChunk c) {
+  constexpr int W = sizeof(GemmParams) / 4;
+  static_assert(sizeof(GemmParams) % 4 == 0, "word copy");
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(c.p);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(c.dst);
+  for (int i = threadIdx.x; i < c.n * W; i += blockDim.x) dst[i] = src[i];
+}
+
 // tile counts and band height of one product, as launch_t sets them
 template <int EPI, int NB>
 static void set_tiles(GemmParams& p) {
@@ -1112,6 +1152,38 @@ static hipError_t launch_grouped_t(const GemmParams* ps, int n, hipStream_t stre
     gg.start[gg.n] = nblk;
     if (gg.n == 0) continue;
     hipLaunchKernelGGL((gemm_bf16_grouped_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream, gg);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <bool NN, int EPI, int QRB = 0, int NB = 8>
+static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table, hipStream_t stream) {
+  for (int i0 = 0; i0 < n; i0 += kMaxTableGroups) {
+    const int cnt = n - i0 < kMaxTableGroups ? n - i0 : kMaxTableGroups;
+    GroupStarts gs{};
+    int nblk = 0;
+    TableChunk tc{};
+    for (int i = 0; i < cnt; ++i) {
+      GemmParams q = ps[i0 + i];
+      set_tiles<EPI, NB>(q);
+      gs.start[i] = nblk;
+      nblk += (q.tiles_m * q.tiles_n + 7) / 8 * 8;
+      tc.p[tc.n++] = q;
+      if (tc.n == kMaxGemmGroups || i == cnt - 1) {  // blocks i - n + 1 .. i of this launch
+        tc.dst = table + (i + 1 - tc.n);
+        hipLaunchKernelGGL(write_table_kernel, dim3(1), dim3(256), 0, stream, tc);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        tc.n = 0;
+      }
+    }
+    gs.start[cnt] = nblk;
+    gs.n = cnt;
+    if (nblk == 0) continue;
+    hipLaunchKernelGGL((gemm_bf16_table_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream,
+                       static_cast<const GemmParams*>(table), gs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1172,6 +1244,27 @@ hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi
     if (p.pj_r16 == 16)
       return narrow ? launch_grouped_t<true, EPI_SWIGLU_BWD, 1, 4>(ps, n, stream)
                     : launch_grouped_t<true, EPI_SWIGLU_BWD, 1, 8>(ps, n, stream);
+    return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_bf16_grouped_table(const GemmParams* ps, int n, int nn, int epi, GemmParams* table,
+                                          hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const GemmParams& p = ps[0];
+  if (!nn && epi == EPI_STORE) return launch_table_t<false, EPI_STORE>(ps, n, table, stream);
+  if (!nn && epi == EPI_SWIGLU_FWD) return launch_table_t<false, EPI_SWIGLU_FWD>(ps, n, table, stream);
+  if (nn && epi == EPI_STORE) return launch_table_t<true, EPI_STORE>(ps, n, table, stream);
+  if (nn && epi == EPI_SWIGLU_BWD) {
+    const bool narrow = p.tile_n == 128;
+    if (p.tile_n != 0 && p.tile_n != 128 && p.tile_n != 256) return hipErrorInvalidValue;
+    if (p.pj_part0 == nullptr)
+      return narrow ? launch_table_t<true, EPI_SWIGLU_BWD, 0, 4>(ps, n, table, stream)
+                    : launch_table_t<true, EPI_SWIGLU_BWD, 0, 8>(ps, n, table, stream);
+    if (p.pj_r16 == 16)
+      return narrow ? launch_table_t<true, EPI_SWIGLU_BWD, 1, 4>(ps, n, table, stream)
+                    : launch_table_t<true, EPI_SWIGLU_BWD, 1, 8>(ps, n, table, stream);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

@@ -81,6 +81,13 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t st
 // The same products, n of them of one kind (grouped MLP experts), in
 // launches of up to kMaxGemmGroups products each.
 hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi, hipStream_t stream);
+// The same with the parameter blocks in device memory: `table` (device, at
+// least n * sizeof(GemmParams) bytes, 16-byte aligned) receives the n blocks
+// through small copy kernels on `stream`, and one launch per
+// kMaxTableGroups products reads them there.
+constexpr int kMaxTableGroups = 512;
+hipError_t launch_gemm_bf16_grouped_table(const GemmParams* ps, int n, int nn, int epi, GemmParams* table,
+                                          hipStream_t stream);
 // NT products whose segment-0 B operand is 4-bit: seg[0].b0/b1 hold the codes
 // ([N][K/2] bytes, seg[0].ldb = K codes per row), seg[0].bs0/bs1 the block
 // scales as fp32 [K/64][N]; K and N multiples of 64. Segment 1 (the

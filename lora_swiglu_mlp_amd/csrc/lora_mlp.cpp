@@ -1150,6 +1150,8 @@ struct MoePlan {
   std::vector<size_t> soff, ssize;          // saved region of each expert
   std::vector<size_t> wfoff, wfsize, wboff, wbsize;  // forward / backward workspace regions
   size_t saved_total = 0, ws_fwd = 0, ws_bwd = 0;
+  size_t tab_fwd = 0, tab_bwd = 0;  // GEMM parameter tables (more experts than one launch's arguments hold)
+  bool table = false;
   Dims d;  // the whole call
 };
 
@@ -1184,7 +1186,7 @@ static int moe_streams(MoeStreams*& out) {  // call with g_moe_mu held
 // phase: each phase's side kernels on the worker streams (expert k of the
 // order on stream k % kMoeStreams), then the GEMMs handed back, grouped by
 // kind, on the caller's stream; until no expert hands back a GEMM.
-static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order,
+static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, GemmParams* table,
                       const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
   std::lock_guard<std::mutex> lock(g_moe_mu);
   MoeStreams* ms = nullptr;
@@ -1226,7 +1228,11 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order,
         grp.push_back(b.gp);
         done[j] = true;
       }
-      LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped(grp.data(), int(grp.size()), ex[k].nn, ex[k].epi, st));
+      if (table && grp.size() > size_t(kMaxGemmGroups))  // parameter blocks through a device table
+        LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped_table(grp.data(), int(grp.size()), ex[k].nn, ex[k].epi,
+                                                               table, st));
+      else
+        LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped(grp.data(), int(grp.size()), ex[k].nn, ex[k].epi, st));
     }
     if (!any) break;
   }
@@ -1266,6 +1272,14 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
     P.wboff[e] = P.ws_bwd;
     P.wbsize[e] = bwd_layout(dd).total;
     P.ws_bwd += dd.T > 0 ? P.wbsize[e] : 0;
+  }
+  P.table = E > kMaxGemmGroups;
+  if (P.table) {
+    const size_t tb = align_up(size_t(E) * sizeof(GemmParams));
+    P.tab_fwd = P.ws_fwd;
+    P.ws_fwd += tb;
+    P.tab_bwd = P.ws_bwd;
+    P.ws_bwd += tb;
   }
   return LMLP_OK;
 }
@@ -1336,7 +1350,8 @@ int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* of
   for (int64_t e = 0; e < n_experts; ++e)
     if (P.dims[e].tokens > 0) order.push_back(e);
   if (order.empty()) return LMLP_OK;
-  return moe_phased(static_cast<hipStream_t>(stream), order, [&](int64_t e, Exec* ex, hipStream_t ws) {
+  GemmParams* tab = P.table ? reinterpret_cast<GemmParams*>(at(workspace, P.tab_fwd)) : nullptr;
+  return moe_phased(static_cast<hipStream_t>(stream), order, tab, [&](int64_t e, Exec* ex, hipStream_t ws) {
     return forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
                         slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu), slice(w_up_scales, e, S.wgu_s),
                         slice(w_down, e, S.wd), slice(w_down_scales, e, S.wd_s), slice(a_gate, e, S.agu),
@@ -1379,7 +1394,8 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
   const MoeStrides S = moe_strides(d);
   std::vector<int64_t> order(n_experts);  // every expert: one without rows gets zero gradients
   for (int64_t e = 0; e < n_experts; ++e) order[e] = e;
-  return moe_phased(static_cast<hipStream_t>(stream), order, [&](int64_t e, Exec* ex, hipStream_t ws) {
+  GemmParams* tab = P.table ? reinterpret_cast<GemmParams*>(at(workspace, P.tab_bwd)) : nullptr;
+  return moe_phased(static_cast<hipStream_t>(stream), order, tab, [&](int64_t e, Exec* ex, hipStream_t ws) {
     const bool any = P.dims[e].tokens > 0;
     return backward_impl(
         &P.dims[e], nullptr, any ? slice(dy, P.row0[e], S.rows) : nullptr, any ? slice(x, P.row0[e], S.rows) : nullptr,

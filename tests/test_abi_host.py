@@ -258,7 +258,8 @@ def _moe_forward_raw(d, offsets, saved_bytes=1 << 40, workspace_bytes=1 << 40):
         FAKE, FAKE, saved_bytes, FAKE, workspace_bytes, None)
 
 
-@pytest.mark.parametrize("counts,dt", [((3, 0, 5, 1), "bf16"), ((4096, 2048, 2048, 0), "bf16"), ((7, 9), "f32")])
+@pytest.mark.parametrize("counts,dt", [((3, 0, 5, 1), "bf16"), ((4096, 2048, 2048, 0), "bf16"), ((7, 9), "f32"),
+                                       (tuple(range(10)), "bf16")])
 def test_moe_sizes(counts, dt):
     T = sum(counts)
     off = [0] + list(np.cumsum(counts))
@@ -268,9 +269,12 @@ def test_moe_sizes(counts, dt):
     # needs no workspace): every expert's intermediates stay resident across
     # the phases of the grouped launches
     assert abi.lora_moe_saved_bytes(d, off) == sum(abi.lora_mlp_saved_bytes(p) for p in per)
+    # more experts than one launch's arguments hold (8): a table of the 416-byte
+    # GEMM parameter blocks follows
+    table = align(len(counts) * 416) if len(counts) > 8 else 0
     for bwd in (False, True):
-        assert abi.lora_moe_workspace_bytes(d, off, bwd) == sum(abi.lora_mlp_workspace_bytes(p, bwd)
-                                                                for c, p in zip(counts, per) if c > 0)
+        assert abi.lora_moe_workspace_bytes(d, off, bwd) == table + sum(abi.lora_mlp_workspace_bytes(p, bwd)
+                                                                        for c, p in zip(counts, per) if c > 0)
 
 
 def test_moe_argument_checks():
