@@ -192,12 +192,10 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
  * with no rows gets zero adapter gradients. Ownership, determinism and
  * errors as for the MLP: every argument is checked for every expert before
  * anything is enqueued. Each GEMM of the pass runs as one grouped launch
- * over every expert's tiles; the experts' small side kernels run on up to
- * four worker streams of the library's own (created on first use per device,
- * default priority), forked from `stream` after the work already on it and
- * joined back into it, so `stream` orders the call as usual. `saved` and the
- * workspace hold one region per expert (none in the workspace for an expert
- * without rows). */
+ * over every expert's tiles, and each of its small side kernels as launches
+ * merged across experts; all on `stream`. `saved` and the workspace hold one
+ * region per expert (none in the workspace for an expert without rows), and
+ * the workspace a table of GEMM parameters beyond 8 experts. */
 size_t lora_moe_saved_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets);
 size_t lora_moe_workspace_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets,
                                 int is_backward);

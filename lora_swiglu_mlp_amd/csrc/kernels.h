@@ -105,9 +105,11 @@ struct RowProjJob {
   int64_t kb;       // elements per slice, a multiple of four MFMA k-steps
   int32_t n1p;      // multiple of 16
   int32_t kslices;
+  int64_t T;        // token rows of this job (0: the launch's T)
 };
+// job capacities: kernel arguments stay under 4 KB
 struct RowProjParams {
-  RowProjJob job[2];
+  RowProjJob job[32];
   int32_t njobs;
   int32_t nsl;      // set by the launcher: 64-column slices of the widest job
   int64_t T;
@@ -133,9 +135,10 @@ struct ProjFinishJob {
   int32_t nparts;
   int32_t n1p;          // multiple of 4
   int32_t col_off;
+  int64_t T;            // token rows of this job (0: the launch's T)
 };
 struct ProjFinishParams {
-  ProjFinishJob job[4];
+  ProjFinishJob job[24];
   int32_t njobs;
   int32_t pad_;
   int64_t T;
@@ -157,9 +160,10 @@ struct ColProjJob {
   int32_t ntb;      // token blocks
   int32_t kblocks;  // feature blocks (256 bf16, 64 fp32)
   int32_t nchunks;  // column chunks (128 bf16, 64 fp32)
+  int64_t T;        // tokens of this job (0: the launch's T)
 };
 struct ColProjParams {
-  ColProjJob job[5];
+  ColProjJob job[24];
   int32_t njobs;
   int32_t pad_;
   int64_t T;
@@ -180,7 +184,7 @@ struct ReduceJob {
   int32_t pad_;
 };
 struct ReduceParams {
-  ReduceJob job[6];
+  ReduceJob job[32];
   int32_t njobs;
   int32_t pad_;
 };
@@ -198,7 +202,7 @@ struct PackJob {
   int32_t pad_;
 };
 struct PackParams {
-  PackJob job[12];
+  PackJob job[40];
   int32_t njobs;
   int32_t pad_;
 };

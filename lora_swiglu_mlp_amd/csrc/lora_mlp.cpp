@@ -34,9 +34,8 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
-#include <map>
-#include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "kernels.h"
@@ -486,8 +485,100 @@ struct Exec {
   GemmParams gp{};
   int nn = 0, epi = 0;
   bool groupable = false;  // a dense bf16 product (the grouped launcher takes it)
+  std::vector<struct SideOp>* rec = nullptr;  // record the batchable side kernels here instead of launching
   bool side() const { return phase < 0 || seg == phase; }
 };
+
+// A recorded side-kernel launch of a grouped pass: its kind, flag (element
+// bytes for pack, bf16 for the others) and jobs (each with its own token
+// count), to be launched merged with the same launch of the other experts.
+enum SideKind { SK_PACK = 0, SK_ROWPROJ, SK_FINISH, SK_COLPROJ, SK_REDUCE };
+struct SideOp {
+  const char* name;
+  int kind, flag;
+  std::vector<char> jobs;  // njobs jobs of the kind's job type
+  int njobs;
+};
+template <typename J>
+SideOp side_op_of(const char* name, int kind, int flag, const J* jobs, int n, int64_t T) {
+  SideOp o{name, kind, flag, {}, n};
+  std::vector<J> js(jobs, jobs + n);
+  if constexpr (!std::is_same<J, PackJob>::value && !std::is_same<J, ReduceJob>::value)
+    for (J& j : js)
+      if (j.T == 0) j.T = T;
+  (void)T;
+  o.jobs.assign(reinterpret_cast<const char*>(js.data()), reinterpret_cast<const char*>(js.data() + n));
+  return o;
+}
+SideOp side_op(const char* n, int kind, const PackParams& p, int flag) {
+  return side_op_of(n, kind, flag, p.job, p.njobs, 0);
+}
+SideOp side_op(const char* n, int kind, const RowProjParams& p, int flag) {
+  return side_op_of(n, kind, flag, p.job, p.njobs, p.T);
+}
+SideOp side_op(const char* n, int kind, const ProjFinishParams& p, int flag) {
+  return side_op_of(n, kind, flag, p.job, p.njobs, p.T);
+}
+SideOp side_op(const char* n, int kind, const ColProjParams& p, int flag) {
+  return side_op_of(n, kind, flag, p.job, p.njobs, p.T);
+}
+SideOp side_op(const char* n, int kind, const ReduceParams& p, int flag) {
+  return side_op_of(n, kind, flag, p.job, p.njobs, 0);
+}
+
+// One kind's recorded jobs, merged into launches of up to the job capacity.
+template <typename P, typename L>
+hipError_t launch_jobs(const std::vector<const SideOp*>& ops, bool has_t, L launch) {
+  using J = typename std::remove_reference<decltype(P{}.job[0])>::type;
+  constexpr int cap = int(sizeof(P{}.job) / sizeof(J));
+  P q{};
+  auto flush = [&]() -> hipError_t {
+    if (q.njobs == 0) return hipSuccess;
+    const hipError_t e = launch(q);
+    q = P{};
+    return e;
+  };
+  for (const SideOp* o : ops) {
+    const J* js = reinterpret_cast<const J*>(o->jobs.data());
+    for (int i = 0; i < o->njobs; ++i) {
+      q.job[q.njobs++] = js[i];
+      if constexpr (!std::is_same<J, PackJob>::value && !std::is_same<J, ReduceJob>::value)
+        if (has_t && js[i].T > q.T) q.T = js[i].T;
+      if (q.njobs == cap) {
+        const hipError_t e = flush();
+        if (e != hipSuccess) return e;
+      }
+    }
+  }
+  return flush();
+}
+
+hipError_t launch_side_group(const std::vector<const SideOp*>& ops, hipStream_t st) {
+  const int kind = ops[0]->kind, flag = ops[0]->flag;
+  switch (kind) {
+    case SK_PACK:
+      return launch_jobs<PackParams>(ops, false, [&](const PackParams& q) { return launch_pack(q, flag, st); });
+    case SK_ROWPROJ:
+      return launch_jobs<RowProjParams>(ops, true, [&](const RowProjParams& q) { return launch_rowproj(q, flag, st); });
+    case SK_FINISH:
+      return launch_jobs<ProjFinishParams>(ops, true,
+                                           [&](const ProjFinishParams& q) { return launch_proj_finish(q, flag, st); });
+    case SK_COLPROJ:
+      return launch_jobs<ColProjParams>(ops, true, [&](const ColProjParams& q) { return launch_colproj(q, flag, st); });
+    case SK_REDUCE:
+      return launch_jobs<ReduceParams>(ops, false, [&](const ReduceParams& q) { return launch_reduce(q, st); });
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+#define LMLP_SIDE_REC(name, kind, params, flag, launch_expr)                   \
+  do {                                                                          \
+    if (ex.side()) {                                                            \
+      if (ex.rec) ex.rec->push_back(side_op(name, kind, params, flag));         \
+      else LMLP_LAUNCH(name, launch_expr);                                      \
+    }                                                                           \
+  } while (0)
 
 #define LMLP_SIDE(name, expr)                  \
   do {                                         \
@@ -723,7 +814,7 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   pk.job[8] = pack_job(at(saved, SL.bgT), I, r16, I, b_gate, r, I, r, true);  // B_g^T
   pk.job[9] = pack_job(at(saved, SL.buT), I, r16, I, b_up, r, I, r, true);    // B_u^T
   pk.njobs = 10;
-  LMLP_SIDE("pack(fwd)", launch_pack(pk, eb, st));
+  LMLP_SIDE_REC("pack(fwd)", SK_PACK, pk, eb, launch_pack(pk, eb, st));
   float* sc_g = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_g)) : nullptr;
   float* sc_u = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_u)) : nullptr;
   float* sc_d = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, FL.sc_d)) : nullptr;
@@ -755,13 +846,13 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   rp.T = T;
   rp.njobs = 1;
   rp.job[0] = rp_job(d, x, H, H, agu_pad, H, int(2 * r16), rpp);
-  LMLP_SIDE("rowproj(X A^T)", launch_rowproj(rp, d.bf16, st));
+  LMLP_SIDE_REC("rowproj(X A^T)", SK_ROWPROJ, rp, d.bf16, launch_rowproj(rp, d.bf16, st));
   ProjFinishParams fp{};
   fp.T = T;
   fp.njobs = 1;
   fp.job[0] = fin_job(rpp, rp.job[0].kslices, T * 2 * r16, 2 * r16, int(2 * r16), Pgu, 2 * r16, aext_gu, 2 * r16,
                       d.s, nullptr, 0, 0);
-  LMLP_SIDE("finish(P_gu)", launch_proj_finish(fp, d.bf16, st));
+  LMLP_SIDE_REC("finish(P_gu)", SK_FINISH, fp, d.bf16, launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gp{};
   gp.nseg = 2;
@@ -777,9 +868,9 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   LMLP_GEMM("gemm(gate/up)", gp, 0, EPI_SWIGLU_FWD);
 
   rp.job[0] = rp_job(d, Z, I, I, ad_pad, I, int(r16), rpp);
-  LMLP_SIDE("rowproj(Z A_d^T)", launch_rowproj(rp, d.bf16, st));
+  LMLP_SIDE_REC("rowproj(Z A_d^T)", SK_ROWPROJ, rp, d.bf16, launch_rowproj(rp, d.bf16, st));
   fp.job[0] = fin_job(rpp, rp.job[0].kslices, T * r16, r16, int(r16), Pd, r16, aext_d, r16, d.s, nullptr, 0, 0);
-  LMLP_SIDE("finish(Pd)", launch_proj_finish(fp, d.bf16, st));
+  LMLP_SIDE_REC("finish(Pd)", SK_FINISH, fp, d.bf16, launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gd{};
   gd.nseg = 2;
@@ -846,7 +937,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     rd.job[4] = rd_job(nullptr, 0, 0, 0, 0, r, H, da_up, H, false, s, d.bf16);
     rd.job[5] = rd_job(nullptr, 0, 0, 0, 0, H, r, db_down, r, false, s, d.bf16);
     rd.njobs = 6;
-    LMLP_SIDE("reduce(zero)", launch_reduce(rd, st));
+    LMLP_SIDE_REC("reduce(zero)", SK_REDUCE, rd, 0, launch_reduce(rd, st));
     return LMLP_OK;
   }
 
@@ -916,7 +1007,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   rp.T = T;
   rp.njobs = 1;
   rp.job[0] = rp_job(d, dy, H, H, bdT, H, int(r16), rpa);
-  LMLP_SIDE("rowproj(dY B_d)", launch_rowproj(rp, d.bf16, st));
+  LMLP_SIDE_REC("rowproj(dY B_d)", SK_ROWPROJ, rp, d.bf16, launch_rowproj(rp, d.bf16, st));
   // Q_d, and (bf16) the transposed copies the column projections read
   ProjFinishParams fp{};
   fp.T = T;
@@ -929,7 +1020,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   }
   if (d.recompute)  // s P_gu in the compute dtype: the gate/up product's adapter segment
     fp.job[fp.njobs++] = fin_job(Pgu, 1, 0, 2 * r16, int(2 * r16), nullptr, 0, aext_gu, 2 * r16, s, nullptr, 0, 0);
-  LMLP_SIDE("finish(Q_d, P^T)", launch_proj_finish(fp, d.bf16, st));
+  LMLP_SIDE_REC("finish(Q_d, P^T)", SK_FINISH, fp, d.bf16, launch_proj_finish(fp, d.bf16, st));
 
   if (d.recompute) {
     // G, U again from X: the forward's gate/up product (its adapter segment
@@ -1013,14 +1104,14 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     rp.njobs = 2;
     rp.job[0] = rp_job(d, dG, I, I, bgT, I, int(r16), rpa);
     rp.job[1] = rp_job(d, dU, I, I, buT, I, int(r16), rpb);
-    LMLP_SIDE("rowproj(dG B_g, dU B_u)", launch_rowproj(rp, d.bf16, st));
+    LMLP_SIDE_REC("rowproj(dG B_g, dU B_u)", SK_ROWPROJ, rp, d.bf16, launch_rowproj(rp, d.bf16, st));
     q_parts = rp.job[0].kslices;
   }
   fp.njobs = 2;
   fp.job[0] = fin_job(rpa, q_parts, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT, 0);
   fp.job[1] = fin_job(rpb, q_parts, T * r16, r16, int(r16), Qgu, 2 * r16, aext_gu, 2 * r16, s, qguT, ldT,
                       int(r16));
-  LMLP_SIDE("finish(Q_gu)", launch_proj_finish(fp, d.bf16, st));
+  LMLP_SIDE_REC("finish(Q_gu)", SK_FINISH, fp, d.bf16, launch_proj_finish(fp, d.bf16, st));
 
   GemmParams gx{};
   gx.nseg = 3;
@@ -1052,7 +1143,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     cp.njobs = 5;
     nsl_i = ntb;
   }
-  LMLP_SIDE("colproj", launch_colproj(cp, d.bf16, st));
+  LMLP_SIDE_REC("colproj", SK_COLPROJ, cp, d.bf16, launch_colproj(cp, d.bf16, st));
 
   rd.job[0] = rd_job(part_dg, I * r16, nsl_i, r16, 0, I, r, db_gate, r, false, s, d.bf16);
   rd.job[1] = rd_job(part_du, I * r16, nsl_i, r16, 0, I, r, db_up, r, false, s, d.bf16);
@@ -1061,7 +1152,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   rd.job[4] = rd_job(part_x, H * 2 * r16, ntb, 2 * r16, int(r16), H, r, da_up, H, true, s, d.bf16);
   rd.job[5] = rd_job(part_dy, H * r16, ntb, r16, 0, H, r, db_down, r, false, s, d.bf16);
   rd.njobs = 6;
-  LMLP_SIDE("reduce", launch_reduce(rd, st));
+  LMLP_SIDE_REC("reduce", SK_REDUCE, rd, 0, launch_reduce(rd, st));
   if (d.norm) {  // dx (so far the gradient of the normalised rows) through the norm, in place
     np.x = x_in;
     np.g = dx;
@@ -1131,18 +1222,17 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
 // leading axis. Every argument is checked for all experts before anything is
 // enqueued; then each expert runs the fused MLP above on its rows and its
 // slices of the stacked tensors, in phases cut at the GEMMs (Exec): in each
-// phase every expert's side kernels run, spread over kMoeStreams worker
-// streams (default priority, non-blocking, created once per device, forked
-// from and joined back to the caller's stream with events), and then the
-// GEMMs they lead to run as one grouped launch per kind over all experts'
-// tiles on the caller's stream (a few hundred rows per expert are only tens
-// of tiles for 256 CUs). `saved` and the workspace hold one region per
-// expert, in expert order, so every expert's intermediates stay resident
-// across the phases. An expert without rows gets zero adapter gradients.
-// Each expert's arithmetic is that of the plain entry point, so results are
-// bitwise reproducible.
+// phase the experts' side kernels (packing, row projections and their
+// finishes, column projections, reduce) go out merged across experts, one
+// launch per kind and round with one job per expert and the expert's own
+// token count, and then the GEMMs they lead to run as one grouped launch per
+// kind over all experts' tiles (a few hundred rows per expert are only tens
+// of tiles for 256 CUs). Everything runs on the caller's stream. `saved` and
+// the workspace hold one region per expert, in expert order, so every
+// expert's intermediates stay resident across the phases. An expert without
+// rows gets zero adapter gradients. Each expert's arithmetic is that of the
+// plain entry point, so results are bitwise reproducible.
 
-constexpr int kMoeStreams = 4;
 
 struct MoePlan {
   std::vector<lmlp_dims> dims;  // per expert: tokens = its rows
@@ -1155,60 +1245,47 @@ struct MoePlan {
   Dims d;  // the whole call
 };
 
-// The worker streams and fork/join events of one device. Enqueueing a grouped
-// call holds g_moe_mu, so calls from several host threads do not interleave
-// their event records.
-struct MoeStreams {
-  hipStream_t s[kMoeStreams];
-  hipEvent_t fork, join[kMoeStreams];
-};
-static std::mutex g_moe_mu;
-static std::map<int, MoeStreams> g_moe_streams;
-
-static int moe_streams(MoeStreams*& out) {  // call with g_moe_mu held
-  int dev = 0;
-  LMLP_TRY(hip_rc(hipGetDevice(&dev), "hipGetDevice"));
-  auto it = g_moe_streams.find(dev);
-  if (it == g_moe_streams.end()) {
-    MoeStreams m{};
-    for (int i = 0; i < kMoeStreams; ++i) {
-      LMLP_TRY(hip_rc(hipStreamCreateWithFlags(&m.s[i], hipStreamNonBlocking), "hipStreamCreateWithFlags"));
-      LMLP_TRY(hip_rc(hipEventCreateWithFlags(&m.join[i], hipEventDisableTiming), "hipEventCreateWithFlags"));
-    }
-    LMLP_TRY(hip_rc(hipEventCreateWithFlags(&m.fork, hipEventDisableTiming), "hipEventCreateWithFlags"));
-    it = g_moe_streams.emplace(dev, m).first;
-  }
-  out = &it->second;
-  return LMLP_OK;
-}
-
-// Run the passes body(e, exec, stream) of the experts in `order` phase by
-// phase: each phase's side kernels on the worker streams (expert k of the
-// order on stream k % kMoeStreams), then the GEMMs handed back, grouped by
-// kind, on the caller's stream; until no expert hands back a GEMM.
+// Run the passes body(e, exec) of the experts in `order` phase by phase, all
+// on the caller's stream: in each phase every expert records its batchable
+// side kernels (its other side launches, the 4-bit decode and scale packing,
+// go out at once: only GEMMs read what they write), the recorded launches go
+// out merged across experts round by round (round r: every expert's r-th
+// launch; one expert's launches keep their order), then the GEMMs the
+// experts reached, grouped by kind; until no expert hands back a GEMM.
 static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, GemmParams* table,
                       const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
-  std::lock_guard<std::mutex> lock(g_moe_mu);
-  MoeStreams* ms = nullptr;
-  LMLP_TRY(moe_streams(ms));
-  const int nw = int(std::min<size_t>(order.size(), kMoeStreams));
   std::vector<Exec> ex(order.size());
+  std::vector<std::vector<SideOp>> ops(order.size());
+  hipStream_t st = caller;
   for (int phase = 0;; ++phase) {
-    LMLP_TRY(hip_rc(hipEventRecord(ms->fork, caller), "hipEventRecord"));
-    for (int i = 0; i < nw; ++i) LMLP_TRY(hip_rc(hipStreamWaitEvent(ms->s[i], ms->fork, 0), "hipStreamWaitEvent"));
+    size_t rounds = 0;
     for (size_t k = 0; k < order.size(); ++k) {
       ex[k] = Exec{};
       ex[k].phase = phase;
-      LMLP_TRY(body(order[k], &ex[k], ms->s[k % size_t(nw)]));
+      ops[k].clear();
+      ex[k].rec = &ops[k];
+      LMLP_TRY(body(order[k], &ex[k], caller));
+      rounds = std::max(rounds, ops[k].size());
     }
-    for (int i = 0; i < nw; ++i) {
-      LMLP_TRY(hip_rc(hipEventRecord(ms->join[i], ms->s[i]), "hipEventRecord"));
-      LMLP_TRY(hip_rc(hipStreamWaitEvent(caller, ms->join[i], 0), "hipStreamWaitEvent"));
+    for (size_t r = 0; r < rounds; ++r) {
+      std::vector<bool> taken(order.size(), false);
+      for (size_t k = 0; k < order.size(); ++k) {
+        if (taken[k] || r >= ops[k].size()) continue;
+        const SideOp& a = ops[k][r];
+        std::vector<const SideOp*> grp;
+        for (size_t j = k; j < order.size(); ++j) {
+          if (taken[j] || r >= ops[j].size()) continue;
+          const SideOp& b = ops[j][r];
+          if (b.kind != a.kind || b.flag != a.flag || std::strcmp(b.name, a.name) != 0) continue;
+          grp.push_back(&b);
+          taken[j] = true;
+        }
+        LMLP_LAUNCH(a.name, launch_side_group(grp, st));
+      }
     }
     // the GEMMs of this phase: dense bf16 ones grouped by kind, the rest one by one
     bool any = false;
     std::vector<bool> done(order.size(), false);
-    hipStream_t st = caller;
     for (size_t k = 0; k < order.size(); ++k) {
       if (!ex[k].sunk || done[k]) continue;
       any = true;

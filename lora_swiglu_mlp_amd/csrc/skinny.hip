@@ -33,6 +33,7 @@ __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
   const RowProjJob& jb = p.job[blockIdx.z / p.nsl];
   const int n_base = (blockIdx.z % p.nsl) * 64;
   if (n_base >= jb.n1p || static_cast<int>(blockIdx.y) >= jb.kslices) return;
+  if (static_cast<int64_t>(blockIdx.x) * RP_ROWS >= jb.T) return;
   const int nfr = min(4, (jb.n1p - n_base) / 16);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t row = row0 + 16 * r;
-    rval[r] = row < p.T;
+    rval[r] = row < jb.T;
     X[r] = static_cast<const T*>(jb.x) + (rval[r] ? row : 0) * jb.ldx;
   }
   const T* W = static_cast<const T*>(jb.w) + static_cast<int64_t>(n_base + lrow) * jb.ldw;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     if (!rval[r]) continue;
-    float* out = jb.part + (static_cast<int64_t>(blockIdx.y) * p.T + row0 + 16 * r) * jb.n1p + n_base + 4 * lch;
+    float* out = jb.part + (static_cast<int64_t>(blockIdx.y) * jb.T + row0 + 16 * r) * jb.n1p + n_base + 4 * lch;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
       if (f < nfr)
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(64) void proj_finish_kernel(ProjFinishParams p) {
   const ProjFinishJob& jb = p.job[blockIdx.z];
   const int n0 = blockIdx.y * 64;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int64_t tmax = jb.outT ? jb.ldT : p.T;
+  const int64_t tmax = jb.outT ? jb.ldT : jb.T;
   if (n0 >= jb.n1p || t0 >= tmax) return;
   const int nc = min(64, jb.n1p - n0);  // a multiple of 4
   const int cpr = nc / 4;               // float4 items per token row
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(64) void proj_finish_kernel(ProjFinishParams p) {
     const int64_t t = t0 + tl;
     const int n = n0 + 4 * c;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < p.T) {
+    if (t < jb.T) {
       const float* src = jb.part + t * jb.ld_part + n;
       int k = 0;
       for (; k + 8 <= jb.nparts; k += 8) {
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(256) void colproj_f32_kernel(ColProjParams p) {
   const int n0 = nc * 64;
   const int nfr = min(4, (jb.n2p - n0) / 16);
   const int64_t tbeg = static_cast<int64_t>(tb) * jb.tr;
-  const int64_t tend = min(p.T, tbeg + jb.tr);
+  const int64_t tend = min(jb.T, tbeg + jb.tr);
 
   __shared__ __attribute__((aligned(16))) T xs[TS][XS];
   __shared__ __attribute__((aligned(16))) T ps[64][PS];
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void colproj_bf16_kernel(ColProjParams p) {
   const int n0 = nc * 128;
   const int nfr = min(8, (jb.n2p - n0) / 16);
   const int64_t tbeg = static_cast<int64_t>(tb) * jb.tr;
-  const int64_t tend = min(p.T, tbeg + jb.tr);
+  const int64_t tend = min(jb.T, tbeg + jb.tr);
   if (tbeg >= tend) return;
   const int nsteps = static_cast<int>((tend - tbeg + CP_TS - 1) / CP_TS);
 
@@ -566,6 +567,7 @@ __global__ __launch_bounds__(256, 2) void rowproj_dma_kernel(RowProjParams p) {
   if (k0 >= k1) return;
   const int nst = static_cast<int>((k1 - k0 + RPD_BK - 1) / RPD_BK);
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * RPD_ROWS;
+  if (r0 >= jb.T) return;  // a job with fewer rows than the launch's widest
 
   __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
   const int lane = threadIdx.x & 63;
@@ -577,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void rowproj_dma_kernel(RowProjParams p) {
   // position lane & 7 holds chunk (lane & 7) ^ (row & 7)
   const uint32_t ldx_b = static_cast<uint32_t>(jb.ldx * 2), ldw_b = static_cast<uint32_t>(jb.ldw * 2);
   const rsrc_t rx = make_rsrc(static_cast<const char*>(jb.x) + r0 * ldx_b,
-                              static_cast<uint32_t>(min<int64_t>(RPD_ROWS, p.T - r0)) * ldx_b);
+                              static_cast<uint32_t>(min<int64_t>(RPD_ROWS, jb.T - r0)) * ldx_b);
   const rsrc_t rw = make_rsrc(static_cast<const char*>(jb.w) + static_cast<int64_t>(n_base) * ldw_b,
                               static_cast<uint32_t>(16 * nfr) * ldw_b);
   uint32_t xo[4], wo[NW];
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(256, 2) void rowproj_dma_kernel(RowProjParams p) {
   for (int i = 0; i < 4; ++i) {
     const int row = 32 * wave + 8 * i + (lane >> 3);
     xc[i] = (lane & 7) ^ (row & 7);
-    xo[i] = r0 + row < p.T ? static_cast<uint32_t>(row) * ldx_b + xc[i] * 16 : DMA_OOB;
+    xo[i] = r0 + row < jb.T ? static_cast<uint32_t>(row) * ldx_b + xc[i] * 16 : DMA_OOB;
   }
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
@@ -648,8 +650,8 @@ __global__ __launch_bounds__(256, 2) void rowproj_dma_kernel(RowProjParams p) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int64_t row = r0 + 32 * wave + 16 * r + lrow;
-    if (row >= p.T) continue;
-    float* out = jb.part + (static_cast<int64_t>(blockIdx.y) * p.T + row) * jb.n1p + n_base + 4 * lch;
+    if (row >= jb.T) continue;
+    float* out = jb.part + (static_cast<int64_t>(blockIdx.y) * jb.T + row) * jb.n1p + n_base + 4 * lch;
 #pragma unroll
     for (int f = 0; f < NF; ++f)
       if (f < nfr)
@@ -662,6 +664,8 @@ __global__ __launch_bounds__(256, 2) void rowproj_dma_kernel(RowProjParams p) {
 hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream) {
   if (p.T <= 0 || p.njobs <= 0) return hipSuccess;
   RowProjParams q = p;
+  for (int i = 0; i < q.njobs; ++i)
+    if (q.job[i].T == 0) q.job[i].T = q.T;
   int maxn = 0, maxks = 0;
   for (int i = 0; i < q.njobs; ++i) {
     maxn = q.job[i].n1p > maxn ? q.job[i].n1p : maxn;
@@ -682,12 +686,15 @@ hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_proj_finish(const ProjFinishParams& p, int dtype_bf16, hipStream_t stream) {
-  if (p.njobs <= 0) return hipSuccess;
+hipError_t launch_proj_finish(const ProjFinishParams& p0, int dtype_bf16, hipStream_t stream) {
+  if (p0.njobs <= 0) return hipSuccess;
+  ProjFinishParams p = p0;
+  for (int i = 0; i < p.njobs; ++i)
+    if (p.job[i].T == 0) p.job[i].T = p.T;
   int64_t maxt = 0;
   int maxn = 0;
   for (int i = 0; i < p.njobs; ++i) {
-    const int64_t t = p.job[i].outT ? p.job[i].ldT : p.T;
+    const int64_t t = p.job[i].outT ? p.job[i].ldT : p.job[i].T;
     maxt = t > maxt ? t : maxt;
     maxn = p.job[i].n1p > maxn ? p.job[i].n1p : maxn;
   }
@@ -698,8 +705,11 @@ hipError_t launch_proj_finish(const ProjFinishParams& p, int dtype_bf16, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_colproj(const ColProjParams& p, int dtype_bf16, hipStream_t stream) {
-  if (p.T <= 0 || p.njobs <= 0) return hipSuccess;
+hipError_t launch_colproj(const ColProjParams& p0, int dtype_bf16, hipStream_t stream) {
+  if (p0.T <= 0 || p0.njobs <= 0) return hipSuccess;
+  ColProjParams p = p0;
+  for (int i = 0; i < p.njobs; ++i)
+    if (p.job[i].T == 0) p.job[i].T = p.T;
   int maxb = 0, maxfr = 0;
   for (int i = 0; i < p.njobs; ++i) {
     const ColProjJob& j = p.job[i];
