@@ -120,3 +120,18 @@ def test_moe_int4_inkernel_mode_bitwise_equal():
     b, _ = run_hip_moe(inp, off, wl, flags=abi.LMLP_INT4_INKERNEL)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_moe_more_experts_than_one_grouped_launch_holds():
+    """600 experts, over 512 of them with rows (and some without): the grouped
+    GEMMs take two launches (512 parameter blocks per launch) and the merged
+    side kernels many chunks of their job arrays; against the oracle."""
+    wl = workload("bf16_routed").replace(tokens=6000, experts=600, top_k=2, hidden=64, inter=128, rank=4,
+                                         alpha=8.0)
+    inp, off = I.make_moe_inputs(wl)
+    counts = np.diff(off)
+    assert (counts > 0).sum() > 512 and (counts == 0).any()
+    print(f"[case] moe 600 experts rows {int(off[-1])} empty {int((counts == 0).sum())} max {int(counts.max())}",
+          flush=True)
+    got, _ = run_hip_moe(inp, off, wl)
+    compare(got, _oracle(inp, off, wl), TOL[wl.dtype], "moe 600 experts")
