@@ -67,15 +67,17 @@ def test_moe_empty_and_single_row_experts():
             assert not got[k][e].any(), (e, k)
 
 
-def test_moe_recompute_mode_and_determinism_bitwise():
+def test_moe_recompute_consume_and_determinism_bitwise():
     wl = workload("bf16_routed")
     inp, off = I.make_moe_inputs(wl)
     a, _ = run_hip_moe(inp, off, wl)
     b, _ = run_hip_moe(inp, off, wl)
     c, _ = run_hip_moe(inp, off, wl, flags=abi.LMLP_RECOMPUTE_GU)
+    d, _ = run_hip_moe(inp, off, wl, flags=abi.LMLP_CONSUME_SAVED)  # dG, dU in place of the saved G, U
     for k in a:
         assert np.array_equal(a[k], b[k]), k
         assert np.array_equal(a[k], c[k]), k
+        assert np.array_equal(a[k], d[k]), k
 
 
 def test_moe_one_expert_with_all_rows_equals_the_mlp_entry_point():
