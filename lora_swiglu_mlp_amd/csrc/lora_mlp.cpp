@@ -1305,6 +1305,9 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, Gem
         grp.push_back(b.gp);
         done[j] = true;
       }
+      // largest products first: workgroups start in order, so the longest
+      // groups begin early and the last wave is made of short ones
+      std::stable_sort(grp.begin(), grp.end(), [](const GemmParams& x, const GemmParams& y) { return x.M > y.M; });
       if (table && grp.size() > size_t(kMaxGemmGroups))  // parameter blocks through a device table
         LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped_table(grp.data(), int(grp.size()), ex[k].nn, ex[k].epi,
                                                                table, st));
