@@ -1071,7 +1071,9 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     gz.pj_ncol = I;
     gz.c2 = nullptr;  // Z is only needed for Q_d^T Z, formed here
   }
-  const int64_t n1 = dz_split(d);  // columns in 256-wide tiles
+  // columns in 256-wide tiles; grouped launches balance over the experts, and
+  // one split for all of them keeps their phases aligned
+  const int64_t n1 = ex.phase < 0 ? dz_split(d) : d.I;
   if (n1 > 0) {
     GemmParams g1 = gz;
     g1.N = n1;
