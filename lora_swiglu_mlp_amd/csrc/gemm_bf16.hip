@@ -37,6 +37,12 @@
 #include "kernels.h"
 #include "lds_dma.h"
 
+#include <cstring>
+#include <deque>
+#include <map>
+#include <mutex>
+#include <vector>
+
 namespace lmlp {
 
 namespace {
@@ -1158,26 +1164,96 @@ static hipError_t launch_grouped_t(const GemmParams* ps, int n, hipStream_t stre
   return hipSuccess;
 }
 
+// Parameter tables reach the device through a pinned host ring and one copy
+// on the stream (one per device, created on first use and kept until the
+// process ends). A region of the ring is written again only after the event
+// recorded behind its previous copy has completed. `done` stays false when
+// the stream is being captured into a graph or the table is larger than the
+// ring: the caller then writes the table with copy kernels.
+constexpr size_t kStageBytes = size_t(4) << 20;
+struct StageUse {
+  size_t off, len;
+  hipEvent_t ev;
+};
+struct TableStage {
+  char* host = nullptr;
+  size_t head = 0;
+  std::deque<StageUse> inflight;  // in ring order: a new region can only overlap the oldest ones
+  std::vector<hipEvent_t> spare;
+};
+std::mutex g_stage_mu;
+std::map<int, TableStage> g_stage;
+
+static hipError_t stage_table(const GemmParams* src, size_t bytes, GemmParams* dst, hipStream_t st, bool& done) {
+  done = false;
+  if (bytes > kStageBytes) return hipSuccess;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return e;
+  if (cs != hipStreamCaptureStatusNone) return hipSuccess;
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_stage_mu);
+  TableStage& S = g_stage[dev];
+  if (!S.host && hipHostMalloc(reinterpret_cast<void**>(&S.host), kStageBytes, hipHostMallocDefault) != hipSuccess) {
+    S.host = nullptr;
+    (void)hipGetLastError();
+    return hipSuccess;  // no staging memory: copy kernels
+  }
+  const size_t len = (bytes + 255) / 256 * 256;
+  if (S.head + len > kStageBytes) S.head = 0;
+  while (!S.inflight.empty()) {
+    const StageUse& u = S.inflight.front();
+    if (!(u.off < S.head + len && S.head < u.off + u.len)) break;
+    e = hipEventSynchronize(u.ev);
+    if (e != hipSuccess) return e;
+    S.spare.push_back(u.ev);
+    S.inflight.pop_front();
+  }
+  char* h = S.host + S.head;
+  std::memcpy(h, src, bytes);
+  e = hipMemcpyAsync(dst, h, bytes, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return e;
+  hipEvent_t ev = nullptr;
+  if (!S.spare.empty()) {
+    ev = S.spare.back();
+    S.spare.pop_back();
+  } else {
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  e = hipEventRecord(ev, st);
+  if (e != hipSuccess) return e;
+  S.inflight.push_back({S.head, len, ev});
+  S.head += len;
+  done = true;
+  return hipSuccess;
+}
+
 template <bool NN, int EPI, int QRB = 0, int NB = 8>
 static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table, hipStream_t stream) {
   for (int i0 = 0; i0 < n; i0 += kMaxTableGroups) {
     const int cnt = n - i0 < kMaxTableGroups ? n - i0 : kMaxTableGroups;
     GroupStarts gs{};
     int nblk = 0;
-    TableChunk tc{};
+    std::vector<GemmParams> qs(ps + i0, ps + i0 + cnt);
     for (int i = 0; i < cnt; ++i) {
-      GemmParams q = ps[i0 + i];
-      set_tiles<EPI, NB>(q);
+      set_tiles<EPI, NB>(qs[i]);
       gs.start[i] = nblk;
-      nblk += (q.tiles_m * q.tiles_n + 7) / 8 * 8;
-      tc.p[tc.n++] = q;
-      if (tc.n == kMaxGemmGroups || i == cnt - 1) {  // blocks i - n + 1 .. i of this launch
-        tc.dst = table + (i + 1 - tc.n);
-        hipLaunchKernelGGL(write_table_kernel, dim3(1), dim3(256), 0, stream, tc);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        tc.n = 0;
-      }
+      nblk += (qs[i].tiles_m * qs[i].tiles_n + 7) / 8 * 8;
+    }
+    bool staged = false;
+    hipError_t se = stage_table(qs.data(), qs.size() * sizeof(GemmParams), table, stream, staged);
+    if (se != hipSuccess) return se;
+    for (int i = 0; !staged && i < cnt; i += kMaxGemmGroups) {  // copy kernels, kMaxGemmGroups blocks each
+      TableChunk tc{};
+      tc.n = cnt - i < kMaxGemmGroups ? cnt - i : kMaxGemmGroups;
+      for (int j = 0; j < tc.n; ++j) tc.p[j] = qs[i + j];
+      tc.dst = table + i;
+      hipLaunchKernelGGL(write_table_kernel, dim3(1), dim3(256), 0, stream, tc);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
     }
     gs.start[cnt] = nblk;
     gs.n = cnt;
