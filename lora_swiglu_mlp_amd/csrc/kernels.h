@@ -107,9 +107,9 @@ struct RowProjJob {
   int32_t kslices;
   int64_t T;        // token rows of this job (0: the launch's T)
 };
-// job capacities: kernel arguments stay under 4 KB
+// job capacities: every parameter block stays under 3.8 KB of kernel arguments
 struct RowProjParams {
-  RowProjJob job[32];
+  RowProjJob job[52];
   int32_t njobs;
   int32_t nsl;      // set by the launcher: 64-column slices of the widest job
   int64_t T;
@@ -138,7 +138,7 @@ struct ProjFinishJob {
   int64_t T;            // token rows of this job (0: the launch's T)
 };
 struct ProjFinishParams {
-  ProjFinishJob job[24];
+  ProjFinishJob job[36];
   int32_t njobs;
   int32_t pad_;
   int64_t T;
@@ -163,7 +163,7 @@ struct ColProjJob {
   int64_t T;        // tokens of this job (0: the launch's T)
 };
 struct ColProjParams {
-  ColProjJob job[24];
+  ColProjJob job[38];
   int32_t njobs;
   int32_t pad_;
   int64_t T;
@@ -184,7 +184,7 @@ struct ReduceJob {
   int32_t pad_;
 };
 struct ReduceParams {
-  ReduceJob job[32];
+  ReduceJob job[46];
   int32_t njobs;
   int32_t pad_;
 };
@@ -202,7 +202,7 @@ struct PackJob {
   int32_t pad_;
 };
 struct PackParams {
-  PackJob job[40];
+  PackJob job[52];
   int32_t njobs;
   int32_t pad_;
 };
