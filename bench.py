@@ -32,18 +32,55 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}    # MI355X published dense MFMA pe
 HBM_PEAK_GBS = 8000.0
 
 
-def kernel_flops(name: str, T: int, H: int, I: int, r: int, linear: bool = False) -> int:
+def dz_split(T: int, I: int, ncu: int) -> int:
+    """Columns of the bf16 dZ product that the library gives 256-wide tiles
+    (the rest runs as a second launch of 128-wide tiles): the rule of the
+    library's dZ launch, restated for the FLOP accounting of each launch."""
+    tm, tn = (T + 255) // 256, (I + 255) // 256
+    tiles = tm * tn
+    rem = tiles % ncu
+    if tiles <= ncu or rem == 0 or 2 * rem > ncu:
+        return I
+    ntail = (rem + tm - 1) // tm
+    if ntail >= tn or tm * ntail * 2 > ncu:
+        return I
+    return (tn - ntail) * 256
+
+
+def kernel_flops(name: str, T: int, H: int, I: int, r: int, linear: bool = False, dz_cols=None) -> int:
     """Algorithmic FLOPs of one launch (2mnk per product, real rank, no padding).
-    For the fused LoRA linear, H is the input and I the output width."""
+    For the fused LoRA linear, H is the input and I the output width. The dZ
+    product may run as two launches over the columns [0, dz_cols) and
+    [dz_cols, I); each is credited with its own columns."""
     if linear:
         return {"gemm(y)": 2 * T * H * I + 2 * T * r * I, "gemm(dX)": 2 * T * I * H + 2 * T * r * H}.get(name, 0)
+    n1 = I if dz_cols is None else dz_cols
     return {
         "gemm(gate/up)": 4 * T * H * I + 4 * T * I * r,
         "gemm(gate/up, recompute)": 4 * T * H * I + 4 * T * I * r,
         "gemm(down)": 2 * T * I * H + 2 * T * H * r,
-        "gemm(dZ)": 2 * T * H * I + 2 * T * r * I,
+        "gemm(dZ)": 2 * T * H * n1 + 2 * T * r * n1,
+        "gemm(dZ tail)": 2 * T * H * (I - n1) + 2 * T * r * (I - n1),
         "gemm(dX)": 4 * T * I * H + 4 * T * r * H,
     }.get(name, 0)
+
+
+# the four products of the step, each summed over its launches
+GEMM_GROUPS = {"gate/up": ("gemm(gate/up)",), "down": ("gemm(down)",), "dZ": ("gemm(dZ)", "gemm(dZ tail)"),
+               "dX": ("gemm(dX)",)}
+
+
+def gemm_table(kern: dict, T: int, H: int, I: int, r: int, peak: float, dz_cols=None) -> dict:
+    """ms per step, TFLOP/s and fraction of peak of each of the four products
+    (a product launched twice is one product over both launches' time)."""
+    out = {}
+    for g, names in GEMM_GROUPS.items():
+        ms = sum(kern[n]["ms"] * kern[n]["launches_per_step"] for n in names if n in kern)
+        f = sum(kernel_flops(n, T, H, I, r, dz_cols=dz_cols) for n in names if n in kern)
+        if ms > 0 and f > 0:
+            tf = f / (ms * 1e-3) / 1e12
+            out[g] = {"ms": ms, "tflops": tf, "frac": tf / peak}
+    return out
 
 
 def kernel_bytes(name: str, T: int, H: int, I: int, r: int, eb: int) -> int:
@@ -109,15 +146,44 @@ def copy_probe(mib: int):
     del a, b
 
 
-def cpu_baseline(inp, wl, seconds: float, norm_eps=None):
-    import numpy as np
-    import oracle
-    from lora_swiglu_mlp_amd import inputs as I
+def host_cpu() -> dict:
+    """What the CPU baseline ran on: logical CPUs of this process and the
+    processor model as lscpu names it."""
+    import subprocess
+    model = ""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:  # pragma: no cover - lscpu missing
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        nproc = os.cpu_count() or 1
+    return {"nproc": nproc, "model": model}
+
+
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count() or 1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count() or 1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def median3(run, n):
+    ts = sorted(run(n) for _ in range(3))
+    return ts[1]
+
+
+def cpu_baseline(inp, wl, seconds: float, norm_eps=None):
+    """The oracle as it stands on the first n tokens: n grows until one
+    forward+backward takes about seconds/3, then the median of 3 runs."""
+    import oracle
+    from lora_swiglu_mlp_amd import inputs as I
     w = {}
     for k in oracle.WEIGHT_KEYS:
         if wl.wfmt == "int4_b64" and k in ("w_gate", "w_up", "w_down"):
@@ -137,18 +203,39 @@ def cpu_baseline(inp, wl, seconds: float, norm_eps=None):
             oracle.rmsnorm.norm_mlp_forward_backward(d, I.to_f64(inp["gamma"], wl.dtype), norm_eps, wl.scale)
         return time.perf_counter() - t0
 
+    target = seconds / 3
     n, t = 32, run(32)
-    while t < seconds / 4 and n < wl.tokens:
+    while t < target / 4 and n < wl.tokens:
         n = min(wl.tokens, n * 2)
         t = run(n)
-    if t < seconds and n < wl.tokens:
-        n = min(wl.tokens, max(n, int(n * seconds / max(t, 1e-3))))
-        t = run(n)
-    return {"value": n / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n} of {wl.tokens} tokens of {wl.name}, "
-                      f"{'RMSNorm then ' if norm_eps is not None else ''}forward+backward, "
-                      f"fp64 numpy (row-local work per token is the full path), {t:.1f} s",
-            "gflops": oracle.flops(n, wl.hidden, wl.inter, wl.rank) / t / 1e9}
+    if t < target and n < wl.tokens:
+        n = min(wl.tokens, max(n, int(n * target / max(t, 1e-3))))
+    t = median3(run, n)
+    out = {"value": n / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+           "sample": f"first {n} of {wl.tokens} tokens of {wl.name}, "
+                     f"{'RMSNorm then ' if norm_eps is not None else ''}forward+backward, "
+                     f"fp64 numpy (row-local work per token is the full path), median of 3 runs of {t:.1f} s",
+           "gflops": oracle.flops(n, wl.hidden, wl.inter, wl.rank) / t / 1e9,
+           "host": host_cpu()}
+    return out
+
+
+def cpu_baseline_tiny_single_thread():
+    """The oracle on the whole tiny fp32 workload with one BLAS thread
+    (median of 3 runs)."""
+    import oracle
+    from lora_swiglu_mlp_amd import inputs as I
+    from threadpoolctl import threadpool_limits
+    wl = I.WORKLOADS["tiny_fp32"]
+    inp = I.make_inputs(wl)
+    d = {k: I.to_f64(v, wl.dtype) for k, v in inp.items()}
+    with threadpool_limits(limits=1):
+        def run(_):
+            t0 = time.perf_counter()
+            oracle.forward_backward(d, wl.scale)
+            return time.perf_counter() - t0
+        t = median3(run, 0)
+    return {"workload": wl.name, "tokens_per_s": wl.tokens / t, "ms": t * 1e3, "cores": 1}
 
 
 def cpu_baseline_linear(inp, wl, seconds: float):
@@ -342,6 +429,8 @@ def main():
                          "(its FLOPs are not counted in the metric)")
     ap.add_argument("--norm", action="store_true",
                     help="RMSNorm (eps 1e-5) in front of the MLP: the library's norm entry points")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the named workload (no sub-lines for the other workloads)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -363,35 +452,15 @@ def main():
         bench_moe(args, I.MOE_WORKLOADS[args.workload])
         return
     wl = I.WORKLOADS[args.workload]
-    T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank
     torch.cuda.set_device(0)
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
-    inp = I.make_inputs(wl)
     norm_eps = I.NORM_EPS if args.norm else None
-    if args.norm:
-        inp["gamma"] = I.make_norm_gamma(wl)
     flags = abi.LMLP_RECOMPUTE_GU if args.recompute else 0
-    m, x, dy = mlp.from_inputs(inp, wl, "cuda:0", flags, norm_eps=norm_eps)
-    saved = m.new_saved()
-    y = torch.empty((T, H), dtype=m.tdtype, device="cuda:0")
-    grads = m.new_grads(x.device)
-    m.workspace(True)
-
-    def step():
-        m.forward(x, y, saved)
-        m.backward(dy, x, saved, grads)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / args.steps
-    flops = 12 * T * H * Iw + 18 * T * r * (H + Iw) + (12 * T * H if args.norm else 0)
+    res = measure_mlp(wl, args.steps, args.warmup, flags, norm_eps, profile=not args.no_profile)
+    T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank
+    ms = res["ms"]
+    flops = mlp_flops(wl, norm_eps)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
 
@@ -405,8 +474,100 @@ def main():
                       "norm": f"rmsnorm eps={norm_eps}" if args.norm else "none"},
            "tflops": tflops, "pct_of_peak": 100.0 * tflops / peak}
 
-    if not args.no_profile:
-        nprof = max(1, min(args.steps, 10))
+    if "kern" in res:
+        kern = res["kern"]
+        out["kernels"] = kern
+        out["kernel_ms_per_step"] = sum(v["ms"] * v["launches_per_step"] for v in kern.values())
+        dom = max((n for n in kern if kernel_flops(n, T, H, Iw, r, dz_cols=res["dz_cols"])),
+                  key=lambda n: kern[n]["ms"] * kern[n]["launches_per_step"])
+        achieved = kern[dom]["tflops"]
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
+                           "unit": "TFLOP/s", "frac": achieved / peak,
+                           "traffic": measured_traffic(dom, wl.name)}
+        out["gemms"] = res["gemms"]
+        out["fwd_kernel_ms"] = res["fwd_kernel_ms"]
+        out["bwd_kernel_ms"] = out["kernel_ms_per_step"] - out["fwd_kernel_ms"]
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(res["inp"], wl, args.cpu_seconds, norm_eps)
+        out["cpu_baseline"]["single_thread"] = cpu_baseline_tiny_single_thread()
+    del res
+
+    # the other workloads of the metric, one sub-line each (fewer steps)
+    if args.workload == "llama3_8b" and not (args.recompute or args.norm or args.no_configs):
+        subs = {}
+        for name in ("tiny_fp32", "qwen2_7b", "tinyllama_long", "llama3_8b_int4"):
+            w2 = I.WORKLOADS[name]
+            r2 = measure_mlp(w2, min(args.steps, 10), min(args.warmup, 3), 0, None, profile=not args.no_profile)
+            f2 = mlp_flops(w2, None)
+            tf2 = f2 / (r2["ms"] * 1e-3) / 1e12
+            e = {"ms_per_step": r2["ms"], "tokens_per_s": w2.tokens / (r2["ms"] * 1e-3), "tflops": tf2,
+                 "pct_of_peak": 100.0 * tf2 / PEAK_TFLOPS[w2.dtype], "dtype": w2.dtype, "weights": w2.wfmt,
+                 "tokens": w2.tokens, "hidden": w2.hidden, "inter": w2.inter, "rank": w2.rank,
+                 "alpha": w2.alpha}
+            if "gemms" in r2:
+                e["gemms"] = {g: round(v["frac"], 4) for g, v in r2["gemms"].items()}
+                e["fwd_kernel_ms"] = r2["fwd_kernel_ms"]
+                e["kernel_ms_per_step"] = sum(v["ms"] * v["launches_per_step"] for v in r2["kern"].values())
+            subs[name] = e
+            del r2
+            torch.cuda.empty_cache()
+        out["configs"] = subs
+
+    print(json.dumps(out), flush=True)
+
+
+FWD_NAMES = ("rmsnorm(fwd)", "pack(fwd)", "rowproj(X A^T)", "gemm(gate/up)", "rowproj(Z A_d^T)", "gemm(down)",
+)
+
+
+def mlp_flops(wl, norm_eps) -> int:
+    T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank
+    return 12 * T * H * Iw + 18 * T * r * (H + Iw) + (norm_flops(T, H) if norm_eps is not None else 0)
+
+
+def norm_flops(T: int, H: int) -> int:
+    """Useful FLOPs of the RMSNorm forward + backward, one per element
+    operation on [T, H] arrays (a sum over H counts H adds): forward x*x, its
+    row sum, x*rstd, *gamma (4); backward x*rstd, g*gamma, their product, its
+    row sum, xhat*c, the difference, *rstd (7). Per-row scalar work (eps,
+    square root, reciprocal, the mean's divide) is not counted."""
+    return 11 * T * H
+
+
+def measure_mlp(wl, steps: int, warmup: int, flags: int, norm_eps, profile: bool = True) -> dict:
+    """Time `steps` forward+backward steps of the MLP on workload wl (after
+    `warmup` untimed ones); with `profile`, a second pass of the same steps
+    records per-launch HIP events for the per-kernel table."""
+    import torch
+    from lora_swiglu_mlp_amd import abi, mlp
+    from lora_swiglu_mlp_amd import inputs as I
+    T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank
+    inp = I.make_inputs(wl)
+    if norm_eps is not None:
+        inp["gamma"] = I.make_norm_gamma(wl)
+    m, x, dy = mlp.from_inputs(inp, wl, "cuda:0", flags, norm_eps=norm_eps)
+    saved = m.new_saved()
+    y = torch.empty((T, H), dtype=m.tdtype, device="cuda:0")
+    grads = m.new_grads(x.device)
+    m.workspace(True)
+
+    def step():
+        m.forward(x, y, saved)
+        m.backward(dy, x, saved, grads)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    res = {"ms": (time.perf_counter() - t0) * 1e3 / steps, "inp": inp}
+    if profile:
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        dz_cols = dz_split(T, Iw, ncu) if wl.dtype == "bf16" else None
+        nprof = max(1, min(steps, 10))
         abi.lora_mlp_profile_begin()
         for _ in range(nprof):
             step()
@@ -420,30 +581,19 @@ def main():
         for name, (tot, cnt) in agg.items():
             avg = tot / cnt
             e = {"ms": avg, "launches_per_step": cnt / nprof}
-            f = kernel_flops(name, T, H, Iw, r)
+            f = kernel_flops(name, T, H, Iw, r, dz_cols=dz_cols)
             if f:
                 e["tflops"] = f / (avg * 1e-3) / 1e12
             b = kernel_bytes(name, T, H, Iw, r, 2 if wl.dtype == "bf16" else 4)
             if b:
                 e["gbps"] = b / (avg * 1e-3) / 1e9
             kern[name] = e
-        out["kernels"] = kern
-        fwd_names = ("rmsnorm(fwd)", "pack(fwd)", "rowproj(X A^T)", "gemm(gate/up)", "rowproj(Z A_d^T)", "gemm(down)")
-        out["kernel_ms_per_step"] = sum(v["ms"] * v["launches_per_step"] for v in kern.values())
-        dom = max((n for n in kern if kernel_flops(n, T, H, Iw, r)),
-                  key=lambda n: kern[n]["ms"] * kern[n]["launches_per_step"])
-        achieved = kern[dom]["tflops"]
-        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                           "unit": "TFLOP/s", "frac": achieved / peak,
-                           "traffic": measured_traffic(dom, wl.name)}
-        out["fwd_kernel_ms"] = sum(kern[n]["ms"] * kern[n]["launches_per_step"]
-                                   for n in kern if n in fwd_names)
-        out["bwd_kernel_ms"] = out["kernel_ms_per_step"] - out["fwd_kernel_ms"]
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds, norm_eps)
-
-    print(json.dumps(out), flush=True)
+        res["kern"] = kern
+        res["dz_cols"] = dz_cols
+        res["gemms"] = gemm_table(kern, T, H, Iw, r, PEAK_TFLOPS[wl.dtype], dz_cols)
+        res["fwd_kernel_ms"] = sum(kern[n]["ms"] * kern[n]["launches_per_step"] for n in kern if n in FWD_NAMES)
+    del m, x, dy, saved, y, grads
+    return res
 
 
 if __name__ == "__main__":

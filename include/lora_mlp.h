@@ -83,9 +83,10 @@ typedef enum { LMLP_W_DENSE = 0, LMLP_W_INT4_B64 = 1 } lmlp_wfmt;
 #define LMLP_RMSNORM 0x8u
 
 typedef struct {
-  int64_t tokens;  /* T >= 0 (T == 0: forward is a no-op, backward writes zero adapter gradients) */
-  int64_t hidden;  /* H >= 1; multiple of 8 (bf16) or 4 (fp32) */
-  int64_t inter;   /* I >= 1; multiple of 8 (bf16) or 4 (fp32) */
+  int64_t tokens;  /* 0 <= T <= 2^24 - 64 (T == 0: forward is a no-op, backward writes zero adapter
+                      gradients) */
+  int64_t hidden;  /* 1 <= H <= 2^22; multiple of 8 (bf16) or 4 (fp32) */
+  int64_t inter;   /* 1 <= I <= 2^22; multiple of 8 (bf16) or 4 (fp32) */
   int64_t rank;    /* r in [1, 256] */
   float scale;     /* s = alpha / r, finite */
   int32_t dtype;   /* lmlp_dtype */
@@ -197,7 +198,10 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
  * region per expert (none in the workspace for an expert without rows), and
  * the workspace a table of GEMM parameters beyond 8 experts, which reaches
  * the device by a copy on `stream` from a small pinned host buffer of the
- * library's own (allocated on first use per device, kept until exit). */
+ * library's own (allocated on first use per device, kept until exit). Where
+ * the region of that buffer a call would reuse is still being copied from,
+ * and under graph capture, small copy kernels on `stream` write the table
+ * instead: the host never waits for the device. */
 size_t lora_moe_saved_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets);
 size_t lora_moe_workspace_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets,
                                 int is_backward);

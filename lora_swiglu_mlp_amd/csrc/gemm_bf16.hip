@@ -1166,10 +1166,11 @@ static hipError_t launch_grouped_t(const GemmParams* ps, int n, hipStream_t stre
 
 // Parameter tables reach the device through a pinned host ring and one copy
 // on the stream (one per device, created on first use and kept until the
-// process ends). A region of the ring is written again only after the event
-// recorded behind its previous copy has completed. `done` stays false when
-// the stream is being captured into a graph or the table is larger than the
-// ring: the caller then writes the table with copy kernels.
+// process ends). A region of the ring is written again only once the event
+// recorded behind its previous copy has completed; the host never waits for
+// it. `done` stays false when that copy is still in flight, when the stream is
+// being captured into a graph, or when the table is larger than the ring: the
+// caller then writes the table with copy kernels on the stream.
 constexpr size_t kStageBytes = size_t(4) << 20;
 struct StageUse {
   size_t off, len;
@@ -1206,7 +1207,11 @@ static hipError_t stage_table(const GemmParams* src, size_t bytes, GemmParams* d
   while (!S.inflight.empty()) {
     const StageUse& u = S.inflight.front();
     if (!(u.off < S.head + len && S.head < u.off + u.len)) break;
-    e = hipEventSynchronize(u.ev);
+    e = hipEventQuery(u.ev);
+    if (e == hipErrorNotReady) {
+      (void)hipGetLastError();  // not an error: the copy kernels take this table
+      return hipSuccess;
+    }
     if (e != hipSuccess) return e;
     S.spare.push_back(u.ev);
     S.inflight.pop_front();

@@ -84,9 +84,10 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
       return fail(LMLP_ERR_UNSUPPORTED, "4-bit weights need hidden and inter multiples of 64");
   }
   // sizes far beyond any one GPU; the DMA kernels address a 256-row operand
-  // panel, or 128 token-contiguous rows, with 32-bit buffer offsets
-  if (d->tokens > (int64_t{1} << 24) || d->hidden > (int64_t{1} << 22) || d->inter > (int64_t{1} << 22))
-    return fail(LMLP_ERR_UNSUPPORTED, "dimension too large (tokens <= 2^24, hidden and inter <= 2^22)");
+  // panel, or 128 token-contiguous bf16 rows of roundup(tokens, 64) elements,
+  // with 32-bit buffer offsets and sizes: 128 * 2 * (2^24 - 64) < 2^32
+  if (d->tokens > (int64_t{1} << 24) - 64 || d->hidden > (int64_t{1} << 22) || d->inter > (int64_t{1} << 22))
+    return fail(LMLP_ERR_UNSUPPORTED, "dimension too large (tokens <= 2^24 - 64, hidden and inter <= 2^22)");
   o.T = d->tokens;
   o.H = d->hidden;
   o.I = d->inter;
@@ -1511,12 +1512,12 @@ size_t lora_linear_workspace_bytes(const lmlp_dims* dims, int is_backward) {
   return is_backward ? lin_bwd_layout(d).total : lin_fwd_layout(d).total;
 }
 
-int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, const void* w_scales, const void* a,
+}  // extern "C"
+
+namespace {
+int linear_forward_impl(const Dims& d, const void* x, const void* w, const void* w_scales, const void* a,
                         const void* b, void* y, void* saved, size_t saved_bytes, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  Dims d;
-  LMLP_TRY(parse_linear_dims(dims, d));
   LMLP_TRY(need_ptr(w, "w"));
   if (d.int4) LMLP_TRY(need_ptr(w_scales, "w_scales"));
   else if (w_scales) return fail(LMLP_ERR_INVALID_ARG, "w_scales must be NULL for dense weights");
@@ -1589,6 +1590,19 @@ int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, con
   gy.tile_n = store_tile_n(d, T, Out);
   LMLP_LAUNCH("gemm(y)", run_gemm(gy, d, 0, EPI_STORE, st));
   return LMLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, const void* w_scales, const void* a,
+                        const void* b, void* y, void* saved, size_t saved_bytes, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Dims d;
+  LMLP_TRY(parse_linear_dims(dims, d));
+  return linear_forward_impl(d, x, w, w_scales, a, b, y, saved, saved_bytes, workspace, workspace_bytes, stream);
 }
 
 int lora_linear_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* w, const void* w_scales,

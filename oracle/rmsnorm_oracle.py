@@ -93,9 +93,3 @@ def bruteforce(x, gamma, eps: float, g):
                 acc += float(g[t, j]) * dj
             dx[t, k] = acc
     return xn, rstd, dx
-
-
-def flops(T: int, H: int) -> int:
-    """Useful FLOPs of the norm's forward (square-sum 2H, scale 2H per row)
-    plus backward (4H for the dot, 4H for the output per row)."""
-    return 12 * T * H

@@ -99,6 +99,10 @@ def test_workspace_sizes_positive_and_consume_flag_saves_memory():
     (dict(inter=346, dtype="f32"), abi.LMLP_ERR_UNSUPPORTED),  # not a multiple of 4
     (dict(wfmt="int4_b64", dtype="f32"), abi.LMLP_ERR_UNSUPPORTED),
     (dict(wfmt="int4_b64", inter=344), abi.LMLP_ERR_UNSUPPORTED),  # not a multiple of 64
+    # 128 token-contiguous bf16 rows of roundup(T, 64) must stay below 2^32 bytes
+    (dict(tokens=(1 << 24) - 63), abi.LMLP_ERR_UNSUPPORTED),
+    (dict(tokens=1 << 24), abi.LMLP_ERR_UNSUPPORTED),
+    (dict(hidden=(1 << 22) + 8), abi.LMLP_ERR_UNSUPPORTED),
 ])
 def test_invalid_dims_rejected(kw, code):
     d = dims(**kw)
@@ -108,6 +112,11 @@ def test_invalid_dims_rejected(kw, code):
     rc = _forward_raw(d, saved_bytes=1 << 40, workspace_bytes=1 << 40)
     assert rc == code, abi.lora_mlp_last_error()
     assert abi.lora_mlp_last_error()
+
+
+def test_largest_token_count_is_accepted():
+    d = dims(tokens=(1 << 24) - 64, hidden=64, inter=64, rank=64)
+    assert abi.lora_mlp_saved_bytes(d) > 0 and abi.lora_mlp_workspace_bytes(d, True) > 0
 
 
 def _forward_raw(d, ptrs=None, saved_bytes=0, workspace_bytes=0, scales=(None, None, None)):
@@ -302,3 +311,4 @@ def test_binding_argument_counts_match_the_header():
         assert m, name
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(params) == len(args), (name, len(params), len(args))
+

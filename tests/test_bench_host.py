@@ -64,3 +64,57 @@ def test_norm_gamma_is_seeded_and_in_range():
     assert np.array_equal(g, I.make_norm_gamma(wl))
     # its own stream: the MLP's draws do not move
     assert np.array_equal(I.make_inputs(wl)["x"], I.make_inputs(wl)["x"])
+
+
+def test_dz_split_and_per_launch_flops_at_llama3_8b():
+    """On 256 compute units the Llama-3-8B dZ product (16 x 56 tiles of 256,
+    3.5 waves) runs 12288 columns in 256-wide tiles and the last 2048 in a
+    second launch; each launch is credited with its own columns, and the two
+    add up to the whole product."""
+    T, H, Iw, r = 4096, 4096, 14336, 16
+    n1 = bench.dz_split(T, Iw, 256)
+    assert n1 == 12288
+    main = bench.kernel_flops("gemm(dZ)", T, H, Iw, r, dz_cols=n1)
+    tail = bench.kernel_flops("gemm(dZ tail)", T, H, Iw, r, dz_cols=n1)
+    assert main == 2 * T * (H + r) * 12288 and tail == 2 * T * (H + r) * 2048
+    assert main + tail == bench.kernel_flops("gemm(dZ)", T, H, Iw, r)
+    # full waves (or less than one) keep every column in one launch
+    assert bench.dz_split(4096, 8192, 256) == 8192
+    assert bench.dz_split(256, 14336, 256) == 14336
+    kern = {"gemm(dZ)": {"ms": 0.4, "launches_per_step": 1.0}, "gemm(dZ tail)": {"ms": 0.1, "launches_per_step": 1.0}}
+    tab = bench.gemm_table(kern, T, H, Iw, r, 2500.0, dz_cols=n1)
+    assert abs(tab["dZ"]["tflops"] - (main + tail) / 0.5e-3 / 1e12) < 1e-9
+
+
+class _OpCount(np.ndarray):
+    """An array that counts the element operations done on full [T, H]
+    operands (ufunc calls, and reductions counted at their input size)."""
+    full = 0
+    ops = 0
+
+    def __array_ufunc__(self, ufunc, method, *inputs, **kw):
+        args = [np.asarray(i) if isinstance(i, _OpCount) else i for i in inputs]
+        if "out" in kw:
+            kw["out"] = tuple(np.asarray(o) if isinstance(o, _OpCount) else o for o in kw["out"])
+        res = getattr(ufunc, method)(*args, **kw)
+        big = max(np.size(a) for a in args if isinstance(a, np.ndarray))
+        if big == _OpCount.full:
+            _OpCount.ops += big
+        return res.view(_OpCount) if isinstance(res, np.ndarray) else res
+
+
+def test_norm_flops_count_the_oracles_operations():
+    """bench's RMSNorm FLOP figure equals the element operations the norm
+    oracle actually performs on [T, H] arrays in its forward and backward."""
+    from oracle import rmsnorm_oracle as R
+    rng = np.random.default_rng(5)
+    T, H = 6, 10
+    x = rng.standard_normal((T, H)).view(_OpCount)
+    gamma = rng.standard_normal(H).view(_OpCount)
+    g = rng.standard_normal((T, H)).view(_OpCount)
+    _OpCount.full, _OpCount.ops = T * H, 0
+    _, rstd = R.forward(x, gamma, 1e-5)
+    fwd = _OpCount.ops
+    R.backward(x, gamma, np.asarray(rstd).view(_OpCount), g)
+    assert fwd == 4 * T * H
+    assert _OpCount.ops == bench.norm_flops(T, H)

@@ -50,3 +50,5 @@ def test_fullsize_recompute_mode_bitwise_equal():
     b, _ = run_hip(inp, wl, flags=abi.LMLP_RECOMPUTE_GU)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+    ref = oracle.forward_backward(oracle_inputs(inp, wl), wl.scale, row_chunk=2048)
+    compare(b, ref, TOL[wl.dtype], "llama3_8b recompute")

@@ -61,6 +61,7 @@ def test_linear_int4_modes_bitwise_equal(name):
     b, _ = run_hip_linear(inp, wl, flags=abi.LMLP_INT4_INKERNEL)
     for k in LIN_KEYS:
         assert np.array_equal(a[k], b[k]), k
+    compare(b, _oracle(inp, wl), TOL[wl.dtype], "linear " + name + " in-kernel")
 
 
 def test_linear_empty_batch_gives_zero_adapter_gradients():

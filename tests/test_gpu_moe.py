@@ -78,6 +78,9 @@ def test_moe_recompute_consume_and_determinism_bitwise():
         assert np.array_equal(a[k], b[k]), k
         assert np.array_equal(a[k], c[k]), k
         assert np.array_equal(a[k], d[k]), k
+    ref = _oracle(inp, off, wl)
+    compare(c, ref, TOL[wl.dtype], "moe recompute")
+    compare(d, ref, TOL[wl.dtype], "moe consume-saved")
 
 
 def test_moe_one_expert_with_all_rows_equals_the_mlp_entry_point():
@@ -122,6 +125,7 @@ def test_moe_int4_inkernel_mode_bitwise_equal():
     b, _ = run_hip_moe(inp, off, wl, flags=abi.LMLP_INT4_INKERNEL)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+    compare(b, _oracle(inp, off, wl), TOL[wl.dtype], "moe int4 in-kernel")
 
 
 def test_moe_more_experts_than_one_grouped_launch_holds():
@@ -137,3 +141,83 @@ def test_moe_more_experts_than_one_grouped_launch_holds():
           flush=True)
     got, _ = run_hip_moe(inp, off, wl)
     compare(got, _oracle(inp, off, wl), TOL[wl.dtype], "moe 600 experts")
+
+
+def _moe600():
+    wl = workload("bf16_routed").replace(tokens=6000, experts=600, top_k=2, hidden=64, inter=128, rank=4,
+                                         alpha=8.0)
+    inp, off = I.make_moe_inputs(wl)
+    return wl, inp, off
+
+
+def _moe_buffers(inp, off, wl):
+    import torch
+    from lora_swiglu_mlp_amd import mlp
+    m, x, dy = mlp.moe_from_inputs(inp, off, wl, "cuda")
+    saved = m.new_saved()
+    y = torch.empty((int(off[-1]), wl.hidden), dtype=m.tdtype, device="cuda")
+    grads = m.new_grads(x.device)
+    m.workspace()
+    return m, x, dy, saved, y, grads
+
+
+def test_moe_parameter_tables_many_calls_in_flight():
+    """Twelve forward+backward calls queued without a host wait: the tables
+    (over 1 MB per call at 600 experts) wrap the 4 MB pinned ring while
+    earlier copies may still be in flight, where the call writes the table
+    with copy kernels instead of waiting. Every call gives the synchronised
+    call's outputs bit for bit."""
+    import torch
+    wl, inp, off = _moe600()
+    m, x, dy, saved, y, grads = _moe_buffers(inp, off, wl)
+    m.forward(x, y, saved)
+    m.backward(dy, x, saved, grads)
+    torch.cuda.synchronize()
+    ref = {"y": y.clone(), **{k: v.clone() for k, v in grads.items()}}
+    outs = []
+    for _ in range(12):
+        yy = torch.empty_like(y)
+        gg = {k: torch.empty_like(v) for k, v in grads.items()}
+        m.forward(x, yy, saved)
+        m.backward(dy, x, saved, gg)
+        outs.append({"y": yy, **gg})
+    torch.cuda.synchronize()
+    for o in outs:
+        for k in ref:
+            assert torch.equal(o[k], ref[k]), k
+
+
+def test_moe_graph_capture_writes_the_tables_with_copy_kernels():
+    """Captured into a HIP graph, the grouped GEMMs' parameter tables are
+    written by copy kernels on the stream (no host ring). Three replays, with
+    eager work and a synchronisation between them, each give the eager
+    outputs bit for bit; the eager outputs match the oracle."""
+    import torch
+    wl, inp, off = _moe600()
+    m, x, dy, saved, y, grads = _moe_buffers(inp, off, wl)
+    m.forward(x, y, saved)
+    m.backward(dy, x, saved, grads)
+    torch.cuda.synchronize()
+    ref = {"y": y.clone(), **{k: v.clone() for k, v in grads.items()}}
+    got = {k: v.float().cpu().numpy().astype(np.float64) for k, v in ref.items()}
+    compare(got, _oracle(inp, off, wl), TOL[wl.dtype], "moe 600 experts eager")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        m.forward(x, y, saved)
+        m.backward(dy, x, saved, grads)
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.zero_()
+        for v in grads.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] replay {i}", flush=True)
+        assert torch.equal(y, ref["y"]), i
+        for k, v in grads.items():
+            assert torch.equal(v, ref[k]), (i, k)

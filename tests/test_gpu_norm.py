@@ -66,6 +66,7 @@ def test_norm_recompute_mode_and_determinism_bitwise():
     for k in a:
         assert np.array_equal(a[k], b[k]), k
         assert np.array_equal(a[k], c[k]), k
+    compare(c, norm_oracle(inp, wl, EPS), TOL[wl.dtype], "norm recompute")
 
 
 def test_norm_eps_matters_and_zero_eps():

@@ -206,6 +206,7 @@ def test_int4_decode_modes_bitwise_equal():
     b, _ = run_hip(inp, wl, flags=abi.LMLP_INT4_INKERNEL)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+    compare(b, oracle.forward_backward(oracle_inputs(inp, wl), wl.scale), TOL["bf16"], "int4_ragged_inkernel")
 
 
 @pytest.mark.parametrize("name,flags", [
@@ -226,6 +227,8 @@ def test_recompute_mode_bitwise_equal(name, flags):
     b, _ = run_hip(inp, wl, flags=flags | abi.LMLP_RECOMPUTE_GU)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+    ref = oracle.forward_backward(oracle_inputs(inp, wl), wl.scale)
+    compare(b, ref, TOL[wl.dtype], f"{name}_recompute")
 
 
 def test_int4_dequant_bit_exact_random():
