@@ -249,6 +249,24 @@ int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, con
                         const void* a, const void* b, void* y, void* saved, size_t saved_bytes,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free variant of lora_linear_forward, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Arguments, results, ownership and errors
+ * are those of lora_linear_forward, except that there is no workspace
+ * argument: the forward's workspace is a device array of the library's own,
+ * LMLP_NOALLOC_SCRATCH_BYTES bytes on each GPU the library runs on (set up
+ * on the first call on that GPU, held until the process ends). The call
+ * allocates nothing. Dims whose lora_linear_workspace_bytes(dims, 0) exceeds
+ * the array return LMLP_ERR_UNSUPPORTED before anything is enqueued. Every
+ * call on one GPU uses the same array, which keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that overlap in time on one
+ * GPU (on different streams, or from several threads) race with each other
+ * and must be ordered by the caller. */
+#define LMLP_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lora_linear_forward_noalloc(const lmlp_dims* dims, const void* x, const void* w, const void* w_scales,
+                                const void* a, const void* b, void* y, void* saved, size_t saved_bytes,
+                                void* stream);
+
 /* dx = dy W + s (dy B) A; da = s (dy B)^T x; db = s dy^T (x A^T), for the
  * same x, w, a, b as the forward that filled `saved` (left unchanged).
  * Outputs are overwritten, in dtype, accumulated in fp32. */

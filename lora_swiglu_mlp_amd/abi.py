@@ -71,6 +71,7 @@ _SIGS = {
     "lora_linear_saved_bytes": (_SZ, [ctypes.POINTER(lmlp_dims)]),
     "lora_linear_workspace_bytes": (_SZ, [ctypes.POINTER(lmlp_dims), ctypes.c_int]),
     "lora_linear_forward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 7 + [_SZ, _P, _SZ, _P]),
+    "lora_linear_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 7 + [_SZ, _P]),
     "lora_linear_backward": (ctypes.c_int, [ctypes.POINTER(lmlp_dims)] + [_P] * 7 + [_SZ] + [_P] * 4
                              + [_SZ, _P]),
     "lora_mlp_dequant_int4": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P]),
@@ -269,6 +270,17 @@ def lora_linear_forward(dims, x, w, w_scales, a, b, y, saved, workspace, stream=
         _nbytes(saved) if saved_bytes is None else saved_bytes,
         _ptr(workspace), _nbytes(workspace) if workspace_bytes is None else workspace_bytes, _stream(stream))
     _check(rc, "lora_linear_forward")
+
+
+def lora_linear_forward_noalloc(dims, x, w, w_scales, a, b, y, saved, stream=None, saved_bytes=None):
+    """lora_linear_forward with the library's own scratch as the workspace."""
+    rc = lib().lora_linear_forward_noalloc(
+        ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(w_scales), _ptr(a), _ptr(b), _ptr(y), _ptr(saved),
+        _nbytes(saved) if saved_bytes is None else saved_bytes, _stream(stream))
+    _check(rc, "lora_linear_forward_noalloc")
+
+
+LMLP_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def lora_linear_backward(dims, dy, x, w, w_scales, a, b, saved, dx, da, db, workspace, stream=None,

@@ -34,6 +34,7 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -1592,6 +1593,32 @@ int linear_forward_impl(const Dims& d, const void* x, const void* w, const void*
   return LMLP_OK;
 }
 
+// Scratch of lora_linear_forward_noalloc: one copy of this array per GPU the
+// library runs on, held until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not the device
+// address): each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is used.
+constexpr size_t kNoAllocScratch = size_t(LMLP_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) char scratch[kNoAllocScratch];
+
+int noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LMLP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(LMLP_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LMLP_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return LMLP_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -1603,6 +1630,25 @@ int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, con
   Dims d;
   LMLP_TRY(parse_linear_dims(dims, d));
   return linear_forward_impl(d, x, w, w_scales, a, b, y, saved, saved_bytes, workspace, workspace_bytes, stream);
+}
+
+int lora_linear_forward_noalloc(const lmlp_dims* dims, const void* x, const void* w, const void* w_scales,
+                                const void* a, const void* b, void* y, void* saved, size_t saved_bytes,
+                                void* stream) {
+  g_last_error.clear();
+  Dims d;
+  LMLP_TRY(parse_linear_dims(dims, d));
+  const size_t need = lin_fwd_layout(d).total;
+  if (need > kNoAllocScratch)
+    return fail(LMLP_ERR_UNSUPPORTED, "workspace of these dims (" + std::to_string(need) +
+                                          " bytes) exceeds the library scratch of " +
+                                          std::to_string(kNoAllocScratch) + " bytes");
+  LMLP_TRY(check_device());
+  void* ws = nullptr;
+  LMLP_TRY(noalloc_scratch(&ws));
+  // nothing in the forward workspace has to start at zero: every byte a
+  // kernel reads was written earlier in the same call
+  return linear_forward_impl(d, x, w, w_scales, a, b, y, saved, saved_bytes, ws, kNoAllocScratch, stream);
 }
 
 int lora_linear_backward(const lmlp_dims* dims, const void* dy, const void* x, const void* w, const void* w_scales,

@@ -6,6 +6,7 @@ in this file reaches a kernel launch.
 """
 import ctypes
 import os
+import re
 import subprocess
 
 import numpy as np
@@ -28,7 +29,8 @@ def test_library_exports_every_header_symbol():
                           "lora_mlp_backward", "lora_mlp_dequant_int4", "lora_mlp_status_string",
                           "lora_mlp_last_error", "lora_mlp_profile_begin", "lora_mlp_profile_end",
                           "lora_linear_saved_bytes", "lora_linear_workspace_bytes", "lora_linear_forward",
-                          "lora_linear_backward", "lora_mlp_norm_forward", "lora_mlp_norm_backward",
+                          "lora_linear_backward", "lora_linear_forward_noalloc",
+                          "lora_mlp_norm_forward", "lora_mlp_norm_backward",
                           "lora_moe_saved_bytes", "lora_moe_workspace_bytes", "lora_moe_forward",
                           "lora_moe_backward"}
     L = abi.lib()
@@ -312,3 +314,20 @@ def test_binding_argument_counts_match_the_header():
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(params) == len(args), (name, len(params), len(args))
 
+
+def test_noalloc_linear_rejects_workspace_beyond_the_scratch():
+    """lora_linear_forward_noalloc refuses, before any device call, dims whose
+    forward workspace exceeds the library's scratch array; the header's size
+    is the binding's."""
+    with open(abi.HEADER) as f:
+        m = re.search(r"#define LMLP_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == abi.LMLP_NOALLOC_SCRATCH_BYTES
+    big = dims(tokens=1 << 20, hidden=4096, inter=4096, rank=64, scale=2.0)
+    assert abi.lora_linear_workspace_bytes(big, False) > abi.LMLP_NOALLOC_SCRATCH_BYTES
+    rc = abi.lib().lora_linear_forward_noalloc(ctypes.byref(big), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                               1 << 40, None)
+    assert rc == abi.LMLP_ERR_UNSUPPORTED and "scratch" in abi.lora_mlp_last_error()
+    bad = dims(rank=0)
+    rc = abi.lib().lora_linear_forward_noalloc(ctypes.byref(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                               1 << 40, None)
+    assert rc == abi.LMLP_ERR_INVALID_ARG
