@@ -314,13 +314,13 @@ __device__ __forceinline__ uint4 f32x8_to_bf16(const float (&f)[8]) {
 // [rows][cols] bf16 in LDS (pitch bytes) -> global, 16 bytes per lane,
 // CHUNKS 16-byte chunks per row, NT threads. Rows past m_rows and chunks past
 // the valid columns are not stored.
-template <int CHUNKS>
+template <int CHUNKS, int NTH = NTHREADS>
 __device__ __forceinline__ void lds_rows_to_global(const char* lds, int pitch, int rows, bf16_t* dst,
                                                    int64_t ldc, uint32_t m_rows, int64_t ncols) {
   const int tid = threadIdx.x;
   const int chunk = tid % CHUNKS;
   const int rsub = tid / CHUNKS;
-  constexpr int RSTEP = NTHREADS / CHUNKS;
+  constexpr int RSTEP = NTH / CHUNKS;
   const bool cval = chunk * 8 < ncols;
 #pragma unroll 4
   for (int r = rsub; r < rows; r += RSTEP) {
@@ -370,12 +370,16 @@ __device__ __forceinline__ void epi_preload(const GemmParams& p, const TileCtx& 
   }
 }
 
-// NB: 16-column blocks per wave (8: 256-wide tiles; 4: 128-wide, the plain
-// and backward epilogues only, with the upper half of the staging left idle).
-template <int EPI, int QRB = 0, int NB = 8>
+// NB: 16-column blocks per wave; NTH: threads of the workgroup. Four waves
+// (NTH 256) hold 2 x 2 blocks of 128 x 16 NB: NB 8 for 256-wide tiles, NB 4
+// for 128-wide ones (the plain and backward epilogues only, with the upper
+// half of the staging left idle). Eight waves (NTH 512) hold 2 x 4 blocks of
+// 128 x 64 (NB 4) of a 256-wide tile.
+template <int EPI, int QRB = 0, int NB = 8, int NTH = NTHREADS>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)[8][NB], const TileCtx& t,
                                              int wm, int wn, char* smem, const EpiPre& pre) {
-  static_assert(NB == 8 || EPI != EPI_SWIGLU_FWD, "gate/up tiles are 256 wide");
+  static_assert(NB == 8 || NTH == 512 || EPI != EPI_SWIGLU_FWD, "gate/up tiles are 256 wide");
+  static_assert(NTH == NTHREADS || QRB == 0, "the fused rank products are laid out for four waves");
   const int lrow = t.lane & 15;
   const int lcol = 4 * (t.lane >> 4);
   if (EPI == EPI_STORE) {
@@ -391,20 +395,20 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       }
     __syncthreads();
     bf16_t* C = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
-    lds_rows_to_global<32>(smem, EP_PITCH_C, 256, C, p.ldc, t.m_rows, t.n_rows);
+    lds_rows_to_global<32, NTH>(smem, EP_PITCH_C, 256, C, p.ldc, t.m_rows, t.n_rows);
   } else if (EPI == EPI_SWIGLU_FWD) {
     // tiles (a, 2q) hold G and (a, 2q+1) hold U of gate/up columns
-    // j0 + wn*64 + 16q + lcol .. +3; both go to LDS rounded to bf16, then one
-    // pass per row chunk stores G and U and forms Z = SiLU(G) U from the same
-    // rounded values
+    // j0 + wn*8*NB + 16q + lcol .. +3; both go to LDS rounded to bf16, then
+    // one pass per row chunk stores G and U and forms Z = SiLU(G) U from the
+    // same rounded values
     char* gbuf = smem;
     char* ubuf = smem + 256 * EP_PITCH_GU;
     __syncthreads();
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int off = (wm * 128 + a * 16 + lrow) * EP_PITCH_GU + (wn * 64 + q * 16 + lcol) * 2;
+      for (int q = 0; q < NB / 2; ++q) {
+        const int off = (wm * 128 + a * 16 + lrow) * EP_PITCH_GU + (wn * 8 * NB + q * 16 + lcol) * 2;
         const f32x4_t& g = acc[a][2 * q];
         const f32x4_t& u = acc[a][2 * q + 1];
         *reinterpret_cast<uint2*>(gbuf + off) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
@@ -421,7 +425,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     bf16_t* Up = p.c1 ? static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.j0 + chunk * 8 : nullptr;
     bf16_t* Zp = p.c2 ? static_cast<bf16_t*>(p.c2) + t.m0 * p.ldc + t.j0 + chunk * 8 : nullptr;
 #pragma unroll 4
-    for (int r = rsub; r < 256; r += NTHREADS / 16) {
+    for (int r = rsub; r < 256; r += NTH / 16) {
       const uint4 gv = *reinterpret_cast<const uint4*>(gbuf + r * EP_PITCH_GU + chunk * 16);
       const uint4 uv = *reinterpret_cast<const uint4*>(ubuf + r * EP_PITCH_GU + chunk * 16);
       if (cval && static_cast<uint32_t>(r) < t.m_rows) {
@@ -446,17 +450,19 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     bf16_t* dGp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
     bf16_t* dUp = static_cast<bf16_t*>(p.c1) + t.m0 * p.ldc + t.n0;
     bf16_t* Zp = p.c2 ? static_cast<bf16_t*>(p.c2) + t.m0 * p.ldc + t.n0 : nullptr;
-    // thread -> 8 consecutive columns (chunk) of rows rsub, rsub + 8, ... of a half
+    // thread -> 8 consecutive columns (chunk) of rows rsub, rsub + RS, ... of a half
+    constexpr int RS = NTH / 32;   // rows per step
+    constexpr int RPT = 128 / RS;  // rows per thread in a half
     const int tid = threadIdx.x;
     const int chunk = tid & 31;
     const int rsub = tid >> 5;
     const bool cval = static_cast<uint32_t>(chunk * 8) < t.n_rows;
-    // G and U of one half-tile (16 rows per thread), fetched before they are
+    // G and U of one half-tile (RPT rows per thread), fetched before they are
     // needed; invalid positions read element 0 and are never stored
-    uint4 gv[16], uv[16];
+    uint4 gv[RPT], uv[RPT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 8 * i + rsub;
+    for (int i = 0; i < RPT; ++i) {
+      const int r = RS * i + rsub;
       const int64_t off = (cval && static_cast<uint32_t>(r) < t.m_rows) ? r * p.ldc + chunk * 8 : 0;
       gv[i] = *reinterpret_cast<const uint4*>(Gp + off);
       uv[i] = *reinterpret_cast<const uint4*>(Up + off);
@@ -474,8 +480,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       }
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rl = 8 * i + rsub;  // row within the half
+      for (int i = 0; i < RPT; ++i) {
+        const int rl = RS * i + rsub;  // row within the half
         const int r = h * 128 + rl;   // row within the tile
         const float4 d0 = *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + chunk * 32);
         const float4 d1 = *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + chunk * 32 + 16);
@@ -830,6 +836,165 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_grouped_kernel(GemmGrou
   gemm_bf16_body<NN, EPI, QRB, NB>(p, local, tiles, smem);
 }
 
+// ---- eight waves, two per SIMD, in ping-pong ---------------------------------
+// The same 256x256 output tile, k-tiles, LDS layout and DMA ring as above,
+// with eight waves of 128 x 64 (acc[8][4], 128 fp32 accumulators per lane, so
+// two waves fit one SIMD's registers). Waves 0-3 (group 0) and 4-7 (group 1)
+// have one wave on each SIMD. Every k-tile c is a memory phase followed by a
+// compute phase for each wave:
+//   memory(c):  read this wave's fragments of tile c (8 A, 4 B chunks) from
+//               LDS and issue its 4 DMA instructions of a later tile
+//   compute(c): the 32 MFMAs of tile c on those fragments
+// with a workgroup barrier after each phase. Group 1 passes one extra
+// barrier at the start, so at every barrier-delimited phase one group
+// multiplies while the other reads and issues: each SIMD has one wave
+// issuing MFMAs back to back and one wave issuing memory instructions.
+// The fragment reads of memory(c) are waited for at the start of compute(c),
+// after the barrier, so the memory phase only issues them.
+// Ring (tile c in stage c % 5): group 0 reads tile c in phase 2c, group 1 in
+// 2c+1, and both have consumed it by the barrier ending 2c+2. Group 0
+// fetches the A tile (wave q: rows 64q .. 64q+63) of tile c+3 in memory(c),
+// phase 2c, into the stage tile c-2 left; group 1 fetches the B tile
+// (K-major rows 64q .. 64q+63; N-major k rows 8q .. 8q+7) of tile c+4 in
+// memory(c), phase 2c+1, into the stage tile c-1 left. Tile c+1 is first
+// read in phase 2c+2, so each wave waits for its share of it as late as it
+// can: group 1 at the end of memory(c), group 0 at the end of compute(c)
+// (phase 2c+1), both before that phase's barrier. Four 1 KB instructions per
+// wave per k-tile, as the four-wave kernel's instructions j = 0-3 (A) and
+// 4-7 (B) of wave q.
+constexpr int NT8 = 512;
+constexpr int STAGES8 = 5;
+static_assert(STAGES8 * STAGE_BYTES <= STAGES * STAGE_BYTES, "ring of the eight-wave kernel");
+
+template <bool NN, int EPI>
+__device__ __forceinline__ void dma8_load_seg(Dma& d, const Seg& S, const TileCtx& t, int grp, int q) {
+  TileCtx tq = t;
+  tq.wave = q;
+  dma_load_seg<NN, EPI>(d, S, tq);
+  (void)grp;
+}
+
+// this wave's four DMA instructions of the next k-tile (a uniform branch on
+// the group, so every offset index is a constant)
+template <bool NN, int EPI>
+__device__ __forceinline__ void dma8_issue4(const Dma& d, char* buf, int nk, const TileCtx& t, int grp, int q) {
+  TileCtx tq = t;
+  tq.wave = q;
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_issue<NN, EPI>(d, i, buf, nk, tq);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_issue<NN, EPI>(d, 4 + i, buf, nk, tq);
+  }
+}
+
+template <bool NN, int EPI>
+__device__ __forceinline__ void dma8_advance(Dma& d, int nseg, const Seg& s0, const Seg& s1, const Seg& s2,
+                                             const TileCtx& t, int grp, int q) {
+  ++d.kt;
+  d.k0 += BK;
+  if (d.k0 >= d.S.K && d.seg + 1 < nseg) {
+    d.k0 = 0;
+    ++d.seg;
+    dma8_load_seg<NN, EPI>(d, seg_pick(d.seg, s0, s1, s2), t, grp, q);
+  }
+}
+
+template <bool NN, int EPI, int QRB>
+__device__ __forceinline__ void gemm8_body(const GemmParams& p, int bid, int nblk, char* smem) {
+  TileCtx t;
+  t.lane = threadIdx.x & 63;
+  t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  t.c1 = (t.lane & 3) ^ ((t.lane >> 3) & 3);
+  const int grp = t.wave >> 2;  // ping-pong group, and the operand it fetches
+  const int q = t.wave & 3;
+  const int wm = grp;           // output rows 128 wm .. +127
+  const int wn = q;             // output columns 64 wn .. +63
+  select_tile<EPI, 8>(p, t, bid, nblk);
+  EpiPre pre;
+  epi_preload<EPI, QRB>(p, t, pre);
+
+  const Seg s0 = seg_at(p, 0), s1 = seg_at(p, 1), s2 = seg_at(p, 2);
+  const int nk = (s0.K + BK - 1) / BK + (s1.K + BK - 1) / BK + (s2.K + BK - 1) / BK;
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int lrow = t.lane & 15;
+  const int lgrp = t.lane >> 4;
+  ReadCtx rc;
+  rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
+  rc.rdB = static_cast<uint32_t>((wn * 64 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
+  rc.nsw = 2 * ((lrow >> 2) | ((lgrp & 1) << 2));
+  rc.wc = wn * 8;
+  rc.rdN = static_cast<uint32_t>((lgrp * 8 + (lrow >> 2)) * 512 + ((lrow & 3) >> 1) * 16 + 8 * (lrow & 1));
+
+  // ---- prologue: group 0 issues tiles 0-2, group 1 tiles 0-3; tile 0 landed
+  Dma d;
+  d.seg = 0;
+  d.kt = 0;
+  d.k0 = 0;
+  dma8_load_seg<NN, EPI>(d, s0, t, grp, q);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    dma8_issue4<NN, EPI>(d, smem + s * STAGE_BYTES, nk, t, grp, q);
+    dma8_advance<NN, EPI>(d, p.nseg, s0, s1, s2, t, grp, q);
+  }
+  if (grp == 1) {
+    dma8_issue4<NN, EPI>(d, smem + 3 * STAGE_BYTES, nk, t, grp, q);
+    dma8_advance<NN, EPI>(d, p.nseg, s0, s1, s2, t, grp, q);
+    wait_vmcnt<12>();
+  } else {
+    wait_vmcnt<8>();
+  }
+  __syncthreads();
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  int st = 0;                   // stage of tile c
+  int st_dma = 3 + grp;         // stage of the tile this wave fetches next (c + 3 + grp)
+  for (int c = 0; c < nk; ++c) {
+    const char* buf = smem + st * STAGE_BYTES;
+    uint4 fa[8], fb[4];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, buf, a);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) fb[b] = read_b<NN, 4>(rc, buf, b);
+    dma8_issue4<NN, EPI>(d, smem + st_dma * STAGE_BYTES, nk, t, grp, q);
+    dma8_advance<NN, EPI>(d, p.nseg, s0, s1, s2, t, grp, q);
+    if (grp == 1) wait_vmcnt<12>();  // group 1's share of tile c + 1 landed
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = mma<bf16_t>::step(fb[b], fa[a], acc[a][b]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0) wait_vmcnt<8>();  // group 0's share of tile c + 1 landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    st = st + 1 == STAGES8 ? 0 : st + 1;
+    st_dma = st_dma + 1 == STAGES8 ? 0 : st_dma + 1;
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
+  // the DMA past the last tile wrote zeros into idle stages: let it retire
+  // before the ring is reused
+  wait_vmcnt<0>();
+
+  epilogue_lds<EPI, QRB, 4, NT8>(p, acc, t, wm, wn, smem, pre);
+}
+
+template <bool NN, int EPI, int QRB>
+__global__ __launch_bounds__(NT8, 1) void gemm8_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  gemm8_body<NN, EPI, QRB>(p, blockIdx.x, gridDim.x, smem);
+}
+
 // ---- 4-bit B operand (NT products with 4-bit block weights) ---------------
 // The weight panel arrives as codes and scales and is decoded in LDS:
 //  * ring stage (24 KB): the A tile (16 KB, as in the dense kernel); the codes
@@ -1089,6 +1254,19 @@ static hipError_t launch_t(GemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool NN, int EPI, int QRB = 0>
+static hipError_t launch8_t(GemmParams p, hipStream_t stream) {
+  p.tiles_m = static_cast<int>((p.M + BM - 1) / BM);
+  p.tiles_n = EPI == EPI_SWIGLU_FWD ? static_cast<int>((p.N + BN / 2 - 1) / (BN / 2))
+                                    : static_cast<int>((p.N + BN - 1) / BN);
+  if (p.group_m <= 0) p.group_m = 8;
+  if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
+  const int nblk = p.tiles_m * p.tiles_n;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm8_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream, p);
+  return hipGetLastError();
+}
+
 // Groups whose parameter blocks sit in device memory (more groups than the
 // kernel arguments hold): the same workgroup -> (group, tile) map, with the
 // group starts in the arguments.
@@ -1293,16 +1471,18 @@ hipError_t launch_gemm_q4(const GemmParams& p, int epi, hipStream_t stream) {
 hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t stream) {
   if (epi == EPI_STORE && p.tile_n != 0 && p.tile_n != 128 && p.tile_n != 256) return hipErrorInvalidValue;
   const bool narrow_store = epi == EPI_STORE && p.tile_n == 128;  // 256 x 128 tiles for narrow products
+  // eight-wave ping-pong where it measured faster (gate/up, and dZ without
+  // the fused rank products); the plain products keep four waves
   if (!nn && epi == EPI_STORE)
     return narrow_store ? launch_t<false, EPI_STORE, 0, 4>(p, stream) : launch_t<false, EPI_STORE>(p, stream);
-  if (!nn && epi == EPI_SWIGLU_FWD) return launch_t<false, EPI_SWIGLU_FWD>(p, stream);
+  if (!nn && epi == EPI_SWIGLU_FWD) return launch8_t<false, EPI_SWIGLU_FWD>(p, stream);
   if (nn && epi == EPI_STORE)
     return narrow_store ? launch_t<true, EPI_STORE, 0, 4>(p, stream) : launch_t<true, EPI_STORE>(p, stream);
   if (nn && epi == EPI_SWIGLU_BWD) {
     const bool narrow = p.tile_n == 128;
     if (p.tile_n != 0 && p.tile_n != 128 && p.tile_n != 256) return hipErrorInvalidValue;
     if (p.pj_part0 == nullptr)
-      return narrow ? launch_t<true, EPI_SWIGLU_BWD, 0, 4>(p, stream) : launch_t<true, EPI_SWIGLU_BWD, 0, 8>(p, stream);
+      return narrow ? launch_t<true, EPI_SWIGLU_BWD, 0, 4>(p, stream) : launch8_t<true, EPI_SWIGLU_BWD, 0>(p, stream);
     if (p.pj_r16 == 16)
       return narrow ? launch_t<true, EPI_SWIGLU_BWD, 1, 4>(p, stream) : launch_t<true, EPI_SWIGLU_BWD, 1, 8>(p, stream);
     return hipErrorInvalidValue;

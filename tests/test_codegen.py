@@ -83,3 +83,24 @@ def test_wide_tile_k_loops_keep_accumulators_in_place(gemm_asm):
     # plain NT, gate/up, plain NN, dZ (both epilogues) and the two 4-bit
     # kernels, and the grouped forms of the five 256-wide bf16 kernels
     assert checked >= 12, checked
+
+
+def test_eight_wave_k_loops_keep_accumulators_in_place(gemm_asm):
+    """The eight-wave ping-pong kernels: 128 accumulators per lane, 32 MFMAs
+    per k-tile, no accumulator moves or scratch traffic in the K loop, and at
+    most 256 registers per lane so that two waves fit one SIMD."""
+    ks = _kernels(gemm_asm)
+    names = [n for n in ks if "gemm8_kernel" in n]
+    assert len(names) >= 2, names
+    for name in names:
+        nmfma, seg = _k_loop(ks[name])
+        assert nmfma == 32, (name, nmfma)
+        ops = collections.Counter(i.split()[0] for i in seg)
+        bad = {o: c for o, c in ops.items() if o.startswith(MOVES)}
+        assert not bad, f"{name}: {bad}"
+        assert ops["s_barrier"] == 2, (name, ops["s_barrier"])
+    for name in names:
+        m = re.search(r"\.set " + re.escape(name) + r"\.num_vgpr, (\d+)", gemm_asm)
+        a = re.search(r"\.set " + re.escape(name) + r"\.num_agpr, (\d+)", gemm_asm)
+        assert m and a, name
+        assert int(m.group(1)) + int(a.group(1)) <= 256, (name, m.group(1), a.group(1))
