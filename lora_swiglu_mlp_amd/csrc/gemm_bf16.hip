@@ -344,21 +344,26 @@ __device__ __forceinline__ void lds_barrier() {
 // c ^ (n & 7); what lies past N (columns) or M (tokens) is zero. Rows 0-31:
 // B_g^T, B_u^T over the tile's columns; rows 32-79: P_g^T, P_u^T, Q_d^T over
 // the tile's tokens.
+// 1024 chunks of B^T rows and 1536 of P^T / Q_d^T rows over NTH threads
+template <int NTH = NTHREADS>
 struct EpiPre {
-  uint4 rk[10];
+  static constexpr int NBT = 1024 / NTH;
+  static constexpr int NPT = 1536 / NTH;
+  uint4 rk[NBT + NPT];
 };
 
-template <int EPI, int QRB>
-__device__ __forceinline__ void epi_preload(const GemmParams& p, const TileCtx& t, EpiPre& pre) {
+template <int EPI, int QRB, int NTH = NTHREADS>
+__device__ __forceinline__ void epi_preload(const GemmParams& p, const TileCtx& t, EpiPre<NTH>& pre) {
   if (EPI != EPI_SWIGLU_BWD || QRB != 1) return;
+  constexpr int NBT = EpiPre<NTH>::NBT, NPT = EpiPre<NTH>::NPT;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 10; ++j) {
-    const int idx = tid + NTHREADS * (j < 4 ? j : j - 4);
+  for (int j = 0; j < NBT + NPT; ++j) {
+    const int idx = tid + NTH * (j < NBT ? j : j - NBT);
     const int row = idx >> 5, c = idx & 31;
     const bf16_t* src;
     bool ok;
-    if (j < 4) {
+    if (j < NBT) {
       src = static_cast<const bf16_t*>(row < 16 ? p.pj_b0 : p.pj_b1) + (row & 15) * p.pj_ldb + t.n0 + 8 * c;
       ok = static_cast<uint32_t>(8 * c) < t.n_rows;
     } else {
@@ -377,9 +382,8 @@ __device__ __forceinline__ void epi_preload(const GemmParams& p, const TileCtx& 
 // 128 x 64 (NB 4) of a 256-wide tile.
 template <int EPI, int QRB = 0, int NB = 8, int NTH = NTHREADS>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)[8][NB], const TileCtx& t,
-                                             int wm, int wn, char* smem, const EpiPre& pre) {
+                                             int wm, int wn, char* smem, const EpiPre<NTH>& pre) {
   static_assert(NB == 8 || NTH == 512 || EPI != EPI_SWIGLU_FWD, "gate/up tiles are 256 wide");
-  static_assert(NTH == NTHREADS || QRB == 0, "the fused rank products are laid out for four waves");
   const int lrow = t.lane & 15;
   const int lcol = 4 * (t.lane >> 4);
   if (EPI == EPI_STORE) {
@@ -523,7 +527,10 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     // (bf16) go to one of two LDS buffers per pass, from which the rank
     // products read their operands and the row-contiguous stores of dG and dU
     // are made.
-    constexpr int JB = NB / 2;  // 16-column blocks of column products per wave
+    constexpr int NW = NTH / 64;     // waves: 2 along M, NW / 2 along N
+    constexpr int TW = NB * NW / 2;  // 16-column blocks of the tile
+    constexpr int JB = TW / NW;      // 16-column blocks of column products per wave
+    constexpr int NBT = EpiPre<NTH>::NBT, NPT = EpiPre<NTH>::NPT;
     const bf16_t* Gp = static_cast<const bf16_t*>(p.g_in) + t.m0 * p.ldc + t.n0;
     const bf16_t* Up = static_cast<const bf16_t*>(p.u_in) + t.m0 * p.ldc + t.n0;
     bf16_t* dGp = static_cast<bf16_t*>(p.c0) + t.m0 * p.ldc + t.n0;
@@ -580,10 +587,10 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     for (int a = 0; a < EP_PF - 1; ++a) fetch(a, pg[a], pu[a]);
     lds_barrier();  // every wave is done with the ring
 #pragma unroll
-    for (int j = 0; j < 10; ++j) {
-      const int idx = tid + NTHREADS * (j < 4 ? j : j - 4);
+    for (int j = 0; j < NBT + NPT; ++j) {
+      const int idx = tid + NTH * (j < NBT ? j : j - NBT);
       const int row = idx >> 5, c = idx & 31;
-      char* dst = (j < 4 ? bt : pt) + row * 512 + ((c ^ (row & 7)) << 4);
+      char* dst = (j < NBT ? bt : pt) + row * 512 + ((c ^ (row & 7)) << 4);
       *reinterpret_cast<uint4*>(dst) = pre.rk[j];
     }
     fetch(EP_PF - 1, pg[EP_PF - 1], pu[EP_PF - 1]);
@@ -594,8 +601,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
     for (int j = 0; j < JB; ++j) cg[j] = cu[j] = cz[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // store k (0 .. NB-1) of pass a's dG (k even) or dU (k odd), row-contiguous
     // from the staging: staging row tid / CH + RS (k >> 1), 16-byte chunk tid % CH
-    constexpr int CH = 4 * NB;         // 16-byte chunks of a staging row
-    constexpr int RS = NTHREADS / CH;  // staging rows per step
+    constexpr int CH = 2 * TW;    // 16-byte chunks of a staging row
+    constexpr int RS = NTH / CH;  // staging rows per step
     static_assert(2 * (32 / RS) == NB, "one store per accumulator block");
     const int chunk = tid % CH;
     const bool cv = static_cast<uint32_t>(chunk * 8) < t.n_rows;
@@ -656,17 +663,17 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
       lds_barrier();  // the pass's staging (and, at pass 0, the rank rows) complete
       __builtin_amdgcn_sched_barrier(0);
       // Row products: Q_g[token][n] = sum over the tile's columns of dG * B_g
-      // (B_g^T row n = l & 15), likewise Q_u: wave w takes token block w & 1 of
-      // the pass and product w >> 1; the staged chunk (row l & 15, chunk
-      // 4 ks + l / 16) is the MFMA source as it stands.
-      {
+      // (B_g^T row n = l & 15), likewise Q_u: wave w < 4 takes token block
+      // w & 1 of the pass and product w >> 1; the staged chunk (row l & 15,
+      // chunk 4 ks + l / 16) is the MFMA source as it stands.
+      if (t.wave < 4) {
         const int tb = t.wave & 1;
         const int pr = t.wave >> 1;
         const char* src = (pr ? sub : sgb) + (tb * 16 + lrow) * EP_SP;
         const char* brow = bt + (pr * 16 + lrow) * 512;
         f32x4_t q = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NB; ++ks) {
+        for (int ks = 0; ks < TW / 2; ++ks) {
           const int ch = ks * 4 + lch;
           const uint4 bv = *reinterpret_cast<const uint4*>(brow + ((ch ^ (lrow & 7)) << 4));
           q = mma<bf16_t>::step(bv, *reinterpret_cast<const uint4*>(src + ch * 16), q);
@@ -675,7 +682,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
         // one split-K slice (this tile column)
         const int r = tb * 128 + 16 * a + lrow;
         if (static_cast<uint32_t>(r) < t.m_rows) {
-          const int64_t base = ((p.pj_slice0 + t.n0 / (32 * NB)) * p.pj_T + t.m0 + r) * 16 + 4 * lch;
+          const int64_t base = ((p.pj_slice0 + t.n0 / (16 * TW)) * p.pj_T + t.m0 + r) * 16 + 4 * lch;
           *reinterpret_cast<f32x4_t*>((pr ? p.pj_part1 : p.pj_part0) + base) = q;
         }
       }
@@ -756,7 +763,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmParams& p, int bid, int
   const int wn = t.wave & 1;
 
   select_tile<EPI, NB>(p, t, bid, nblk);
-  EpiPre pre;
+  EpiPre<> pre;
   epi_preload<EPI, QRB>(p, t, pre);
 
   const Seg s0 = seg_at(p, 0), s1 = seg_at(p, 1), s2 = seg_at(p, 2);
@@ -912,8 +919,8 @@ __device__ __forceinline__ void gemm8_body(const GemmParams& p, int bid, int nbl
   const int wm = grp;           // output rows 128 wm .. +127
   const int wn = q;             // output columns 64 wn .. +63
   select_tile<EPI, 8>(p, t, bid, nblk);
-  EpiPre pre;
-  epi_preload<EPI, QRB>(p, t, pre);
+  EpiPre<NT8> pre;
+  epi_preload<EPI, QRB, NT8>(p, t, pre);
 
   const Seg s0 = seg_at(p, 0), s1 = seg_at(p, 1), s2 = seg_at(p, 2);
   const int nk = (s0.K + BK - 1) / BK + (s1.K + BK - 1) / BK + (s2.K + BK - 1) / BK;
@@ -1229,7 +1236,7 @@ __device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
     }
   }
 
-  const EpiPre none{};
+  const EpiPre<> none{};
   epilogue_lds<EPI>(p, acc, t, wm, wn, smem, none);
 }
 
@@ -1484,7 +1491,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t st
     if (p.pj_part0 == nullptr)
       return narrow ? launch_t<true, EPI_SWIGLU_BWD, 0, 4>(p, stream) : launch8_t<true, EPI_SWIGLU_BWD, 0>(p, stream);
     if (p.pj_r16 == 16)
-      return narrow ? launch_t<true, EPI_SWIGLU_BWD, 1, 4>(p, stream) : launch_t<true, EPI_SWIGLU_BWD, 1, 8>(p, stream);
+      return narrow ? launch_t<true, EPI_SWIGLU_BWD, 1, 4>(p, stream) : launch8_t<true, EPI_SWIGLU_BWD, 1>(p, stream);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
