@@ -61,13 +61,20 @@ typedef enum { LMLP_W_DENSE = 0, LMLP_W_INT4_B64 = 1 } lmlp_wfmt;
 
 /* flags */
 #define LMLP_CONSUME_SAVED 0x1u /* backward may overwrite `saved` (saves 2*T*I elements of workspace) */
-/* 4-bit weights only. Without this flag, each call decodes the three weights
- * once into bf16 copies in the workspace and runs the dense bf16 products
- * (fastest; the workspace grows by 2*(2*I*H + H*I) bytes). With it, the
- * forward products decode the 4-bit codes inside their operand staging
- * instead (no bf16 copies in the forward workspace; slower). Backward always
- * uses the bf16 copies for its two products with the transposed weights. */
+/* 4-bit weights: every product (forward gate/up and down, backward dZ and
+ * dX) decodes the 4-bit codes inside its operand staging, so the workspace
+ * holds no bf16 weights (only the block scales as fp32). This is the
+ * default; the flag is accepted and changes nothing. */
 #define LMLP_INT4_INKERNEL 0x2u
+/* 4-bit weights: decode the three weights once per call into bf16 copies in
+ * the workspace and run the dense bf16 products instead (faster products;
+ * each workspace grows by 2*(2*I*H + H*I) bytes, and the decode passes read
+ * the codes and write the copies). Not together with LMLP_INT4_INKERNEL.
+ * Both modes decode by the same rule and give the same weights; the results
+ * agree bit for bit except that at some shapes the backward splits its dZ
+ * product differently, which changes the summation order of the rank
+ * products. */
+#define LMLP_INT4_BF16_COPIES 0x10u
 /* Full recompute (the gradient-checkpointing variant of the fused MLP): the
  * forward keeps only the rank-r projections and the packed adapter factors
  * in `saved` (no G, U: `saved` shrinks by 2*T*I elements of dtype and the
@@ -91,8 +98,8 @@ typedef struct {
   float scale;     /* s = alpha / r, finite */
   int32_t dtype;   /* lmlp_dtype */
   int32_t wfmt;    /* lmlp_wfmt */
-  uint32_t flags;  /* bitwise OR of LMLP_CONSUME_SAVED, LMLP_INT4_INKERNEL, LMLP_RECOMPUTE_GU,
-                      LMLP_RMSNORM, or 0 */
+  uint32_t flags;  /* bitwise OR of LMLP_CONSUME_SAVED, LMLP_INT4_INKERNEL or LMLP_INT4_BF16_COPIES,
+                      LMLP_RECOMPUTE_GU, LMLP_RMSNORM, or 0 */
 } lmlp_dims;
 
 /* Bytes of the forward->backward `saved` buffer: the gate and up
@@ -236,7 +243,7 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
  *
  * dims: `hidden` is the input width (in), `inter` the output width (out);
  * tokens, rank, scale, dtype and wfmt as for the MLP; flags 0 or
- * LMLP_INT4_INKERNEL. Shapes: x [T,in]; w [out,in] (dense: dtype; INT4_B64:
+ * LMLP_INT4_INKERNEL and LMLP_INT4_BF16_COPIES. Shapes: x [T,in]; w [out,in] (dense: dtype; INT4_B64:
  * packed bytes [out,in/2] with w_scales [out,in/64] fp16, else w_scales
  * NULL); a [r,in]; b [out,r]; y, dy [T,out]; dx [T,in]; da [r,in]; db
  * [out,r]. Ownership, streams and errors as for the MLP. */

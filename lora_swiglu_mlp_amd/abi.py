@@ -24,6 +24,7 @@ LMLP_CONSUME_SAVED = 0x1
 LMLP_INT4_INKERNEL = 0x2
 LMLP_RECOMPUTE_GU = 0x4
 LMLP_RMSNORM = 0x8
+LMLP_INT4_BF16_COPIES = 0x10
 
 
 class lmlp_dims(ctypes.Structure):

@@ -1002,88 +1002,6 @@ __global__ __launch_bounds__(NT8, 1) void gemm8_kernel(GemmParams p) {
   gemm8_body<NN, EPI, QRB>(p, blockIdx.x, gridDim.x, smem);
 }
 
-// ---- 4-bit B operand (NT products with 4-bit block weights) ---------------
-// The weight panel arrives as codes and scales and is decoded in LDS:
-//  * ring stage (24 KB): the A tile (16 KB, as in the dense kernel); the codes
-//    [256 packed rows][16 bytes] (one DMA per wave, lane = row); the fp32
-//    scales of the k-tile's 64-block, one 1 KB slot per wave (64 rows, lanes
-//    0-15 carry four rows each, the rest of the slot reads zero).
-//  * two decoded B tiles (16 KB each, the dense K-major layout) outside the
-//    ring. During k-tile kt every thread decodes one packed row of tile kt+2
-//    (a row its own wave fetched, so only its own vmcnt wait is needed) into
-//    buffer kt & 1, while the waves read tile kt+1's B fragments from buffer
-//    (kt + 1) & 1; the barrier of tile kt+1 publishes the decoded rows.
-//    Each packed row is decoded once per workgroup (decoding inside the
-//    fragment reads would repeat it in both waves of a B half; measured
-//    about 8% slower at the Llama-3-8B shapes).
-// Packed row order: gate/up tiles hold gate rows j0 .. j0+127 in packed rows
-// 0-127 and the up rows in 128-255 (waves 0-1 fetch gate, 2-3 up); the
-// decoded tile interleaves them every 16 rows as the dense kernel does.
-// Decoding is the block rule of the 4-bit format: w = bf16_rne(q * scale),
-// exact in fp32 before the one rounding (dq_chunk).
-// The adapter segment (dense bf16) follows the 4-bit loop as a short
-// unpipelined tail.
-constexpr int Q4_CODES = TILE_BYTES;             // offset of the codes in a stage
-constexpr int Q4_SCALES = TILE_BYTES + 4096;     // offset of the scale slots
-constexpr int Q4_STAGE = TILE_BYTES + 8192;      // 24 KB
-constexpr int Q4_STAGES = 5;
-constexpr int Q4_DEC = Q4_STAGES * Q4_STAGE;     // decoded B tiles start here
-constexpr int Q4_LDS0 = Q4_DEC + 2 * TILE_BYTES;  // 152 KB
-constexpr int Q4_LDS = Q4_LDS0 > EP_LDS_BYTES ? Q4_LDS0 : EP_LDS_BYTES;
-
-struct Q4Dma {
-  rsrc_t rA;            // activation panel of this tile row block
-  uint32_t offA[4];
-  uint32_t lda_b;
-  const char* codes;    // first packed row of this wave's 64 rows
-  uint32_t ldq_b;       // bytes per packed row (K / 2)
-  uint32_t qrows;       // valid rows of this wave's 64 (0 or 64)
-  const char* scales;   // fp32 [K/64][N] at this wave's first row
-  uint32_t ld_sc_b;     // bytes per scale block row (N * 4)
-  int k0, kt;
-};
-
-template <int EPI>
-__device__ __forceinline__ void q4_dma_init(Q4Dma& d, const GemmParams& p, const TileCtx& t) {
-  const GemmSeg& g = p.seg[0];
-  d.lda_b = static_cast<uint32_t>(g.lda * 2);
-  d.rA = make_rsrc(static_cast<const char*>(g.a) + t.m0 * d.lda_b, t.m_rows * d.lda_b);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    d.offA[i] = static_cast<uint32_t>(64 * t.wave + 16 * i + (t.lane >> 2)) * d.lda_b + (t.c1 << 4);
-  d.ldq_b = static_cast<uint32_t>(g.ldb / 2);
-  const bool up = EPI == EPI_SWIGLU_FWD && t.wave >= 2;
-  const int64_t row0 = EPI == EPI_SWIGLU_FWD ? t.j0 + 64 * (t.wave & 1) : t.n0 + 64 * t.wave;
-  d.qrows = row0 < p.N ? 64u : 0u;  // N and row0 are multiples of 64
-  d.codes = static_cast<const char*>(up ? g.b1 : g.b0) + row0 * d.ldq_b;
-  d.scales = static_cast<const char*>(up ? g.bs1 : g.bs0) + row0 * 4;
-  d.ld_sc_b = static_cast<uint32_t>(p.N * 4);
-  d.k0 = 0;
-  d.kt = 0;
-}
-
-// DMA instruction j (0..5) of k-tile d.kt into stage `st`: 0-3 the A tile,
-// 4 the codes, 5 the scales. Past the last 4-bit k-tile everything reads zero.
-__device__ __forceinline__ void q4_dma_issue(const Q4Dma& d, int j, char* st, int nkq, const TileCtx& t) {
-  const bool live = d.kt < nkq;
-  if (j < 4) {
-    dma16(d.rA, st + (64 * t.wave + 16 * j) * 64, live ? d.offA[j] : OOB, d.k0 * 2);
-  } else if (j == 4) {
-    const rsrc_t r = make_rsrc(d.codes, (live ? d.qrows : 0u) * d.ldq_b);
-    dma16(r, st + Q4_CODES + t.wave * 1024, static_cast<uint32_t>(t.lane) * d.ldq_b, d.k0 / 2);
-  } else {
-    // the 64-block of this k-tile: one descriptor per block row, so the
-    // range check covers exactly this wave's 64 scales
-    const rsrc_t r = make_rsrc(d.scales + static_cast<int64_t>(d.k0 / 64) * d.ld_sc_b, live ? d.qrows * 4 : 0u);
-    dma16(r, st + Q4_SCALES + t.wave * 1024, t.lane < 16 ? static_cast<uint32_t>(t.lane) * 16 : OOB, 0);
-  }
-}
-
-__device__ __forceinline__ void q4_dma_advance(Q4Dma& d) {
-  ++d.kt;
-  d.k0 += BK;
-}
-
 // decoded-tile row of packed row pr (gate/up: interleave the two panels)
 template <int EPI>
 __device__ __forceinline__ int q4_dense_row(int pr) {
@@ -1092,158 +1010,350 @@ __device__ __forceinline__ int q4_dense_row(int pr) {
   return (r >> 4) * 32 + panel * 16 + (r & 15);
 }
 
-// decode chunk c (8 codes) of this thread's packed row into the decoded tile
-template <int EPI>
-__device__ __forceinline__ void q4_decode_chunk(char* dec, int c, uint32_t codes, float sc, int drow) {
-  *reinterpret_cast<uint4*>(dec + drow * 64 + ((c ^ ((drow >> 1) & 3)) << 4)) = dq_chunk(codes, sc);
+// ---- eight waves with a 4-bit B operand --------------------------------------
+// The leading K segments hold 4-bit block weights (seg.bint4): codes and
+// scales are staged through the ring, and each group decodes its half of a
+// later k-tile in its compute phases into one of three bf16 B tiles outside
+// the ring, laid out exactly as the DMA of a dense B tile would leave it
+// (K-major rows for NT, N-major k rows for NN), so the fragment reads and the
+// MFMA sequence are the dense kernel's and so are the results, bit for bit.
+// Decoding is the block rule of the 4-bit format, w = bf16_rne(q * scale)
+// with the product exact in fp32 (dq_chunk).
+//  * ring stage (22 KB): the A tile (16 KB), the codes (4 KB: NT [256 B rows:
+//    gate rows, then up rows][16 B]; NN [32 k rows][128 B]) and two 1 KB
+//    scale slots (fp32; NT: slot h = B rows 128h .. 128h+127; NN: slot h =
+//    k rows 16h .. 16h+15, four 64-column blocks each)
+//  * three DMA instructions per wave and k-tile: group 0 fetches rows
+//    64q .. 64q+47 of the A tile of tile c+3 in memory(c); group 1 rows
+//    64q+48 .. 64q+63 of the A tile, its quarter of the codes and the scales
+//    (waves 4-5; waves 6-7 issue an instruction whose lanes all fail the
+//    range check into a dummy 1 KB) of tile c+4
+//  * the decode runs in the compute phases, between the MFMAs (one MFMA,
+//    two decode instructions; decoding in the memory phases instead, beside
+//    the other group's MFMAs, measured 5 % slower per product): group 0
+//    decodes its half of tile c+1 in compute(c) (phase 2c+1), group 1 its
+//    half of tile c+2 in compute(c) (phase 2c+2), each into buffer
+//    tile % 3; tile c+1 is first read in phase 2c+2, after both halves. The
+//    codes are in LDS in time because group 1 waited for its share of tile
+//    c+2 at the end of memory(c) (phase 2c+1); buffer (c+1) % 3 last held
+//    tile c-2, consumed by the barrier ending phase 2c-2, buffer (c+2) % 3
+//    tile c-1, consumed by the one ending 2c; every decode write has
+//    completed before its phase's barrier
+//  * the dense segments after the 4-bit ones (the adapter K steps) run after
+//    the loop, one k-tile at a time through stage 0
+constexpr int Q8_CODES = TILE_BYTES;               // codes in a stage
+constexpr int Q8_SC = TILE_BYTES + 4096;           // two scale slots
+constexpr int Q8_STAGE = TILE_BYTES + 6144;        // 22 KB
+constexpr int Q8_DEC = STAGES8 * Q8_STAGE;         // three decoded B tiles
+constexpr int Q8_DUMMY = Q8_DEC + 3 * TILE_BYTES;  // 1 KB target of the idle scale instructions
+static_assert(Q8_DUMMY + 1024 <= STAGES * STAGE_BYTES, "LDS of the 4-bit eight-wave kernel");
+
+// a descriptor known to be uniform, kept in scalar registers
+__device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, uint32_t nbytes) {
+  rsrc_t r = make_rsrc(base, nbytes);
+  r.x = __builtin_amdgcn_readfirstlane(r.x);
+  r.y = __builtin_amdgcn_readfirstlane(r.y);
+  r.z = __builtin_amdgcn_readfirstlane(r.z);
+  r.w = __builtin_amdgcn_readfirstlane(r.w);
+  return r;
 }
 
-__device__ __forceinline__ uint4 read_bq(const ReadCtx& rc, const char* dec, int b) {
-  return *reinterpret_cast<const uint4*>(dec + rc.rdB + b * 1024);
-}
+struct Q8Dma {
+  rsrc_t rA;          // A panel of this tile row block
+  uint32_t offA[3];
+  uint32_t lda_b;
+  rsrc_t rq;          // group 1: this wave's quarter of the codes
+  uint32_t offq;
+  uint32_t ldq_b;     // bytes per code row
+  rsrc_t rs;          // group 1 waves 0-1: scales
+  uint32_t offs;
+  uint32_t ld_sc_b;   // bytes per scale row (NT: block row of N scales; NN: k row)
+  int seg, k0, kt;
+};
 
-// One 4-bit k-tile kt (stage st_cur, decoded B fragments already in fb).
-template <int EPI>
-__device__ __forceinline__ void q4_tile(f32x4_t (&acc)[8][8], uint4 (&fa)[8], const uint4 (&fb)[8],
-                                        uint4 (&fbn)[8], Q4Dma& d, int& st_cur, char* smem, const ReadCtx& rc,
-                                        const TileCtx& t, int nkq, int kt) {
-  const int st_nxt = st_cur + 1 == Q4_STAGES ? 0 : st_cur + 1;
-  const int st_dma = st_cur == 0 ? Q4_STAGES - 1 : st_cur - 1;  // tile kt-1's stage
-  const int st_dec = st_nxt + 1 == Q4_STAGES ? 0 : st_nxt + 1;  // tile kt+2's stage
-  const char* nxt = smem + st_nxt * Q4_STAGE;
-  char* dbuf = smem + st_dma * Q4_STAGE;
-  char* dec_w = smem + Q4_DEC + (kt & 1) * TILE_BYTES;              // tile kt+2, decoded now
-  const char* dec_r = smem + Q4_DEC + ((kt + 1) & 1) * TILE_BYTES;  // tile kt+1
-  mfma_group<8>(acc, 0, fa, fb);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<6>();  // tiles kt+1 and kt+2 landed (this wave); kt+3 may fly
-  __syncthreads();
-  const int pr = 64 * t.wave + t.lane;
-  const char* qsrc = smem + st_dec * Q4_STAGE + Q4_CODES + pr * 16;
-  const char* ssrc = smem + st_dec * Q4_STAGE + Q4_SCALES + t.wave * 1024 + t.lane * 4;
+// descriptors of 4-bit segment S for this wave's role
+template <bool NN, int EPI>
+__device__ __forceinline__ void q8_load_seg(Q8Dma& d, const GemmSeg& g, const TileCtx& t, int grp, int q,
+                                            int64_t Ntot) {
+  // A rows: group 0 instructions i = 0-2 of wave q, group 1 instruction 3
+  d.lda_b = static_cast<uint32_t>(g.lda * 2);
+  d.rA = make_rsrc_u(static_cast<const char*>(g.a) + t.m0 * d.lda_b, t.m_rows * d.lda_b);
 #pragma unroll
-  for (int g = 1; g < 8; ++g) {
-    mfma_group<8>(acc, g, fa, fb);
-    __builtin_amdgcn_sched_barrier(0);
-    if (g <= 6) q4_dma_issue(d, g - 1, dbuf, nkq, t);
-    fa[g - 1] = read_a(rc, nxt, g - 1);
-    if (g <= 4) {
-      fbn[2 * g - 2] = read_bq(rc, dec_r, 2 * g - 2);
-      fbn[2 * g - 1] = read_bq(rc, dec_r, 2 * g - 1);
-    }
-    if (g >= 2 && g <= 5)
-      q4_decode_chunk<EPI>(dec_w, g - 2, *reinterpret_cast<const uint32_t*>(qsrc + 4 * (g - 2)),
-                           *reinterpret_cast<const float*>(ssrc), q4_dense_row<EPI>(pr));
-    __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < 3; ++i)
+    d.offA[i] = static_cast<uint32_t>(64 * q + 16 * (grp == 0 ? i : 3) + (t.lane >> 2)) * d.lda_b + (t.c1 << 4);
+  if (grp == 0) {
+    d.rq = d.rs = d.rA;  // unused by this group
+    d.offq = d.offs = OOB;
+    d.ldq_b = d.ld_sc_b = 0;
+    return;
   }
-  q4_dma_advance(d);
-  fa[7] = read_a(rc, nxt, 7);
-  __builtin_amdgcn_sched_barrier(0);
-  st_cur = st_nxt;
+  d.ldq_b = static_cast<uint32_t>(g.ldb / 2);
+  if (!NN) {
+    // code rows: B tile rows in codes order, 64 per wave
+    const bool fwd = EPI == EPI_SWIGLU_FWD;
+    const int64_t row0 = fwd ? t.j0 + 64 * (q & 1) : t.n0 + 64 * q;
+    const int64_t nvalid = fwd ? static_cast<int64_t>(t.n_rows) - 64 * (q & 1)
+                               : static_cast<int64_t>(t.n_rows) - 64 * q;
+    const uint32_t rows = static_cast<uint32_t>(nvalid < 0 ? 0 : (nvalid > 64 ? 64 : nvalid));
+    const char* cb = static_cast<const char*>(fwd && q >= 2 ? g.b1 : g.b0);
+    d.rq = make_rsrc_u(cb + row0 * d.ldq_b, rows * d.ldq_b);
+    d.offq = static_cast<uint32_t>(t.lane) * d.ldq_b;
+    // scales, block-major fp32 [K/64][Ntot]: slot q (q < 2) = 128 B rows
+    d.ld_sc_b = static_cast<uint32_t>(Ntot * 4);
+    const int64_t srow0 = fwd ? t.j0 : t.n0 + 128 * q;
+    const int64_t svalid = fwd ? static_cast<int64_t>(t.n_rows) : static_cast<int64_t>(t.n_rows) - 128 * q;
+    const char* sb = static_cast<const char*>(fwd && q == 1 ? g.bs1 : g.bs0);
+    d.rs = make_rsrc_u(sb + srow0 * 4, static_cast<uint32_t>(g.K / 64) * d.ld_sc_b);
+    d.offs = (q < 2 && t.lane < 32 && 4 * t.lane < svalid) ? static_cast<uint32_t>(t.lane) * 16 : OOB;
+  } else {
+    // code rows: k rows 8q .. 8q+7, 128 bytes (256 columns) each
+    d.rq = make_rsrc_u(static_cast<const char*>(g.b0) + t.n0 / 2, static_cast<uint32_t>(g.K) * d.ldq_b);
+    const int cchunk = t.lane & 7;
+    d.offq = (32 * cchunk < static_cast<int>(t.n_rows))
+                 ? static_cast<uint32_t>(8 * q + (t.lane >> 3)) * d.ldq_b + cchunk * 16
+                 : OOB;
+    // scales, row-major fp32 [K][ld_sc], ld_sc a multiple of 4: slot q (q < 2)
+    // = k rows 16q .. 16q+15, the tile's four 64-column blocks each
+    const int64_t ld_sc = (Ntot / 64 + 3) / 4 * 4;
+    d.ld_sc_b = static_cast<uint32_t>(ld_sc * 4);
+    d.rs = make_rsrc_u(static_cast<const char*>(g.bs0) + (t.n0 / 64) * 4, static_cast<uint32_t>(g.K) * d.ld_sc_b);
+    d.offs = (q < 2 && t.lane < 16) ? static_cast<uint32_t>(16 * q + t.lane) * d.ld_sc_b : OOB;
+  }
 }
 
-template <int EPI>
-__device__ __forceinline__ void gemm_q4_body(const GemmParams& p) {
-  __shared__ __attribute__((aligned(1024))) char smem[Q4_LDS];
+// this wave's DMA of k-tile d.kt (past the 4-bit tiles: every lane fails the
+// range check and the instructions only write zeros into idle stages)
+template <bool NN>
+__device__ __forceinline__ void q8_issue(const Q8Dma& d, char* st, char* dummy, int nkq, const TileCtx& t, int grp,
+                                         int q) {
+  const bool live = d.kt < nkq;
+  const uint32_t soff = static_cast<uint32_t>(d.k0) * 2;
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) dma16(d.rA, st + (64 * q + 16 * i) * 64, live ? d.offA[i] : OOB, soff);
+  } else {
+    dma16(d.rA, st + (64 * q + 48) * 64, live ? d.offA[0] : OOB, soff);
+    const uint32_t soq = NN ? static_cast<uint32_t>(d.k0) * d.ldq_b : static_cast<uint32_t>(d.k0 / 2);
+    dma16(d.rq, st + Q8_CODES + q * 1024, live ? d.offq : OOB, soq);
+    const uint32_t sos = NN ? static_cast<uint32_t>(d.k0) * d.ld_sc_b : static_cast<uint32_t>(d.k0 / 64) * d.ld_sc_b;
+    dma16(d.rs, q < 2 ? st + Q8_SC + q * 1024 : dummy, live ? d.offs : OOB, sos);
+  }
+}
 
+// this thread's 16 codes and their scale of a staged k-tile (the half its
+// group decodes)
+struct Q8Codes {
+  uint2 codes;
+  float sc;
+};
+template <bool NN>
+__device__ __forceinline__ Q8Codes q8_read_codes(const char* st, int grp, int tid_g) {
+  Q8Codes c;
+  if (NN) {
+    const int kr = 16 * grp + (tid_g >> 4);  // k row
+    const int cp = tid_g & 15;               // pair of 8-column chunks
+    c.codes = *reinterpret_cast<const uint2*>(st + Q8_CODES + kr * 128 + cp * 8);
+    c.sc = *reinterpret_cast<const float*>(st + Q8_SC + grp * 1024 + (kr & 15) * 16 + (cp >> 2) * 4);
+  } else {
+    const int cr = 128 * grp + (tid_g >> 1);  // code row
+    const int h = tid_g & 1;                  // 16 k of the row's 32
+    c.codes = *reinterpret_cast<const uint2*>(st + Q8_CODES + cr * 16 + h * 8);
+    c.sc = *reinterpret_cast<const float*>(st + Q8_SC + grp * 1024 + (cr & 127) * 4);
+  }
+  return c;
+}
+
+// decode them into the dense B tile layout
+template <bool NN, int EPI>
+__device__ __forceinline__ void q8_decode(const Q8Codes& c, char* dec, int grp, int tid_g) {
+  if (NN) {
+    const int kr = 16 * grp + (tid_g >> 4);
+    const int cp = tid_g & 15;
+    const int sw = nn_swz(kr);
+    *reinterpret_cast<uint4*>(dec + kr * 512 + (((2 * cp) ^ sw) << 4)) = dq_chunk(c.codes.x, c.sc);
+    *reinterpret_cast<uint4*>(dec + kr * 512 + (((2 * cp + 1) ^ sw) << 4)) = dq_chunk(c.codes.y, c.sc);
+  } else {
+    const int cr = 128 * grp + (tid_g >> 1);
+    const int h = tid_g & 1;
+    const int drow = q4_dense_row<EPI>(cr);
+    const int sw = (drow >> 1) & 3;
+    *reinterpret_cast<uint4*>(dec + drow * 64 + (((2 * h) ^ sw) << 4)) = dq_chunk(c.codes.x, c.sc);
+    *reinterpret_cast<uint4*>(dec + drow * 64 + (((2 * h + 1) ^ sw) << 4)) = dq_chunk(c.codes.y, c.sc);
+  }
+}
+
+template <bool NN, int EPI, int QRB>
+__device__ __forceinline__ void gemm8q4_body(const GemmParams& p, int bid, int nblk, char* smem) {
   TileCtx t;
   t.lane = threadIdx.x & 63;
   t.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   t.c1 = (t.lane & 3) ^ ((t.lane >> 3) & 3);
-  const int wm = t.wave >> 1;
-  const int wn = t.wave & 1;
-  select_tile<EPI>(p, t, blockIdx.x, gridDim.x);
+  const int grp = t.wave >> 2;
+  const int q = t.wave & 3;
+  const int wm = grp;
+  const int wn = q;
+  const int tid_g = threadIdx.x & 255;
+  select_tile<EPI, 8>(p, t, bid, nblk);
+  EpiPre<NT8> pre;
+  epi_preload<EPI, QRB, NT8>(p, t, pre);
 
-  const int nkq = static_cast<int>(p.seg[0].K / BK);  // K is a multiple of 64: an even count
+  // the 4-bit segments lead; nq (1 or 2) of them
+  int nq = 0;
+  while (nq < p.nseg && nq < 2 && p.seg[nq].bint4) ++nq;
+  int nkq = 0;
+  for (int s2 = 0; s2 < nq; ++s2) nkq += static_cast<int>(p.seg[s2].K / BK);  // multiples of 64
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[8][4];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int lrow = t.lane & 15;
   const int lgrp = t.lane >> 4;
   ReadCtx rc;
   rc.rdA = static_cast<uint32_t>((wm * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
-  rc.rdB = static_cast<uint32_t>((wn * 128 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
-  rc.nsw = 0;
-  rc.rdN = 0;
+  rc.rdB = static_cast<uint32_t>((wn * 64 + lrow) * 64 + ((lgrp ^ ((lrow >> 1) & 3)) << 4));
+  rc.nsw = 2 * ((lrow >> 2) | ((lgrp & 1) << 2));
+  rc.wc = wn * 8;
+  rc.rdN = static_cast<uint32_t>((lgrp * 8 + (lrow >> 2)) * 512 + ((lrow & 3) >> 1) * 16 + 8 * (lrow & 1));
 
-  // ---- prologue: DMA of tiles 0-3, decode of tiles 0 and 1
-  Q4Dma d;
-  q4_dma_init<EPI>(d, p, t);
-#pragma unroll
-  for (int s = 0; s < Q4_STAGES - 1; ++s) {
-#pragma unroll
-    for (int j = 0; j < 6; ++j) q4_dma_issue(d, j, smem + s * Q4_STAGE, nkq, t);
-    q4_dma_advance(d);
-  }
-  wait_vmcnt<6>();  // tiles 0-2 landed (this wave)
-  {
-    const int pr = 64 * t.wave + t.lane;
-    const int drow = q4_dense_row<EPI>(pr);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint4 codes = *reinterpret_cast<const uint4*>(smem + s * Q4_STAGE + Q4_CODES + pr * 16);
-      const float sc = *reinterpret_cast<const float*>(smem + s * Q4_STAGE + Q4_SCALES + t.wave * 1024 + t.lane * 4);
-      char* dec = smem + Q4_DEC + s * TILE_BYTES;
-      q4_decode_chunk<EPI>(dec, 0, codes.x, sc, drow);
-      q4_decode_chunk<EPI>(dec, 1, codes.y, sc, drow);
-      q4_decode_chunk<EPI>(dec, 2, codes.z, sc, drow);
-      q4_decode_chunk<EPI>(dec, 3, codes.w, sc, drow);
+  char* dummy = smem + Q8_DUMMY;
+  // the segments by constant index (held in registers: a runtime index
+  // would load from the argument block, and the wait for that load would
+  // drain the fragment reads in flight)
+  const GemmSeg g0 = p.seg[0], g1 = p.seg[1];
+  Q8Dma d;
+  d.seg = 0;
+  d.kt = 0;
+  d.k0 = 0;
+  int cur_k = static_cast<int>(g0.K);
+  q8_load_seg<NN, EPI>(d, g0, t, grp, q, p.N);
+  // at most two 4-bit segments (dG and dU of the dX product)
+  auto advance = [&]() {
+    ++d.kt;
+    d.k0 += BK;
+    if (d.k0 >= cur_k && d.seg + 1 < nq) {
+      d.k0 = 0;
+      ++d.seg;
+      cur_k = static_cast<int>(g1.K);
+      q8_load_seg<NN, EPI>(d, g1, t, grp, q, p.N);
     }
+  };
+
+  // ---- prologue: A of tiles 0-2, codes of tiles 0-3; tile 0 decoded
+#pragma unroll
+  for (int s2 = 0; s2 < 3; ++s2) {
+    q8_issue<NN>(d, smem + s2 * Q8_STAGE, dummy, nkq, t, grp, q);
+    advance();
   }
+  if (grp == 1) {
+    q8_issue<NN>(d, smem + 3 * Q8_STAGE, dummy, nkq, t, grp, q);
+    advance();
+  }
+  wait_vmcnt<6>();  // group 0: tile 0; group 1: tiles 0 and 1
   __syncthreads();
-  uint4 fa[8], fbA[8], fbB[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) fbA[b] = read_bq(rc, smem + Q4_DEC, b);
-#pragma unroll
-  for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, a);
+  // tile 0 by both groups; group 1's half of tile 1, which group 1 would
+  // have decoded in compute(-1)
+  if (nkq > 0) q8_decode<NN, EPI>(q8_read_codes<NN>(smem, grp, tid_g), smem + Q8_DEC, grp, tid_g);
+  if (grp == 1 && nkq > 1)
+    q8_decode<NN, EPI>(q8_read_codes<NN>(smem + Q8_STAGE, grp, tid_g), smem + Q8_DEC + TILE_BYTES, grp, tid_g);
+  __syncthreads();
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 
-  int st_cur = 0;
-  // one k-tile per trip: with the decode in the groups, a two-tile body
-  // makes the register allocator shuffle the accumulators every trip; the
-  // copy of the next B fragments (32 moves) is the cheaper price
-  for (int kt = 0; kt < nkq; ++kt) {
-    q4_tile<EPI>(acc, fa, fbA, fbB, d, st_cur, smem, rc, t, nkq, kt);
+  int st = 0;                // stage of tile c
+  int st_dma = 3 + grp;      // stage of the tile this wave fetches next
+  int dc = 0;                // decoded buffer of tile c
+  for (int c = 0; c < nkq; ++c) {
+    const char* buf = smem + st * Q8_STAGE;
+    const char* dbuf = smem + Q8_DEC + dc * TILE_BYTES;
+    const int st1 = st + 1 == STAGES8 ? 0 : st + 1;
+    const int dc1 = dc + 1 == 3 ? 0 : dc + 1;
+    uint4 fa[8], fb[4];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) fbA[b] = fbB[b];
+    for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, buf, a);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) fb[b] = read_b<NN, 4>(rc, dbuf - TILE_BYTES, b);
+    q8_issue<NN>(d, smem + st_dma * Q8_STAGE, dummy, nkq, t, grp, q);
+    advance();
+    if (grp == 1) wait_vmcnt<6>();  // tile c + 2 landed (group 1's share)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // compute(c): the MFMAs of tile c and this group's decode of tile td
+    const int td = c + 1 + grp;
+    const int st_td = grp == 0 ? st1 : (st1 + 1 == STAGES8 ? 0 : st1 + 1);
+    const int dc_td = grp == 0 ? dc1 : (dc1 + 1 == 3 ? 0 : dc1 + 1);
+    // (past the last tile the decode writes stale codes into a buffer no
+    // one reads again: the dense tail and the epilogue use other LDS, after
+    // this phase's writes have completed)
+    (void)td;
+    const Q8Codes cd = q8_read_codes<NN>(smem + st_td * Q8_STAGE, grp, tid_g);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = mma<bf16_t>::step(fb[b], fa[a], acc[a][b]);
+    q8_decode<NN, EPI>(cd, smem + Q8_DEC + dc_td * TILE_BYTES, grp, tid_g);
+    // issue order: the code reads first, then one MFMA and two VALU
+    // instructions (the decode) at a time, the decoded chunks' writes last
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 30; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the decode writes complete
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0) wait_vmcnt<6>();  // group 0's share of tile c + 1 landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    st = st1;
+    st_dma = st_dma + 1 == STAGES8 ? 0 : st_dma + 1;
+    dc = dc1;
   }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
   wait_vmcnt<0>();
+  __syncthreads();
 
-  // ---- adapter segment: dense bf16 k-tiles, one at a time
-  if (p.nseg > 1 && p.seg[1].K > 0) {
-    const Seg s1 = seg_at(p, 1);
-    Dma da;
-    da.seg = 1;
-    da.kt = 0;
-    da.k0 = 0;
-    dma_load_seg<false, EPI>(da, s1, t);
-    for (int k0 = 0; k0 < s1.K; k0 += BK) {
-      __syncthreads();  // every wave is done with the LDS it is about to reuse
-      da.k0 = k0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dma_issue<false, EPI>(da, j, smem, 1, t);
+  // ---- the dense segments after the 4-bit ones, one k-tile at a time
+  for (int sg = nq; sg < p.nseg; ++sg) {
+    const Seg S = seg_at(p, sg);
+    Dma dd;
+    dd.seg = sg;
+    dd.kt = 0;
+    dd.k0 = 0;
+    dma8_load_seg<NN, EPI>(dd, S, t, grp, q);
+    for (int k0 = 0; k0 < S.K; k0 += BK) {
+      dd.k0 = k0;
+      dma8_issue4<NN, EPI>(dd, smem, 1, t, grp, q);
       wait_vmcnt<0>();
       __syncthreads();
-#pragma unroll
-      for (int b = 0; b < 8; ++b) fbA[b] = read_b<false>(rc, smem, b);
+      uint4 fa[8], fb[4];
 #pragma unroll
       for (int a = 0; a < 8; ++a) fa[a] = read_a(rc, smem, a);
 #pragma unroll
-      for (int g = 0; g < 8; ++g) mfma_group<8>(acc, g, fa, fbA);
+      for (int b = 0; b < 4; ++b) fb[b] = read_b<NN, 4>(rc, smem, b);
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = mma<bf16_t>::step(fb[b], fa[a], acc[a][b]);
+      __syncthreads();  // every wave is done with stage 0 before the next DMA
     }
   }
 
-  const EpiPre<> none{};
-  epilogue_lds<EPI>(p, acc, t, wm, wn, smem, none);
+  epilogue_lds<EPI, QRB, 4, NT8>(p, acc, t, wm, wn, smem, pre);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_q4_kernel(GemmParams p) {
-  gemm_q4_body<EPI>(p);
+template <bool NN, int EPI, int QRB>
+__global__ __launch_bounds__(NT8, 1) void gemm8q4_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  gemm8q4_body<NN, EPI, QRB>(p, blockIdx.x, gridDim.x, smem);
 }
+
 
 }  // namespace
 
@@ -1456,8 +1566,8 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
   return hipSuccess;
 }
 
-template <int EPI>
-static hipError_t launch_q4(GemmParams p, hipStream_t stream) {
+template <bool NN, int EPI, int QRB = 0>
+static hipError_t launch8q4_t(GemmParams p, hipStream_t stream) {
   p.tiles_m = static_cast<int>((p.M + BM - 1) / BM);
   p.tiles_n = EPI == EPI_SWIGLU_FWD ? static_cast<int>((p.N + BN / 2 - 1) / (BN / 2))
                                     : static_cast<int>((p.N + BN - 1) / BN);
@@ -1465,13 +1575,21 @@ static hipError_t launch_q4(GemmParams p, hipStream_t stream) {
   if (p.group_m > p.tiles_m) p.group_m = p.tiles_m;
   const int nblk = p.tiles_m * p.tiles_n;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_q4_kernel<EPI>), dim3(nblk), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL((gemm8q4_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_q4(const GemmParams& p, int epi, hipStream_t stream) {
-  if (epi == EPI_STORE) return launch_q4<EPI_STORE>(p, stream);
-  if (epi == EPI_SWIGLU_FWD) return launch_q4<EPI_SWIGLU_FWD>(p, stream);
+hipError_t launch_gemm_bf16_q4(const GemmParams& p, int nn, int epi, hipStream_t stream) {
+  if (p.tile_n != 0 && p.tile_n != 256) return hipErrorInvalidValue;  // 256-wide tiles only
+  // one or two leading 4-bit segments, the rest dense
+  if (p.nseg < 1 || !p.seg[0].bint4 || (p.nseg > 2 && p.seg[2].bint4)) return hipErrorInvalidValue;
+  if (!nn && epi == EPI_STORE) return launch8q4_t<false, EPI_STORE>(p, stream);
+  if (!nn && epi == EPI_SWIGLU_FWD) return launch8q4_t<false, EPI_SWIGLU_FWD>(p, stream);
+  if (nn && epi == EPI_STORE) return launch8q4_t<true, EPI_STORE>(p, stream);
+  if (nn && epi == EPI_SWIGLU_BWD) {
+    if (p.pj_part0 == nullptr) return launch8q4_t<true, EPI_SWIGLU_BWD, 0>(p, stream);
+    if (p.pj_r16 == 16) return launch8q4_t<true, EPI_SWIGLU_BWD, 1>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 

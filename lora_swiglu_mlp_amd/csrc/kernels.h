@@ -88,11 +88,14 @@ hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi
 constexpr int kMaxTableGroups = 512;
 hipError_t launch_gemm_bf16_grouped_table(const GemmParams* ps, int n, int nn, int epi, GemmParams* table,
                                           hipStream_t stream);
-// NT products whose segment-0 B operand is 4-bit: seg[0].b0/b1 hold the codes
-// ([N][K/2] bytes, seg[0].ldb = K codes per row), seg[0].bs0/bs1 the block
-// scales as fp32 [K/64][N]; K and N multiples of 64. Segment 1 (the
-// adapter) is dense bf16.
-hipError_t launch_gemm_q4(const GemmParams& p, int epi, hipStream_t stream);
+// Products whose leading K segments have a 4-bit B operand (seg.bint4), on
+// the eight-wave kernel: NT (gate/up, down): codes [N][K/2] bytes (ldb = K),
+// scales fp32 block-major [K/64][N] (bs0/bs1); NN (dZ, dX): codes [K][N/2]
+// bytes (ldb = N), scales fp32 row-major [K][ld_sc] with ld_sc =
+// roundup(N/64, 4) (bs0). K and N multiples of 64; the segments after the
+// 4-bit ones are dense bf16.
+hipError_t launch_gemm_bf16_q4(const GemmParams& p, int nn, int epi, hipStream_t stream);
+
 
 // Row projection, split along K: part[ks][t][n] = sum over k in slice ks of
 // X[t][k] * W[n][k] (slice ks = [ks*kb, (ks+1)*kb)), for up to two jobs per
@@ -209,10 +212,15 @@ struct PackParams {
 hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream);
 
 // fp16 block scales [rows][nb] -> fp32 [nb][ld_dst]
+// fp16 block scales [rows][nb] -> fp32: block-major dst[b][r] (row_major 0,
+// the NT products' layout) or row-major dst[r][b] (row_major 1, the NN
+// products'); ld_dst is the destination row stride in elements
 struct ScalePackJob {
   const __half* src;
   float* dst;
   int64_t rows, nb, ld_dst;
+  int32_t row_major;
+  int32_t pad_;
 };
 struct ScalePackParams {
   ScalePackJob job[3];

@@ -57,7 +57,7 @@ struct Dims {
   float s;
   bool bf16, int4, consume;
   bool recompute;    // G, U not saved: the backward recomputes them
-  bool q4_inkernel;  // forward decodes 4-bit codes inside the GEMM staging
+  bool q4_inkernel;  // 4-bit codes decoded inside the GEMM staging (else into bf16 copies)
   bool norm;         // RMSNorm in front of the MLP (the norm entry points)
   int eb;  // element bytes
 };
@@ -73,8 +73,11 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   if (!std::isfinite(d->scale)) return fail(LMLP_ERR_INVALID_ARG, "scale is not finite");
   if (d->dtype != LMLP_F32 && d->dtype != LMLP_BF16) return fail(LMLP_ERR_INVALID_ARG, "unknown dtype");
   if (d->wfmt != LMLP_W_DENSE && d->wfmt != LMLP_W_INT4_B64) return fail(LMLP_ERR_INVALID_ARG, "unknown wfmt");
-  if (d->flags & ~(LMLP_CONSUME_SAVED | LMLP_INT4_INKERNEL | LMLP_RECOMPUTE_GU | LMLP_RMSNORM))
+  if (d->flags & ~(LMLP_CONSUME_SAVED | LMLP_INT4_INKERNEL | LMLP_RECOMPUTE_GU | LMLP_RMSNORM |
+                   LMLP_INT4_BF16_COPIES))
     return fail(LMLP_ERR_INVALID_ARG, "unknown flag bits");
+  if ((d->flags & LMLP_INT4_INKERNEL) && (d->flags & LMLP_INT4_BF16_COPIES))
+    return fail(LMLP_ERR_INVALID_ARG, "LMLP_INT4_INKERNEL and LMLP_INT4_BF16_COPIES together");
   if (d->rank > 256) return fail(LMLP_ERR_UNSUPPORTED, "rank > 256");
   const int ch = d->dtype == LMLP_BF16 ? 8 : 4;
   if (d->hidden % ch || d->inter % ch)
@@ -99,16 +102,17 @@ int parse_dims(const lmlp_dims* d, Dims& o) {
   o.int4 = d->wfmt == LMLP_W_INT4_B64;
   o.recompute = (d->flags & LMLP_RECOMPUTE_GU) != 0;
   o.consume = !o.recompute && (d->flags & LMLP_CONSUME_SAVED) != 0;
-  o.q4_inkernel = o.int4 && (d->flags & LMLP_INT4_INKERNEL) != 0;
+  o.q4_inkernel = o.int4 && (d->flags & LMLP_INT4_BF16_COPIES) == 0;
   o.norm = (d->flags & LMLP_RMSNORM) != 0;
   o.eb = o.bf16 ? 2 : 4;
   return LMLP_OK;
 }
 
 // The linear takes the MLP's dims (hidden = in, inter = out); of the flags
-// only LMLP_INT4_INKERNEL applies to it.
+// only LMLP_INT4_INKERNEL and LMLP_INT4_BF16_COPIES apply to it.
 int parse_linear_dims(const lmlp_dims* d, Dims& o) {
-  if (d && (d->flags & ~LMLP_INT4_INKERNEL)) return fail(LMLP_ERR_INVALID_ARG, "flags other than INT4_INKERNEL");
+  if (d && (d->flags & ~(LMLP_INT4_INKERNEL | LMLP_INT4_BF16_COPIES)))
+    return fail(LMLP_ERR_INVALID_ARG, "flags other than INT4_INKERNEL, INT4_BF16_COPIES");
   return parse_dims(d, o);
 }
 
@@ -239,6 +243,10 @@ int64_t colproj_tr(int64_t T, int ntb) {
 }
 int64_t ld_tok(const Dims& d) { return (d.T + 63) / 64 * 64; }  // token-contiguous rows
 
+// fp32 scales per row of a 4-bit weight in the NN products' layout: the
+// in/64 blocks padded to a multiple of 4 (16-byte rows)
+int64_t sc_ld4(int64_t in) { return (in / 64 + 3) / 4 * 4; }
+
 struct FwdLayout {
   size_t z, aext_gu, aext_d, bext_d, rp_part, sc_g, sc_u, sc_d;
   size_t wq_g, wq_u, wq_d, xn, total;
@@ -267,7 +275,7 @@ FwdLayout fwd_layout(const Dims& d) {
 
 struct BwdLayout {
   size_t g_rc, u_rc, dg, du, z, qd, aext_d, qgu, aext_gu;
-  size_t rp_a, rp_b, pguT, pdT, qdT, qguT, wq_g, wq_u, wq_d;
+  size_t rp_a, rp_b, pguT, pdT, qdT, qguT, wq_g, wq_u, wq_d, scn_g, scn_u, scn_d, sct_g, sct_u;
   size_t part_dg, part_du, part_z, part_x, part_dy, xn, total;
   int ntb;
   int64_t tr;
@@ -297,10 +305,19 @@ BwdLayout bwd_layout(const Dims& d) {
   L.pdT = c.take(d.r16 * trow);
   L.qdT = c.take(d.r16 * trow);
   L.qguT = c.take(2 * d.r16 * trow);
-  // 4-bit weights: bf16 copies for the NN products (decoded once per call)
-  L.wq_g = d.int4 ? c.take(size_t(d.I) * d.H * 2) : 0;
-  L.wq_u = d.int4 ? c.take(size_t(d.I) * d.H * 2) : 0;
-  L.wq_d = d.int4 ? c.take(size_t(d.H) * d.I * 2) : 0;
+  // 4-bit weights: bf16 copies for the products (decoded once per call), or
+  // with the decode in the GEMM staging the fp32 block scales: row-major with
+  // rows padded to 4 blocks for the NN products, block-major for the gate/up
+  // product the recompute mode reruns
+  const bool cp = d.int4 && !d.q4_inkernel, ink = d.q4_inkernel;
+  L.wq_g = cp ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.wq_u = cp ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.wq_d = cp ? c.take(size_t(d.H) * d.I * 2) : 0;
+  L.scn_g = ink ? c.take(size_t(d.I) * sc_ld4(d.H) * 4 + 16) : 0;
+  L.scn_u = ink ? c.take(size_t(d.I) * sc_ld4(d.H) * 4 + 16) : 0;
+  L.scn_d = ink ? c.take(size_t(d.H) * sc_ld4(d.I) * 4 + 16) : 0;
+  L.sct_g = ink && d.recompute ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
+  L.sct_u = ink && d.recompute ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
   const size_t nsl_i = fused_q(d) ? size_t(col_slices(d)) : size_t(L.ntb);
   L.part_dg = c.take(nsl_i * d.I * d.r16 * 4);
   L.part_du = c.take(nsl_i * d.I * d.r16 * 4);
@@ -341,7 +358,7 @@ LinFwdLayout lin_fwd_layout(const Dims& d) {
   return L;
 }
 struct LinBwdLayout {
-  size_t q, aext, qT, rp_part, part_x, part_dy, wq, total;
+  size_t q, aext, qT, rp_part, part_x, part_dy, wq, scn, total;
   int ntb;
   int64_t tr;
 };
@@ -356,7 +373,10 @@ LinBwdLayout lin_bwd_layout(const Dims& d) {
   L.rp_part = c.take(rp_part_bytes(d, d.I, int(d.r16)));
   L.part_x = c.take(size_t(L.ntb) * d.H * d.r16 * 4);
   L.part_dy = c.take(size_t(L.ntb) * d.I * d.r16 * 4);
-  L.wq = d.int4 ? c.take(size_t(d.I) * d.H * 2) : 0;  // bf16 copy of W for the NN product
+  // 4-bit W: a bf16 copy for the NN product, or (decoded in the staging) its
+  // fp32 scales, row-major with rows padded to 4 blocks
+  L.wq = d.int4 && !d.q4_inkernel ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.scn = d.q4_inkernel ? c.take(size_t(d.I) * sc_ld4(d.H) * 4 + 16) : 0;
   L.total = c.off;
   return L;
 }
@@ -607,9 +627,16 @@ char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 
 // bf16 products take the LDS-DMA kernels (4-bit weights decoded in the
 // staging: the decoding variant); fp32 products the general kernel.
+// products with 4-bit B segments: the eight-wave decoding kernel, 256-wide tiles
+hipError_t run_q4(const GemmParams& p, int nn, int epi, hipStream_t st) {
+  GemmParams q = p;
+  q.tile_n = 0;
+  return launch_gemm_bf16_q4(q, nn, epi, st);
+}
+
 hipError_t run_gemm(const GemmParams& p, const Dims& d, int nn, int epi, hipStream_t st) {
   if (!d.bf16) return launch_gemm_f32(p, nn, epi, st);
-  if (p.seg[0].bint4) return launch_gemm_q4(p, epi, st);
+  if (p.seg[0].bint4) return run_q4(p, nn, epi, st);
   return launch_gemm_bf16(p, nn, epi, st);
 }
 
@@ -993,7 +1020,13 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   const void* wg = w_gate;
   const void* wu = w_up;
   const void* wd = w_down;
-  if (d.int4) {
+  const bool ink = d.q4_inkernel;
+  float* scn_g = ink ? reinterpret_cast<float*>(at(workspace, BL.scn_g)) : nullptr;
+  float* scn_u = ink ? reinterpret_cast<float*>(at(workspace, BL.scn_u)) : nullptr;
+  float* scn_d = ink ? reinterpret_cast<float*>(at(workspace, BL.scn_d)) : nullptr;
+  float* sct_g = ink && d.recompute ? reinterpret_cast<float*>(at(workspace, BL.sct_g)) : nullptr;
+  float* sct_u = ink && d.recompute ? reinterpret_cast<float*>(at(workspace, BL.sct_u)) : nullptr;
+  if (d.int4 && !ink) {
     char* wq_g = at(workspace, BL.wq_g);
     char* wq_u = at(workspace, BL.wq_u);
     char* wq_d = at(workspace, BL.wq_d);
@@ -1003,6 +1036,21 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     wg = wq_g;
     wu = wq_u;
     wd = wq_d;
+  }
+  if (ink) {  // scales for the decode inside the GEMM staging
+    ScalePackParams sp{};
+    sp.job[0] = {static_cast<const __half*>(w_gate_scales), scn_g, I, H / 64, sc_ld4(H), 1, 0};
+    sp.job[1] = {static_cast<const __half*>(w_up_scales), scn_u, I, H / 64, sc_ld4(H), 1, 0};
+    sp.job[2] = {static_cast<const __half*>(w_down_scales), scn_d, H, I / 64, sc_ld4(I), 1, 0};
+    sp.njobs = 3;
+    LMLP_SIDE("pack(scales)", launch_scale_pack(sp, st));
+    if (d.recompute) {
+      ScalePackParams sq{};
+      sq.job[0] = {static_cast<const __half*>(w_gate_scales), sct_g, I, H / 64, I, 0, 0};
+      sq.job[1] = {static_cast<const __half*>(w_up_scales), sct_u, I, H / 64, I, 0, 0};
+      sq.njobs = 2;
+      LMLP_SIDE("pack(scales)", launch_scale_pack(sq, st));
+    }
   }
 
   RowProjParams rp{};
@@ -1030,7 +1078,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
     // free until finish(Q_gu) overwrites it.
     GemmParams gp{};
     gp.nseg = 2;
-    gp.seg[0] = seg(x, H, wg, wu, H, H);
+    gp.seg[0] = seg(x, H, wg, wu, H, H, ink, sct_g, sct_u);
     gp.seg[1] = seg(aext_gu, 2 * r16, at(saved, SL.bext_g), at(saved, SL.bext_u), 2 * r16, 2 * r16);
     gp.M = T;
     gp.N = I;
@@ -1044,7 +1092,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
 
   GemmParams gz{};
   gz.nseg = 2;
-  gz.seg[0] = seg(dy, H, wd, nullptr, I, H);
+  gz.seg[0] = seg(dy, H, wd, nullptr, I, H, ink, scn_d, nullptr);
   gz.seg[1] = seg(aext_d, r16, ad_pad, nullptr, I, r16);
   gz.M = T;
   gz.N = I;
@@ -1075,7 +1123,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   }
   // columns in 256-wide tiles; grouped launches balance over the experts, and
   // one split for all of them keeps their phases aligned
-  const int64_t n1 = ex.phase < 0 ? dz_split(d) : d.I;
+  const int64_t n1 = ex.phase < 0 && !ink ? dz_split(d) : d.I;
   if (n1 > 0) {
     GemmParams g1 = gz;
     g1.N = n1;
@@ -1119,8 +1167,8 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
 
   GemmParams gx{};
   gx.nseg = 3;
-  gx.seg[0] = seg(dG, I, wg, nullptr, H, I);
-  gx.seg[1] = seg(dU, I, wu, nullptr, H, I);
+  gx.seg[0] = seg(dG, I, wg, nullptr, H, I, ink, scn_g, nullptr);
+  gx.seg[1] = seg(dU, I, wu, nullptr, H, I, ink, scn_u, nullptr);
   gx.seg[2] = seg(aext_gu, 2 * r16, agu_pad, nullptr, H, 2 * r16);
   gx.M = T;
   gx.N = H;
@@ -1294,7 +1342,7 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, Gem
       if (!ex[k].sunk || done[k]) continue;
       any = true;
       if (!ex[k].groupable) {
-        LMLP_LAUNCH(ex[k].name, ex[k].gp.seg[0].bint4 ? launch_gemm_q4(ex[k].gp, ex[k].epi, st)
+        LMLP_LAUNCH(ex[k].name, ex[k].gp.seg[0].bint4 ? run_q4(ex[k].gp, ex[k].nn, ex[k].epi, st)
                                                       : launch_gemm_f32(ex[k].gp, ex[k].nn, ex[k].epi, st));
         done[k] = true;
         continue;
@@ -1702,7 +1750,13 @@ int lora_linear_backward(const lmlp_dims* dims, const void* dy, const void* x, c
   const int64_t ldT = ld_tok(d);
 
   const void* wk = w;
-  if (d.int4) {
+  float* scn = d.q4_inkernel ? reinterpret_cast<float*>(at(workspace, BL.scn)) : nullptr;
+  if (d.q4_inkernel) {
+    ScalePackParams sp{};
+    sp.job[0] = {static_cast<const __half*>(w_scales), scn, Out, In / 64, sc_ld4(In), 1, 0};
+    sp.njobs = 1;
+    LMLP_LAUNCH("pack(scales)", launch_scale_pack(sp, st));
+  } else if (d.int4) {
     char* wq = at(workspace, BL.wq);
     LMLP_LAUNCH("dequant(W)", launch_dequant_int4(w, w_scales, Out, In, wq, st));
     wk = wq;
@@ -1720,7 +1774,7 @@ int lora_linear_backward(const lmlp_dims* dims, const void* dy, const void* x, c
 
   GemmParams gx{};
   gx.nseg = 2;
-  gx.seg[0] = seg(dy, Out, wk, nullptr, In, Out);
+  gx.seg[0] = seg(dy, Out, wk, nullptr, In, Out, d.q4_inkernel, scn, nullptr);
   gx.seg[1] = seg(aext, r16, a_pad, nullptr, In, r16);
   gx.M = T;
   gx.N = In;

@@ -514,8 +514,13 @@ __global__ __launch_bounds__(256) void scale_pack_kernel(ScalePackParams p) {
   const int64_t n = jb.rows * jb.nb;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < n;
        idx += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t b = idx / jb.rows, r = idx % jb.rows;
-    jb.dst[b * jb.ld_dst + r] = __half2float(jb.src[r * jb.nb + b]);
+    if (jb.row_major) {
+      const int64_t r = idx / jb.nb, b = idx % jb.nb;
+      jb.dst[r * jb.ld_dst + b] = __half2float(jb.src[idx]);
+    } else {
+      const int64_t b = idx / jb.rows, r = idx % jb.rows;
+      jb.dst[b * jb.ld_dst + r] = __half2float(jb.src[r * jb.nb + b]);
+    }
   }
 }
 

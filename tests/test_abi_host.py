@@ -94,7 +94,8 @@ def test_workspace_sizes_positive_and_consume_flag_saves_memory():
     (dict(scale=float("inf")), abi.LMLP_ERR_INVALID_ARG),
     (dict(dtype=7), abi.LMLP_ERR_INVALID_ARG),
     (dict(wfmt=3), abi.LMLP_ERR_INVALID_ARG),
-    (dict(flags=0x10), abi.LMLP_ERR_INVALID_ARG),
+    (dict(flags=0x20), abi.LMLP_ERR_INVALID_ARG),
+    (dict(flags=abi.LMLP_INT4_INKERNEL | abi.LMLP_INT4_BF16_COPIES), abi.LMLP_ERR_INVALID_ARG),
     (dict(flags=0x8), abi.LMLP_ERR_INVALID_ARG),  # the norm flag on the plain entry point
     (dict(rank=257), abi.LMLP_ERR_UNSUPPORTED),
     (dict(hidden=132), abi.LMLP_ERR_UNSUPPORTED),          # not a multiple of 8 for bf16
@@ -331,3 +332,19 @@ def test_noalloc_linear_rejects_workspace_beyond_the_scratch():
     rc = abi.lib().lora_linear_forward_noalloc(ctypes.byref(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                                                1 << 40, None)
     assert rc == abi.LMLP_ERR_INVALID_ARG
+
+
+def test_int4_workspaces_hold_no_bf16_weights_by_default():
+    """4-bit weights decoded in the GEMM staging (the default): the forward
+    and backward workspaces of the Llama-3-8B MLP are within a few MB of the
+    dense bf16 ones (fp32 block scales only); the decoded-copy mode adds the
+    2 (2 I H + H I) bytes of bf16 weights to each."""
+    T, H, I, r = 4096, 4096, 14336, 16
+    dense = dims(tokens=T, hidden=H, inter=I, rank=r, scale=1.0)
+    q4 = dims(tokens=T, hidden=H, inter=I, rank=r, scale=1.0, wfmt="int4_b64")
+    cp = dims(tokens=T, hidden=H, inter=I, rank=r, scale=1.0, wfmt="int4_b64", flags=abi.LMLP_INT4_BF16_COPIES)
+    for bwd in (False, True):
+        wd = abi.lora_mlp_workspace_bytes(dense, bwd)
+        wq = abi.lora_mlp_workspace_bytes(q4, bwd)
+        assert wd < wq < wd + 16 * 2**20, (bwd, wd, wq)
+        assert abi.lora_mlp_workspace_bytes(cp, bwd) >= wd + 2 * (2 * I * H + H * I), bwd

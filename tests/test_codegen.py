@@ -73,28 +73,43 @@ def test_wide_tile_k_loops_keep_accumulators_in_place(gemm_asm):
         assert loop is not None, name
         nmfma, seg = loop
         # 256-wide tiles: 8 x 8 MFMAs per wave and k-tile, two k-tiles per
-        # iteration; the 4-bit kernels: one k-tile per iteration
+        # iteration
         if nmfma not in (64, 128) or ("gemm_bf16" in name and nmfma != 128):
             continue
         ops = collections.Counter(i.split()[0] for i in seg)
         bad = {o: c for o, c in ops.items() if o.startswith(MOVES)}
         assert not bad, f"{name}: {bad}"
         checked += 1
-    # plain NT, gate/up, plain NN, dZ (both epilogues) and the two 4-bit
-    # kernels, and the grouped forms of the five 256-wide bf16 kernels
+    # plain NT, gate/up, plain NN, dZ (both epilogues), their grouped and
+    # table-driven forms (the four-wave kernels)
     assert checked >= 12, checked
 
 
+def _dma_loops(body):
+    """Backward-branch loops that issue LDS DMA (the K loops of the staged kernels)."""
+    labels = {l[:-1]: k for k, l in enumerate(body) if re.match(r"^\.LBB\w+:$", l)}
+    out = []
+    for k, l in enumerate(body):
+        m = re.match(r"s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", l)
+        if m and m.group(1) in labels and labels[m.group(1)] < k:
+            seg = body[labels[m.group(1)]:k]
+            if any(x.startswith("buffer_load_dwordx4") and x.endswith("lds") for x in seg):
+                out.append(seg)
+    return out
+
+
 def test_eight_wave_k_loops_keep_accumulators_in_place(gemm_asm):
-    """The eight-wave ping-pong kernels: 128 accumulators per lane, 32 MFMAs
-    per k-tile, no accumulator moves or scratch traffic in the K loop, and at
-    most 256 registers per lane so that two waves fit one SIMD."""
+    """The eight-wave ping-pong kernels (dense and 4-bit): 128 accumulators per
+    lane, 32 MFMAs per k-tile, no accumulator moves or scratch traffic in the
+    K loop, and at most 256 registers per lane so that two waves fit one
+    SIMD."""
     ks = _kernels(gemm_asm)
-    names = [n for n in ks if "gemm8_kernel" in n]
-    assert len(names) >= 2, names
+    names = [n for n in ks if "gemm8_kernel" in n or "gemm8q4_kernel" in n]
+    assert len(names) >= 8, names
     for name in names:
-        nmfma, seg = _k_loop(ks[name])
-        assert nmfma == 32, (name, nmfma)
+        loops = [x for x in _dma_loops(ks[name]) if sum("v_mfma" in i for i in x) == 32]
+        assert loops, name
+        seg = max(loops, key=len)
         ops = collections.Counter(i.split()[0] for i in seg)
         bad = {o: c for o, c in ops.items() if o.startswith(MOVES)}
         assert not bad, f"{name}: {bad}"

@@ -18,12 +18,12 @@ from lmlp_testutil import TOL, compare, oracle_inputs, run_hip
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["llama3_8b", "llama3_8b_int4", "llama3_8b_int4_inkernel", "tinyllama_long",
+@pytest.mark.parametrize("name", ["llama3_8b", "llama3_8b_int4", "llama3_8b_int4_copies", "tinyllama_long",
                                   "qwen2_7b"])
 def test_fullsize_parity(name):
     flags = 0
-    if name.endswith("_inkernel"):  # 4-bit codes decoded inside the forward GEMM staging
-        name, flags = name[: -len("_inkernel")], abi.LMLP_INT4_INKERNEL
+    if name.endswith("_copies"):  # 4-bit weights decoded into bf16 copies first
+        name, flags = name[: -len("_copies")], abi.LMLP_INT4_BF16_COPIES
     wl = I.WORKLOADS[name]
     print(f"[case] {name} T={wl.tokens} H={wl.hidden} I={wl.inter} r={wl.rank} s={wl.scale} "
           f"{wl.dtype} {wl.wfmt}", flush=True)

@@ -53,15 +53,15 @@ def test_linear_parity(name):
 
 @pytest.mark.parametrize("name", ["int4_small", "int4_ragged"])
 def test_linear_int4_modes_bitwise_equal(name):
-    """Decoding inside the forward product's staging gives the same weights as
-    the bf16 copy, in the same k order."""
+    """Decoding inside the products' staging (the default) gives the same
+    weights as the bf16 copy, in the same k order."""
     wl = workload(name)
     inp = I.make_linear_inputs(wl)
     a, _ = run_hip_linear(inp, wl)
-    b, _ = run_hip_linear(inp, wl, flags=abi.LMLP_INT4_INKERNEL)
+    b, _ = run_hip_linear(inp, wl, flags=abi.LMLP_INT4_BF16_COPIES)
     for k in LIN_KEYS:
         assert np.array_equal(a[k], b[k]), k
-    compare(b, _oracle(inp, wl), TOL[wl.dtype], "linear " + name + " in-kernel")
+    compare(b, _oracle(inp, wl), TOL[wl.dtype], "linear " + name + " copies")
 
 
 def test_linear_empty_batch_gives_zero_adapter_gradients():

@@ -114,18 +114,17 @@ def test_moe_fullsize_parity(name):
     compare(got, ref, TOL[wl.dtype], name)
 
 
-def test_moe_int4_inkernel_mode_bitwise_equal():
-    """4-bit weights decoded inside the forward products' staging (those
+def test_moe_int4_decode_modes_bitwise_equal():
+    """4-bit weights decoded inside the products' staging (the default; those
     products are launched expert by expert, not grouped) give the outputs of
-    the decoded-copy mode bit for bit; that mode is checked against the
-    oracle above."""
+    the decoded-copy mode bit for bit; both are checked against the oracle."""
     wl = workload("int4_routed")
     inp, off = I.make_moe_inputs(wl)
     a, _ = run_hip_moe(inp, off, wl)
-    b, _ = run_hip_moe(inp, off, wl, flags=abi.LMLP_INT4_INKERNEL)
+    b, _ = run_hip_moe(inp, off, wl, flags=abi.LMLP_INT4_BF16_COPIES)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
-    compare(b, _oracle(inp, off, wl), TOL[wl.dtype], "moe int4 in-kernel")
+    compare(b, _oracle(inp, off, wl), TOL[wl.dtype], "moe int4 copies")
 
 
 def test_moe_more_experts_than_one_grouped_launch_holds():

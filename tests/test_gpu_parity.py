@@ -187,32 +187,34 @@ def _dequant_gpu(packed, scales, out, inn):
 
 
 @pytest.mark.parametrize("name", ["int4_small", "int4_ragged"])
-def test_int4_inkernel_decode_parity(name):
-    """4-bit weights decoded inside the forward GEMMs' operand staging."""
+def test_int4_bf16_copies_parity(name):
+    """4-bit weights decoded once into bf16 copies (LMLP_INT4_BF16_COPIES)
+    instead of inside the GEMM staging."""
     wl = workload(name)
-    print(f"[case] {name} in-kernel decode", flush=True)
+    print(f"[case] {name} bf16 copies", flush=True)
     inp = I.make_inputs(wl)
-    got, _ = run_hip(inp, wl, flags=abi.LMLP_INT4_INKERNEL)
+    got, _ = run_hip(inp, wl, flags=abi.LMLP_INT4_BF16_COPIES)
     ref = oracle.forward_backward(oracle_inputs(inp, wl), wl.scale)
-    compare(got, ref, TOL["bf16"], name + "_inkernel")
+    compare(got, ref, TOL["bf16"], name + "_copies")
 
 
 def test_int4_decode_modes_bitwise_equal():
-    """Decoding in the staging and decoding to bf16 copies first give the same
-    weights, fed to the same MFMA sequence in the same k order."""
+    """Decoding in the staging (all four products) and decoding to bf16
+    copies first give the same weights, fed to the same MFMA sequence in the
+    same k order."""
     wl = workload("int4_ragged")
     inp = I.make_inputs(wl)
     a, _ = run_hip(inp, wl)
-    b, _ = run_hip(inp, wl, flags=abi.LMLP_INT4_INKERNEL)
+    b, _ = run_hip(inp, wl, flags=abi.LMLP_INT4_BF16_COPIES)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
-    compare(b, oracle.forward_backward(oracle_inputs(inp, wl), wl.scale), TOL["bf16"], "int4_ragged_inkernel")
+    compare(b, oracle.forward_backward(oracle_inputs(inp, wl), wl.scale), TOL["bf16"], "int4_ragged_copies")
 
 
 @pytest.mark.parametrize("name,flags", [
     ("tiny_fp32", 0), ("f32_ragged", 0), ("bf16_ragged", 0), ("bf16_multi", 0), ("bf16_rank64", 0),
     ("bf16_dz_tail", 0), ("bf16_rank8", abi.LMLP_CONSUME_SAVED), ("int4_ragged", 0),
-    ("int4_ragged", abi.LMLP_INT4_INKERNEL)])
+    ("int4_ragged", abi.LMLP_INT4_BF16_COPIES)])
 def test_recompute_mode_bitwise_equal(name, flags):
     """LMLP_RECOMPUTE_GU (the gradient-checkpointing variant): the backward
     recomputes G and U with the forward's gate/up product from the same
