@@ -134,6 +134,36 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
+def mfma_ceiling(reps: int = 40, iters: int = 4096) -> dict:
+    """The bf16 matrix-core ceiling measured on this GPU: the library's probe
+    (8 waves per compute unit, 32 independent 16x16x32 MFMAs each on random
+    operand bits, no memory traffic) launched `reps` times on the current
+    stream; the rate is the median of the last 10 launches, after the clock
+    has settled under the load."""
+    import torch
+    from lora_swiglu_mlp_amd import abi
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    gen = torch.Generator().manual_seed(1)
+    ops = torch.randn(ncu * 8 * 768 * 8, generator=gen).to(torch.bfloat16).to("cuda:0")
+    sink = torch.empty(ncu * 512, dtype=torch.float32, device="cuda:0")
+    flops = ncu * 8 * iters * 32 * 16384
+    ms = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        abi.lora_mlp_mfma_probe(ops, sink, ncu, iters)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    last = sorted(ms[-10:])
+    med = (last[4] + last[5]) / 2
+    return {"tflops": flops / (med * 1e-3) / 1e12, "ms_per_launch": med, "launches": reps,
+            "first_launch_tflops": flops / (ms[0] * 1e-3) / 1e12,
+            "what": f"{ncu} workgroups x 8 waves x {iters} x 32 MFMA 16x16x32 bf16 on random operands, "
+                    f"median of the last 10 of {reps} launches"}
+
+
 def copy_probe(mib: int):
     """A plain elementwise pass over `mib` MiB (reads and writes that many
     bytes): the reference reading for the HBM byte counters."""
@@ -485,6 +515,13 @@ def main():
                            "unit": "TFLOP/s", "frac": achieved / peak,
                            "traffic": measured_traffic(dom, wl.name)}
         out["gemms"] = res["gemms"]
+        if wl.dtype == "bf16":
+            ceil = mfma_ceiling()
+            out["mfma_ceiling"] = ceil
+            out["roofline"]["frac_of_mfma_ceiling"] = achieved / ceil["tflops"]
+            for g in out["gemms"].values():
+                g["frac_of_mfma_ceiling"] = g["tflops"] / ceil["tflops"]
+            out["pct_of_mfma_ceiling"] = 100.0 * tflops / ceil["tflops"]
         out["fwd_kernel_ms"] = res["fwd_kernel_ms"]
         out["bwd_kernel_ms"] = out["kernel_ms_per_step"] - out["fwd_kernel_ms"]
 

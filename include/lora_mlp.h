@@ -305,6 +305,20 @@ typedef struct {
 int lora_mlp_profile_begin(void);
 int lora_mlp_profile_end(lmlp_kernel_time* out, int capacity, int* count);
 
+/* The bf16 matrix-core ceiling the GEMMs are measured against (measurement
+ * support): one launch of `blocks` workgroups of eight waves, each wave
+ * running `iters` rounds of 32 independent 16x16x32 bf16 MFMAs (fp32
+ * accumulation) on operands read once from `operands`, device memory of at
+ * least blocks * 8 * 768 * 16 bytes holding the bits to multiply (random
+ * data keeps the arithmetic as busy as a real product's), with no other
+ * memory traffic. It performs blocks * 8 * iters * 32 * 16384 FLOPs and
+ * writes one float per thread to `sink` (blocks * 512 floats) so that
+ * nothing is optimised away. Time it with events on `stream`. Returns
+ * LMLP_OK, LMLP_ERR_INVALID_ARG (null pointer, blocks or iters < 1,
+ * operand_bytes too small) or LMLP_ERR_HIP. */
+int lora_mlp_mfma_probe(const void* operands, size_t operand_bytes, float* sink, int blocks, int iters,
+                        void* stream);
+
 /* Static name of a status code. */
 const char* lora_mlp_status_string(int status);
 

@@ -79,6 +79,7 @@ _SIGS = {
     "lora_mlp_profile_begin": (ctypes.c_int, []),
     "lora_mlp_profile_end": (ctypes.c_int, [ctypes.POINTER(lmlp_kernel_time), ctypes.c_int,
                                             ctypes.POINTER(ctypes.c_int)]),
+    "lora_mlp_mfma_probe": (ctypes.c_int, [_P, _SZ, _P, ctypes.c_int, ctypes.c_int, _P]),
     "lora_mlp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lora_mlp_last_error": (ctypes.c_char_p, []),
 }
@@ -310,3 +311,10 @@ def lora_mlp_profile_end(capacity: int = 65536):
     n = ctypes.c_int(0)
     _check(lib().lora_mlp_profile_end(buf, capacity, ctypes.byref(n)), "lora_mlp_profile_end")
     return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(n.value)]
+
+
+def lora_mlp_mfma_probe(operands, sink, blocks: int, iters: int, stream=None):
+    """One launch of the matrix-core ceiling probe (see the header)."""
+    rc = lib().lora_mlp_mfma_probe(_ptr(operands), _nbytes(operands), _ptr(sink), int(blocks), int(iters),
+                                   _stream(stream))
+    _check(rc, "lora_mlp_mfma_probe")

@@ -1355,7 +1355,47 @@ __global__ __launch_bounds__(NT8, 1) void gemm8q4_kernel(GemmParams p) {
 }
 
 
+// The matrix-core ceiling: each wave multiplies 8 A and 4 B operand chunks of
+// random bits into 32 accumulators, rotating the A chunks every round so the
+// inputs keep changing, with no memory traffic inside the loop.
+__global__ __launch_bounds__(NT8, 1) void mfma_probe_kernel(const uint4* __restrict__ ops, float* sink, int iters) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint4* src = ops + (static_cast<int64_t>(blockIdx.x) * 8 + wave) * 768;
+  uint4 a[8], b[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = src[i * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = src[512 + i * 64 + lane];
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma<bf16_t>::step(b[j], a[i], acc[i][j]);
+    const uint4 t0 = a[0];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) a[i] = a[i + 1];
+    a[7] = make_uint4(t0.y, t0.z, t0.w, t0.x);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
+  sink[static_cast<int64_t>(blockIdx.x) * NT8 + threadIdx.x] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(const void* ops, float* sink, int blocks, int iters, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(NT8), 0, stream, static_cast<const uint4*>(ops), sink,
+                     iters);
+  return hipGetLastError();
+}
 
 template <bool NN, int EPI, int QRB = 0, int NB = 8>
 static hipError_t launch_t(GemmParams p, hipStream_t stream) {

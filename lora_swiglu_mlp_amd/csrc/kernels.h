@@ -229,6 +229,10 @@ struct ScalePackParams {
 };
 hipError_t launch_scale_pack(const ScalePackParams& p, hipStream_t stream);
 
+// bf16 matrix-core ceiling: blocks x 8 waves x iters x 32 MFMA 16x16x32 on
+// operands read once from `ops` (blocks * 8 * 768 uint4)
+hipError_t launch_mfma_probe(const void* ops, float* sink, int blocks, int iters, hipStream_t stream);
+
 // 4-bit block weight -> bf16 (same decode as the GEMM loaders).
 hipError_t launch_dequant_int4(const void* packed, const void* scales, int64_t out, int64_t in,
                                void* w_bf16, hipStream_t stream);

@@ -1813,6 +1813,19 @@ int lora_mlp_dequant_int4(const void* packed, const void* scales, int64_t out, i
   return LMLP_OK;
 }
 
+int lora_mlp_mfma_probe(const void* operands, size_t operand_bytes, float* sink, int blocks, int iters,
+                        void* stream) {
+  g_last_error.clear();
+  LMLP_TRY(need_ptr(operands, "operands"));
+  LMLP_TRY(need_ptr(sink, "sink"));
+  if (blocks < 1 || iters < 1) return fail(LMLP_ERR_INVALID_ARG, "blocks and iters must be >= 1");
+  if (operand_bytes < size_t(blocks) * 8 * 768 * 16)
+    return fail(LMLP_ERR_INVALID_ARG, "operands smaller than blocks * 8 * 768 * 16 bytes");
+  LMLP_TRY(check_device());
+  return hip_rc(launch_mfma_probe(operands, sink, blocks, iters, static_cast<hipStream_t>(stream)),
+                "mfma probe launch");
+}
+
 int lora_mlp_profile_begin(void) {
   g_last_error.clear();
   g_prof.recs.clear();

@@ -29,7 +29,7 @@ def test_library_exports_every_header_symbol():
                           "lora_mlp_backward", "lora_mlp_dequant_int4", "lora_mlp_status_string",
                           "lora_mlp_last_error", "lora_mlp_profile_begin", "lora_mlp_profile_end",
                           "lora_linear_saved_bytes", "lora_linear_workspace_bytes", "lora_linear_forward",
-                          "lora_linear_backward", "lora_linear_forward_noalloc",
+                          "lora_linear_backward", "lora_linear_forward_noalloc", "lora_mlp_mfma_probe",
                           "lora_mlp_norm_forward", "lora_mlp_norm_backward",
                           "lora_moe_saved_bytes", "lora_moe_workspace_bytes", "lora_moe_forward",
                           "lora_moe_backward"}
@@ -348,3 +348,11 @@ def test_int4_workspaces_hold_no_bf16_weights_by_default():
         wq = abi.lora_mlp_workspace_bytes(q4, bwd)
         assert wd < wq < wd + 16 * 2**20, (bwd, wd, wq)
         assert abi.lora_mlp_workspace_bytes(cp, bwd) >= wd + 2 * (2 * I * H + H * I), bwd
+
+
+def test_mfma_probe_validates_before_launching():
+    L = abi.lib()
+    assert L.lora_mlp_mfma_probe(None, 1 << 20, FAKE, 1, 1, None) == abi.LMLP_ERR_INVALID_ARG
+    assert L.lora_mlp_mfma_probe(FAKE, 1 << 20, FAKE, 0, 1, None) == abi.LMLP_ERR_INVALID_ARG
+    assert L.lora_mlp_mfma_probe(FAKE, 1 << 20, FAKE, 1, 0, None) == abi.LMLP_ERR_INVALID_ARG
+    assert L.lora_mlp_mfma_probe(FAKE, 8 * 768 * 16 - 1, FAKE, 1, 1, None) == abi.LMLP_ERR_INVALID_ARG
