@@ -461,6 +461,9 @@ def main():
                     help="RMSNorm (eps 1e-5) in front of the MLP: the library's norm entry points")
     ap.add_argument("--no-configs", action="store_true",
                     help="measure only the named workload (no sub-lines for the other workloads)")
+    ap.add_argument("--int4-copies", action="store_true",
+                    help="4-bit weights decoded once per call into bf16 workspace copies "
+                         "(LMLP_INT4_BF16_COPIES) instead of inside the products' operand staging")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -487,6 +490,8 @@ def main():
         copy_probe(args.copy_probe_mib)
     norm_eps = I.NORM_EPS if args.norm else None
     flags = abi.LMLP_RECOMPUTE_GU if args.recompute else 0
+    if args.int4_copies:
+        flags |= abi.LMLP_INT4_BF16_COPIES
     res = measure_mlp(wl, args.steps, args.warmup, flags, norm_eps, profile=not args.no_profile)
     T, H, Iw, r = wl.tokens, wl.hidden, wl.inter, wl.rank
     ms = res["ms"]
@@ -502,7 +507,10 @@ def main():
                       "alpha": wl.alpha, "weights": wl.wfmt, "parallelism": "single-gpu",
                       "saved": "recompute G, U" if args.recompute else "G, U",
                       "norm": f"rmsnorm eps={norm_eps}" if args.norm else "none"},
-           "tflops": tflops, "pct_of_peak": 100.0 * tflops / peak}
+           "tflops": tflops, "pct_of_peak": 100.0 * tflops / peak,
+           "workspace_bytes": res["workspace_bytes"], "saved_bytes": res["saved_bytes"]}
+    if wl.wfmt != "dense":
+        out["config"]["int4_decode"] = "bf16 copies" if args.int4_copies else "in the operand staging"
 
     if "kern" in res:
         kern = res["kern"]
@@ -533,15 +541,19 @@ def main():
     # the other workloads of the metric, one sub-line each (fewer steps)
     if args.workload == "llama3_8b" and not (args.recompute or args.norm or args.no_configs):
         subs = {}
-        for name in ("tiny_fp32", "qwen2_7b", "tinyllama_long", "llama3_8b_int4"):
-            w2 = I.WORKLOADS[name]
-            r2 = measure_mlp(w2, min(args.steps, 10), min(args.warmup, 3), 0, None, profile=not args.no_profile)
+        for name in ("tiny_fp32", "qwen2_7b", "tinyllama_long", "llama3_8b_int4", "llama3_8b_int4 (bf16 copies)"):
+            copies = name.endswith("(bf16 copies)")
+            w2 = I.WORKLOADS[name.split()[0]]
+            r2 = measure_mlp(w2, min(args.steps, 10), min(args.warmup, 3),
+                             abi.LMLP_INT4_BF16_COPIES if copies else 0, None, profile=not args.no_profile)
             f2 = mlp_flops(w2, None)
             tf2 = f2 / (r2["ms"] * 1e-3) / 1e12
             e = {"ms_per_step": r2["ms"], "tokens_per_s": w2.tokens / (r2["ms"] * 1e-3), "tflops": tf2,
                  "pct_of_peak": 100.0 * tf2 / PEAK_TFLOPS[w2.dtype], "dtype": w2.dtype, "weights": w2.wfmt,
                  "tokens": w2.tokens, "hidden": w2.hidden, "inter": w2.inter, "rank": w2.rank,
-                 "alpha": w2.alpha}
+                 "alpha": w2.alpha, "workspace_bytes": r2["workspace_bytes"], "saved_bytes": r2["saved_bytes"]}
+            if w2.wfmt != "dense":
+                e["int4_decode"] = "bf16 copies" if copies else "in the operand staging"
             if "gemms" in r2:
                 e["gemms"] = {g: round(v["frac"], 4) for g, v in r2["gemms"].items()}
                 e["fwd_kernel_ms"] = r2["fwd_kernel_ms"]
@@ -601,9 +613,11 @@ def measure_mlp(wl, steps: int, warmup: int, flags: int, norm_eps, profile: bool
         step()
     torch.cuda.synchronize()
     res = {"ms": (time.perf_counter() - t0) * 1e3 / steps, "inp": inp}
+    res["workspace_bytes"] = max(abi.lora_mlp_workspace_bytes(m.dims, False),
+                                 abi.lora_mlp_workspace_bytes(m.dims, True))
+    res["saved_bytes"] = abi.lora_mlp_saved_bytes(m.dims)
     if profile:
         ncu = torch.cuda.get_device_properties(0).multi_processor_count
-        dz_cols = dz_split(T, Iw, ncu) if wl.dtype == "bf16" else None
         nprof = max(1, min(steps, 10))
         abi.lora_mlp_profile_begin()
         for _ in range(nprof):
@@ -614,6 +628,8 @@ def measure_mlp(wl, steps: int, warmup: int, flags: int, norm_eps, profile: bool
             a = agg.setdefault(name, [0.0, 0])
             a[0] += t
             a[1] += 1
+        # the library's column split of the dZ product, when it ran as two launches
+        dz_cols = dz_split(T, Iw, ncu) if "gemm(dZ tail)" in agg else None
         kern = {}
         for name, (tot, cnt) in agg.items():
             avg = tot / cnt

@@ -251,7 +251,11 @@ size_t lora_linear_saved_bytes(const lmlp_dims* dims);
 size_t lora_linear_workspace_bytes(const lmlp_dims* dims, int is_backward);
 
 /* y = x W^T + s (x A^T) B^T. `saved` receives x A^T (fp32) and the adapter
- * factors in the layouts the backward reads. */
+ * factors in the layouts the backward reads. A bf16 product with dense
+ * weights whose 256 x 256 output tiles would not fill the GPU once (few
+ * tokens or a narrow output, e.g. a k/v projection) is split along K: the
+ * splits' fp32 partials (in the workspace, at most 64 MiB) are summed in a
+ * fixed order, so results stay bitwise reproducible. */
 int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, const void* w_scales,
                         const void* a, const void* b, void* y, void* saved, size_t saved_bytes,
                         void* workspace, size_t workspace_bytes, void* stream);
@@ -269,7 +273,7 @@ int lora_linear_forward(const lmlp_dims* dims, const void* x, const void* w, con
  * (nothing in it needs to start at zero): calls that overlap in time on one
  * GPU (on different streams, or from several threads) race with each other
  * and must be ordered by the caller. */
-#define LMLP_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define LMLP_NOALLOC_SCRATCH_BYTES (96u << 20)
 int lora_linear_forward_noalloc(const lmlp_dims* dims, const void* x, const void* w, const void* w_scales,
                                 const void* a, const void* b, void* y, void* saved, size_t saved_bytes,
                                 void* stream);

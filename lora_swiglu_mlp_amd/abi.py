@@ -282,7 +282,7 @@ def lora_linear_forward_noalloc(dims, x, w, w_scales, a, b, y, saved, stream=Non
     _check(rc, "lora_linear_forward_noalloc")
 
 
-LMLP_NOALLOC_SCRATCH_BYTES = 32 << 20
+LMLP_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 def lora_linear_backward(dims, dy, x, w, w_scales, a, b, saved, dx, da, db, workspace, stream=None,

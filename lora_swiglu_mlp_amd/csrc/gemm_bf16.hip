@@ -386,7 +386,34 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, f32x4_t (&acc)
   static_assert(NB == 8 || NTH == 512 || EPI != EPI_SWIGLU_FWD, "gate/up tiles are 256 wide");
   const int lrow = t.lane & 15;
   const int lcol = 4 * (t.lane >> 4);
-  if (EPI == EPI_STORE) {
+  if (EPI == EPI_STORE_F32) {
+    // a split-K partial, the accumulators unrounded: staged through LDS one
+    // 128-row half at a time (as the backward stages dZ), then stored
+    // row-contiguous, 16 bytes (four columns) per lane
+    float* C = static_cast<float*>(p.c0) + t.m0 * p.ldc + t.n0;
+    constexpr int CH = 8 * NB;  // 16-byte chunks of a staged row
+    __syncthreads();            // every wave is done with the ring
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            *reinterpret_cast<f32x4_t*>(smem + (a * 16 + lrow) * EP_PITCH_DZ + (wn * 16 * NB + b * 16 + lcol) * 4) =
+                acc[a][b];
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < 128 * CH; i += NTH) {
+        const int rl = i / CH, c = i % CH;
+        const int r = h * 128 + rl;
+        if (static_cast<uint32_t>(r) < t.m_rows && static_cast<uint32_t>(4 * c) < t.n_rows)
+          *reinterpret_cast<float4*>(C + r * p.ldc + 4 * c) =
+              *reinterpret_cast<const float4*>(smem + rl * EP_PITCH_DZ + c * 16);
+      }
+      __syncthreads();
+    }
+  } else if (EPI == EPI_STORE) {
     __syncthreads();  // every wave is done with the ring
 #pragma unroll
     for (int a = 0; a < 8; ++a)
@@ -1659,6 +1686,11 @@ hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi
   if (n <= 0) return hipSuccess;
   const GemmParams& p = ps[0];  // every product of one call is of one kind
   if (!nn && epi == EPI_STORE) return launch_grouped_t<false, EPI_STORE>(ps, n, stream);
+  if (!nn && epi == EPI_STORE_F32) {  // split-K partials: 256 x 256 tiles, N a multiple of 4
+    for (int i = 0; i < n; ++i)
+      if ((ps[i].tile_n != 0 && ps[i].tile_n != 256) || ps[i].N % 4 || ps[i].ldc % 4) return hipErrorInvalidValue;
+    return launch_grouped_t<false, EPI_STORE_F32>(ps, n, stream);
+  }
   if (!nn && epi == EPI_SWIGLU_FWD) return launch_grouped_t<false, EPI_SWIGLU_FWD>(ps, n, stream);
   if (nn && epi == EPI_STORE) return launch_grouped_t<true, EPI_STORE>(ps, n, stream);
   if (nn && epi == EPI_SWIGLU_BWD) {

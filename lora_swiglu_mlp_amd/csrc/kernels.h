@@ -7,7 +7,8 @@
 
 namespace lmlp {
 
-enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
+// EPI_STORE_F32: the fp32 accumulators themselves (a split-K partial), no rounding.
+enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2, EPI_STORE_F32 = 3 };
 
 // One K segment of a GEMM: C += A[:, seg] * B[seg, :].
 struct GemmSeg {
@@ -232,6 +233,10 @@ hipError_t launch_scale_pack(const ScalePackParams& p, hipStream_t stream);
 // bf16 matrix-core ceiling: blocks x 8 waves x iters x 32 MFMA 16x16x32 on
 // operands read once from `ops` (blocks * 8 * 768 uint4)
 hipError_t launch_mfma_probe(const void* ops, float* sink, int blocks, int iters, hipStream_t stream);
+
+// Split-K finish: y[i] = bf16_rne(part[0][i] + part[1][i] + ... + part[nsplit-1][i]),
+// summed in that order; part holds nsplit slices of n fp32 values (n a multiple of 4).
+hipError_t launch_splitk_sum(const float* part, int nsplit, int64_t n, void* y_bf16, hipStream_t stream);
 
 // 4-bit block weight -> bf16 (same decode as the GEMM loaders).
 hipError_t launch_dequant_int4(const void* packed, const void* scales, int64_t out, int64_t in,

@@ -214,6 +214,23 @@ int store_tile_n(const Dims& d, int64_t M, int64_t N) {
   return tiles < device_cus() ? 128 : 0;
 }
 
+// K splits of the linear's bf16 forward product when its 256 x 256 tiles
+// would fill less than one wave of the device: each split runs every tile
+// over a slice of K and stores fp32 partials, which a sum kernel adds in
+// split order. At most 8 splits, each over at least 512 of K, partials of at
+// most 64 MiB, N a multiple of 4. Dense weights only. 1 = no split.
+int linear_splitk(const Dims& d) {
+  if (!d.bf16 || d.int4 || d.T == 0 || d.I % 4) return 1;
+  const int64_t tiles = ((d.T + 255) / 256) * ((d.I + 255) / 256);
+  const int64_t ncu = device_cus();
+  if (tiles >= ncu) return 1;
+  int64_t s = (ncu + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, 8);
+  s = std::min<int64_t>(s, d.H / 512);
+  while (s > 1 && s * d.T * d.I * 4 > (int64_t(64) << 20)) --s;
+  return s > 1 ? static_cast<int>(s) : 1;
+}
+
 // Columns of the dZ GEMM (bf16) covered by 256-wide tiles; the rest, when the
 // last wave of workgroups would be at most half full, goes to a second launch
 // of 128-wide tiles that fill one wave with twice as many half-size tiles.
@@ -345,7 +362,8 @@ LinSavedLayout lin_saved_layout(const Dims& d) {
   return L;
 }
 struct LinFwdLayout {
-  size_t aext, rp_part, sc, wq, total;
+  size_t aext, rp_part, sc, wq, ypart, total;
+  int nsplit;
 };
 LinFwdLayout lin_fwd_layout(const Dims& d) {
   Carver c;
@@ -354,6 +372,8 @@ LinFwdLayout lin_fwd_layout(const Dims& d) {
   L.rp_part = c.take(rp_part_bytes(d, d.H, int(d.r16)));
   L.sc = d.q4_inkernel ? c.take(size_t(d.H / 64) * d.I * 4 + 16) : 0;
   L.wq = d.int4 && !d.q4_inkernel ? c.take(size_t(d.I) * d.H * 2) : 0;
+  L.nsplit = linear_splitk(d);
+  L.ypart = L.nsplit > 1 ? c.take(size_t(L.nsplit) * d.T * d.I * 4) : 0;  // fp32 split-K partials of y
   L.total = c.off;
   return L;
 }
@@ -1636,6 +1656,27 @@ int linear_forward_impl(const Dims& d, const void* x, const void* w, const void*
   gy.ldc = Out;
   gy.c0 = y;
   gy.group_m = 8;
+  if (FL.nsplit > 1) {
+    // split s multiplies K range [k0, k1) of x W^T (multiples of 32), the last
+    // split also the adapter segment; one grouped launch, then the ordered sum
+    const int S = FL.nsplit;
+    float* part = reinterpret_cast<float*>(at(workspace, FL.ypart));
+    GemmParams gs[8];
+    const int64_t kt = (In + 31) / 32;
+    for (int i = 0; i < S; ++i) {
+      const int64_t k0 = kt * i / S * 32, k1 = std::min<int64_t>(kt * (i + 1) / S * 32, In);
+      gs[i] = gy;
+      gs[i].seg[0] = seg(static_cast<const char*>(x) + k0 * eb, In, static_cast<const char*>(wk) + k0 * eb, nullptr,
+                         In, k1 - k0);
+      gs[i].nseg = i == S - 1 ? 2 : 1;
+      if (i != S - 1) gs[i].seg[1] = GemmSeg{};
+      gs[i].c0 = part + i * T * Out;
+      gs[i].tile_n = 0;
+    }
+    LMLP_LAUNCH("gemm(y)", launch_gemm_bf16_grouped(gs, S, 0, EPI_STORE_F32, st));
+    LMLP_LAUNCH("sum(y)", launch_splitk_sum(part, S, T * Out, y, st));
+    return LMLP_OK;
+  }
   gy.tile_n = store_tile_n(d, T, Out);
   LMLP_LAUNCH("gemm(y)", run_gemm(gy, d, 0, EPI_STORE, st));
   return LMLP_OK;

@@ -538,6 +538,25 @@ __global__ __launch_bounds__(256) void dequant_int4_kernel(const uint8_t* packed
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-K finish: four consecutive outputs per thread, the slices summed in
+// slice order, one rounding to bf16.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ part, int nsplit, int64_t n4,
+                                                         int64_t stride, uint2* __restrict__ y) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float4 acc = reinterpret_cast<const float4*>(part)[i];
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 v = reinterpret_cast<const float4*>(part + s * stride)[i];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    y[i] = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+  }
+}
+
 int grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
   if (g > 65535) g = 65535;
@@ -752,6 +771,17 @@ hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream) 
   dim3 grid(grid_for((maxn + 3) / 4), p.njobs);
   if (elem_bytes == 2) hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(pack_kernel<uint32_t>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_sum(const float* part, int nsplit, int64_t n, void* y_bf16, hipStream_t stream) {
+  if (nsplit < 1 || n % 4) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  const int64_t n4 = n / 4;
+  int64_t g = (n4 + 255) / 256;
+  if (g > 4096) g = 4096;
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3(static_cast<int>(g)), dim3(256), 0, stream, part, nsplit, n4, n,
+                     static_cast<uint2*>(y_bf16));
   return hipGetLastError();
 }
 

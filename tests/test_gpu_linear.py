@@ -25,6 +25,10 @@ CASES = {
     "bf16_rank256": (128, 256, 256, 256, 256.0, "bf16", "dense"),
     "bf16_one_token": (1, 64, 128, 8, 16.0, "bf16", "dense"),
     "bf16_min_width": (40, 8, 8, 2, 4.0, "bf16", "dense"),
+    # few output tiles: the forward product splits K (8 splits with a K tail
+    # in the last; 3 even splits)
+    "bf16_splitk8": (300, 4136, 264, 16, 32.0, "bf16", "dense"),
+    "bf16_splitk3": (2000, 1536, 520, 8, 16.0, "bf16", "dense"),
     "int4_small": (192, 256, 384, 16, 16.0, "bf16", "int4_b64"),
     "int4_ragged": (300, 192, 320, 12, 24.0, "bf16", "int4_b64"),
 }
@@ -49,6 +53,24 @@ def test_linear_parity(name):
     compare(got, _oracle(inp, wl), TOL[wl.dtype], "linear " + name)
     assert np.linalg.norm(got["da"]) > 0 and np.linalg.norm(got["db"]) > 0
     assert all(np.isfinite(v).all() for v in got.values())
+
+
+@pytest.mark.parametrize("name", ["bf16_splitk8", "bf16_splitk3", "bf16_narrow_out"])
+def test_linear_split_k_forward(name):
+    """Products whose output tiles do not fill the GPU split K and sum fp32
+    partials in split order: the split path runs (its sum launch is
+    recorded), matches the oracle, and repeats bit for bit."""
+    wl = workload(name)
+    inp = I.make_linear_inputs(wl)
+    print(f"[case] linear split-K {name} {CASES[name]}", flush=True)
+    abi.lora_mlp_profile_begin()
+    a, _ = run_hip_linear(inp, wl)
+    names = [n for n, _ in abi.lora_mlp_profile_end()]
+    assert "sum(y)" in names, names
+    b, _ = run_hip_linear(inp, wl)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    compare(a, _oracle(inp, wl), TOL[wl.dtype], "linear split-K " + name)
 
 
 @pytest.mark.parametrize("name", ["int4_small", "int4_ragged"])
