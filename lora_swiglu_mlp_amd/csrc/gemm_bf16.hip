@@ -1547,7 +1547,7 @@ struct TableStage {
 std::mutex g_stage_mu;
 std::map<int, TableStage> g_stage;
 
-static hipError_t stage_table(const GemmParams* src, size_t bytes, GemmParams* dst, hipStream_t st, bool& done) {
+static hipError_t stage_table(const void* src, size_t bytes, void* dst, hipStream_t st, bool& done) {
   done = false;
   if (bytes > kStageBytes) return hipSuccess;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -1627,6 +1627,41 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
     if (nblk == 0) continue;
     hipLaunchKernelGGL((gemm_bf16_table_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream,
                        static_cast<const GemmParams*>(table), gs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+namespace {
+// copy kernel of stage_device_table: up to 3.5 KB of words per launch, in
+// its arguments
+struct WordChunk {
+  uint32_t w[896];
+  uint32_t* dst;
+  int32_t n;
+};
+__global__ __launch_bounds__(256) void write_words_kernel(WordChunk c) {
+  for (int i = threadIdx.x; i < c.n; i += blockDim.x) c.dst[i] = c.w[i];
+}
+
+}  // namespace
+
+hipError_t stage_device_table(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  if (bytes % 4) return hipErrorInvalidValue;
+  bool staged = false;
+  const hipError_t se = stage_table(src, bytes, dst, stream, staged);
+  if (se != hipSuccess || staged) return se;
+  const uint32_t* s = static_cast<const uint32_t*>(src);
+  uint32_t* d = static_cast<uint32_t*>(dst);
+  const size_t n = bytes / 4;
+  for (size_t i = 0; i < n; i += 896) {
+    WordChunk c;
+    c.n = static_cast<int32_t>(n - i < 896 ? n - i : 896);
+    std::memcpy(c.w, s + i, size_t(c.n) * 4);
+    c.dst = d + i;
+    hipLaunchKernelGGL(write_words_kernel, dim3(1), dim3(256), 0, stream, c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

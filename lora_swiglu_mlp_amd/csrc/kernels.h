@@ -112,13 +112,19 @@ struct RowProjJob {
   int64_t T;        // token rows of this job (0: the launch's T)
 };
 // job capacities: every parameter block stays under 3.8 KB of kernel arguments
+// (table: when set, the launch's njobs jobs are read from this device array
+// instead of job[], so that one launch can carry more jobs than the kernel
+// arguments hold; the launcher then takes the same jobs on the host as
+// `hjobs`, with every T filled in, to size the grid.)
 struct RowProjParams {
   RowProjJob job[52];
   int32_t njobs;
   int32_t nsl;      // set by the launcher: 64-column slices of the widest job
   int64_t T;
+  const RowProjJob* table;
 };
-hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream);
+hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream,
+                          const RowProjJob* hjobs = nullptr);
 
 // v(t, n) = sum_k part[k][t][n] (k < nparts, in order), n < n1p; written as
 // out_f32[t][col_off + n] (fp32), out_c[t][col_off + n] = scale * v (compute
@@ -146,8 +152,10 @@ struct ProjFinishParams {
   int32_t njobs;
   int32_t pad_;
   int64_t T;
+  const ProjFinishJob* table;
 };
-hipError_t launch_proj_finish(const ProjFinishParams& p, int dtype_bf16, hipStream_t stream);
+hipError_t launch_proj_finish(const ProjFinishParams& p, int dtype_bf16, hipStream_t stream,
+                              const ProjFinishJob* hjobs = nullptr);
 
 // Column projection: part[tb][k][n] = sum_{t in block tb} X[t][k] * P[t][n]
 // (fp32 partials over token blocks; reduced by launch_reduce). bf16 reads the
@@ -171,8 +179,10 @@ struct ColProjParams {
   int32_t njobs;
   int32_t pad_;
   int64_t T;
+  const ColProjJob* table;
 };
-hipError_t launch_colproj(const ColProjParams& p, int dtype_bf16, hipStream_t stream);
+hipError_t launch_colproj(const ColProjParams& p, int dtype_bf16, hipStream_t stream,
+                          const ColProjJob* hjobs = nullptr);
 
 // Fixed-order sum of partials into a final, scaled, optionally transposed
 // matrix in fp32 or bf16: dst(i, j) = scale * sum_c src[c][i][col_off + j].
@@ -191,8 +201,9 @@ struct ReduceParams {
   ReduceJob job[46];
   int32_t njobs;
   int32_t pad_;
+  const ReduceJob* table;
 };
-hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream, const ReduceJob* hjobs = nullptr);
 
 // Zero-padded copy of an adapter factor into a GEMM/projection operand
 // layout: dst[i][j] = src(i, j) (or src(j, i) if transpose) inside the source
@@ -209,8 +220,9 @@ struct PackParams {
   PackJob job[52];
   int32_t njobs;
   int32_t pad_;
+  const PackJob* table;
 };
-hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream);
+hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream, const PackJob* hjobs = nullptr);
 
 // fp16 block scales [rows][nb] -> fp32 [nb][ld_dst]
 // fp16 block scales [rows][nb] -> fp32: block-major dst[b][r] (row_major 0,
@@ -233,6 +245,12 @@ hipError_t launch_scale_pack(const ScalePackParams& p, hipStream_t stream);
 // bf16 matrix-core ceiling: blocks x 8 waves x iters x 32 MFMA 16x16x32 on
 // operands read once from `ops` (blocks * 8 * 768 uint4)
 hipError_t launch_mfma_probe(const void* ops, float* sink, int blocks, int iters, hipStream_t stream);
+
+// Copy `bytes` of host data to the device array `dst` on `stream`, ordered
+// with the stream's other work: through a pinned host ring and one copy when
+// it can, else with copy kernels (under stream capture, or while the ring
+// region is still being copied). The host never waits.
+hipError_t stage_device_table(const void* src, size_t bytes, void* dst, hipStream_t stream);
 
 // Split-K finish: y[i] = bf16_rne(part[0][i] + part[1][i] + ... + part[nsplit-1][i]),
 // summed in that order; part holds nsplit slices of n fp32 values (n a multiple of 4).

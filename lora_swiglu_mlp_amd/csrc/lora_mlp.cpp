@@ -568,15 +568,47 @@ SideOp side_op(const char* n, int kind, const ReduceParams& p, int flag) {
   return side_op_of(n, kind, flag, p.job, p.njobs, 0);
 }
 
-// One kind's recorded jobs, merged into launches of up to the job capacity.
+// Device job tables of the merged side launches: room per expert for the
+// most jobs one of its side launches carries (the forward's packing, 10).
+constexpr size_t kSideJobBytes = 96;
+constexpr size_t kSideJobsPerExpert = 10;
+static_assert(sizeof(PackJob) <= kSideJobBytes && sizeof(RowProjJob) <= kSideJobBytes &&
+                  sizeof(ProjFinishJob) <= kSideJobBytes && sizeof(ColProjJob) <= kSideJobBytes &&
+                  sizeof(ReduceJob) <= kSideJobBytes,
+              "side job table entries");
+
+// One kind's recorded jobs: with a device job table big enough, one launch
+// reading its jobs from the table (staged on the stream); else merged into
+// launches of up to the job capacity of the kernel arguments.
 template <typename P, typename L>
-hipError_t launch_jobs(const std::vector<const SideOp*>& ops, bool has_t, L launch) {
+hipError_t launch_jobs(const std::vector<const SideOp*>& ops, bool has_t, void* dtab, size_t dtab_bytes,
+                       hipStream_t st, L launch) {
   using J = typename std::remove_reference<decltype(P{}.job[0])>::type;
   constexpr int cap = int(sizeof(P{}.job) / sizeof(J));
+  size_t total = 0;
+  for (const SideOp* o : ops) total += size_t(o->njobs);
+  if (dtab && total > size_t(cap) && total * sizeof(J) <= dtab_bytes) {
+    std::vector<J> all;
+    all.reserve(total);
+    P q{};
+    for (const SideOp* o : ops) {
+      const J* js = reinterpret_cast<const J*>(o->jobs.data());
+      for (int i = 0; i < o->njobs; ++i) {
+        all.push_back(js[i]);
+        if constexpr (!std::is_same<J, PackJob>::value && !std::is_same<J, ReduceJob>::value)
+          if (has_t && js[i].T > q.T) q.T = js[i].T;
+      }
+    }
+    const hipError_t e = stage_device_table(all.data(), total * sizeof(J), dtab, st);
+    if (e != hipSuccess) return e;
+    q.njobs = static_cast<int32_t>(total);
+    q.table = static_cast<const J*>(dtab);
+    return launch(q, all.data());
+  }
   P q{};
   auto flush = [&]() -> hipError_t {
     if (q.njobs == 0) return hipSuccess;
-    const hipError_t e = launch(q);
+    const hipError_t e = launch(q, nullptr);
     q = P{};
     return e;
   };
@@ -595,20 +627,33 @@ hipError_t launch_jobs(const std::vector<const SideOp*>& ops, bool has_t, L laun
   return flush();
 }
 
-hipError_t launch_side_group(const std::vector<const SideOp*>& ops, hipStream_t st) {
+hipError_t launch_side_group(const std::vector<const SideOp*>& ops, hipStream_t st, void* dtab, size_t dtab_bytes) {
   const int kind = ops[0]->kind, flag = ops[0]->flag;
   switch (kind) {
     case SK_PACK:
-      return launch_jobs<PackParams>(ops, false, [&](const PackParams& q) { return launch_pack(q, flag, st); });
+      return launch_jobs<PackParams>(ops, false, dtab, dtab_bytes, st, [&](const PackParams& q, const PackJob* h) {
+        return launch_pack(q, flag, st, h);
+      });
     case SK_ROWPROJ:
-      return launch_jobs<RowProjParams>(ops, true, [&](const RowProjParams& q) { return launch_rowproj(q, flag, st); });
+      return launch_jobs<RowProjParams>(ops, true, dtab, dtab_bytes, st,
+                                        [&](const RowProjParams& q, const RowProjJob* h) {
+                                          return launch_rowproj(q, flag, st, h);
+                                        });
     case SK_FINISH:
-      return launch_jobs<ProjFinishParams>(ops, true,
-                                           [&](const ProjFinishParams& q) { return launch_proj_finish(q, flag, st); });
+      return launch_jobs<ProjFinishParams>(ops, true, dtab, dtab_bytes, st,
+                                           [&](const ProjFinishParams& q, const ProjFinishJob* h) {
+                                             return launch_proj_finish(q, flag, st, h);
+                                           });
     case SK_COLPROJ:
-      return launch_jobs<ColProjParams>(ops, true, [&](const ColProjParams& q) { return launch_colproj(q, flag, st); });
+      return launch_jobs<ColProjParams>(ops, true, dtab, dtab_bytes, st,
+                                        [&](const ColProjParams& q, const ColProjJob* h) {
+                                          return launch_colproj(q, flag, st, h);
+                                        });
     case SK_REDUCE:
-      return launch_jobs<ReduceParams>(ops, false, [&](const ReduceParams& q) { return launch_reduce(q, st); });
+      return launch_jobs<ReduceParams>(ops, false, dtab, dtab_bytes, st,
+                                       [&](const ReduceParams& q, const ReduceJob* h) {
+                                         return launch_reduce(q, st, h);
+                                       });
     default:
       return hipErrorInvalidValue;
   }
@@ -1313,6 +1358,7 @@ struct MoePlan {
   std::vector<size_t> wfoff, wfsize, wboff, wbsize;  // forward / backward workspace regions
   size_t saved_total = 0, ws_fwd = 0, ws_bwd = 0;
   size_t tab_fwd = 0, tab_bwd = 0;  // GEMM parameter tables (more experts than one launch's arguments hold)
+  size_t side_fwd = 0, side_bwd = 0, side_bytes = 0;  // side-kernel job tables
   bool table = false;
   Dims d;  // the whole call
 };
@@ -1324,8 +1370,8 @@ struct MoePlan {
 // out merged across experts round by round (round r: every expert's r-th
 // launch; one expert's launches keep their order), then the GEMMs the
 // experts reached, grouped by kind; until no expert hands back a GEMM.
-static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, GemmParams* table,
-                      const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
+static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, GemmParams* table, void* side_table,
+                      size_t side_bytes, const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
   std::vector<Exec> ex(order.size());
   std::vector<std::vector<SideOp>> ops(order.size());
   hipStream_t st = caller;
@@ -1352,7 +1398,7 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, Gem
           grp.push_back(&b);
           taken[j] = true;
         }
-        LMLP_LAUNCH(a.name, launch_side_group(grp, st));
+        LMLP_LAUNCH(a.name, launch_side_group(grp, st, side_table, side_bytes));
       }
     }
     // the GEMMs of this phase: dense bf16 ones grouped by kind, the rest one by one
@@ -1432,6 +1478,12 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
     P.ws_fwd += tb;
     P.tab_bwd = P.ws_bwd;
     P.ws_bwd += tb;
+    // side-kernel job tables: one launch per merged side launch however many experts
+    P.side_bytes = align_up(size_t(E) * kSideJobsPerExpert * kSideJobBytes);
+    P.side_fwd = P.ws_fwd;
+    P.ws_fwd += P.side_bytes;
+    P.side_bwd = P.ws_bwd;
+    P.ws_bwd += P.side_bytes;
   }
   return LMLP_OK;
 }
@@ -1503,7 +1555,9 @@ int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* of
     if (P.dims[e].tokens > 0) order.push_back(e);
   if (order.empty()) return LMLP_OK;
   GemmParams* tab = P.table ? reinterpret_cast<GemmParams*>(at(workspace, P.tab_fwd)) : nullptr;
-  return moe_phased(static_cast<hipStream_t>(stream), order, tab, [&](int64_t e, Exec* ex, hipStream_t ws) {
+  void* stab = P.table ? at(workspace, P.side_fwd) : nullptr;
+  return moe_phased(static_cast<hipStream_t>(stream), order, tab, stab, P.side_bytes,
+                    [&](int64_t e, Exec* ex, hipStream_t ws) {
     return forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
                         slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu), slice(w_up_scales, e, S.wgu_s),
                         slice(w_down, e, S.wd), slice(w_down_scales, e, S.wd_s), slice(a_gate, e, S.agu),
@@ -1547,7 +1601,9 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
   std::vector<int64_t> order(n_experts);  // every expert: one without rows gets zero gradients
   for (int64_t e = 0; e < n_experts; ++e) order[e] = e;
   GemmParams* tab = P.table ? reinterpret_cast<GemmParams*>(at(workspace, P.tab_bwd)) : nullptr;
-  return moe_phased(static_cast<hipStream_t>(stream), order, tab, [&](int64_t e, Exec* ex, hipStream_t ws) {
+  void* stab = P.table ? at(workspace, P.side_bwd) : nullptr;
+  return moe_phased(static_cast<hipStream_t>(stream), order, tab, stab, P.side_bytes,
+                    [&](int64_t e, Exec* ex, hipStream_t ws) {
     const bool any = P.dims[e].tokens > 0;
     return backward_impl(
         &P.dims[e], nullptr, any ? slice(dy, P.row0[e], S.rows) : nullptr, any ? slice(x, P.row0[e], S.rows) : nullptr,

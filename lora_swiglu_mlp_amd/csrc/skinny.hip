@@ -25,12 +25,30 @@ namespace {
 // activation chunks and the matching factor chunks) before their MFMAs; each
 // factor chunk feeds four row tiles. The slice partials are summed in fixed
 // order by proj_finish_kernel. (bf16 uses rowproj_dma_kernel below.)
+// job i of a launch: from the kernel arguments, or from the device job table
+// when the launch carries more jobs than they hold (a uniform branch). Every
+// lane reads the same job; its words are made scalar so that buffer
+// descriptors built from it stay in SGPRs.
+template <typename J, typename P>
+__device__ __forceinline__ J job_at(const P& p, int i) {
+  static_assert(sizeof(J) % 4 == 0, "job words");
+  J j;
+  if (p.table) j = p.table[i];
+  else j = p.job[i];
+  uint32_t w[sizeof(J) / 4];
+  __builtin_memcpy(w, &j, sizeof(J));
+#pragma unroll
+  for (int k = 0; k < int(sizeof(J) / 4); ++k) w[k] = __builtin_amdgcn_readfirstlane(w[k]);
+  __builtin_memcpy(&j, w, sizeof(J));
+  return j;
+}
+
 constexpr int RP_ROWS = 256;  // token rows per workgroup
 template <typename T>
 __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
   constexpr int CH = elem<T>::CH;
   constexpr int KSTEP = 4 * CH;  // elements per MFMA k-step
-  const RowProjJob& jb = p.job[blockIdx.z / p.nsl];
+  const RowProjJob jb = job_at<RowProjJob>(p, blockIdx.z / p.nsl);
   const int n_base = (blockIdx.z % p.nsl) * 64;
   if (n_base >= jb.n1p || static_cast<int>(blockIdx.y) >= jb.kslices) return;
   if (static_cast<int64_t>(blockIdx.x) * RP_ROWS >= jb.T) return;
@@ -97,7 +115,7 @@ __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
 // added (still in slice order), and the transposed write goes through LDS.
 template <typename T>
 __global__ __launch_bounds__(64) void proj_finish_kernel(ProjFinishParams p) {
-  const ProjFinishJob& jb = p.job[blockIdx.z];
+  const ProjFinishJob jb = job_at<ProjFinishJob>(p, blockIdx.z);
   const int n0 = blockIdx.y * 64;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t tmax = jb.outT ? jb.ldT : jb.T;
@@ -168,7 +186,7 @@ __global__ __launch_bounds__(256) void colproj_f32_kernel(ColProjParams p) {
   constexpr int TS = 32;                 // tokens per step
   constexpr int XS = 64 + 4;             // X tile row stride (elements)
   constexpr int PS = TS + 16 / EB;       // P^T tile row stride (elements)
-  const ColProjJob& jb = p.job[blockIdx.z];
+  const ColProjJob jb = job_at<ColProjJob>(p, blockIdx.z);
   const int nblocks = jb.kblocks * jb.ntb * jb.nchunks;
   if (static_cast<int>(blockIdx.x) >= nblocks) return;
   int b = blockIdx.x;
@@ -301,7 +319,7 @@ __device__ __forceinline__ void cp_issue(CpDma& d, char* stage, int step, int wa
 
 template <int PI>
 __global__ __launch_bounds__(256, 2) void colproj_bf16_kernel(ColProjParams p) {
-  const ColProjJob& jb = p.job[blockIdx.z];
+  const ColProjJob jb = job_at<ColProjJob>(p, blockIdx.z);
   const int nblocks = jb.kblocks * jb.ntb * jb.nchunks;
   if (static_cast<int>(blockIdx.x) >= nblocks) return;
   int b = blockIdx.x;
@@ -409,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void colproj_bf16_kernel(ColProjParams p) {
 // partial order), and the transposed case goes through LDS so that its writes
 // also run along destination rows. nchunk = 0 writes zeros.
 __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
-  const ReduceJob& jb = p.job[blockIdx.z];
+  const ReduceJob jb = job_at<ReduceJob>(p, blockIdx.z);
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t j0 = static_cast<int64_t>(blockIdx.y) * 64;
   if (i0 >= jb.rows || j0 >= jb.cols) return;
@@ -485,7 +503,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
 // arithmetic (every factor has far fewer than 2^31 elements).
 template <typename E>
 __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
-  const PackJob& jb = p.job[blockIdx.y];
+  const PackJob jb = job_at<PackJob>(p, blockIdx.y);
   const uint32_t cols = static_cast<uint32_t>(jb.cols);
   const uint32_t cq = (cols + 3) / 4;  // groups of four per destination row
   const uint32_t n = static_cast<uint32_t>(jb.rows) * cq;
@@ -582,7 +600,7 @@ template <int NF, int NS>
 __global__ __launch_bounds__(256, 2) void rowproj_dma_kernel(RowProjParams p) {
   constexpr int STAGE = RPD_XT + 16 * NF * 128;
   constexpr int NW = NF / 2;  // factor DMA instructions per wave and stage
-  const RowProjJob& jb = p.job[blockIdx.z / p.nsl];
+  const RowProjJob jb = job_at<RowProjJob>(p, blockIdx.z / p.nsl);
   const int n_base = (blockIdx.z % p.nsl) * 16 * NF;
   if (n_base >= jb.n1p || static_cast<int>(blockIdx.y) >= jb.kslices) return;
   const int nfr = min(NF, (jb.n1p - n_base) / 16);
@@ -685,17 +703,21 @@ __global__ __launch_bounds__(256, 2) void rowproj_dma_kernel(RowProjParams p) {
 
 }  // namespace
 
-hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream) {
+hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t stream, const RowProjJob* hjobs) {
   if (p.T <= 0 || p.njobs <= 0) return hipSuccess;
+  if ((hjobs != nullptr) != (p.table != nullptr) || (!hjobs && p.njobs > 52)) return hipErrorInvalidValue;
   RowProjParams q = p;
-  for (int i = 0; i < q.njobs; ++i)
-    if (q.job[i].T == 0) q.job[i].T = q.T;
+  if (!hjobs)
+    for (int i = 0; i < q.njobs; ++i)
+      if (q.job[i].T == 0) q.job[i].T = q.T;
+  const RowProjJob* js = hjobs ? hjobs : q.job;
   int maxn = 0, maxks = 0;
   for (int i = 0; i < q.njobs; ++i) {
-    maxn = q.job[i].n1p > maxn ? q.job[i].n1p : maxn;
-    maxks = q.job[i].kslices > maxks ? q.job[i].kslices : maxks;
+    maxn = js[i].n1p > maxn ? js[i].n1p : maxn;
+    maxks = js[i].kslices > maxks ? js[i].kslices : maxks;
   }
   if (maxks == 0 || maxn == 0) return hipSuccess;
+  if (q.njobs * static_cast<int64_t>((maxn + 31) / 32) > 65535) return hipErrorInvalidValue;  // grid.z
   if (dtype_bf16) {
     const bool wide = maxn > 32;  // 64 columns a pass (4 stages of 24 KB would not fit twice)
     q.nsl = wide ? (maxn + 63) / 64 : (maxn + 31) / 32;
@@ -710,17 +732,22 @@ hipError_t launch_rowproj(const RowProjParams& p, int dtype_bf16, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_proj_finish(const ProjFinishParams& p0, int dtype_bf16, hipStream_t stream) {
+hipError_t launch_proj_finish(const ProjFinishParams& p0, int dtype_bf16, hipStream_t stream,
+                              const ProjFinishJob* hjobs) {
   if (p0.njobs <= 0) return hipSuccess;
+  if ((hjobs != nullptr) != (p0.table != nullptr) || (!hjobs && p0.njobs > 36) || p0.njobs > 65535)
+    return hipErrorInvalidValue;
   ProjFinishParams p = p0;
-  for (int i = 0; i < p.njobs; ++i)
-    if (p.job[i].T == 0) p.job[i].T = p.T;
+  if (!hjobs)
+    for (int i = 0; i < p.njobs; ++i)
+      if (p.job[i].T == 0) p.job[i].T = p.T;
+  const ProjFinishJob* js = hjobs ? hjobs : p.job;
   int64_t maxt = 0;
   int maxn = 0;
   for (int i = 0; i < p.njobs; ++i) {
-    const int64_t t = p.job[i].outT ? p.job[i].ldT : p.job[i].T;
+    const int64_t t = js[i].outT ? js[i].ldT : js[i].T;
     maxt = t > maxt ? t : maxt;
-    maxn = p.job[i].n1p > maxn ? p.job[i].n1p : maxn;
+    maxn = js[i].n1p > maxn ? js[i].n1p : maxn;
   }
   if (maxt <= 0 || maxn <= 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>((maxt + 15) / 16), (maxn + 63) / 64, p.njobs);
@@ -729,14 +756,18 @@ hipError_t launch_proj_finish(const ProjFinishParams& p0, int dtype_bf16, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_colproj(const ColProjParams& p0, int dtype_bf16, hipStream_t stream) {
+hipError_t launch_colproj(const ColProjParams& p0, int dtype_bf16, hipStream_t stream, const ColProjJob* hjobs) {
   if (p0.T <= 0 || p0.njobs <= 0) return hipSuccess;
+  if ((hjobs != nullptr) != (p0.table != nullptr) || (!hjobs && p0.njobs > 38) || p0.njobs > 65535)
+    return hipErrorInvalidValue;
   ColProjParams p = p0;
-  for (int i = 0; i < p.njobs; ++i)
-    if (p.job[i].T == 0) p.job[i].T = p.T;
+  if (!hjobs)
+    for (int i = 0; i < p.njobs; ++i)
+      if (p.job[i].T == 0) p.job[i].T = p.T;
+  const ColProjJob* js = hjobs ? hjobs : p.job;
   int maxb = 0, maxfr = 0;
   for (int i = 0; i < p.njobs; ++i) {
-    const ColProjJob& j = p.job[i];
+    const ColProjJob& j = js[i];
     const int nb = j.kblocks * j.ntb * j.nchunks;
     maxb = nb > maxb ? nb : maxb;
     const int fr = (j.n2p < 128 ? j.n2p : 128) / 16;
@@ -750,12 +781,15 @@ hipError_t launch_colproj(const ColProjParams& p0, int dtype_bf16, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream) {
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream, const ReduceJob* hjobs) {
   if (p.njobs <= 0) return hipSuccess;
+  if ((hjobs != nullptr) != (p.table != nullptr) || (!hjobs && p.njobs > 46) || p.njobs > 65535)
+    return hipErrorInvalidValue;
+  const ReduceJob* js = hjobs ? hjobs : p.job;
   int64_t maxr = 0, maxc = 0;
   for (int i = 0; i < p.njobs; ++i) {
-    maxr = p.job[i].rows > maxr ? p.job[i].rows : maxr;
-    maxc = p.job[i].cols > maxc ? p.job[i].cols : maxc;
+    maxr = js[i].rows > maxr ? js[i].rows : maxr;
+    maxc = js[i].cols > maxc ? js[i].cols : maxc;
   }
   if (maxr == 0 || maxc == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>((maxr + 15) / 16), static_cast<unsigned>((maxc + 63) / 64), p.njobs);
@@ -763,10 +797,13 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream) {
+hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream, const PackJob* hjobs) {
   if (p.njobs <= 0) return hipSuccess;
+  if ((hjobs != nullptr) != (p.table != nullptr) || (!hjobs && p.njobs > 52) || p.njobs > 65535)
+    return hipErrorInvalidValue;
+  const PackJob* js = hjobs ? hjobs : p.job;
   int64_t maxn = 0;
-  for (int i = 0; i < p.njobs; ++i) maxn = p.job[i].rows * p.job[i].cols > maxn ? p.job[i].rows * p.job[i].cols : maxn;
+  for (int i = 0; i < p.njobs; ++i) maxn = js[i].rows * js[i].cols > maxn ? js[i].rows * js[i].cols : maxn;
   if (maxn == 0) return hipSuccess;
   dim3 grid(grid_for((maxn + 3) / 4), p.njobs);
   if (elem_bytes == 2) hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
