@@ -60,6 +60,10 @@ struct Dims {
   bool q4_inkernel;  // 4-bit codes decoded inside the GEMM staging (else into bf16 copies)
   bool norm;         // RMSNorm in front of the MLP (the norm entry points)
   int eb;  // element bytes
+  // tokens that size the row projections' K split (0: T). An expert of the
+  // grouped MLP plans with the whole call's rows: its row projections run
+  // merged with every other expert's, which fill the GPU together.
+  int64_t t_split = 0;
 };
 
 constexpr size_t kAlign = 256;
@@ -162,8 +166,9 @@ struct RpPlan {
   int64_t kb;
 };
 RpPlan rp_plan(const Dims& d, int64_t K, int n1p) {
+  const int64_t Ts = d.t_split > 0 ? d.t_split : d.T;
   if (d.bf16) {
-    const int64_t work = std::max<int64_t>(1, (d.T + 127) / 128 * (n1p > 32 ? (n1p + 63) / 64 : 1));
+    const int64_t work = std::max<int64_t>(1, (Ts + 127) / 128 * (n1p > 32 ? (n1p + 63) / 64 : 1));
     int64_t ks = (256 + work - 1) / work;
     ks = std::min(std::max<int64_t>(ks, 1), std::max<int64_t>(1, K / 128));
     int64_t kb = (K + ks - 1) / ks;
@@ -171,7 +176,7 @@ RpPlan rp_plan(const Dims& d, int64_t K, int n1p) {
     return {static_cast<int>((K + kb - 1) / kb), kb};
   }
   const int64_t unit = 4 * 16;  // one load batch: four MFMA k-steps
-  const int64_t work = std::max<int64_t>(1, (d.T + 255) / 256 * ((n1p + 63) / 64));
+  const int64_t work = std::max<int64_t>(1, (Ts + 255) / 256 * ((n1p + 63) / 64));
   int64_t ks = (768 + work - 1) / work;
   ks = std::min(std::max<int64_t>(ks, 1), std::max<int64_t>(1, K / 256));
   int64_t kb = (K + ks - 1) / ks;
@@ -520,6 +525,7 @@ struct ProfScope {
 // pass returns there); a pass with no GEMM left hands back nothing. Running
 // phases 0, 1, ... in order launches the same work in the same order.
 struct Exec {
+  int64_t t_split = 0;  // Dims::t_split of the pass (grouped MLP)
   int phase = -1;
   int seg = 0;  // GEMMs passed so far
   bool sunk = false;
@@ -848,6 +854,7 @@ static int forward_impl(const lmlp_dims* dims, const void* gamma, float eps, con
   Exec& ex = exec ? *exec : local_exec;
   Dims d;
   LMLP_TRY(parse_dims(dims, d));
+  d.t_split = ex.t_split;
   if (d.norm) LMLP_TRY(need_ptr(gamma, "gamma"));
   LMLP_TRY(check_weights(d, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales));
   LMLP_TRY(check_adapters(a_gate, b_gate, a_up, b_up, a_down, b_down));
@@ -993,6 +1000,7 @@ static int backward_impl(const lmlp_dims* dims, const void* gamma, const void* d
   Exec& ex = exec ? *exec : local_exec;
   Dims d;
   LMLP_TRY(parse_dims(dims, d));
+  d.t_split = ex.t_split;
   if (d.norm) LMLP_TRY(need_ptr(gamma, "gamma"));
   LMLP_TRY(check_weights(d, w_gate, w_gate_scales, w_up, w_up_scales, w_down, w_down_scales));
   LMLP_TRY(check_adapters(a_gate, b_gate, a_up, b_up, a_down, b_down));
@@ -1370,8 +1378,9 @@ struct MoePlan {
 // out merged across experts round by round (round r: every expert's r-th
 // launch; one expert's launches keep their order), then the GEMMs the
 // experts reached, grouped by kind; until no expert hands back a GEMM.
-static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, GemmParams* table, void* side_table,
-                      size_t side_bytes, const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
+static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int64_t t_split, GemmParams* table,
+                      void* side_table, size_t side_bytes,
+                      const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
   std::vector<Exec> ex(order.size());
   std::vector<std::vector<SideOp>> ops(order.size());
   hipStream_t st = caller;
@@ -1379,6 +1388,7 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, Gem
     size_t rounds = 0;
     for (size_t k = 0; k < order.size(); ++k) {
       ex[k] = Exec{};
+      ex[k].t_split = t_split;
       ex[k].phase = phase;
       ops[k].clear();
       ex[k].rec = &ops[k];
@@ -1457,6 +1467,7 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
     de.tokens = off[e + 1] - off[e];
     Dims dd;
     LMLP_TRY(parse_dims(&de, dd));
+    dd.t_split = P.d.T;
     P.dims[e] = de;
     P.row0[e] = off[e];
     P.soff[e] = P.saved_total;
@@ -1556,7 +1567,7 @@ int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* of
   if (order.empty()) return LMLP_OK;
   GemmParams* tab = P.table ? reinterpret_cast<GemmParams*>(at(workspace, P.tab_fwd)) : nullptr;
   void* stab = P.table ? at(workspace, P.side_fwd) : nullptr;
-  return moe_phased(static_cast<hipStream_t>(stream), order, tab, stab, P.side_bytes,
+  return moe_phased(static_cast<hipStream_t>(stream), order, P.d.T, tab, stab, P.side_bytes,
                     [&](int64_t e, Exec* ex, hipStream_t ws) {
     return forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
                         slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu), slice(w_up_scales, e, S.wgu_s),
@@ -1602,7 +1613,7 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
   for (int64_t e = 0; e < n_experts; ++e) order[e] = e;
   GemmParams* tab = P.table ? reinterpret_cast<GemmParams*>(at(workspace, P.tab_bwd)) : nullptr;
   void* stab = P.table ? at(workspace, P.side_bwd) : nullptr;
-  return moe_phased(static_cast<hipStream_t>(stream), order, tab, stab, P.side_bytes,
+  return moe_phased(static_cast<hipStream_t>(stream), order, P.d.T, tab, stab, P.side_bytes,
                     [&](int64_t e, Exec* ex, hipStream_t ws) {
     const bool any = P.dims[e].tokens > 0;
     return backward_impl(

@@ -10,6 +10,8 @@
 // Both are HBM-bound streams over one [T, K] activation; they run on MFMA
 // because at r >= 16 their arithmetic intensity (up to 4r FLOP/byte) is past
 // what the fp32 vector units sustain at 8 TB/s.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -428,72 +430,80 @@ __global__ __launch_bounds__(256, 2) void colproj_bf16_kernel(ColProjParams p) {
 // also run along destination rows. nchunk = 0 writes zeros.
 __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   const ReduceJob jb = job_at<ReduceJob>(p, blockIdx.z);
-  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int64_t j0 = static_cast<int64_t>(blockIdx.y) * 64;
-  if (i0 >= jb.rows || j0 >= jb.cols) return;
+  // the job's 16 x 64 tiles, numbered row-major, grid-strided over blockIdx.x
+  // (a merged launch's jobs differ in shape: tall and wide ones)
+  const int64_t ntj = (jb.cols + 63) / 64;
+  const int64_t ntiles = (jb.rows + 15) / 16 * ntj;
   __shared__ float tile[64][17];
   const int lane = threadIdx.x;
-  const int64_t ncols = min<int64_t>(64, jb.cols - j0);
-  const int cpr = static_cast<int>((ncols + 3) / 4);  // float4 items per source row
+  for (int64_t id = blockIdx.x; id < ntiles; id += gridDim.x) {
+    const int64_t i0 = id / ntj * 16;
+    const int64_t j0 = id % ntj * 64;
+    const int64_t ncols = min<int64_t>(64, jb.cols - j0);
+    const int cpr = static_cast<int>((ncols + 3) / 4);  // float4 items per source row
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int it = lane + 64 * q;
-    if (it >= 16 * cpr) break;
-    const int il = it / cpr, c = it % cpr;
-    const int64_t i = i0 + il;
-    const int64_t j = j0 + 4 * c;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (i < jb.rows) {
-      const float* s = jb.src + i * jb.ld_src + jb.col_off + j;
-      int k = 0;
-      for (; k + 8 <= jb.nchunk; k += 8) {
-        float4 x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(k + e) * jb.chunk_stride);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v[0] += x[e].x;
-          v[1] += x[e].y;
-          v[2] += x[e].z;
-          v[3] += x[e].w;
-        }
-      }
-      for (; k < jb.nchunk; ++k) {
-        const float4 x = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(k) * jb.chunk_stride);
-        v[0] += x.x;
-        v[1] += x.y;
-        v[2] += x.z;
-        v[3] += x.w;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] *= jb.scale;
-    if (!jb.transpose) {
+    for (int q = 0; q < 4; ++q) {
+      const int it = lane + 64 * q;
+      if (it >= 16 * cpr) break;
+      const int il = it / cpr, c = it % cpr;
+      const int64_t i = i0 + il;
+      const int64_t j = j0 + 4 * c;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
       if (i < jb.rows) {
+        const float* s = jb.src + i * jb.ld_src + jb.col_off + j;
+        int k = 0;
+        for (; k + 8 <= jb.nchunk; k += 8) {
+          float4 x[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (j + e >= jb.cols) break;
-          const int64_t o = i * jb.ld_dst + j + e;
-          if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(v[e]);
-          else static_cast<float*>(jb.dst)[o] = v[e];
+          for (int e = 0; e < 8; ++e)
+            x[e] = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(k + e) * jb.chunk_stride);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[0] += x[e].x;
+            v[1] += x[e].y;
+            v[2] += x[e].z;
+            v[3] += x[e].w;
+          }
+        }
+        for (; k < jb.nchunk; ++k) {
+          const float4 x = *reinterpret_cast<const float4*>(s + static_cast<int64_t>(k) * jb.chunk_stride);
+          v[0] += x.x;
+          v[1] += x.y;
+          v[2] += x.z;
+          v[3] += x.w;
         }
       }
-    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile[4 * c + e][il] = v[e];
+      for (int e = 0; e < 4; ++e) v[e] *= jb.scale;
+      if (!jb.transpose) {
+        if (i < jb.rows) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (j + e >= jb.cols) break;
+            const int64_t o = i * jb.ld_dst + j + e;
+            if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(v[e]);
+            else static_cast<float*>(jb.dst)[o] = v[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[4 * c + e][il] = v[e];
+      }
     }
-  }
-  if (!jb.transpose) return;  // uniform over the workgroup
-  __syncthreads();
-  const int64_t j = j0 + lane;
-  if (lane >= ncols) return;
+    if (!jb.transpose) continue;  // uniform over the workgroup
+    __syncthreads();
+    const int64_t j = j0 + lane;
+    if (lane < ncols) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int64_t i = i0 + e;
-    if (i >= jb.rows) break;
-    const int64_t o = j * jb.ld_dst + i;
-    if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(tile[lane][e]);
-    else static_cast<float*>(jb.dst)[o] = tile[lane][e];
+      for (int e = 0; e < 16; ++e) {
+        const int64_t i = i0 + e;
+        if (i >= jb.rows) break;
+        const int64_t o = j * jb.ld_dst + i;
+        if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(tile[lane][e]);
+        else static_cast<float*>(jb.dst)[o] = tile[lane][e];
+      }
+    }
+    __syncthreads();  // the next tile overwrites the staging
   }
 }
 
@@ -786,13 +796,15 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream, const Reduce
   if ((hjobs != nullptr) != (p.table != nullptr) || (!hjobs && p.njobs > 46) || p.njobs > 65535)
     return hipErrorInvalidValue;
   const ReduceJob* js = hjobs ? hjobs : p.job;
-  int64_t maxr = 0, maxc = 0;
+  int64_t maxt = 0;  // 16 x 64 tiles of the largest job
   for (int i = 0; i < p.njobs; ++i) {
-    maxr = js[i].rows > maxr ? js[i].rows : maxr;
-    maxc = js[i].cols > maxc ? js[i].cols : maxc;
+    const int64_t t = (js[i].rows + 15) / 16 * ((js[i].cols + 63) / 64);
+    maxt = t > maxt ? t : maxt;
   }
-  if (maxr == 0 || maxc == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((maxr + 15) / 16), static_cast<unsigned>((maxc + 63) / 64), p.njobs);
+  if (maxt == 0) return hipSuccess;
+  // about 16 K workgroups in all; each strides over its job's tiles
+  const int64_t cap = std::max<int64_t>(1, 16384 / p.njobs);
+  dim3 grid(static_cast<unsigned>(std::min<int64_t>(maxt, cap)), 1, p.njobs);
   hipLaunchKernelGGL(reduce_kernel, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
@@ -805,7 +817,9 @@ hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream, 
   int64_t maxn = 0;
   for (int i = 0; i < p.njobs; ++i) maxn = js[i].rows * js[i].cols > maxn ? js[i].rows * js[i].cols : maxn;
   if (maxn == 0) return hipSuccess;
-  dim3 grid(grid_for((maxn + 3) / 4), p.njobs);
+  // about 4 K workgroups in all (the kernel strides over its job)
+  dim3 grid(static_cast<unsigned>(std::min<int64_t>(grid_for((maxn + 3) / 4), std::max<int64_t>(1, 4096 / p.njobs))),
+            p.njobs);
   if (elem_bytes == 2) hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(pack_kernel<uint32_t>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
