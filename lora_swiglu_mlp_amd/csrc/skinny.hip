@@ -11,6 +11,7 @@
 // because at r >= 16 their arithmetic intensity (up to 4r FLOP/byte) is past
 // what the fp32 vector units sustain at 8 TB/s.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -118,60 +119,67 @@ __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
 template <typename T>
 __global__ __launch_bounds__(64) void proj_finish_kernel(ProjFinishParams p) {
   const ProjFinishJob jb = job_at<ProjFinishJob>(p, blockIdx.z);
-  const int n0 = blockIdx.y * 64;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t tmax = jb.outT ? jb.ldT : jb.T;
-  if (n0 >= jb.n1p || t0 >= tmax) return;
-  const int nc = min(64, jb.n1p - n0);  // a multiple of 4
-  const int cpr = nc / 4;               // float4 items per token row
+  // the job's 16-token x 64-column tiles, grid-strided over blockIdx.x (a
+  // merged launch's jobs differ in token count)
+  const int64_t ntn = (jb.n1p + 63) / 64;
+  const int64_t ntiles = (tmax + 15) / 16 * ntn;
   __shared__ float tile[64][17];
   const int lane = threadIdx.x;
+  for (int64_t id = blockIdx.x; id < ntiles; id += gridDim.x) {
+    const int n0 = static_cast<int>(id % ntn) * 64;
+    const int64_t t0 = id / ntn * 16;
+    const int nc = min(64, jb.n1p - n0);  // a multiple of 4
+    const int cpr = nc / 4;               // float4 items per token row
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int it = lane + 64 * q;
-    if (it >= 16 * cpr) break;
-    const int tl = it / cpr, c = it % cpr;
-    const int64_t t = t0 + tl;
-    const int n = n0 + 4 * c;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < jb.T) {
-      const float* src = jb.part + t * jb.ld_part + n;
-      int k = 0;
-      for (; k + 8 <= jb.nparts; k += 8) {
-        float4 x[8];
+    for (int q = 0; q < 4; ++q) {
+      const int it = lane + 64 * q;
+      if (it >= 16 * cpr) break;
+      const int tl = it / cpr, c = it % cpr;
+      const int64_t t = t0 + tl;
+      const int n = n0 + 4 * c;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < jb.T) {
+        const float* src = jb.part + t * jb.ld_part + n;
+        int k = 0;
+        for (; k + 8 <= jb.nparts; k += 8) {
+          float4 x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(k + e) * jb.part_stride);
+          for (int e = 0; e < 8; ++e)
+            x[e] = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(k + e) * jb.part_stride);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v.x += x[e].x;
-          v.y += x[e].y;
-          v.z += x[e].z;
-          v.w += x[e].w;
+          for (int e = 0; e < 8; ++e) {
+            v.x += x[e].x;
+            v.y += x[e].y;
+            v.z += x[e].z;
+            v.w += x[e].w;
+          }
         }
+        for (; k < jb.nparts; ++k) {
+          const float4 x = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(k) * jb.part_stride);
+          v.x += x.x;
+          v.y += x.y;
+          v.z += x.z;
+          v.w += x.w;
+        }
+        if (jb.out_f32) *reinterpret_cast<float4*>(jb.out_f32 + t * jb.ld_f32 + jb.col_off + n) = v;
+        if (jb.out_c)
+          store4(static_cast<T*>(jb.out_c) + t * jb.ld_c + jb.col_off + n, jb.scale * v.x, jb.scale * v.y,
+                 jb.scale * v.z, jb.scale * v.w);
       }
-      for (; k < jb.nparts; ++k) {
-        const float4 x = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(k) * jb.part_stride);
-        v.x += x.x;
-        v.y += x.y;
-        v.z += x.z;
-        v.w += x.w;
-      }
-      if (jb.out_f32) *reinterpret_cast<float4*>(jb.out_f32 + t * jb.ld_f32 + jb.col_off + n) = v;
-      if (jb.out_c)
-        store4(static_cast<T*>(jb.out_c) + t * jb.ld_c + jb.col_off + n, jb.scale * v.x, jb.scale * v.y,
-               jb.scale * v.z, jb.scale * v.w);
+      tile[4 * c + 0][tl] = v.x;
+      tile[4 * c + 1][tl] = v.y;
+      tile[4 * c + 2][tl] = v.z;
+      tile[4 * c + 3][tl] = v.w;
     }
-    tile[4 * c + 0][tl] = v.x;
-    tile[4 * c + 1][tl] = v.y;
-    tile[4 * c + 2][tl] = v.z;
-    tile[4 * c + 3][tl] = v.w;
-  }
-  if (!jb.outT) return;  // uniform over the workgroup
-  __syncthreads();
-  if (lane < nc) {  // t0 + 16 <= ldT: ldT is a multiple of 64
-    T* dst = static_cast<T*>(jb.outT) + static_cast<int64_t>(jb.col_off + n0 + lane) * jb.ldT + t0;
+    if (!jb.outT) continue;  // uniform over the workgroup
+    __syncthreads();
+    if (lane < nc) {  // t0 + 16 <= ldT: ldT is a multiple of 64
+      T* dst = static_cast<T*>(jb.outT) + static_cast<int64_t>(jb.col_off + n0 + lane) * jb.ldT + t0;
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) store4(dst + e, tile[lane][e], tile[lane][e + 1], tile[lane][e + 2], tile[lane][e + 3]);
+      for (int e = 0; e < 16; e += 4) store4(dst + e, tile[lane][e], tile[lane][e + 1], tile[lane][e + 2], tile[lane][e + 3]);
+    }
+    __syncthreads();  // the next tile overwrites the staging
   }
 }
 
@@ -520,16 +528,33 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   const uint32_t srows = static_cast<uint32_t>(jb.srows), scols = static_cast<uint32_t>(jb.scols);
   const E* src = static_cast<const E*>(jb.src);
   E* dst = static_cast<E*>(jb.dst);
+  // four elements in one access where rows keep 4-element alignment
+  typedef typename std::conditional<sizeof(E) == 2, uint2, uint4>::type V;
+  const bool vdst = jb.ld_dst % 4 == 0 && reinterpret_cast<uintptr_t>(dst) % sizeof(V) == 0;
+  const bool vsrc = src && !jb.transpose && jb.ld_src % 4 == 0 && reinterpret_cast<uintptr_t>(src) % sizeof(V) == 0;
   for (uint32_t idx = blockIdx.x * 256 + threadIdx.x; idx < n; idx += gridDim.x * 256) {
     const uint32_t i = idx / cq, j0 = (idx % cq) * 4;
+    E v[4] = {0, 0, 0, 0};
+    if (vsrc && i < srows && j0 + 3 < scols) {
+      const V w = *reinterpret_cast<const V*>(src + static_cast<int64_t>(i) * jb.ld_src + j0);
+      __builtin_memcpy(v, &w, sizeof(V));
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t j = j0 + e;
-      if (j >= cols) break;
-      const uint32_t si = jb.transpose ? j : i, sj = jb.transpose ? i : j;
-      E v = 0;
-      if (src && si < srows && sj < scols) v = src[static_cast<int64_t>(si) * jb.ld_src + sj];
-      dst[static_cast<int64_t>(i) * jb.ld_dst + j] = v;
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t j = j0 + e;
+        const uint32_t si = jb.transpose ? j : i, sj = jb.transpose ? i : j;
+        if (src && j < cols && si < srows && sj < scols) v[e] = src[static_cast<int64_t>(si) * jb.ld_src + sj];
+      }
+    }
+    E* d = dst + static_cast<int64_t>(i) * jb.ld_dst + j0;
+    if (vdst && j0 + 3 < cols) {
+      V w;
+      __builtin_memcpy(&w, v, sizeof(V));
+      *reinterpret_cast<V*>(d) = w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + e < cols) d[e] = v[e];
     }
   }
 }
@@ -752,15 +777,15 @@ hipError_t launch_proj_finish(const ProjFinishParams& p0, int dtype_bf16, hipStr
     for (int i = 0; i < p.njobs; ++i)
       if (p.job[i].T == 0) p.job[i].T = p.T;
   const ProjFinishJob* js = hjobs ? hjobs : p.job;
-  int64_t maxt = 0;
-  int maxn = 0;
+  int64_t maxtiles = 0;  // 16 x 64 tiles of the largest job
   for (int i = 0; i < p.njobs; ++i) {
     const int64_t t = js[i].outT ? js[i].ldT : js[i].T;
-    maxt = t > maxt ? t : maxt;
-    maxn = js[i].n1p > maxn ? js[i].n1p : maxn;
+    const int64_t nt = (t + 15) / 16 * ((js[i].n1p + 63) / 64);
+    maxtiles = nt > maxtiles ? nt : maxtiles;
   }
-  if (maxt <= 0 || maxn <= 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((maxt + 15) / 16), (maxn + 63) / 64, p.njobs);
+  if (maxtiles <= 0) return hipSuccess;
+  // about 16 K workgroups in all; each strides over its job's tiles
+  dim3 grid(static_cast<unsigned>(std::min<int64_t>(maxtiles, std::max<int64_t>(1, 16384 / p.njobs))), 1, p.njobs);
   if (dtype_bf16) hipLaunchKernelGGL(proj_finish_kernel<bf16_t>, grid, dim3(64), 0, stream, p);
   else hipLaunchKernelGGL(proj_finish_kernel<float>, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
@@ -817,9 +842,8 @@ hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream, 
   int64_t maxn = 0;
   for (int i = 0; i < p.njobs; ++i) maxn = js[i].rows * js[i].cols > maxn ? js[i].rows * js[i].cols : maxn;
   if (maxn == 0) return hipSuccess;
-  // about 4 K workgroups in all (the kernel strides over its job)
-  dim3 grid(static_cast<unsigned>(std::min<int64_t>(grid_for((maxn + 3) / 4), std::max<int64_t>(1, 4096 / p.njobs))),
-            p.njobs);
+  // the largest job in at most four passes of its workgroups (the kernel strides over its job)
+  dim3 grid(static_cast<unsigned>(grid_for(((maxn + 3) / 4 + 3) / 4)), p.njobs);
   if (elem_bytes == 2) hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(pack_kernel<uint32_t>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
