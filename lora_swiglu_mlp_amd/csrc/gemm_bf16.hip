@@ -1029,6 +1029,21 @@ __global__ __launch_bounds__(NT8, 1) void gemm8_kernel(GemmParams p) {
   gemm8_body<NN, EPI, QRB>(p, blockIdx.x, gridDim.x, smem);
 }
 
+// grouped forms (the experts of a grouped MLP) of the eight-wave kernel, as
+// gemm_bf16_grouped_kernel and gemm_bf16_table_kernel below
+template <bool NN, int EPI, int QRB>
+__global__ __launch_bounds__(NT8, 1) void gemm8_grouped_kernel(GemmGroups gg) {
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  const int bid = blockIdx.x;
+  int g = 0;
+  while (g + 1 < gg.n && bid >= gg.start[g + 1]) ++g;
+  const GemmParams& p = gg.p[g];
+  const int local = bid - gg.start[g];
+  const int tiles = p.tiles_m * p.tiles_n;
+  if (local >= tiles) return;
+  gemm8_body<NN, EPI, QRB>(p, local, tiles, smem);
+}
+
 // decoded-tile row of packed row pr (gate/up: interleave the two panels)
 template <int EPI>
 __device__ __forceinline__ int q4_dense_row(int pr) {
@@ -1477,6 +1492,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_table_kernel(const Gemm
   gemm_bf16_body<NN, EPI, QRB, NB>(p, local, tiles, smem);
 }
 
+template <bool NN, int EPI, int QRB>
+__global__ __launch_bounds__(NT8, 1) void gemm8_table_kernel(const GemmParams* __restrict__ table, GroupStarts gs) {
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  const int bid = blockIdx.x;
+  int lo = 0, hi = gs.n - 1;  // the last group whose start is <= bid
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gs.start[mid] <= bid) lo = mid;
+    else hi = mid - 1;
+  }
+  const GemmParams& p = table[lo];
+  const int local = bid - gs.start[lo];
+  const int tiles = p.tiles_m * p.tiles_n;
+  if (local >= tiles) return;
+  gemm8_body<NN, EPI, QRB>(p, local, tiles, smem);
+}
+
+// the gate/up and dZ products run on eight waves as in a single launch
+template <int EPI, int NB>
+constexpr bool kGrouped8 = NB == 8 && (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD);
+
 // copy of up to kMaxGemmGroups parameter blocks into a device table
 struct TableChunk {
   GemmParams p[kMaxGemmGroups];
@@ -1519,7 +1555,10 @@ static hipError_t launch_grouped_t(const GemmParams* ps, int n, hipStream_t stre
     }
     gg.start[gg.n] = nblk;
     if (gg.n == 0) continue;
-    hipLaunchKernelGGL((gemm_bf16_grouped_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream, gg);
+    if constexpr (kGrouped8<EPI, NB>)
+      hipLaunchKernelGGL((gemm8_grouped_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream, gg);
+    else
+      hipLaunchKernelGGL((gemm_bf16_grouped_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream, gg);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1625,7 +1664,11 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
     gs.start[cnt] = nblk;
     gs.n = cnt;
     if (nblk == 0) continue;
-    hipLaunchKernelGGL((gemm_bf16_table_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream,
+    if constexpr (kGrouped8<EPI, NB>)
+      hipLaunchKernelGGL((gemm8_table_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream,
+                         static_cast<const GemmParams*>(table), gs);
+    else
+      hipLaunchKernelGGL((gemm_bf16_table_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream,
                        static_cast<const GemmParams*>(table), gs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

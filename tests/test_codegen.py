@@ -80,9 +80,9 @@ def test_wide_tile_k_loops_keep_accumulators_in_place(gemm_asm):
         bad = {o: c for o, c in ops.items() if o.startswith(MOVES)}
         assert not bad, f"{name}: {bad}"
         checked += 1
-    # plain NT, gate/up, plain NN, dZ (both epilogues), their grouped and
-    # table-driven forms (the four-wave kernels)
-    assert checked >= 12, checked
+    # the four-wave kernels: plain NT and NN, their grouped and table-driven
+    # forms (gate/up and dZ run on eight waves, checked below)
+    assert checked >= 6, checked
 
 
 def _dma_loops(body):
@@ -99,13 +99,13 @@ def _dma_loops(body):
 
 
 def test_eight_wave_k_loops_keep_accumulators_in_place(gemm_asm):
-    """The eight-wave ping-pong kernels (dense and 4-bit): 128 accumulators per
-    lane, 32 MFMAs per k-tile, no accumulator moves or scratch traffic in the
-    K loop, and at most 256 registers per lane so that two waves fit one
-    SIMD."""
+    """The eight-wave ping-pong kernels (dense, 4-bit, and the grouped forms
+    of the MoE path): 128 accumulators per lane, 32 MFMAs per k-tile, no
+    accumulator moves or scratch traffic in the K loop, and at most 256
+    registers per lane so that two waves fit one SIMD."""
     ks = _kernels(gemm_asm)
-    names = [n for n in ks if "gemm8_kernel" in n or "gemm8q4_kernel" in n]
-    assert len(names) >= 8, names
+    names = [n for n in ks if "gemm8" in n]
+    assert len(names) >= 14, names
     for name in names:
         loops = [x for x in _dma_loops(ks[name]) if sum("v_mfma" in i for i in x) == 32]
         assert loops, name
