@@ -607,9 +607,17 @@ hipError_t launch_jobs(const std::vector<const SideOp*>& ops, bool has_t, void* 
     }
     const hipError_t e = stage_device_table(all.data(), total * sizeof(J), dtab, st);
     if (e != hipSuccess) return e;
-    q.njobs = static_cast<int32_t>(total);
-    q.table = static_cast<const J*>(dtab);
-    return launch(q, all.data());
+    // at most 8190 jobs per launch: the job index rides in a grid dimension
+    // (65535), times up to 8 column slices for the row projections
+    constexpr size_t kMaxJobs = 8190;
+    for (size_t j0 = 0; j0 < total; j0 += kMaxJobs) {
+      const size_t nj = std::min(kMaxJobs, total - j0);
+      q.njobs = static_cast<int32_t>(nj);
+      q.table = static_cast<const J*>(dtab) + j0;
+      const hipError_t le = launch(q, all.data() + j0);
+      if (le != hipSuccess) return le;
+    }
+    return hipSuccess;
   }
   P q{};
   auto flush = [&]() -> hipError_t {
