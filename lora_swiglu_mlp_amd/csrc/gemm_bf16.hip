@@ -36,9 +36,9 @@
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
+#include "stage_ring.h"
 
 #include <cstring>
-#include <deque>
 #include <map>
 #include <mutex>
 #include <vector>
@@ -1566,22 +1566,17 @@ static hipError_t launch_grouped_t(const GemmParams* ps, int n, hipStream_t stre
 }
 
 // Parameter tables reach the device through a pinned host ring and one copy
-// on the stream (one per device, created on first use and kept until the
+// on the stream (one ring per device, created on first use and kept until the
 // process ends). A region of the ring is written again only once the event
-// recorded behind its previous copy has completed; the host never waits for
-// it. `done` stays false when that copy is still in flight, when the stream is
-// being captured into a graph, or when the table is larger than the ring: the
-// caller then writes the table with copy kernels on the stream.
-constexpr size_t kStageBytes = size_t(4) << 20;
-struct StageUse {
-  size_t off, len;
-  hipEvent_t ev;
-};
+// recorded behind every earlier copy from memory it overlaps has completed;
+// the host never waits for it. `done` stays false when such a copy is still in
+// flight, when the stream is being captured into a graph, or when the table
+// is larger than the ring: the caller then writes the table with copy kernels
+// on the stream.
+constexpr size_t kStageBytes = size_t(16) << 20;
 struct TableStage {
   char* host = nullptr;
-  size_t head = 0;
-  std::deque<StageUse> inflight;  // in ring order: a new region can only overlap the oldest ones
-  std::vector<hipEvent_t> spare;
+  StageRing<hipEvent_t> ring{kStageBytes};
 };
 std::mutex g_stage_mu;
 std::map<int, TableStage> g_stage;
@@ -1604,35 +1599,32 @@ static hipError_t stage_table(const void* src, size_t bytes, void* dst, hipStrea
     return hipSuccess;  // no staging memory: copy kernels
   }
   const size_t len = (bytes + 255) / 256 * 256;
-  if (S.head + len > kStageBytes) S.head = 0;
-  while (!S.inflight.empty()) {
-    const StageUse& u = S.inflight.front();
-    if (!(u.off < S.head + len && S.head < u.off + u.len)) break;
-    e = hipEventQuery(u.ev);
-    if (e == hipErrorNotReady) {
+  size_t off = 0;
+  hipError_t qe = hipSuccess;
+  const int got = S.ring.acquire(len, off, [&qe](hipEvent_t ev) {
+    const hipError_t r = hipEventQuery(ev);
+    if (r == hipSuccess) return 1;
+    if (r == hipErrorNotReady) {
       (void)hipGetLastError();  // not an error: the copy kernels take this table
-      return hipSuccess;
+      return 0;
     }
-    if (e != hipSuccess) return e;
-    S.spare.push_back(u.ev);
-    S.inflight.pop_front();
-  }
-  char* h = S.host + S.head;
+    qe = r;
+    return -1;
+  });
+  if (got < 0) return qe;
+  if (got == 0) return hipSuccess;
+  char* h = S.host + off;
   std::memcpy(h, src, bytes);
   e = hipMemcpyAsync(dst, h, bytes, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return e;
   hipEvent_t ev = nullptr;
-  if (!S.spare.empty()) {
-    ev = S.spare.back();
-    S.spare.pop_back();
-  } else {
+  if (!S.ring.take_spare(ev)) {
     e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
     if (e != hipSuccess) return e;
   }
   e = hipEventRecord(ev, st);
   if (e != hipSuccess) return e;
-  S.inflight.push_back({S.head, len, ev});
-  S.head += len;
+  S.ring.commit(off, len, ev);
   done = true;
   return hipSuccess;
 }

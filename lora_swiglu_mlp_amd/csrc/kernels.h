@@ -248,8 +248,8 @@ hipError_t launch_mfma_probe(const void* ops, float* sink, int blocks, int iters
 
 // Copy `bytes` of host data to the device array `dst` on `stream`, ordered
 // with the stream's other work: through a pinned host ring and one copy when
-// it can, else with copy kernels (under stream capture, or while the ring
-// region is still being copied). The host never waits.
+// it can, else with copy kernels (under stream capture, or while a copy from
+// the ring region it would reuse has not run yet). The host never waits.
 hipError_t stage_device_table(const void* src, size_t bytes, void* dst, hipStream_t stream);
 
 // Split-K finish: y[i] = bf16_rne(part[0][i] + part[1][i] + ... + part[nsplit-1][i]),

@@ -161,10 +161,8 @@ def _moe_buffers(inp, off, wl):
 
 
 def test_moe_parameter_tables_many_calls_in_flight():
-    """Twelve forward+backward calls queued without a host wait: the tables
-    (over 1 MB per call at 600 experts) wrap the 4 MB pinned ring while
-    earlier copies may still be in flight, where the call writes the table
-    with copy kernels instead of waiting. Every call gives the synchronised
+    """Twelve forward+backward calls queued without a host wait, the tables
+    over 1 MB per call at 600 experts. Every call gives the synchronised
     call's outputs bit for bit."""
     import torch
     wl, inp, off = _moe600()
@@ -184,6 +182,36 @@ def test_moe_parameter_tables_many_calls_in_flight():
     for o in outs:
         for k in ref:
             assert torch.equal(o[k], ref[k]), k
+
+
+def test_moe_deep_queue_of_calls():
+    """128 forward+backward steps at the Qwen3-30B-A3B MoE shape queued
+    without a host wait: the host can run more than one lap of the 16 MB
+    pinned table ring ahead of the device, so tables meet regions whose
+    earlier copies have not run yet and go through the copy kernels instead.
+    Every eighth step's outputs (and the last step's) equal the synchronised
+    step's bit for bit."""
+    import torch
+    wl = I.MOE_WORKLOADS["moe_qwen3"]
+    inp, off = I.make_moe_inputs(wl)
+    print(f"[case] moe_qwen3 deep queue: 128 steps, rows {int(off[-1])}", flush=True)
+    m, x, dy, saved, y, grads = _moe_buffers(inp, off, wl)
+    m.forward(x, y, saved)
+    m.backward(dy, x, saved, grads)
+    torch.cuda.synchronize()
+    ref = {"y": y.clone(), **{k: v.clone() for k, v in grads.items()}}
+    scratch = {"y": torch.empty_like(y), **{k: torch.empty_like(v) for k, v in grads.items()}}
+    kept = []
+    for i in range(128):
+        o = {k: torch.empty_like(v) for k, v in ref.items()} if (i % 8 == 0 or i == 127) else scratch
+        m.forward(x, o["y"], saved)
+        m.backward(dy, x, saved, {k: o[k] for k in grads})
+        if o is not scratch:
+            kept.append((i, o))
+    torch.cuda.synchronize()
+    for i, o in kept:
+        for k in ref:
+            assert torch.equal(o[k], ref[k]), (i, k)
 
 
 def test_moe_graph_capture_writes_the_tables_with_copy_kernels():
