@@ -203,12 +203,13 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
  * over every expert's tiles, and each of its small side kernels as launches
  * merged across experts; all on `stream`. `saved` and the workspace hold one
  * region per expert (none in the workspace for an expert without rows), and
- * the workspace a table of GEMM parameters beyond 8 experts, which reaches
- * the device by a copy on `stream` from a small pinned host buffer of the
- * library's own (16 MB, allocated on first use per device, kept until exit).
- * Where a copy from the region of that buffer a call would reuse has not run
- * yet, and under graph capture, small copy kernels on `stream` write the
- * table instead: the host never waits for the device. */
+ * the workspace a table of GEMM parameters beyond 8 experts, which one
+ * workgroup on `stream` reads into the workspace from a pinned host buffer of
+ * the library's own (16 MB plus 512 KB of completion marks, allocated on
+ * first use per device, kept until exit). Where the read from the region of
+ * that buffer a call would reuse has not run yet, and under graph capture,
+ * small copy kernels on `stream` write the table instead: the host never
+ * waits for the device. */
 size_t lora_moe_saved_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets);
 size_t lora_moe_workspace_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets,
                                 int is_backward);

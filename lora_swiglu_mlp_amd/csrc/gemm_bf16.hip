@@ -1540,10 +1540,12 @@ static void set_tiles(GemmParams& p) {
 
 template <bool NN, int EPI, int QRB = 0, int NB = 8>
 static hipError_t launch_grouped_t(const GemmParams* ps, int n, hipStream_t stream) {
-  for (int i0 = 0; i0 < n; i0 += kMaxGemmGroups) {
+  // up to kMaxGemmGroups products with tiles per launch; each product is
+  // taken once (products without tiles are skipped, not counted)
+  for (int i = 0; i < n;) {
     GemmGroups gg{};
     int nblk = 0;
-    for (int i = i0; i < n && gg.n < kMaxGemmGroups; ++i) {
+    for (; i < n && gg.n < kMaxGemmGroups; ++i) {
       GemmParams q = ps[i];
       set_tiles<EPI, NB>(q);
       const int tiles = q.tiles_m * q.tiles_n;
@@ -1565,25 +1567,64 @@ static hipError_t launch_grouped_t(const GemmParams* ps, int n, hipStream_t stre
   return hipSuccess;
 }
 
-// Parameter tables reach the device through a pinned host ring and one copy
-// on the stream (one ring per device, created on first use and kept until the
-// process ends). A region of the ring is written again only once the event
-// recorded behind every earlier copy from memory it overlaps has completed;
-// the host never waits for it. `done` stays false when such a copy is still in
-// flight, when the stream is being captured into a graph, or when the table
-// is larger than the ring: the caller then writes the table with copy kernels
-// on the stream.
+// Parameter tables reach the device through a pinned host ring (one per
+// device, created on first use and kept until the process ends): the host
+// writes a table into a region of the ring, and one workgroup on the stream
+// (fetch_table_kernel) reads it from host memory into the device table, then
+// stores the region's tag into that region's completion slot, also in pinned
+// host memory. So the table moves in stream order with no copy engine and no
+// event: a copy handed to the DMA engine makes the next kernel on the stream
+// wait for a cross-engine signal, about 20 microseconds each on MI355X. A
+// region is written again only once every earlier use it overlaps shows its
+// tag in its slot; the host never waits for it. `done` stays false when such
+// a use is still pending, when the stream is being captured into a graph, or
+// when the table is larger than the ring: the caller then writes the table
+// with copy kernels on the stream.
 constexpr size_t kStageBytes = size_t(16) << 20;
+constexpr size_t kStageAlign = 256;
+constexpr size_t kStageSlots = kStageBytes / kStageAlign;  // one per possible region start
+
+// A use's tag and completion slot, packed: tag << 16 | slot.
+static_assert(kStageSlots <= 65536, "slot index in 16 bits");
+
+__global__ __launch_bounds__(1024) void fetch_table_kernel(const uint64_t* src, uint64_t* dst, int64_t n8,
+                                                           const uint32_t* src_tail, uint32_t* dst_tail,
+                                                           uint64_t* slot, uint64_t tag) {
+  // system-scope loads: the ring is host memory the host rewrites between
+  // uses, so no cached copy of an earlier use may serve them
+  for (int64_t i = threadIdx.x; i < n8; i += 8 * 1024) {
+    uint64_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t j = i + int64_t(k) * 1024;
+      v[k] = j < n8 ? __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t j = i + int64_t(k) * 1024;
+      if (j < n8) dst[j] = v[k];
+    }
+  }
+  if (src_tail != nullptr && threadIdx.x == 0)
+    *dst_tail = __hip_atomic_load(src_tail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  // every thread's loads have returned (their values were stored above); the
+  // mark only tells the host the region was read, so it needs no release
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(slot, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 struct TableStage {
-  char* host = nullptr;
-  StageRing<hipEvent_t> ring{kStageBytes};
+  char* host = nullptr;       // ring, then kStageSlots completion slots
+  char* dev = nullptr;        // the same memory as the device addresses it
+  uint64_t next_tag = 1;
+  StageRing<uint64_t> ring{kStageBytes};
 };
 std::mutex g_stage_mu;
 std::map<int, TableStage> g_stage;
 
 static hipError_t stage_table(const void* src, size_t bytes, void* dst, hipStream_t st, bool& done) {
   done = false;
-  if (bytes > kStageBytes) return hipSuccess;
+  if (bytes > kStageBytes || bytes % 4 || reinterpret_cast<uintptr_t>(dst) % 8) return hipSuccess;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(st, &cs);
   if (e != hipSuccess) return e;
@@ -1593,38 +1634,42 @@ static hipError_t stage_table(const void* src, size_t bytes, void* dst, hipStrea
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lk(g_stage_mu);
   TableStage& S = g_stage[dev];
-  if (!S.host && hipHostMalloc(reinterpret_cast<void**>(&S.host), kStageBytes, hipHostMallocDefault) != hipSuccess) {
-    S.host = nullptr;
-    (void)hipGetLastError();
-    return hipSuccess;  // no staging memory: copy kernels
-  }
-  const size_t len = (bytes + 255) / 256 * 256;
-  size_t off = 0;
-  hipError_t qe = hipSuccess;
-  const int got = S.ring.acquire(len, off, [&qe](hipEvent_t ev) {
-    const hipError_t r = hipEventQuery(ev);
-    if (r == hipSuccess) return 1;
-    if (r == hipErrorNotReady) {
-      (void)hipGetLastError();  // not an error: the copy kernels take this table
-      return 0;
+  if (!S.host) {
+    const size_t total = kStageBytes + kStageSlots * sizeof(uint64_t);
+    void* d = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void**>(&S.host), total, hipHostMallocDefault) != hipSuccess ||
+        hipHostGetDevicePointer(&d, S.host, 0) != hipSuccess) {
+      if (S.host) (void)hipHostFree(S.host);
+      S.host = nullptr;
+      (void)hipGetLastError();
+      return hipSuccess;  // no staging memory: copy kernels
     }
-    qe = r;
-    return -1;
-  });
-  if (got < 0) return qe;
-  if (got == 0) return hipSuccess;
-  char* h = S.host + off;
-  std::memcpy(h, src, bytes);
-  e = hipMemcpyAsync(dst, h, bytes, hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return e;
-  hipEvent_t ev = nullptr;
-  if (!S.ring.take_spare(ev)) {
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
+    std::memset(S.host + kStageBytes, 0, kStageSlots * sizeof(uint64_t));
+    S.dev = static_cast<char*>(d);
   }
-  e = hipEventRecord(ev, st);
+  volatile uint64_t* slots = reinterpret_cast<volatile uint64_t*>(S.host + kStageBytes);
+  const size_t len = (bytes + kStageAlign - 1) / kStageAlign * kStageAlign;
+  size_t off = 0;
+  const int got = S.ring.acquire(len, off, [slots](uint64_t ev) {
+    return slots[ev & 0xffff] == (ev >> 16) ? 1 : 0;
+  });
+  uint64_t spent = 0;
+  while (S.ring.take_spare(spent)) {
+  }
+  if (got <= 0) return hipSuccess;
+  std::memcpy(S.host + off, src, bytes);
+  const uint64_t slot = off / kStageAlign;
+  const uint64_t tag = S.next_tag++;
+  const int64_t n8 = static_cast<int64_t>(bytes / 8);
+  const bool tail = bytes % 8 != 0;
+  hipLaunchKernelGGL(fetch_table_kernel, dim3(1), dim3(1024), 0, st,
+                     reinterpret_cast<const uint64_t*>(S.dev + off), static_cast<uint64_t*>(dst), n8,
+                     tail ? reinterpret_cast<const uint32_t*>(S.dev + off + bytes - 4) : nullptr,
+                     tail ? reinterpret_cast<uint32_t*>(static_cast<char*>(dst) + bytes - 4) : nullptr,
+                     reinterpret_cast<uint64_t*>(S.dev + kStageBytes) + slot, tag);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  S.ring.commit(off, len, ev);
+  S.ring.commit(off, len, tag << 16 | slot);
   done = true;
   return hipSuccess;
 }

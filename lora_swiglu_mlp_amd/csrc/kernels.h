@@ -247,9 +247,10 @@ hipError_t launch_scale_pack(const ScalePackParams& p, hipStream_t stream);
 hipError_t launch_mfma_probe(const void* ops, float* sink, int blocks, int iters, hipStream_t stream);
 
 // Copy `bytes` of host data to the device array `dst` on `stream`, ordered
-// with the stream's other work: through a pinned host ring and one copy when
-// it can, else with copy kernels (under stream capture, or while a copy from
-// the ring region it would reuse has not run yet). The host never waits.
+// with the stream's other work: through a pinned host ring, read by one
+// workgroup on the stream, when it can, else with copy kernels that carry the
+// data in their arguments (under stream capture, or while a read from the
+// ring region it would reuse has not run yet). The host never waits.
 hipError_t stage_device_table(const void* src, size_t bytes, void* dst, hipStream_t stream);
 
 // Split-K finish: y[i] = bf16_rne(part[0][i] + part[1][i] + ... + part[nsplit-1][i]),

@@ -2,9 +2,10 @@
 // reach the device (host code only, no HIP calls, so that it can be checked
 // on its own).
 //
-// A table is written into a region of the ring and copied to the device by a
-// copy enqueued on a stream, followed by an event. The region may be written
-// again only once that copy has run. Regions are handed out in ring order; a
+// A table is written into a region of the ring and read into device memory
+// by work enqueued on a stream, which then marks the use complete (an event,
+// a completion slot). The region may be written again only once that read
+// has run. Regions are handed out in ring order; a
 // table that does not fit before the end starts again at offset 0 and leaves
 // the tail unused, so a use listed earlier can lie anywhere in the ring: every
 // listed use that overlaps a new region is checked, not only the oldest.
