@@ -38,6 +38,7 @@
 #include "lds_dma.h"
 #include "stage_ring.h"
 
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -1584,33 +1585,36 @@ constexpr size_t kStageBytes = size_t(16) << 20;
 constexpr size_t kStageAlign = 256;
 constexpr size_t kStageSlots = kStageBytes / kStageAlign;  // one per possible region start
 
-// A use's tag and completion slot, packed: tag << 16 | slot.
 static_assert(kStageSlots <= 65536, "slot index in 16 bits");
 
-__global__ __launch_bounds__(1024) void fetch_table_kernel(const uint64_t* src, uint64_t* dst, int64_t n8,
-                                                           const uint32_t* src_tail, uint32_t* dst_tail,
-                                                           uint64_t* slot, uint64_t tag) {
+// Workgroup w of the fetch copies words [w * per, (w + 1) * per) of the
+// table (the last also the 4-byte tail) and then marks slot w of the use.
+__global__ __launch_bounds__(256) void fetch_table_kernel(const uint64_t* src, uint64_t* dst, int64_t n8, int64_t per,
+                                                          const uint32_t* src_tail, uint32_t* dst_tail,
+                                                          uint64_t* slots, uint64_t tag) {
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t hi = lo + per < n8 ? lo + per : n8;
   // system-scope loads: the ring is host memory the host rewrites between
   // uses, so no cached copy of an earlier use may serve them
-  for (int64_t i = threadIdx.x; i < n8; i += 8 * 1024) {
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 8 * 256) {
     uint64_t v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int64_t j = i + int64_t(k) * 1024;
-      v[k] = j < n8 ? __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
+      const int64_t j = i + int64_t(k) * 256;
+      v[k] = j < hi ? __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int64_t j = i + int64_t(k) * 1024;
-      if (j < n8) dst[j] = v[k];
+      const int64_t j = i + int64_t(k) * 256;
+      if (j < hi) dst[j] = v[k];
     }
   }
-  if (src_tail != nullptr && threadIdx.x == 0)
+  if (src_tail != nullptr && blockIdx.x + 1 == gridDim.x && threadIdx.x == 0)
     *dst_tail = __hip_atomic_load(src_tail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   // every thread's loads have returned (their values were stored above); the
   // mark only tells the host the region was read, so it needs no release
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(slot, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (threadIdx.x == 0) __hip_atomic_store(slots + blockIdx.x, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 struct TableStage {
@@ -1649,9 +1653,20 @@ static hipError_t stage_table(const void* src, size_t bytes, void* dst, hipStrea
   }
   volatile uint64_t* slots = reinterpret_cast<volatile uint64_t*>(S.host + kStageBytes);
   const size_t len = (bytes + kStageAlign - 1) / kStageAlign * kStageAlign;
+  // one workgroup per 16 KB (at most 64), each marking its own slot: the
+  // slots of a use are those of its own 256-byte blocks, so live uses never
+  // share one
+  const int64_t n8 = static_cast<int64_t>(bytes / 8);
+  int nwg = static_cast<int>((bytes + 16383) / 16384);
+  nwg = std::max(1, std::min({nwg, 64, static_cast<int>(len / kStageAlign)}));
+  const int64_t per = (n8 + nwg - 1) / nwg;
   size_t off = 0;
+  // a use is packed as tag << 22 | workgroups << 16 | first slot
   const int got = S.ring.acquire(len, off, [slots](uint64_t ev) {
-    return slots[ev & 0xffff] == (ev >> 16) ? 1 : 0;
+    const uint64_t first = ev & 0xffff, cnt = (ev >> 16) & 0x3f, tg = ev >> 22;
+    for (uint64_t w = 0; w <= cnt; ++w)
+      if (slots[first + w] != tg) return 0;
+    return 1;
   });
   uint64_t spent = 0;
   while (S.ring.take_spare(spent)) {
@@ -1660,16 +1675,15 @@ static hipError_t stage_table(const void* src, size_t bytes, void* dst, hipStrea
   std::memcpy(S.host + off, src, bytes);
   const uint64_t slot = off / kStageAlign;
   const uint64_t tag = S.next_tag++;
-  const int64_t n8 = static_cast<int64_t>(bytes / 8);
   const bool tail = bytes % 8 != 0;
-  hipLaunchKernelGGL(fetch_table_kernel, dim3(1), dim3(1024), 0, st,
-                     reinterpret_cast<const uint64_t*>(S.dev + off), static_cast<uint64_t*>(dst), n8,
+  hipLaunchKernelGGL(fetch_table_kernel, dim3(nwg), dim3(256), 0, st,
+                     reinterpret_cast<const uint64_t*>(S.dev + off), static_cast<uint64_t*>(dst), n8, per,
                      tail ? reinterpret_cast<const uint32_t*>(S.dev + off + bytes - 4) : nullptr,
                      tail ? reinterpret_cast<uint32_t*>(static_cast<char*>(dst) + bytes - 4) : nullptr,
                      reinterpret_cast<uint64_t*>(S.dev + kStageBytes) + slot, tag);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  S.ring.commit(off, len, tag << 16 | slot);
+  S.ring.commit(off, len, tag << 22 | uint64_t(nwg - 1) << 16 | slot);
   done = true;
   return hipSuccess;
 }

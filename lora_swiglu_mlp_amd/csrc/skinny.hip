@@ -516,45 +516,84 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Zero-padded copy of an adapter factor (flat index over the destination),
-// four consecutive destination elements of one row per thread, 32-bit index
-// arithmetic (every factor has far fewer than 2^31 elements).
+// Zero-padded copy of an adapter factor, dst[i][j] = src[i][j] where the
+// source has that element, else 0 (i < rows, j < cols), or with transpose
+// dst[i][j] = src[j][i]. Plain copies: a thread moves groups of 16 bytes (G
+// consecutive destination elements of one row), four groups in flight per
+// iteration, with 16-byte accesses wherever rows and pointers allow.
+// Transposes (at most 64 destination rows, the rank): 64 source rows at a
+// time through LDS, read along source rows and written along destination
+// rows. 32-bit index arithmetic (every factor has far fewer than 2^31
+// elements).
 template <typename E>
 __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
+  __shared__ E tile[64 * 65];
   const PackJob jb = job_at<PackJob>(p, blockIdx.y);
-  const uint32_t cols = static_cast<uint32_t>(jb.cols);
-  const uint32_t cq = (cols + 3) / 4;  // groups of four per destination row
-  const uint32_t n = static_cast<uint32_t>(jb.rows) * cq;
+  const uint32_t rows = static_cast<uint32_t>(jb.rows), cols = static_cast<uint32_t>(jb.cols);
   const uint32_t srows = static_cast<uint32_t>(jb.srows), scols = static_cast<uint32_t>(jb.scols);
   const E* src = static_cast<const E*>(jb.src);
   E* dst = static_cast<E*>(jb.dst);
-  // four elements in one access where rows keep 4-element alignment
-  typedef typename std::conditional<sizeof(E) == 2, uint2, uint4>::type V;
-  const bool vdst = jb.ld_dst % 4 == 0 && reinterpret_cast<uintptr_t>(dst) % sizeof(V) == 0;
-  const bool vsrc = src && !jb.transpose && jb.ld_src % 4 == 0 && reinterpret_cast<uintptr_t>(src) % sizeof(V) == 0;
-  for (uint32_t idx = blockIdx.x * 256 + threadIdx.x; idx < n; idx += gridDim.x * 256) {
-    const uint32_t i = idx / cq, j0 = (idx % cq) * 4;
-    E v[4] = {0, 0, 0, 0};
-    if (vsrc && i < srows && j0 + 3 < scols) {
-      const V w = *reinterpret_cast<const V*>(src + static_cast<int64_t>(i) * jb.ld_src + j0);
-      __builtin_memcpy(v, &w, sizeof(V));
-    } else {
+  const uint32_t ld_dst = static_cast<uint32_t>(jb.ld_dst), ld_src = static_cast<uint32_t>(jb.ld_src);
+  if (jb.transpose && rows <= 64) {
+    for (uint32_t j0 = blockIdx.x * 64; j0 < cols; j0 += gridDim.x * 64) {
+      // source rows j0 .. j0 + 63, their first `rows` elements
+      for (uint32_t e = threadIdx.x; e < 64 * rows; e += 256) {
+        const uint32_t jj = e / rows, i = e % rows, j = j0 + jj;
+        E v = 0;
+        if (src && j < srows && i < scols && j < cols) v = src[j * ld_src + i];
+        tile[jj * 65 + i] = v;
+      }
+      __syncthreads();
+      for (uint32_t e = threadIdx.x; e < rows * 64; e += 256) {
+        const uint32_t i = e / 64, jj = e % 64, j = j0 + jj;
+        if (j < cols) dst[i * ld_dst + j] = tile[jj * 65 + i];
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  constexpr uint32_t G = 16 / sizeof(E);  // elements per group
+  const uint32_t cq = (cols + G - 1) / G;  // groups per destination row
+  const uint32_t n = rows * cq;
+  const bool vdst = ld_dst % G == 0 && reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+  const bool vsrc = src && !jb.transpose && ld_src % G == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0;
+  const uint32_t stride = gridDim.x * 256;
+  for (uint32_t base = blockIdx.x * 256 + threadIdx.x; base < n; base += 4 * stride) {
+    E v[4][G];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t j = j0 + e;
-        const uint32_t si = jb.transpose ? j : i, sj = jb.transpose ? i : j;
-        if (src && j < cols && si < srows && sj < scols) v[e] = src[static_cast<int64_t>(si) * jb.ld_src + sj];
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t idx = base + u * stride;
+      const uint32_t i = idx / cq, j0 = (idx % cq) * G;
+#pragma unroll
+      for (uint32_t e = 0; e < G; ++e) v[u][e] = 0;
+      if (idx >= n || !src) continue;
+      if (vsrc && i < srows && j0 + G - 1 < scols) {
+        const uint4 w = *reinterpret_cast<const uint4*>(src + i * ld_src + j0);
+        __builtin_memcpy(v[u], &w, 16);
+      } else {
+#pragma unroll
+        for (uint32_t e = 0; e < G; ++e) {
+          const uint32_t j = j0 + e;
+          const uint32_t si = jb.transpose ? j : i, sj = jb.transpose ? i : j;
+          if (j < cols && si < srows && sj < scols) v[u][e] = src[si * ld_src + sj];
+        }
       }
     }
-    E* d = dst + static_cast<int64_t>(i) * jb.ld_dst + j0;
-    if (vdst && j0 + 3 < cols) {
-      V w;
-      __builtin_memcpy(&w, v, sizeof(V));
-      *reinterpret_cast<V*>(d) = w;
-    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j0 + e < cols) d[e] = v[e];
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t idx = base + u * stride;
+      if (idx >= n) continue;
+      const uint32_t i = idx / cq, j0 = (idx % cq) * G;
+      E* d = dst + i * ld_dst + j0;
+      if (vdst && j0 + G - 1 < cols) {
+        uint4 w;
+        __builtin_memcpy(&w, v[u], 16);
+        *reinterpret_cast<uint4*>(d) = w;
+      } else {
+#pragma unroll
+        for (uint32_t e = 0; e < G; ++e)
+          if (j0 + e < cols) d[e] = v[u][e];
+      }
     }
   }
 }
@@ -842,8 +881,17 @@ hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream, 
   int64_t maxn = 0;
   for (int i = 0; i < p.njobs; ++i) maxn = js[i].rows * js[i].cols > maxn ? js[i].rows * js[i].cols : maxn;
   if (maxn == 0) return hipSuccess;
-  // the largest job in at most four passes of its workgroups (the kernel strides over its job)
-  dim3 grid(static_cast<unsigned>(grid_for(((maxn + 3) / 4 + 3) / 4)), p.njobs);
+  if (elem_bytes != 2 && elem_bytes != 4) return hipErrorInvalidValue;
+  // the largest job in one pass of its workgroups: plain copies move four
+  // groups of 16 bytes per thread, transposes 64 columns per workgroup
+  int64_t maxg = 1;
+  for (int i = 0; i < p.njobs; ++i) {
+    const int64_t g = js[i].transpose && js[i].rows <= 64
+                          ? (js[i].cols + 63) / 64
+                          : (js[i].rows * ((js[i].cols * elem_bytes + 15) / 16) + 1023) / 1024;
+    maxg = g > maxg ? g : maxg;
+  }
+  dim3 grid(static_cast<unsigned>(std::min<int64_t>(maxg, 65535)), p.njobs);
   if (elem_bytes == 2) hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(pack_kernel<uint32_t>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
