@@ -1470,44 +1470,70 @@ static hipError_t launch8_t(GemmParams p, hipStream_t stream) {
 // Groups whose parameter blocks sit in device memory (more groups than the
 // kernel arguments hold): the same workgroup -> (group, tile) map, with the
 // group starts in the arguments.
+//
+// With many small groups (the experts of a fine-grained MoE), each group's
+// tiles can instead all run on one XCD (`pinned`): workgroup b runs on XCD
+// b % 8 as its slot b / 8 there; the groups of XCD x are xfirst[x] ..
+// xfirst[x+1]-1 and group g takes slots start[g] .. of its XCD. A group's
+// tiles then occupy consecutive slots of one XCD, so they run at about the
+// same time and share its L2: the expert's weight panels are fetched once
+// for all its row tiles, and each row panel once for all its column tiles,
+// where spread over eight XCDs every XCD fetched its own copies.
 struct GroupStarts {
   int32_t start[kMaxTableGroups + 1];
   int32_t n;
+  int32_t pinned;
+  int32_t xfirst[9];
 };
+
+// (group, tile within the group) of workgroup bid; false for an idle one
+__device__ __forceinline__ bool group_of(const GroupStarts& gs, int bid, int& g, int& local) {
+  int lo, hi, s;
+  if (gs.pinned) {
+    s = bid >> 3;
+    lo = gs.xfirst[bid & 7];
+    hi = gs.xfirst[(bid & 7) + 1] - 1;
+    if (lo > hi) return false;
+  } else {
+    s = bid;
+    lo = 0;
+    hi = gs.n - 1;
+  }
+  while (lo < hi) {  // the last group whose start is <= s
+    const int mid = (lo + hi + 1) >> 1;
+    if (gs.start[mid] <= s) lo = mid;
+    else hi = mid - 1;
+  }
+  g = lo;
+  local = s - gs.start[lo];
+  return true;
+}
 
 template <bool NN, int EPI, int QRB, int NB>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_table_kernel(const GemmParams* __restrict__ table,
                                                                      GroupStarts gs) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
-  const int bid = blockIdx.x;
-  int lo = 0, hi = gs.n - 1;  // the last group whose start is <= bid
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (gs.start[mid] <= bid) lo = mid;
-    else hi = mid - 1;
-  }
-  const GemmParams& p = table[lo];
-  const int local = bid - gs.start[lo];
+  int g, local;
+  if (!group_of(gs, blockIdx.x, g, local)) return;
+  const GemmParams& p = table[g];
   const int tiles = p.tiles_m * p.tiles_n;
   if (local >= tiles) return;
-  gemm_bf16_body<NN, EPI, QRB, NB>(p, local, tiles, smem);
+  // pinned: the group's tiles in plain order on one XCD (bid 8 * local of
+  // 8 * tiles maps to tile `local`)
+  if (gs.pinned) gemm_bf16_body<NN, EPI, QRB, NB>(p, 8 * local, 8 * tiles, smem);
+  else gemm_bf16_body<NN, EPI, QRB, NB>(p, local, tiles, smem);
 }
 
 template <bool NN, int EPI, int QRB>
 __global__ __launch_bounds__(NT8, 1) void gemm8_table_kernel(const GemmParams* __restrict__ table, GroupStarts gs) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
-  const int bid = blockIdx.x;
-  int lo = 0, hi = gs.n - 1;  // the last group whose start is <= bid
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (gs.start[mid] <= bid) lo = mid;
-    else hi = mid - 1;
-  }
-  const GemmParams& p = table[lo];
-  const int local = bid - gs.start[lo];
+  int g, local;
+  if (!group_of(gs, blockIdx.x, g, local)) return;
+  const GemmParams& p = table[g];
   const int tiles = p.tiles_m * p.tiles_n;
   if (local >= tiles) return;
-  gemm8_body<NN, EPI, QRB>(p, local, tiles, smem);
+  if (gs.pinned) gemm8_body<NN, EPI, QRB>(p, 8 * local, 8 * tiles, smem);
+  else gemm8_body<NN, EPI, QRB>(p, local, tiles, smem);
 }
 
 // the gate/up and dZ products run on eight waves as in a single launch
@@ -1695,10 +1721,48 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
     GroupStarts gs{};
     int nblk = 0;
     std::vector<GemmParams> qs(ps + i0, ps + i0 + cnt);
+    int maxt = 0;
     for (int i = 0; i < cnt; ++i) {
       set_tiles<EPI, NB>(qs[i]);
-      gs.start[i] = nblk;
-      nblk += (qs[i].tiles_m * qs[i].tiles_n + 7) / 8 * 8;
+      maxt = std::max(maxt, qs[i].tiles_m * qs[i].tiles_n);
+    }
+    // pinned when there are many groups and each fits about two waves of one
+    // XCD's 32 compute units; else every group spread over the eight XCDs
+    gs.pinned = cnt >= 16 && maxt <= 64;
+    if (gs.pinned) {
+      // longest groups first, each to the XCD with the fewest slots so far
+      std::vector<int> ord(cnt), xcd(cnt);
+      for (int i = 0; i < cnt; ++i) ord[i] = i;
+      std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) {
+        return qs[a].tiles_m * qs[a].tiles_n > qs[b].tiles_m * qs[b].tiles_n;
+      });
+      int load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int i : ord) {
+        const int x = static_cast<int>(std::min_element(load, load + 8) - load);
+        xcd[i] = x;
+        load[x] += qs[i].tiles_m * qs[i].tiles_n;
+      }
+      std::vector<GemmParams> by;
+      by.reserve(cnt);
+      int k = 0;
+      for (int x = 0; x < 8; ++x) {
+        gs.xfirst[x] = k;
+        int slot = 0;
+        for (int i : ord) {
+          if (xcd[i] != x) continue;
+          by.push_back(qs[i]);
+          gs.start[k++] = slot;
+          slot += qs[i].tiles_m * qs[i].tiles_n;
+        }
+      }
+      gs.xfirst[8] = k;
+      qs.swap(by);
+      nblk = 8 * *std::max_element(load, load + 8);
+    } else {
+      for (int i = 0; i < cnt; ++i) {
+        gs.start[i] = nblk;
+        nblk += (qs[i].tiles_m * qs[i].tiles_n + 7) / 8 * 8;
+      }
     }
     bool staged = false;
     hipError_t se = stage_table(qs.data(), qs.size() * sizeof(GemmParams), table, stream, staged);
@@ -1712,7 +1776,7 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    gs.start[cnt] = nblk;
+    if (!gs.pinned) gs.start[cnt] = nblk;
     gs.n = cnt;
     if (nblk == 0) continue;
     if constexpr (kGrouped8<EPI, NB>)
