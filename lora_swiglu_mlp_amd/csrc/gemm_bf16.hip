@@ -1715,7 +1715,8 @@ static hipError_t stage_table(const void* src, size_t bytes, void* dst, hipStrea
 }
 
 template <bool NN, int EPI, int QRB = 0, int NB = 8>
-static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table, hipStream_t stream) {
+static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table, hipStream_t stream,
+                                 TableBatch* batch) {
   for (int i0 = 0; i0 < n; i0 += kMaxTableGroups) {
     const int cnt = n - i0 < kMaxTableGroups ? n - i0 : kMaxTableGroups;
     GroupStarts gs{};
@@ -1764,6 +1765,29 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
         nblk += (qs[i].tiles_m * qs[i].tiles_n + 7) / 8 * 8;
       }
     }
+    if (!gs.pinned) gs.start[cnt] = nblk;
+    gs.n = cnt;
+    if (nblk == 0) continue;
+    if (batch) {
+      const size_t bytes = qs.size() * sizeof(GemmParams);
+      void* dt = batch->add(qs.data(), bytes);
+      if (!dt) {
+        const hipError_t me = batch->make_room();
+        if (me != hipSuccess) return me;
+        dt = batch->add(qs.data(), bytes);
+        if (!dt) return hipErrorInvalidValue;  // larger than the whole batch
+      }
+      const GemmParams* tp = static_cast<const GemmParams*>(dt);
+      batch->defer([tp, gs, nblk, stream]() -> hipError_t {
+        if constexpr (kGrouped8<EPI, NB>)
+          hipLaunchKernelGGL((gemm8_table_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream, tp, gs);
+        else
+          hipLaunchKernelGGL((gemm_bf16_table_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream, tp,
+                             gs);
+        return hipGetLastError();
+      });
+      continue;
+    }
     bool staged = false;
     hipError_t se = stage_table(qs.data(), qs.size() * sizeof(GemmParams), table, stream, staged);
     if (se != hipSuccess) return se;
@@ -1776,9 +1800,6 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    if (!gs.pinned) gs.start[cnt] = nblk;
-    gs.n = cnt;
-    if (nblk == 0) continue;
     if constexpr (kGrouped8<EPI, NB>)
       hipLaunchKernelGGL((gemm8_table_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream,
                          static_cast<const GemmParams*>(table), gs);
@@ -1901,21 +1922,21 @@ hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi
 }
 
 hipError_t launch_gemm_bf16_grouped_table(const GemmParams* ps, int n, int nn, int epi, GemmParams* table,
-                                          hipStream_t stream) {
+                                          hipStream_t stream, TableBatch* batch) {
   if (n <= 0) return hipSuccess;
   const GemmParams& p = ps[0];
-  if (!nn && epi == EPI_STORE) return launch_table_t<false, EPI_STORE>(ps, n, table, stream);
-  if (!nn && epi == EPI_SWIGLU_FWD) return launch_table_t<false, EPI_SWIGLU_FWD>(ps, n, table, stream);
-  if (nn && epi == EPI_STORE) return launch_table_t<true, EPI_STORE>(ps, n, table, stream);
+  if (!nn && epi == EPI_STORE) return launch_table_t<false, EPI_STORE>(ps, n, table, stream, batch);
+  if (!nn && epi == EPI_SWIGLU_FWD) return launch_table_t<false, EPI_SWIGLU_FWD>(ps, n, table, stream, batch);
+  if (nn && epi == EPI_STORE) return launch_table_t<true, EPI_STORE>(ps, n, table, stream, batch);
   if (nn && epi == EPI_SWIGLU_BWD) {
     const bool narrow = p.tile_n == 128;
     if (p.tile_n != 0 && p.tile_n != 128 && p.tile_n != 256) return hipErrorInvalidValue;
     if (p.pj_part0 == nullptr)
-      return narrow ? launch_table_t<true, EPI_SWIGLU_BWD, 0, 4>(ps, n, table, stream)
-                    : launch_table_t<true, EPI_SWIGLU_BWD, 0, 8>(ps, n, table, stream);
+      return narrow ? launch_table_t<true, EPI_SWIGLU_BWD, 0, 4>(ps, n, table, stream, batch)
+                    : launch_table_t<true, EPI_SWIGLU_BWD, 0, 8>(ps, n, table, stream, batch);
     if (p.pj_r16 == 16)
-      return narrow ? launch_table_t<true, EPI_SWIGLU_BWD, 1, 4>(ps, n, table, stream)
-                    : launch_table_t<true, EPI_SWIGLU_BWD, 1, 8>(ps, n, table, stream);
+      return narrow ? launch_table_t<true, EPI_SWIGLU_BWD, 1, 4>(ps, n, table, stream, batch)
+                    : launch_table_t<true, EPI_SWIGLU_BWD, 1, 8>(ps, n, table, stream, batch);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

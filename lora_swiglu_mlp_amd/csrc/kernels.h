@@ -5,6 +5,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <functional>
+
 namespace lmlp {
 
 // EPI_STORE_F32: the fp32 accumulators themselves (a split-K partial), no rounding.
@@ -82,13 +84,27 @@ hipError_t launch_gemm_bf16(const GemmParams& p, int nn, int epi, hipStream_t st
 // The same products, n of them of one kind (grouped MLP experts), in
 // launches of up to kMaxGemmGroups products each.
 hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi, hipStream_t stream);
+// Tables of several launches staged together (one read of the pinned ring
+// for all of them): add() copies a table into the batch and returns the
+// device address it will have (nullptr: no room left; make_room() then
+// enqueues what the batch holds so far); defer() queues a launch that reads
+// such a table, to go out, in order, once the batch is staged.
+struct TableBatch {
+  virtual ~TableBatch() = default;
+  virtual void* add(const void* src, size_t bytes) = 0;
+  virtual hipError_t make_room() = 0;
+  virtual void defer(std::function<hipError_t()> launch) = 0;
+};
+
 // The same with the parameter blocks in device memory: `table` (device, at
 // least n * sizeof(GemmParams) bytes, 16-byte aligned) receives the n blocks
-// through small copy kernels on `stream`, and one launch per
-// kMaxTableGroups products reads them there.
+// on `stream` (through the pinned ring, or small copy kernels), and one
+// launch per kMaxTableGroups products reads them there. With `batch`, the
+// blocks go into the batch instead (`table` unused) and the launches are
+// deferred to it.
 constexpr int kMaxTableGroups = 512;
 hipError_t launch_gemm_bf16_grouped_table(const GemmParams* ps, int n, int nn, int epi, GemmParams* table,
-                                          hipStream_t stream);
+                                          hipStream_t stream, TableBatch* batch = nullptr);
 // Products whose leading K segments have a 4-bit B operand (seg.bint4), on
 // the eight-wave kernel: NT (gate/up, down): codes [N][K/2] bytes (ldb = K),
 // scales fp32 block-major [K/64][N] (bs0/bs1); NN (dZ, dX): codes [K][N/2]

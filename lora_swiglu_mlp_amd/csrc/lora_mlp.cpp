@@ -34,6 +34,7 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <type_traits>
@@ -583,46 +584,56 @@ static_assert(sizeof(PackJob) <= kSideJobBytes && sizeof(RowProjJob) <= kSideJob
                   sizeof(ReduceJob) <= kSideJobBytes,
               "side job table entries");
 
-// One kind's recorded jobs: with a device job table big enough, one launch
-// reading its jobs from the table (staged on the stream); else merged into
-// launches of up to the job capacity of the kernel arguments.
+// One kind's recorded jobs: with a job table batch, one launch (at most 8190
+// jobs each) reading its jobs from the table, deferred to the batch; else
+// merged into launches of up to the job capacity of the kernel arguments
+// (deferred to the batch too when there is one, so that the order holds).
 template <typename P, typename L>
-hipError_t launch_jobs(const std::vector<const SideOp*>& ops, bool has_t, void* dtab, size_t dtab_bytes,
-                       hipStream_t st, L launch) {
+hipError_t launch_jobs(const std::vector<const SideOp*>& ops, bool has_t, TableBatch* tb, L launch) {
   using J = typename std::remove_reference<decltype(P{}.job[0])>::type;
   constexpr int cap = int(sizeof(P{}.job) / sizeof(J));
   size_t total = 0;
   for (const SideOp* o : ops) total += size_t(o->njobs);
-  if (dtab && total > size_t(cap) && total * sizeof(J) <= dtab_bytes) {
-    std::vector<J> all;
-    all.reserve(total);
+  if (tb && total > size_t(cap)) {
+    auto all = std::make_shared<std::vector<J>>();
+    all->reserve(total);
     P q{};
     for (const SideOp* o : ops) {
       const J* js = reinterpret_cast<const J*>(o->jobs.data());
       for (int i = 0; i < o->njobs; ++i) {
-        all.push_back(js[i]);
+        all->push_back(js[i]);
         if constexpr (!std::is_same<J, PackJob>::value && !std::is_same<J, ReduceJob>::value)
           if (has_t && js[i].T > q.T) q.T = js[i].T;
       }
     }
-    const hipError_t e = stage_device_table(all.data(), total * sizeof(J), dtab, st);
-    if (e != hipSuccess) return e;
+    void* dtab = tb->add(all->data(), total * sizeof(J));
+    if (!dtab) {
+      const hipError_t e = tb->make_room();
+      if (e != hipSuccess) return e;
+      dtab = tb->add(all->data(), total * sizeof(J));
+      if (!dtab) return hipErrorInvalidValue;  // larger than the whole batch
+    }
     // at most 8190 jobs per launch: the job index rides in a grid dimension
     // (65535), times up to 8 column slices for the row projections
     constexpr size_t kMaxJobs = 8190;
     for (size_t j0 = 0; j0 < total; j0 += kMaxJobs) {
-      const size_t nj = std::min(kMaxJobs, total - j0);
-      q.njobs = static_cast<int32_t>(nj);
-      q.table = static_cast<const J*>(dtab) + j0;
-      const hipError_t le = launch(q, all.data() + j0);
-      if (le != hipSuccess) return le;
+      P qj = q;
+      qj.njobs = static_cast<int32_t>(std::min(kMaxJobs, total - j0));
+      qj.table = static_cast<const J*>(dtab) + j0;
+      tb->defer([qj, all, j0, launch]() { return launch(qj, all->data() + j0); });
     }
     return hipSuccess;
   }
   P q{};
   auto flush = [&]() -> hipError_t {
     if (q.njobs == 0) return hipSuccess;
-    const hipError_t e = launch(q, nullptr);
+    hipError_t e = hipSuccess;
+    if (tb) {
+      const P qq = q;
+      tb->defer([qq, launch]() { return launch(qq, nullptr); });
+    } else {
+      e = launch(q, nullptr);
+    }
     q = P{};
     return e;
   };
@@ -641,33 +652,30 @@ hipError_t launch_jobs(const std::vector<const SideOp*>& ops, bool has_t, void* 
   return flush();
 }
 
-hipError_t launch_side_group(const std::vector<const SideOp*>& ops, hipStream_t st, void* dtab, size_t dtab_bytes) {
+hipError_t launch_side_group(const std::vector<const SideOp*>& ops, hipStream_t st, TableBatch* tb) {
   const int kind = ops[0]->kind, flag = ops[0]->flag;
   switch (kind) {
     case SK_PACK:
-      return launch_jobs<PackParams>(ops, false, dtab, dtab_bytes, st, [&](const PackParams& q, const PackJob* h) {
+      return launch_jobs<PackParams>(ops, false, tb, [flag, st](const PackParams& q, const PackJob* h) {
         return launch_pack(q, flag, st, h);
       });
     case SK_ROWPROJ:
-      return launch_jobs<RowProjParams>(ops, true, dtab, dtab_bytes, st,
-                                        [&](const RowProjParams& q, const RowProjJob* h) {
-                                          return launch_rowproj(q, flag, st, h);
-                                        });
+      return launch_jobs<RowProjParams>(ops, true, tb, [flag, st](const RowProjParams& q, const RowProjJob* h) {
+        return launch_rowproj(q, flag, st, h);
+      });
     case SK_FINISH:
-      return launch_jobs<ProjFinishParams>(ops, true, dtab, dtab_bytes, st,
-                                           [&](const ProjFinishParams& q, const ProjFinishJob* h) {
+      return launch_jobs<ProjFinishParams>(ops, true, tb,
+                                           [flag, st](const ProjFinishParams& q, const ProjFinishJob* h) {
                                              return launch_proj_finish(q, flag, st, h);
                                            });
     case SK_COLPROJ:
-      return launch_jobs<ColProjParams>(ops, true, dtab, dtab_bytes, st,
-                                        [&](const ColProjParams& q, const ColProjJob* h) {
-                                          return launch_colproj(q, flag, st, h);
-                                        });
+      return launch_jobs<ColProjParams>(ops, true, tb, [flag, st](const ColProjParams& q, const ColProjJob* h) {
+        return launch_colproj(q, flag, st, h);
+      });
     case SK_REDUCE:
-      return launch_jobs<ReduceParams>(ops, false, dtab, dtab_bytes, st,
-                                       [&](const ReduceParams& q, const ReduceJob* h) {
-                                         return launch_reduce(q, st, h);
-                                       });
+      return launch_jobs<ReduceParams>(ops, false, tb, [st](const ReduceParams& q, const ReduceJob* h) {
+        return launch_reduce(q, st, h);
+      });
     default:
       return hipErrorInvalidValue;
   }
@@ -1373,8 +1381,9 @@ struct MoePlan {
   std::vector<size_t> soff, ssize;          // saved region of each expert
   std::vector<size_t> wfoff, wfsize, wboff, wbsize;  // forward / backward workspace regions
   size_t saved_total = 0, ws_fwd = 0, ws_bwd = 0;
-  size_t tab_fwd = 0, tab_bwd = 0;  // GEMM parameter tables (more experts than one launch's arguments hold)
-  size_t side_fwd = 0, side_bwd = 0, side_bytes = 0;  // side-kernel job tables
+  // one region per pass for the tables of a phase (more experts than one
+  // launch's arguments hold): GEMM parameter blocks and side-kernel jobs
+  size_t tab_fwd = 0, tab_bwd = 0, tab_bytes = 0;
   bool table = false;
   Dims d;  // the whole call
 };
@@ -1386,13 +1395,72 @@ struct MoePlan {
 // out merged across experts round by round (round r: every expert's r-th
 // launch; one expert's launches keep their order), then the GEMMs the
 // experts reached, grouped by kind; until no expert hands back a GEMM.
-static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int64_t t_split, GemmParams* table,
-                      void* side_table, size_t side_bytes,
-                      const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
+// The job and parameter tables of one phase of the grouped MLP, in one
+// batch: laid out back to back (256-byte aligned) in a host buffer whose
+// device copy is the pass's table region of the workspace, with the launches
+// that read them queued; flush() stages the buffer with one read of the
+// pinned ring and then enqueues the launches in order, each timed under its
+// name when profiling is on.
+class PhaseTables final : public TableBatch {
+ public:
+  PhaseTables(void* dev, size_t cap, hipStream_t st) : dev_(static_cast<char*>(dev)), cap_(cap), st_(st) {}
+  const char* name = "";  // of the launches deferred next
+  void* add(const void* src, size_t bytes) override {
+    const size_t off = (host_.size() + 255) / 256 * 256;
+    if (off + bytes > cap_) return nullptr;
+    host_.resize(off + bytes);
+    std::memcpy(host_.data() + off, src, bytes);
+    return dev_ + off;
+  }
+  void defer(std::function<hipError_t()> launch) override { q_.push_back({name, std::move(launch)}); }
+  hipError_t make_room() override {
+    failed_ = nullptr;
+    return run();
+  }
+  int flush() {
+    failed_ = nullptr;
+    const hipError_t e = run();
+    return e == hipSuccess ? LMLP_OK : hip_rc(e, failed_ ? failed_ : "tables");
+  }
+
+ private:
+  hipError_t run() {
+    hipStream_t st = st_;
+    if (!host_.empty()) {
+      ProfScope ps(st, "tables");
+      const hipError_t e = stage_device_table(host_.data(), host_.size(), dev_, st);
+      if (e != hipSuccess) return e;
+      ps.done();
+    }
+    for (auto& l : q_) {
+      ProfScope ps(st, l.first);
+      const hipError_t e = l.second();
+      if (e != hipSuccess) {
+        failed_ = l.first;
+        return e;
+      }
+      ps.done();
+    }
+    host_.clear();
+    q_.clear();
+    return hipSuccess;
+  }
+  char* dev_;
+  size_t cap_;
+  hipStream_t st_;
+  std::vector<char> host_;
+  std::vector<std::pair<const char*, std::function<hipError_t()>>> q_;
+  const char* failed_ = nullptr;
+};
+
+static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int64_t t_split, void* tables,
+                      size_t table_bytes, const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
   std::vector<Exec> ex(order.size());
   std::vector<std::vector<SideOp>> ops(order.size());
   hipStream_t st = caller;
   for (int phase = 0;; ++phase) {
+    PhaseTables tb(tables, table_bytes, st);
+    PhaseTables* tbp = tables ? &tb : nullptr;
     size_t rounds = 0;
     for (size_t k = 0; k < order.size(); ++k) {
       ex[k] = Exec{};
@@ -1416,7 +1484,12 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int
           grp.push_back(&b);
           taken[j] = true;
         }
-        LMLP_LAUNCH(a.name, launch_side_group(grp, st, side_table, side_bytes));
+        if (tbp) {
+          tb.name = a.name;
+          LMLP_TRY(hip_rc(launch_side_group(grp, st, tbp), a.name));
+        } else {
+          LMLP_LAUNCH(a.name, launch_side_group(grp, st, nullptr));
+        }
       }
     }
     // the GEMMs of this phase: dense bf16 ones grouped by kind, the rest one by one
@@ -1426,8 +1499,17 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int
       if (!ex[k].sunk || done[k]) continue;
       any = true;
       if (!ex[k].groupable) {
-        LMLP_LAUNCH(ex[k].name, ex[k].gp.seg[0].bint4 ? run_q4(ex[k].gp, ex[k].nn, ex[k].epi, st)
-                                                      : launch_gemm_f32(ex[k].gp, ex[k].nn, ex[k].epi, st));
+        const GemmParams gp = ex[k].gp;
+        const int nn = ex[k].nn, epi = ex[k].epi;
+        auto one = [gp, nn, epi, st]() {
+          return gp.seg[0].bint4 ? run_q4(gp, nn, epi, st) : launch_gemm_f32(gp, nn, epi, st);
+        };
+        if (tbp) {
+          tb.name = ex[k].name;
+          tb.defer(one);
+        } else {
+          LMLP_LAUNCH(ex[k].name, one());
+        }
         done[k] = true;
         continue;
       }
@@ -1444,12 +1526,19 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int
       // largest products first: workgroups start in order, so the longest
       // groups begin early and the last wave is made of short ones
       std::stable_sort(grp.begin(), grp.end(), [](const GemmParams& x, const GemmParams& y) { return x.M > y.M; });
-      if (table && grp.size() > size_t(kMaxGemmGroups))  // parameter blocks through a device table
-        LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped_table(grp.data(), int(grp.size()), ex[k].nn, ex[k].epi,
-                                                               table, st));
-      else
-        LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped(grp.data(), int(grp.size()), ex[k].nn, ex[k].epi, st));
+      const int nn = ex[k].nn, epi = ex[k].epi;
+      if (tbp && grp.size() > size_t(kMaxGemmGroups)) {  // parameter blocks through the phase's tables
+        tb.name = ex[k].name;
+        LMLP_TRY(hip_rc(launch_gemm_bf16_grouped_table(grp.data(), int(grp.size()), nn, epi, nullptr, st, tbp),
+                        ex[k].name));
+      } else if (tbp) {
+        tb.name = ex[k].name;
+        tb.defer([grp, nn, epi, st]() { return launch_gemm_bf16_grouped(grp.data(), int(grp.size()), nn, epi, st); });
+      } else {
+        LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped(grp.data(), int(grp.size()), nn, epi, st));
+      }
     }
+    if (tbp) LMLP_TRY(tb.flush());
     if (!any) break;
   }
   return LMLP_OK;
@@ -1492,17 +1581,15 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
   }
   P.table = E > kMaxGemmGroups;
   if (P.table) {
-    const size_t tb = align_up(size_t(E) * sizeof(GemmParams));
+    // a phase's tables: room for two GEMM kinds' parameter blocks and two
+    // side launches of kSideJobsPerExpert jobs per expert each; a phase that
+    // needs more stages its tables in more than one batch
+    P.tab_bytes = 2 * (align_up(size_t(E) * sizeof(GemmParams)) +
+                       align_up(size_t(E) * kSideJobsPerExpert * kSideJobBytes));
     P.tab_fwd = P.ws_fwd;
-    P.ws_fwd += tb;
+    P.ws_fwd += P.tab_bytes;
     P.tab_bwd = P.ws_bwd;
-    P.ws_bwd += tb;
-    // side-kernel job tables: one launch per merged side launch however many experts
-    P.side_bytes = align_up(size_t(E) * kSideJobsPerExpert * kSideJobBytes);
-    P.side_fwd = P.ws_fwd;
-    P.ws_fwd += P.side_bytes;
-    P.side_bwd = P.ws_bwd;
-    P.ws_bwd += P.side_bytes;
+    P.ws_bwd += P.tab_bytes;
   }
   return LMLP_OK;
 }
@@ -1573,9 +1660,8 @@ int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* of
   for (int64_t e = 0; e < n_experts; ++e)
     if (P.dims[e].tokens > 0) order.push_back(e);
   if (order.empty()) return LMLP_OK;
-  GemmParams* tab = P.table ? reinterpret_cast<GemmParams*>(at(workspace, P.tab_fwd)) : nullptr;
-  void* stab = P.table ? at(workspace, P.side_fwd) : nullptr;
-  return moe_phased(static_cast<hipStream_t>(stream), order, P.d.T, tab, stab, P.side_bytes,
+  void* tab = P.table ? at(workspace, P.tab_fwd) : nullptr;
+  return moe_phased(static_cast<hipStream_t>(stream), order, P.d.T, tab, P.tab_bytes,
                     [&](int64_t e, Exec* ex, hipStream_t ws) {
     return forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
                         slice(w_gate_scales, e, S.wgu_s), slice(w_up, e, S.wgu), slice(w_up_scales, e, S.wgu_s),
@@ -1619,9 +1705,8 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
   const MoeStrides S = moe_strides(d);
   std::vector<int64_t> order(n_experts);  // every expert: one without rows gets zero gradients
   for (int64_t e = 0; e < n_experts; ++e) order[e] = e;
-  GemmParams* tab = P.table ? reinterpret_cast<GemmParams*>(at(workspace, P.tab_bwd)) : nullptr;
-  void* stab = P.table ? at(workspace, P.side_bwd) : nullptr;
-  return moe_phased(static_cast<hipStream_t>(stream), order, P.d.T, tab, stab, P.side_bytes,
+  void* tab = P.table ? at(workspace, P.tab_bwd) : nullptr;
+  return moe_phased(static_cast<hipStream_t>(stream), order, P.d.T, tab, P.tab_bytes,
                     [&](int64_t e, Exec* ex, hipStream_t ws) {
     const bool any = P.dims[e].tokens > 0;
     return backward_impl(
