@@ -1539,6 +1539,21 @@ __global__ __launch_bounds__(NT8, 1) void gemm8_table_kernel(const GemmParams* _
 // the gate/up and dZ products run on eight waves as in a single launch
 template <int EPI, int NB>
 constexpr bool kGrouped8 = NB == 8 && (EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD);
+// plain stores run on eight waves too when each group is pinned to one XCD
+// (short K loops of small experts); spread, the four-wave kernel is faster
+template <int EPI, int NB>
+constexpr bool kPinned8 = NB == 8 && EPI == EPI_STORE;
+
+template <bool NN, int EPI, int QRB, int NB>
+static void launch_table_kernel(const GemmParams* tp, const GroupStarts& gs, int nblk, hipStream_t stream) {
+  if constexpr (kGrouped8<EPI, NB> || kPinned8<EPI, NB>) {
+    if (kGrouped8<EPI, NB> || gs.pinned) {
+      hipLaunchKernelGGL((gemm8_table_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream, tp, gs);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_table_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream, tp, gs);
+}
 
 // copy of up to kMaxGemmGroups parameter blocks into a device table
 struct TableChunk {
@@ -1779,11 +1794,7 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
       }
       const GemmParams* tp = static_cast<const GemmParams*>(dt);
       batch->defer([tp, gs, nblk, stream]() -> hipError_t {
-        if constexpr (kGrouped8<EPI, NB>)
-          hipLaunchKernelGGL((gemm8_table_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream, tp, gs);
-        else
-          hipLaunchKernelGGL((gemm_bf16_table_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream, tp,
-                             gs);
+        launch_table_kernel<NN, EPI, QRB, NB>(tp, gs, nblk, stream);
         return hipGetLastError();
       });
       continue;
@@ -1800,12 +1811,7 @@ static hipError_t launch_table_t(const GemmParams* ps, int n, GemmParams* table,
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    if constexpr (kGrouped8<EPI, NB>)
-      hipLaunchKernelGGL((gemm8_table_kernel<NN, EPI, QRB>), dim3(nblk), dim3(NT8), 0, stream,
-                         static_cast<const GemmParams*>(table), gs);
-    else
-      hipLaunchKernelGGL((gemm_bf16_table_kernel<NN, EPI, QRB, NB>), dim3(nblk), dim3(NTHREADS), 0, stream,
-                       static_cast<const GemmParams*>(table), gs);
+    launch_table_kernel<NN, EPI, QRB, NB>(table, gs, nblk, stream);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
