@@ -1906,10 +1906,10 @@ hipError_t launch_gemm_bf16_grouped(const GemmParams* ps, int n, int nn, int epi
   if (n <= 0) return hipSuccess;
   const GemmParams& p = ps[0];  // every product of one call is of one kind
   if (!nn && epi == EPI_STORE) return launch_grouped_t<false, EPI_STORE>(ps, n, stream);
-  if (!nn && epi == EPI_STORE_F32) {  // split-K partials: 256 x 256 tiles, N a multiple of 4
+  if (epi == EPI_STORE_F32) {  // split-K partials: 256 x 256 tiles, N a multiple of 4
     for (int i = 0; i < n; ++i)
       if ((ps[i].tile_n != 0 && ps[i].tile_n != 256) || ps[i].N % 4 || ps[i].ldc % 4) return hipErrorInvalidValue;
-    return launch_grouped_t<false, EPI_STORE_F32>(ps, n, stream);
+    return nn ? launch_grouped_t<true, EPI_STORE_F32>(ps, n, stream) : launch_grouped_t<false, EPI_STORE_F32>(ps, n, stream);
   }
   if (!nn && epi == EPI_SWIGLU_FWD) return launch_grouped_t<false, EPI_SWIGLU_FWD>(ps, n, stream);
   if (nn && epi == EPI_STORE) return launch_grouped_t<true, EPI_STORE>(ps, n, stream);
@@ -1931,6 +1931,12 @@ hipError_t launch_gemm_bf16_grouped_table(const GemmParams* ps, int n, int nn, i
                                           hipStream_t stream, TableBatch* batch) {
   if (n <= 0) return hipSuccess;
   const GemmParams& p = ps[0];
+  if (epi == EPI_STORE_F32) {  // split-K partials: 256 x 256 tiles, N a multiple of 4
+    for (int i = 0; i < n; ++i)
+      if ((ps[i].tile_n != 0 && ps[i].tile_n != 256) || ps[i].N % 4 || ps[i].ldc % 4) return hipErrorInvalidValue;
+    return nn ? launch_table_t<true, EPI_STORE_F32>(ps, n, table, stream, batch)
+              : launch_table_t<false, EPI_STORE_F32>(ps, n, table, stream, batch);
+  }
   if (!nn && epi == EPI_STORE) return launch_table_t<false, EPI_STORE>(ps, n, table, stream, batch);
   if (!nn && epi == EPI_SWIGLU_FWD) return launch_table_t<false, EPI_SWIGLU_FWD>(ps, n, table, stream, batch);
   if (nn && epi == EPI_STORE) return launch_table_t<true, EPI_STORE>(ps, n, table, stream, batch);

@@ -1385,6 +1385,10 @@ struct MoePlan {
   // launch's arguments hold): GEMM parameter blocks and side-kernel jobs
   size_t tab_fwd = 0, tab_bwd = 0, tab_bytes = 0;
   bool table = false;
+  // K splits of the grouped down (forward) and dX (backward) products, with
+  // their fp32 partials [S][tokens][H] in the workspace (1: no split)
+  int split_down = 1, split_dx = 1;
+  size_t part_fwd = 0, part_bwd = 0;
   Dims d;  // the whole call
 };
 
@@ -1453,8 +1457,51 @@ class PhaseTables final : public TableBatch {
   const char* failed_ = nullptr;
 };
 
+// A grouped product of the plain store kind run as S splits of K, each
+// expert's split s storing fp32 partials at its rows of part[s], then one
+// ordered sum over all rows into `out` (the experts' row blocks tile it).
+struct MoeSplitK {
+  const char* name = nullptr;  // the GEMM kind
+  int S = 1;
+  float* part = nullptr;  // [S][rows][N]
+  void* out = nullptr;    // [rows][N], bf16
+  int64_t rows = 0, N = 0;
+};
+
+// Split s of a plain-store product (256-wide tiles) over K: the down
+// product's one large segment is cut in two at a multiple of 32 (the
+// adapter segment goes with the second half); dX's two large segments (dG
+// W_g, dU W_u) go one to each split, the adapter with the second.
+static GemmParams split_params(const GemmParams& g, int s, int nn) {
+  GemmParams q = g;
+  if (nn) {  // dX: seg 0 | seg 1 + seg 2
+    if (s == 0) {
+      q.nseg = 1;
+      q.seg[1] = q.seg[2] = GemmSeg{};
+    } else {
+      q.nseg = g.nseg - 1;
+      q.seg[0] = g.seg[1];
+      q.seg[1] = g.seg[2];
+      q.seg[2] = GemmSeg{};
+    }
+    return q;
+  }
+  const int64_t kh = g.seg[0].K / 64 * 32;  // first half, a multiple of 32
+  if (s == 0) {
+    q.nseg = 1;
+    q.seg[0].K = kh;
+    q.seg[1] = q.seg[2] = GemmSeg{};
+  } else {
+    q.seg[0].a = static_cast<const uint16_t*>(g.seg[0].a) + kh;    // bf16 elements
+    q.seg[0].b0 = static_cast<const uint16_t*>(g.seg[0].b0) + kh;  // NT: K contiguous in B's rows
+    q.seg[0].K = g.seg[0].K - kh;
+  }
+  return q;
+}
+
 static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int64_t t_split, void* tables,
-                      size_t table_bytes, const std::function<int(int64_t, Exec*, hipStream_t)>& body) {
+                      size_t table_bytes, const std::function<int(int64_t, Exec*, hipStream_t)>& body,
+                      const MoeSplitK& split = MoeSplitK{}) {
   std::vector<Exec> ex(order.size());
   std::vector<std::vector<SideOp>> ops(order.size());
   hipStream_t st = caller;
@@ -1527,7 +1574,27 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int
       // groups begin early and the last wave is made of short ones
       std::stable_sort(grp.begin(), grp.end(), [](const GemmParams& x, const GemmParams& y) { return x.M > y.M; });
       const int nn = ex[k].nn, epi = ex[k].epi;
-      if (tbp && grp.size() > size_t(kMaxGemmGroups)) {  // parameter blocks through the phase's tables
+      if (tbp && split.S > 1 && epi == EPI_STORE && std::strcmp(ex[k].name, split.name) == 0) {
+        // every expert's S splits in one table launch (largest first), then the sum
+        std::vector<GemmParams> sg;
+        for (const GemmParams& g : grp) {
+          const int64_t row = (static_cast<const char*>(g.c0) - static_cast<const char*>(split.out)) /
+                              static_cast<int64_t>(split.N * sizeof(uint16_t));
+          for (int sp = 0; sp < split.S; ++sp) {
+            GemmParams q = split_params(g, sp, nn);
+            q.c0 = split.part + (sp * split.rows + row) * split.N;
+            q.tile_n = 0;
+            sg.push_back(q);
+          }
+        }
+        std::stable_sort(sg.begin(), sg.end(), [](const GemmParams& x, const GemmParams& y) { return x.M > y.M; });
+        tb.name = ex[k].name;
+        LMLP_TRY(hip_rc(launch_gemm_bf16_grouped_table(sg.data(), int(sg.size()), nn, EPI_STORE_F32, nullptr, st, tbp),
+                        ex[k].name));
+        const MoeSplitK sk = split;
+        tb.name = nn ? "sum(dX)" : "sum(down)";
+        tb.defer([sk, st]() { return launch_splitk_sum(sk.part, sk.S, sk.rows * sk.N, sk.out, st); });
+      } else if (tbp && grp.size() > size_t(kMaxGemmGroups)) {  // parameter blocks through the phase's tables
         tb.name = ex[k].name;
         LMLP_TRY(hip_rc(launch_gemm_bf16_grouped_table(grp.data(), int(grp.size()), nn, epi, nullptr, st, tbp),
                         ex[k].name));
@@ -1579,7 +1646,33 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
     P.wbsize[e] = bwd_layout(dd).total;
     P.ws_bwd += dd.T > 0 ? P.wbsize[e] : 0;
   }
-  P.table = E > kMaxGemmGroups;
+  // K splits of the grouped down and dX products (few large experts, dense
+  // bf16 weights): when their 256 x 256 tiles leave the last wave at most
+  // half full, two splits over K double the tiles (e.g. 592 -> 1184 tiles,
+  // 2.3 -> 4.6 waves on 256 compute units) at the cost of fp32 partials and
+  // their sum, which pays only for long K: at the Mixtral-8x7B shape dX (K =
+  // 2I = 28672) went 2.10 -> 1.96 ms with its sum, down (K = I = 14336)
+  // 1.03 -> 1.04 ms. So a product splits when its K is at least 16384.
+  if (E <= kMaxGemmGroups && P.d.bf16 && !P.d.int4 && P.d.H % 4 == 0) {
+    int64_t tiles = 0;
+    for (int64_t e = 0; e < E; ++e) tiles += (off[e + 1] - off[e] + 255) / 256 * ((P.d.H + 255) / 256);
+    const int64_t ncu = device_cus();
+    const int64_t rem = tiles % ncu;
+    if (tiles > ncu && rem > 0 && 2 * rem <= ncu) {
+      const size_t pb = align_up(size_t(2) * P.d.T * P.d.H * sizeof(float));
+      if (P.d.I >= 16384) {
+        P.split_down = 2;
+        P.part_fwd = P.ws_fwd;
+        P.ws_fwd += pb;
+      }
+      if (2 * P.d.I >= 16384) {
+        P.split_dx = 2;
+        P.part_bwd = P.ws_bwd;
+        P.ws_bwd += pb;
+      }
+    }
+  }
+  P.table = E > kMaxGemmGroups || P.split_down > 1 || P.split_dx > 1;
   if (P.table) {
     // a phase's tables: room for two GEMM kinds' parameter blocks and two
     // side launches of kSideJobsPerExpert jobs per expert each; a phase that
@@ -1661,6 +1754,15 @@ int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* of
     if (P.dims[e].tokens > 0) order.push_back(e);
   if (order.empty()) return LMLP_OK;
   void* tab = P.table ? at(workspace, P.tab_fwd) : nullptr;
+  MoeSplitK sk;
+  if (P.split_down > 1) {
+    sk.name = "gemm(down)";
+    sk.S = P.split_down;
+    sk.part = reinterpret_cast<float*>(at(workspace, P.part_fwd));
+    sk.out = y;
+    sk.rows = P.d.T;
+    sk.N = P.d.H;
+  }
   return moe_phased(static_cast<hipStream_t>(stream), order, P.d.T, tab, P.tab_bytes,
                     [&](int64_t e, Exec* ex, hipStream_t ws) {
     return forward_impl(&P.dims[e], nullptr, 0.f, slice(x, P.row0[e], S.rows), slice(w_gate, e, S.wgu),
@@ -1669,7 +1771,7 @@ int lora_moe_forward(const lmlp_dims* dims, int64_t n_experts, const int64_t* of
                         slice(b_gate, e, S.bgu), slice(a_up, e, S.agu), slice(b_up, e, S.bgu), slice(a_down, e, S.ad),
                         slice(b_down, e, S.bd), slice(y, P.row0[e], S.rows), at(saved, P.soff[e]), P.ssize[e],
                         at(workspace, P.wfoff[e]), P.wfsize[e], ws, ex);
-  });
+  }, sk);
 }
 
 int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets, const void* dy,
@@ -1706,6 +1808,15 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
   std::vector<int64_t> order(n_experts);  // every expert: one without rows gets zero gradients
   for (int64_t e = 0; e < n_experts; ++e) order[e] = e;
   void* tab = P.table ? at(workspace, P.tab_bwd) : nullptr;
+  MoeSplitK sk;
+  if (P.split_dx > 1) {
+    sk.name = "gemm(dX)";
+    sk.S = P.split_dx;
+    sk.part = reinterpret_cast<float*>(at(workspace, P.part_bwd));
+    sk.out = dx;
+    sk.rows = P.d.T;
+    sk.N = P.d.H;
+  }
   return moe_phased(static_cast<hipStream_t>(stream), order, P.d.T, tab, P.tab_bytes,
                     [&](int64_t e, Exec* ex, hipStream_t ws) {
     const bool any = P.dims[e].tokens > 0;
@@ -1718,7 +1829,7 @@ int lora_moe_backward(const lmlp_dims* dims, int64_t n_experts, const int64_t* o
         any ? slice(dx, P.row0[e], S.rows) : nullptr, slice(da_gate, e, S.agu), slice(db_gate, e, S.bgu),
         slice(da_up, e, S.agu), slice(db_up, e, S.bgu), slice(da_down, e, S.ad), slice(db_down, e, S.bd),
         any ? at(workspace, P.wboff[e]) : nullptr, P.wbsize[e], ws, ex);
-  });
+  }, sk);
 }
 
 // ---- fused LoRA linear ----------------------------------------------------
