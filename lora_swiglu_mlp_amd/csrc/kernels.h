@@ -216,7 +216,7 @@ struct ReduceJob {
 struct ReduceParams {
   ReduceJob job[46];
   int32_t njobs;
-  int32_t pad_;
+  int32_t tall;  // set by the launcher: rank-wide jobs in 64-row tiles
   const ReduceJob* table;
 };
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream, const ReduceJob* hjobs = nullptr);

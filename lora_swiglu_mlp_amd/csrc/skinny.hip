@@ -432,27 +432,36 @@ __global__ __launch_bounds__(256, 2) void colproj_bf16_kernel(ColProjParams p) {
 // ---------------------------------------------------------------------------
 // Fixed-order sum of partials: v(i, j) = scale * sum_c src[c][i][col_off + j]
 // for i < rows, j < cols, written to dst[i][j] or, with transpose, dst[j][i],
-// in fp32 or bf16. Workgroup = one wave on a 16 x 64 source tile; reads are 16
-// bytes per lane along source rows with eight partials in flight (summed in
-// partial order), and the transposed case goes through LDS so that its writes
-// also run along destination rows. nchunk = 0 writes zeros.
+// in fp32 or bf16. Workgroup = one wave on a 16 x 64 tile or, in a launch
+// with many tiles (TALL: a merged launch over many experts), on a tile of
+// 1024 elements: CW = min(64, cols rounded up to 16) columns by 1024 / CW
+// rows, so a rank-wide job (16 columns) gets 64-row tiles and every lane
+// still has its four 16-byte items (with few tiles the 16-row ones keep
+// more workgroups busy). Reads are 16 bytes per lane along source rows with eight
+// partials in flight (summed in partial order); the transposed case goes
+// through LDS so that its writes also run along destination rows. nchunk =
+// 0 writes zeros.
+template <bool TALL>
 __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   const ReduceJob jb = job_at<ReduceJob>(p, blockIdx.z);
-  // the job's 16 x 64 tiles, numbered row-major, grid-strided over blockIdx.x
-  // (a merged launch's jobs differ in shape: tall and wide ones)
-  const int64_t ntj = (jb.cols + 63) / 64;
-  const int64_t ntiles = (jb.rows + 15) / 16 * ntj;
-  __shared__ float tile[64][17];
+  if (jb.rows <= 0 || jb.cols <= 0) return;
+  const int cw = TALL ? static_cast<int>(min<int64_t>(64, (jb.cols + 15) / 16 * 16)) : 64;  // tile columns
+  const int tr = TALL ? 1024 / cw : 16;                                                    // tile rows: 16 .. 64
+  // the job's tiles, numbered row-major, grid-strided over blockIdx.x (a
+  // merged launch's jobs differ in shape: tall and wide ones)
+  const int64_t ntj = (jb.cols + cw - 1) / cw;
+  const int64_t ntiles = (jb.rows + tr - 1) / tr * ntj;
+  __shared__ float tile[64 * 17];  // [column][row], row pitch tr + 1: cw (tr + 1) <= 1088 for every cw
   const int lane = threadIdx.x;
   for (int64_t id = blockIdx.x; id < ntiles; id += gridDim.x) {
-    const int64_t i0 = id / ntj * 16;
-    const int64_t j0 = id % ntj * 64;
-    const int64_t ncols = min<int64_t>(64, jb.cols - j0);
+    const int64_t i0 = id / ntj * tr;
+    const int64_t j0 = id % ntj * cw;
+    const int64_t ncols = min<int64_t>(cw, jb.cols - j0);
     const int cpr = static_cast<int>((ncols + 3) / 4);  // float4 items per source row
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int it = lane + 64 * q;
-      if (it >= 16 * cpr) break;
+      if (it >= tr * cpr) break;
       const int il = it / cpr, c = it % cpr;
       const int64_t i = i0 + il;
       const int64_t j = j0 + 4 * c;
@@ -495,21 +504,36 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tile[4 * c + e][il] = v[e];
+        for (int e = 0; e < 4; ++e) tile[(4 * c + e) * (tr + 1) + il] = v[e];
       }
     }
     if (!jb.transpose) continue;  // uniform over the workgroup
     __syncthreads();
-    const int64_t j = j0 + lane;
-    if (lane < ncols) {
+    if (tr == 16) {  // lane j writes its column's 16 rows
+      const int64_t j = j0 + lane;
+      if (lane < ncols) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t i = i0 + e;
-        if (i >= jb.rows) break;
-        const int64_t o = j * jb.ld_dst + i;
-        if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(tile[lane][e]);
-        else static_cast<float*>(jb.dst)[o] = tile[lane][e];
+        for (int e = 0; e < 16; ++e) {
+          const int64_t i = i0 + e;
+          if (i >= jb.rows) break;
+          const int64_t o = j * jb.ld_dst + i;
+          const float v = tile[lane * 17 + e];
+          if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(v);
+          else static_cast<float*>(jb.dst)[o] = v;
+        }
       }
+      __syncthreads();  // the next tile overwrites the staging
+      continue;
+    }
+    // destination rows j (the tile's columns), tr consecutive elements each
+    for (int e = lane; e < ncols * tr; e += 64) {
+      const int jl = e / tr, il = e % tr;
+      const int64_t i = i0 + il;
+      if (i >= jb.rows) continue;
+      const int64_t o = (j0 + jl) * jb.ld_dst + i;
+      const float v = tile[jl * (tr + 1) + il];
+      if (jb.dst_bf16) static_cast<uint16_t*>(jb.dst)[o] = f32_to_bf16(v);
+      else static_cast<float*>(jb.dst)[o] = v;
     }
     __syncthreads();  // the next tile overwrites the staging
   }
@@ -860,16 +884,24 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream, const Reduce
   if ((hjobs != nullptr) != (p.table != nullptr) || (!hjobs && p.njobs > 46) || p.njobs > 65535)
     return hipErrorInvalidValue;
   const ReduceJob* js = hjobs ? hjobs : p.job;
-  int64_t maxt = 0;  // 16 x 64 tiles of the largest job
+  // 16 x 64 tiles in all; past 8192 of them, rank-wide jobs go in taller tiles
+  int64_t all = 0;
+  for (int i = 0; i < p.njobs; ++i) all += (js[i].rows + 15) / 16 * ((js[i].cols + 63) / 64);
+  ReduceParams q = p;
+  q.tall = all > 8192 ? 1 : 0;
+  int64_t maxt = 0;  // tiles of the largest job, as the kernel cuts them
   for (int i = 0; i < p.njobs; ++i) {
-    const int64_t t = (js[i].rows + 15) / 16 * ((js[i].cols + 63) / 64);
+    if (js[i].rows <= 0 || js[i].cols <= 0) continue;
+    const int64_t cw = q.tall ? std::min<int64_t>(64, (js[i].cols + 15) / 16 * 16) : 64;
+    const int64_t t = (js[i].rows + 1024 / cw - 1) / (1024 / cw) * ((js[i].cols + cw - 1) / cw);
     maxt = t > maxt ? t : maxt;
   }
   if (maxt == 0) return hipSuccess;
   // about 16 K workgroups in all; each strides over its job's tiles
   const int64_t cap = std::max<int64_t>(1, 16384 / p.njobs);
   dim3 grid(static_cast<unsigned>(std::min<int64_t>(maxt, cap)), 1, p.njobs);
-  hipLaunchKernelGGL(reduce_kernel, grid, dim3(64), 0, stream, p);
+  if (q.tall) hipLaunchKernelGGL(reduce_kernel<true>, grid, dim3(64), 0, stream, q);
+  else hipLaunchKernelGGL(reduce_kernel<false>, grid, dim3(64), 0, stream, q);
   return hipGetLastError();
 }
 
