@@ -166,7 +166,7 @@ struct ProjFinishJob {
 struct ProjFinishParams {
   ProjFinishJob job[36];
   int32_t njobs;
-  int32_t pad_;
+  int32_t tall;  // set by the launcher: narrow jobs in up to 64-token tiles
   int64_t T;
   const ProjFinishJob* table;
 };

@@ -116,25 +116,30 @@ __global__ __launch_bounds__(256) void rowproj_kernel(RowProjParams p) {
 // zero for T <= t < ldT), to outT; each output is optional. Workgroup = one
 // wave on 16 tokens x 64 columns; eight partials are loaded before they are
 // added (still in slice order), and the transposed write goes through LDS.
-template <typename T>
+template <typename T, bool TALL>
 __global__ __launch_bounds__(64) void proj_finish_kernel(ProjFinishParams p) {
   const ProjFinishJob jb = job_at<ProjFinishJob>(p, blockIdx.z);
   const int64_t tmax = jb.outT ? jb.ldT : jb.T;
-  // the job's 16-token x 64-column tiles, grid-strided over blockIdx.x (a
-  // merged launch's jobs differ in token count)
-  const int64_t ntn = (jb.n1p + 63) / 64;
-  const int64_t ntiles = (tmax + 15) / 16 * ntn;
-  __shared__ float tile[64][17];
+  if (jb.n1p <= 0 || tmax <= 0) return;
+  // the job's tiles of tr tokens x cw columns, grid-strided over blockIdx.x
+  // (a merged launch's jobs differ in token count): 16 x 64, or (TALL: a
+  // launch with many tiles) 1024 elements, cw = min(64, n1p rounded up to
+  // 16), so that a rank-wide job still gives every lane four items
+  const int cw = TALL ? min(64, (jb.n1p + 15) / 16 * 16) : 64;
+  const int tr = TALL ? 1024 / cw : 16;  // 16 .. 64, divides ldT
+  const int64_t ntn = (jb.n1p + cw - 1) / cw;
+  const int64_t ntiles = (tmax + tr - 1) / tr * ntn;
+  __shared__ float tile[64 * 17];  // [column][token], token pitch tr + 1: cw (tr + 1) <= 1088
   const int lane = threadIdx.x;
   for (int64_t id = blockIdx.x; id < ntiles; id += gridDim.x) {
-    const int n0 = static_cast<int>(id % ntn) * 64;
-    const int64_t t0 = id / ntn * 16;
-    const int nc = min(64, jb.n1p - n0);  // a multiple of 4
+    const int n0 = static_cast<int>(id % ntn) * cw;
+    const int64_t t0 = id / ntn * tr;
+    const int nc = min(cw, jb.n1p - n0);  // a multiple of 4
     const int cpr = nc / 4;               // float4 items per token row
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int it = lane + 64 * q;
-      if (it >= 16 * cpr) break;
+      if (it >= tr * cpr) break;
       const int tl = it / cpr, c = it % cpr;
       const int64_t t = t0 + tl;
       const int n = n0 + 4 * c;
@@ -167,17 +172,29 @@ __global__ __launch_bounds__(64) void proj_finish_kernel(ProjFinishParams p) {
           store4(static_cast<T*>(jb.out_c) + t * jb.ld_c + jb.col_off + n, jb.scale * v.x, jb.scale * v.y,
                  jb.scale * v.z, jb.scale * v.w);
       }
-      tile[4 * c + 0][tl] = v.x;
-      tile[4 * c + 1][tl] = v.y;
-      tile[4 * c + 2][tl] = v.z;
-      tile[4 * c + 3][tl] = v.w;
+      tile[(4 * c + 0) * (tr + 1) + tl] = v.x;
+      tile[(4 * c + 1) * (tr + 1) + tl] = v.y;
+      tile[(4 * c + 2) * (tr + 1) + tl] = v.z;
+      tile[(4 * c + 3) * (tr + 1) + tl] = v.w;
     }
     if (!jb.outT) continue;  // uniform over the workgroup
     __syncthreads();
-    if (lane < nc) {  // t0 + 16 <= ldT: ldT is a multiple of 64
-      T* dst = static_cast<T*>(jb.outT) + static_cast<int64_t>(jb.col_off + n0 + lane) * jb.ldT + t0;
+    if (!TALL) {
+      if (lane < nc) {  // t0 + 16 <= ldT: ldT is a multiple of 64
+        T* dst = static_cast<T*>(jb.outT) + static_cast<int64_t>(jb.col_off + n0 + lane) * jb.ldT + t0;
+        const float* src = tile + lane * 17;
 #pragma unroll
-      for (int e = 0; e < 16; e += 4) store4(dst + e, tile[lane][e], tile[lane][e + 1], tile[lane][e + 2], tile[lane][e + 3]);
+        for (int e = 0; e < 16; e += 4) store4(dst + e, src[e], src[e + 1], src[e + 2], src[e + 3]);
+      }
+    } else {
+      // rows n of the token-contiguous copy, four consecutive tokens per lane
+      // (t0 + tr <= ldT: ldT is a multiple of 64)
+      for (int e = lane; e < nc * (tr / 4); e += 64) {
+        const int nl = e / (tr / 4), tq = 4 * (e % (tr / 4));
+        T* dst = static_cast<T*>(jb.outT) + static_cast<int64_t>(jb.col_off + n0 + nl) * jb.ldT + t0 + tq;
+        const float* src = tile + nl * (tr + 1) + tq;
+        store4(dst, src[0], src[1], src[2], src[3]);
+      }
     }
     __syncthreads();  // the next tile overwrites the staging
   }
@@ -840,17 +857,31 @@ hipError_t launch_proj_finish(const ProjFinishParams& p0, int dtype_bf16, hipStr
     for (int i = 0; i < p.njobs; ++i)
       if (p.job[i].T == 0) p.job[i].T = p.T;
   const ProjFinishJob* js = hjobs ? hjobs : p.job;
-  int64_t maxtiles = 0;  // 16 x 64 tiles of the largest job
+  // 16 x 64 tiles in all; past 1024 of them, narrow jobs go in taller tiles
+  int64_t all = 0;
   for (int i = 0; i < p.njobs; ++i) {
     const int64_t t = js[i].outT ? js[i].ldT : js[i].T;
-    const int64_t nt = (t + 15) / 16 * ((js[i].n1p + 63) / 64);
+    all += (t + 15) / 16 * ((js[i].n1p + 63) / 64);
+  }
+  p.tall = all > 1024 ? 1 : 0;
+  int64_t maxtiles = 0;  // tiles of the largest job, as the kernel cuts them
+  for (int i = 0; i < p.njobs; ++i) {
+    const int64_t t = js[i].outT ? js[i].ldT : js[i].T;
+    if (js[i].n1p <= 0 || t <= 0) continue;
+    const int64_t cw = p.tall ? std::min<int64_t>(64, (js[i].n1p + 15) / 16 * 16) : 64;
+    const int64_t nt = (t + 1024 / cw - 1) / (1024 / cw) * ((js[i].n1p + cw - 1) / cw);
     maxtiles = nt > maxtiles ? nt : maxtiles;
   }
   if (maxtiles <= 0) return hipSuccess;
   // about 16 K workgroups in all; each strides over its job's tiles
   dim3 grid(static_cast<unsigned>(std::min<int64_t>(maxtiles, std::max<int64_t>(1, 16384 / p.njobs))), 1, p.njobs);
-  if (dtype_bf16) hipLaunchKernelGGL(proj_finish_kernel<bf16_t>, grid, dim3(64), 0, stream, p);
-  else hipLaunchKernelGGL(proj_finish_kernel<float>, grid, dim3(64), 0, stream, p);
+  if (dtype_bf16) {
+    if (p.tall) hipLaunchKernelGGL((proj_finish_kernel<bf16_t, true>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((proj_finish_kernel<bf16_t, false>), grid, dim3(64), 0, stream, p);
+  } else {
+    if (p.tall) hipLaunchKernelGGL((proj_finish_kernel<float, true>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((proj_finish_kernel<float, false>), grid, dim3(64), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
