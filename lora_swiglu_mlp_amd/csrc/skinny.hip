@@ -945,12 +945,14 @@ hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream, 
   for (int i = 0; i < p.njobs; ++i) maxn = js[i].rows * js[i].cols > maxn ? js[i].rows * js[i].cols : maxn;
   if (maxn == 0) return hipSuccess;
   if (elem_bytes != 2 && elem_bytes != 4) return hipErrorInvalidValue;
-  // the largest job in one pass of its workgroups: plain copies move four
-  // groups of 16 bytes per thread, transposes 64 columns per workgroup
+  // plain copies in one pass of their workgroups (four groups of 16 bytes
+  // per thread), transposes four 64-column tiles per workgroup: a merged
+  // launch's grid is as wide as its widest job, so fewer, fuller workgroups
+  // leave fewer idle ones for the small jobs
   int64_t maxg = 1;
   for (int i = 0; i < p.njobs; ++i) {
     const int64_t g = js[i].transpose && js[i].rows <= 64
-                          ? (js[i].cols + 63) / 64
+                          ? (js[i].cols + 255) / 256
                           : (js[i].rows * ((js[i].cols * elem_bytes + 15) / 16) + 1023) / 1024;
     maxg = g > maxg ? g : maxg;
   }
