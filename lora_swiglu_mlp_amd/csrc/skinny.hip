@@ -946,15 +946,21 @@ hipError_t launch_pack(const PackParams& p, int elem_bytes, hipStream_t stream, 
   if (maxn == 0) return hipSuccess;
   if (elem_bytes != 2 && elem_bytes != 4) return hipErrorInvalidValue;
   // plain copies in one pass of their workgroups (four groups of 16 bytes
-  // per thread), transposes four 64-column tiles per workgroup: a merged
-  // launch's grid is as wide as its widest job, so fewer, fuller workgroups
-  // leave fewer idle ones for the small jobs
+  // per thread), transposes one 64-column tile per workgroup; a merged
+  // launch's grid is as wide as its widest job, so when that leaves over
+  // 8192 workgroups (many experts' jobs) transposes take four tiles per
+  // workgroup: fewer, fuller workgroups, fewer idle ones for the small jobs
   int64_t maxg = 1;
-  for (int i = 0; i < p.njobs; ++i) {
-    const int64_t g = js[i].transpose && js[i].rows <= 64
-                          ? (js[i].cols + 255) / 256
-                          : (js[i].rows * ((js[i].cols * elem_bytes + 15) / 16) + 1023) / 1024;
-    maxg = g > maxg ? g : maxg;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t per = pass == 0 ? 64 : 256;  // columns per transposing workgroup
+    maxg = 1;
+    for (int i = 0; i < p.njobs; ++i) {
+      const int64_t g = js[i].transpose && js[i].rows <= 64
+                            ? (js[i].cols + per - 1) / per
+                            : (js[i].rows * ((js[i].cols * elem_bytes + 15) / 16) + 1023) / 1024;
+      maxg = g > maxg ? g : maxg;
+    }
+    if (maxg * p.njobs <= 8192) break;
   }
   dim3 grid(static_cast<unsigned>(std::min<int64_t>(maxg, 65535)), p.njobs);
   if (elem_bytes == 2) hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
