@@ -1399,7 +1399,7 @@ struct MoePlan {
 // out merged across experts round by round (round r: every expert's r-th
 // launch; one expert's launches keep their order), then the GEMMs the
 // experts reached, grouped by kind; until no expert hands back a GEMM.
-// The job and parameter tables of one phase of the grouped MLP, in one
+// The job and parameter tables of one pass of the grouped MLP, in one
 // batch: laid out back to back (256-byte aligned) in a host buffer whose
 // device copy is the pass's table region of the workspace, with the launches
 // that read them queued; flush() stages the buffer with one read of the
@@ -1505,9 +1505,12 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int
   std::vector<Exec> ex(order.size());
   std::vector<std::vector<SideOp>> ops(order.size());
   hipStream_t st = caller;
+  // one batch for the whole pass: its phases are recorded one after another
+  // (the host plans them without the device), their launches queued in order,
+  // and the tables read with one fetch (more when they outgrow the region)
+  PhaseTables tb(tables, table_bytes, st);
+  PhaseTables* tbp = tables ? &tb : nullptr;
   for (int phase = 0;; ++phase) {
-    PhaseTables tb(tables, table_bytes, st);
-    PhaseTables* tbp = tables ? &tb : nullptr;
     size_t rounds = 0;
     for (size_t k = 0; k < order.size(); ++k) {
       ex[k] = Exec{};
@@ -1605,9 +1608,9 @@ static int moe_phased(hipStream_t caller, const std::vector<int64_t>& order, int
         LMLP_LAUNCH(ex[k].name, launch_gemm_bf16_grouped(grp.data(), int(grp.size()), nn, epi, st));
       }
     }
-    if (tbp) LMLP_TRY(tb.flush());
     if (!any) break;
   }
+  if (tbp) LMLP_TRY(tb.flush());
   return LMLP_OK;
 }
 
@@ -1674,10 +1677,10 @@ static int moe_plan(const lmlp_dims* dims, int64_t E, const int64_t* off, MoePla
   }
   P.table = E > kMaxGemmGroups || P.split_down > 1 || P.split_dx > 1;
   if (P.table) {
-    // a phase's tables: room for two GEMM kinds' parameter blocks and two
-    // side launches of kSideJobsPerExpert jobs per expert each; a phase that
+    // a pass's tables: room for four GEMM kinds' parameter blocks and four
+    // side launches of kSideJobsPerExpert jobs per expert each; a pass that
     // needs more stages its tables in more than one batch
-    P.tab_bytes = 2 * (align_up(size_t(E) * sizeof(GemmParams)) +
+    P.tab_bytes = 4 * (align_up(size_t(E) * sizeof(GemmParams)) +
                        align_up(size_t(E) * kSideJobsPerExpert * kSideJobBytes));
     P.tab_fwd = P.ws_fwd;
     P.ws_fwd += P.tab_bytes;

@@ -282,9 +282,9 @@ def test_moe_sizes(counts, dt):
     # the phases of the grouped launches
     assert abi.lora_moe_saved_bytes(d, off) == sum(abi.lora_mlp_saved_bytes(p) for p in per)
     # more experts than one launch's arguments hold (8): the region for one
-    # phase's tables follows, room for two GEMM kinds' 416-byte parameter
-    # blocks and two side launches of 10 jobs of at most 96 bytes per expert
-    table = 2 * (align(len(counts) * 416) + align(len(counts) * 10 * 96)) if len(counts) > 8 else 0
+    # pass's tables follows, room for four GEMM kinds' 416-byte parameter
+    # blocks and four side launches of 10 jobs of at most 96 bytes per expert
+    table = 4 * (align(len(counts) * 416) + align(len(counts) * 10 * 96)) if len(counts) > 8 else 0
     for bwd in (False, True):
         assert abi.lora_moe_workspace_bytes(d, off, bwd) == table + sum(abi.lora_mlp_workspace_bytes(p, bwd)
                                                                         for c, p in zip(counts, per) if c > 0)
