@@ -202,14 +202,20 @@ int lora_mlp_norm_backward(const lmlp_dims* dims, const void* dy, const void* x,
  * anything is enqueued. Each GEMM of the pass runs as one grouped launch
  * over every expert's tiles, and each of its small side kernels as launches
  * merged across experts; all on `stream`. `saved` and the workspace hold one
- * region per expert (none in the workspace for an expert without rows), and
- * the workspace a table of GEMM parameters beyond 8 experts, which one
- * workgroup on `stream` reads into the workspace from a pinned host buffer of
- * the library's own (16 MB plus 512 KB of completion marks, allocated on
- * first use per device, kept until exit). Where the read from the region of
- * that buffer a call would reuse has not run yet, and under graph capture,
- * small copy kernels on `stream` write the table instead: the host never
- * waits for the device. */
+ * region per expert (none in the workspace for an expert without rows). The
+ * workspace also holds, beyond 8 experts (or when a K split is planned), a
+ * region for the pass's parameter and job tables, which workgroups on
+ * `stream` read into it from a pinned host buffer of the library's own (16 MB
+ * plus 512 KB of completion marks, allocated on first use per device, kept
+ * until exit). Where the read from the region of that buffer a call would
+ * reuse has not run yet, and under graph capture, small copy kernels on
+ * `stream` write the tables instead: the host never waits for the device.
+ * With at most 8 experts of dense bf16 weights whose dX (or down) product's
+ * 256 x 256 tiles would leave the device's last wave at most half full and
+ * whose K is at least 16384, that product runs as two K splits, and the
+ * workspace holds their fp32 partials, 2 * tokens * H * 4 bytes, summed in
+ * split order (results stay deterministic). The sizes depend on the device's
+ * compute-unit count: query them on the device that runs the call. */
 size_t lora_moe_saved_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets);
 size_t lora_moe_workspace_bytes(const lmlp_dims* dims, int64_t n_experts, const int64_t* offsets,
                                 int is_backward);
