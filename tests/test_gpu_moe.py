@@ -19,6 +19,10 @@ pytestmark = pytest.mark.gpu
 CASES = {
     # name: (tokens, E, top_k, H, I, r, alpha, dtype, wfmt)
     "tiny_fp32": (96, 4, 2, 128, 344, 8, 16.0, "f32", "dense"),
+    # more than 8 experts: tables and deferred launches, with products that
+    # are not grouped (fp32, 4-bit weights) queued among the grouped ones
+    "fp32_12experts": (160, 12, 2, 128, 264, 8, 16.0, "f32", "dense"),
+    "int4_12experts": (240, 12, 3, 256, 384, 16, 16.0, "bf16", "int4_b64"),
     "bf16_routed": (300, 6, 2, 256, 520, 16, 32.0, "bf16", "dense"),
     "bf16_many_small": (200, 32, 4, 128, 256, 16, 16.0, "bf16", "dense"),
     "bf16_rank64": (160, 3, 2, 256, 384, 64, 128.0, "bf16", "dense"),
@@ -130,11 +134,12 @@ def torch_cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def test_moe_int4_decode_modes_bitwise_equal():
+@pytest.mark.parametrize("name", ["int4_routed", "int4_12experts"])
+def test_moe_int4_decode_modes_bitwise_equal(name):
     """4-bit weights decoded inside the products' staging (the default; those
     products are launched expert by expert, not grouped) give the outputs of
     the decoded-copy mode bit for bit; both are checked against the oracle."""
-    wl = workload("int4_routed")
+    wl = workload(name)
     inp, off = I.make_moe_inputs(wl)
     a, _ = run_hip_moe(inp, off, wl)
     b, _ = run_hip_moe(inp, off, wl, flags=abi.LMLP_INT4_BF16_COPIES)
