@@ -102,6 +102,23 @@ def kernel_bytes(name: str, T: int, H: int, I: int, r: int, eb: int) -> int:
     }.get(name, 0)
 
 
+def moe_gemm_bytes(name: str, rows: int, experts: int, H: int, I: int, r: int, eb: int) -> int:
+    """Algorithmic HBM bytes of one grouped (MoE) product over all routed
+    rows: every operand read once (the weights of each expert with rows, the
+    activations of every routed row, the rank-r adapter segments) and every
+    output written once."""
+    return {
+        # X, W_g and W_u; P_g, P_u [rows, 2r] and the B_g, B_u segments; G, U, Z out
+        "gemm(gate/up)": (rows * H + experts * 2 * I * H + rows * 2 * r + experts * 2 * I * r + 3 * rows * I) * eb,
+        # Z, W_d, the adapter segments; y out
+        "gemm(down)": (rows * I + experts * H * I + rows * r + experts * H * r + rows * H) * eb,
+        # dY, W_d, G, U in; dG, dU out
+        "gemm(dZ)": (rows * H + experts * H * I + 4 * rows * I) * eb,
+        # dG, dU, W_g, W_u, the adapter segments in; dX out
+        "gemm(dX)": (2 * rows * I + experts * 2 * I * H + rows * 2 * r + experts * 2 * r * H + rows * H) * eb,
+    }.get(name, 0)
+
+
 # sources of the bf16 GEMM kernels: a measured HBM traffic figure applies only
 # while these are unchanged
 GEMM_SOURCES = ("lora_swiglu_mlp_amd/csrc/gemm_bf16.hip", "lora_swiglu_mlp_amd/csrc/lds_dma.h",
@@ -368,15 +385,27 @@ def bench_moe(args, wl):
         # per kernel: time per step summed over the experts' launches; FLOPs over all routed rows
         kern = {name: {"ms_per_step": tot / nprof, "launches_per_step": cnt / nprof}
                 for name, (tot, cnt) in agg.items()}
+        active = sum(1 for c in counts if c > 0)
+        eb = 2 if wl.dtype == "bf16" else 4
         for name, e in kern.items():
             f = kernel_flops(name, rows, H, Iw, r)
             if f:
                 e["tflops"] = f / (e["ms_per_step"] * 1e-3) / 1e12
+                b = moe_gemm_bytes(name, rows, active, H, Iw, r, eb)
+                if b:
+                    e["gbps"] = b / (e["ms_per_step"] * 1e-3) / 1e9
+                    # below the ridge point (peak FLOP/s over peak bytes/s) HBM bounds the product
+                    e["bound"] = "hbm" if f / b < peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
         out["kernels"] = kern
         out["kernel_ms_per_step"] = sum(e["ms_per_step"] for e in kern.values())
         dom = max((n for n in kern if "tflops" in kern[n]), key=lambda n: kern[n]["ms_per_step"])
-        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"], "peak": peak,
-                           "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / peak, "traffic": None}
+        if kern[dom].get("bound") == "hbm":
+            out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["gbps"], "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": kern[dom]["gbps"] / HBM_PEAK_GBS, "traffic": None,
+                               "tflops": kern[dom]["tflops"]}
+        else:
+            out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"], "peak": peak,
+                               "unit": "TFLOP/s", "frac": kern[dom]["tflops"] / peak, "traffic": None}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_moe(inp, offsets, wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

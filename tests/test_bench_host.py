@@ -118,3 +118,27 @@ def test_norm_flops_count_the_oracles_operations():
     R.backward(x, gamma, np.asarray(rstd).view(_OpCount), g)
     assert fwd == 4 * T * H
     assert _OpCount.ops == bench.norm_flops(T, H)
+
+
+def test_moe_bytes_and_bound():
+    """The grouped products' algorithmic bytes, counted by hand for a small
+    case, and the bound they give: the Qwen3-30B-A3B MoE shape (small
+    experts) sits below the ridge point of 2500 TFLOP/s over 8 TB/s, the
+    Mixtral-8x7B shape above it."""
+    rows, E, H, Iw, r = 10, 3, 8, 6, 2
+    # gate/up: X 80, W 3*2*6*8 = 288, P 40, B 3*2*6*2 = 72, G U Z 180 -> 660 elements
+    assert bench.moe_gemm_bytes("gemm(gate/up)", rows, E, H, Iw, r, 2) == 2 * 660
+    # down: Z 60, W_d 144, P_d 20, B_d 48, y 80 -> 352
+    assert bench.moe_gemm_bytes("gemm(down)", rows, E, H, Iw, r, 2) == 2 * 352
+    # dZ: dY 80, W_d 144, G U dG dU 240 -> 464
+    assert bench.moe_gemm_bytes("gemm(dZ)", rows, E, H, Iw, r, 2) == 2 * 464
+    # dX: dG dU 120, W_g W_u 288, Q 40, A_g A_u 96, dx 80 -> 624
+    assert bench.moe_gemm_bytes("gemm(dX)", rows, E, H, Iw, r, 2) == 2 * 624
+    ridge = bench.PEAK_TFLOPS["bf16"] * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
+    for wl, below in (("moe_qwen3", True), ("moe_mixtral", False)):
+        w = I.MOE_WORKLOADS[wl]
+        n = w.tokens * w.top_k
+        for k in ("gemm(gate/up)", "gemm(down)", "gemm(dZ)", "gemm(dX)"):
+            f = bench.kernel_flops(k, n, w.hidden, w.inter, w.rank)
+            b = bench.moe_gemm_bytes(k, n, w.experts, w.hidden, w.inter, w.rank, 2)
+            assert (f / b < ridge) == below, (wl, k, f / b)
